@@ -1,0 +1,168 @@
+"""ctypes wrapper around the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its binding.  It takes
+numpy arrays, hands raw pointers to the C code and returns numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.orc_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
+    lib.orc_philox4x32_10.restype = None
+    lib.orc_u01.argtypes = [ctypes.c_uint32]
+    lib.orc_u01.restype = ctypes.c_double
+    lib.orc_random_word.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.orc_random_word.restype = ctypes.c_uint32
+    lib.orc_draft.argtypes = [_f32p, _f32p, _f32p, _i32p, _f32p, _i32p,
+                              ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_uint64, ctypes.c_uint64,
+                              _i32p, _f64p, _f64p, _f64p]
+    lib.orc_draft.restype = ctypes.c_int
+    lib.orc_verify.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p, _i32p,
+                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_uint64, ctypes.c_uint64,
+                               _i32p, _i32p, _f64p, _f64p, _f64p, _f64p]
+    lib.orc_verify.restype = ctypes.c_int
+    lib.orc_schedule.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _f64p, ctypes.c_int,
+                                 _i32p, _f64p, _f64p, _i32p]
+    lib.orc_schedule.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def philox4x32_10(counter, key):
+    """Raw Philox4x32-10 block: 4 counter words, 2 key words -> 4 words."""
+    lib = _load()
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib.orc_philox4x32_10(_ptr(c, ctypes.c_uint32), _ptr(k, ctypes.c_uint32), _ptr(out, ctypes.c_uint32))
+    return out
+
+
+def u01(word):
+    return _load().orc_u01(int(word))
+
+
+def random_word(seed, round_id, stream, k, req, v):
+    return _load().orc_random_word(seed, round_id, stream, k, req, v)
+
+
+def draft(U, W1, W2, anchor, temperature, seed, round_id, req_ids=None):
+    """Markov-head draft sampling.  U [B, gamma, V], W1/W2 [V, r] (float32
+    values; bf16 weights pass their exact float32 value).  Returns a dict of
+    x [B, gamma] int32 and lse, qx, margin [B, gamma] float64."""
+    lib = _load()
+    U = _f32(U)
+    W1 = _f32(W1)
+    W2 = _f32(W2)
+    anchor = _i32(anchor)
+    temperature = _f32(temperature)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    assert W1.shape == (V, r) and W2.shape == (V, r)
+    rid = None if req_ids is None else _i32(req_ids)
+    x = np.zeros((B, gamma), np.int32)
+    lse = np.zeros((B, gamma), np.float64)
+    qx = np.zeros((B, gamma), np.float64)
+    margin = np.zeros((B, gamma), np.float64)
+    st = lib.orc_draft(_ptr(U, ctypes.c_float), _ptr(W1, ctypes.c_float), _ptr(W2, ctypes.c_float),
+                       _ptr(anchor, ctypes.c_int32), _ptr(temperature, ctypes.c_float),
+                       _ptr(rid, ctypes.c_int32), B, gamma, V, r, seed, round_id,
+                       _ptr(x, ctypes.c_int32), _ptr(lse, ctypes.c_double),
+                       _ptr(qx, ctypes.c_double), _ptr(margin, ctypes.c_double))
+    if st != 0:
+        raise ValueError("orc_draft: bad arguments")
+    return {"x": x, "lse": lse, "qx": qx, "margin": margin}
+
+
+def verify(target, ell, U, W1, W2, anchor, x, temperature, seed, round_id,
+           req_ids=None, row_offsets=None):
+    """Exact rejection-sampling verification against packed target rows
+    [sum(1 + ell), V].  Returns n [B], tokens [B, gamma+1], diag
+    [B, gamma+1, 2], resid [B], accept_margin [B, gamma], pick_margin [B]."""
+    lib = _load()
+    target = _f32(target)
+    U = _f32(U)
+    W1 = _f32(W1)
+    W2 = _f32(W2)
+    ell = _i32(ell)
+    anchor = _i32(anchor)
+    x = _i32(x)
+    temperature = _f32(temperature)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    rid = None if req_ids is None else _i32(req_ids)
+    off = None if row_offsets is None else _i32(row_offsets)
+    n = np.zeros(B, np.int32)
+    tokens = np.zeros((B, gamma + 1), np.int32)
+    diag = np.zeros((B, gamma + 1, 2), np.float64)
+    resid = np.zeros(B, np.float64)
+    am = np.zeros((B, gamma), np.float64)
+    pm = np.zeros(B, np.float64)
+    st = lib.orc_verify(_ptr(target, ctypes.c_float), _ptr(off, ctypes.c_int32), _ptr(ell, ctypes.c_int32),
+                        _ptr(U, ctypes.c_float), _ptr(W1, ctypes.c_float), _ptr(W2, ctypes.c_float),
+                        _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32),
+                        _ptr(temperature, ctypes.c_float), _ptr(rid, ctypes.c_int32),
+                        B, gamma, V, r, seed, round_id,
+                        _ptr(n, ctypes.c_int32), _ptr(tokens, ctypes.c_int32),
+                        _ptr(diag, ctypes.c_double), _ptr(resid, ctypes.c_double),
+                        _ptr(am, ctypes.c_double), _ptr(pm, ctypes.c_double))
+    if st != 0:
+        raise ValueError("orc_verify: bad arguments")
+    return {"n": n, "tokens": tokens, "diag": diag, "resid": resid,
+            "accept_margin": am, "pick_margin": pm}
+
+
+def schedule(c, sps):
+    """Confidence-scheduled prefix lengths.  c [R, gamma] float64, sps
+    [sps_len] float64 (SPS(B) for B = 0..sps_len-1).  Returns
+    (ell [R] int32, theta, tau, B)."""
+    lib = _load()
+    c = np.ascontiguousarray(c, dtype=np.float64)
+    sps = np.ascontiguousarray(sps, dtype=np.float64)
+    R, gamma = c.shape
+    ell = np.zeros(R, np.int32)
+    theta = ctypes.c_double()
+    tau = ctypes.c_double()
+    Bo = ctypes.c_int32()
+    st = lib.orc_schedule(_ptr(c, ctypes.c_double), R, gamma, _ptr(sps, ctypes.c_double), len(sps),
+                          _ptr(ell, ctypes.c_int32), ctypes.byref(theta), ctypes.byref(tau), ctypes.byref(Bo))
+    if st != 0:
+        raise ValueError("orc_schedule: bad arguments")
+    return ell, theta.value, tau.value, Bo.value

@@ -1,0 +1,483 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for one DSpark draft-and-verify round.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file or the library built from it: only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * code, header, constant table or helper with the HIP library; the two meet
+ * only through the seeded synthetic inputs handed to both.
+ *
+ * Every quantity is computed in IEEE double precision, in the order the
+ * pages describe, with no blocking, fusion or reordering.  Inputs arrive as
+ * float32 arrays (bf16 weights are exactly representable in float32) and are
+ * widened to double element by element.
+ *
+ * Sources (page title -- section):
+ *  [MG] "DSpark：DeepSeek 线上跑的投机解码，半自回归 + 置信度调度怎么做到的"
+ *       (marsggbo.github.io) -- 3.2 Sequential Stage (Markov head and the
+ *       sequential sampling loop), 4.1 (acceptance = 1 - TV), 4.3 Hardware-Aware
+ *       Prefix Scheduler (survival products, B, tau, Theta, greedy with early stop).
+ *  [CE] "DeepSeek DSpark explained" interactive page (share.concentrate1.com)
+ *       -- section 03 (q_k = softmax(U_k + B_k), B_k = W1[x_{k-1}] W2),
+ *       section 02 (first rejection truncates the suffix, bonus token when all
+ *       drafts pass), section 04 (a_j, B, tau, Theta, SPS), section 05
+ *       (alpha = min(1, p/q), residual r(v) = max(p-q,0)/sum max(p-q,0)).
+ *  Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+ *       Easy as 1, 2, 3", SC'11 -- the 10-round Philox block function.
+ *
+ * Readings of points the pages leave open (each one is also listed in the
+ * design notes of the repository):
+ *  - The draft sampler is Gumbel-max on z = (U_k + B_k)/T with Philox
+ *    uniforms; the pages sample with a multinomial draw, which has the same
+ *    distribution.  Temperature 0 means greedy: lowest index wins ties.
+ *  - Philox counter: word0 = (stream << 24) | k, word1 = v >> 2 for the draft
+ *    stream (0 otherwise), word2 = request index, word3 = low 32 bits of the
+ *    round id; key = (seed low 32, seed high 32).  The draft stream takes
+ *    output word (v & 3); the accept stream (1) and the resample stream (2)
+ *    take word 0.  Uniform: u = ((w >> 8) + 0.5) * 2^-24, never 0 or 1.
+ *  - Accept iff u * q(x) < p(x).  Resample by inverse CDF: the smallest v
+ *    with C(v) > u' * S (C the running sum of the mass, S its total); if
+ *    rounding leaves no such v, the last v with positive mass.  S = 0 on a
+ *    rejection (only possible through rounding) falls back to p_j.
+ *  - ell_r drafts are verified; ell_r = 0 still emits one token drawn from p_1.
+ *  - Scheduler candidates are ordered by (-a, r, j); improvement must be
+ *    strict; SPS beyond the table is 0; candidates with a = 0 are dropped.
+ *
+ * parity pins: the Philox block function is pinned to published known-answer
+ * vectors and to rocRAND's implementation; the sampling, verification and
+ * scheduling functions are pinned to the pages' worked examples, closed forms
+ * and brute force (see tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11)                                */
+/* ------------------------------------------------------------------ */
+
+void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    const uint32_t mul_a = 0xD2511F53u, mul_b = 0xCD9E8D57u; /* round multipliers */
+    const uint32_t weyl_a = 0x9E3779B9u, weyl_b = 0xBB67AE85u; /* key schedule increments */
+    uint32_t x0 = ctr_in[0], x1 = ctr_in[1], x2 = ctr_in[2], x3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) { /* the key is bumped before every round but the first */
+            k0 += weyl_a;
+            k1 += weyl_b;
+        }
+        uint64_t pa = (uint64_t)mul_a * (uint64_t)x0;
+        uint64_t pb = (uint64_t)mul_b * (uint64_t)x2;
+        uint32_t pa_hi = (uint32_t)(pa >> 32), pa_lo = (uint32_t)pa;
+        uint32_t pb_hi = (uint32_t)(pb >> 32), pb_lo = (uint32_t)pb;
+        uint32_t n0 = pb_hi ^ x1 ^ k0;
+        uint32_t n1 = pb_lo;
+        uint32_t n2 = pa_hi ^ x3 ^ k1;
+        uint32_t n3 = pa_lo;
+        x0 = n0; x1 = n1; x2 = n2; x3 = n3;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+double orc_u01(uint32_t w)
+{
+    return ((double)(w >> 8) + 0.5) * (1.0 / 16777216.0);
+}
+
+/* One 32-bit random word of the round's streams.
+ * stream 0: Gumbel noise for vocabulary entry v at draft position k;
+ * stream 1: accept uniform at position k; stream 2: resample uniform at j. */
+uint32_t orc_random_word(uint64_t seed, uint64_t round_id, int stream, int k, int req, int v)
+{
+    uint32_t ctr[4], key[2], out[4];
+    ctr[0] = ((uint32_t)stream << 24) | (uint32_t)k;
+    ctr[1] = (stream == 0) ? ((uint32_t)v >> 2) : 0u;
+    ctr[2] = (uint32_t)req;
+    ctr[3] = (uint32_t)round_id;
+    key[0] = (uint32_t)seed;
+    key[1] = (uint32_t)(seed >> 32);
+    orc_philox4x32_10(ctr, key, out);
+    return (stream == 0) ? out[v & 3] : out[0];
+}
+
+/* ------------------------------------------------------------------ */
+/* Shared pieces of the draft and verify halves                        */
+/* ------------------------------------------------------------------ */
+
+/* z(v) = (U_k(v) + B_k(v)) / T with B_k(v) = sum_i W1[prev][i] * W2[v][i]
+ * ([MG] 3.2 Markov head; [CE] 03).  T = 0 leaves the raw logit. */
+static void orc_logits(const float *Uk, const float *W1, const float *W2, int prev,
+                       double T, int V, int r, double *z)
+{
+    const float *e = W1 + (size_t)prev * (size_t)r;
+    for (int v = 0; v < V; ++v) {
+        const float *w = W2 + (size_t)v * (size_t)r;
+        double bias = 0.0;
+        for (int i = 0; i < r; ++i)
+            bias += (double)e[i] * (double)w[i];
+        double logit = (double)Uk[v] + bias;
+        z[v] = (T > 0.0) ? logit / T : logit;
+    }
+}
+
+/* log sum_v exp(z(v)); -inf when no entry is finite. */
+static double orc_logsumexp(const double *z, int V)
+{
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if (z[v] > m) m = z[v];
+    if (m == -INFINITY) return -INFINITY;
+    double s = 0.0;
+    for (int v = 0; v < V; ++v)
+        s += exp(z[v] - m);
+    return m + log(s);
+}
+
+/* Index of the largest entry (lowest index among equals) and the gap to the
+ * runner-up (+inf when V == 1). */
+static int orc_argmax(const double *z, int V, double *gap)
+{
+    int best = 0;
+    for (int v = 1; v < V; ++v)
+        if (z[v] > z[best]) best = v;
+    double second = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if (v != best && z[v] > second) second = z[v];
+    if (gap) *gap = z[best] - second;
+    return best;
+}
+
+/* Inverse-CDF draw from an unnormalised non-negative mass: the smallest v with
+ * C(v) > u * S, where C is the running sum and S = C(V-1); the last entry of
+ * positive mass if rounding leaves no such v.  *margin receives the distance
+ * of u*S to the two CDF values that bracket the pick, divided by S. */
+static int orc_inverse_cdf(const double *mass, int V, double u, double *margin)
+{
+    double S = 0.0;
+    for (int v = 0; v < V; ++v) S += mass[v];
+    double target = u * S;
+    double below = 0.0, c = 0.0;
+    int pick = -1;
+    for (int v = 0; v < V; ++v) {
+        below = c;
+        c += mass[v];
+        if (c > target) { pick = v; break; }
+    }
+    if (pick < 0) {
+        for (int v = V - 1; v >= 0; --v)
+            if (mass[v] > 0.0) { pick = v; break; }
+        if (pick < 0) pick = V - 1;
+        if (margin) *margin = 0.0;
+        return pick;
+    }
+    if (margin) {
+        double lo = target - below, hi = c - target;
+        *margin = (S > 0.0) ? fmin(lo, hi) / S : 0.0;
+    }
+    return pick;
+}
+
+/* ------------------------------------------------------------------ */
+/* Draft half: the sequential Markov-head sampling loop                */
+/* ------------------------------------------------------------------ */
+
+/* For each request b and k = 1..gamma ([MG] 3.2, [CE] 03):
+ *   z = (U_k + W1[x_{k-1}] W2^T) / T,  x_0 = anchor,
+ *   lse = logsumexp(z),  q_k(v) = exp(z(v) - lse),
+ *   T > 0: x_k = argmax_v z(v) + G(v),  G = -log(-log u), u from stream 0;
+ *   T = 0: x_k = argmax_v z(v) (lowest index wins), q_k one-hot.
+ * Outputs per (b, k): x, lse (the max logit for T = 0), q_k(x_k) (1 for
+ * T = 0), and the gap between the two best scores.
+ * req_ids (nullable) gives the request index used in the Philox counter. */
+int orc_draft(const float *U, const float *W1, const float *W2,
+              const int32_t *anchor, const float *temperature, const int32_t *req_ids,
+              int B, int gamma, int V, int r, uint64_t seed, uint64_t round_id,
+              int32_t *x_out, double *lse_out, double *qx_out, double *margin_out)
+{
+    if (B < 0 || gamma < 1 || V < 1 || r < 1) return ORC_ERR_ARG;
+    if (!U || !W1 || !W2 || !anchor || !temperature || !x_out) return ORC_ERR_ARG;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        double *z = (double *)malloc((size_t)V * sizeof(double));
+        if (!z) { status = ORC_ERR_ARG; continue; }
+        int req = req_ids ? req_ids[b] : b;
+        double T = (double)temperature[b];
+        int prev = anchor[b];
+        for (int k = 1; k <= gamma; ++k) {
+            const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
+            orc_logits(Uk, W1, W2, prev, T, V, r, z);
+            int x;
+            double lse, qx, margin;
+            if (T > 0.0) {
+                lse = orc_logsumexp(z, V);
+                double best = -INFINITY, second = -INFINITY;
+                x = 0;
+                for (int v = 0; v < V; ++v) {
+                    double u = orc_u01(orc_random_word(seed, round_id, 0, k, req, v));
+                    double score = z[v] - log(-log(u));
+                    if (v == 0 || score > best) {
+                        if (v > 0) second = best;
+                        best = score;
+                        x = v;
+                    } else if (score > second) {
+                        second = score;
+                    }
+                }
+                qx = exp(z[x] - lse);
+                margin = best - second;
+            } else {
+                x = orc_argmax(z, V, &margin);
+                lse = z[x];
+                qx = 1.0;
+            }
+            size_t o = (size_t)b * (size_t)gamma + (size_t)(k - 1);
+            x_out[o] = x;
+            if (lse_out) lse_out[o] = lse;
+            if (qx_out) qx_out[o] = qx;
+            if (margin_out) margin_out[o] = margin;
+            prev = x;
+        }
+        free(z);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------ */
+/* Verify half: exact rejection sampling with per-request lengths      */
+/* ------------------------------------------------------------------ */
+
+/* Target rows are packed: request b owns rows off_b .. off_b + ell_b, row
+ * off_b + (k-1) holding the target logits for position k (k = ell_b + 1 is
+ * the bonus row).  off (nullable) is the exclusive scan of (1 + ell).
+ *
+ * For each request ([CE] 02 and 05; [MG] 1 and 4.1):
+ *   p_k = softmax(t_k / T) (T = 0: one-hot at the lowest-index argmax),
+ *   q_k = softmax(z_k) recomputed from U_k, W1[x_{k-1}], W2 as in the draft;
+ *   k = 1..ell: u from stream 1, accept iff u * q_k(x_k) < p_k(x_k)
+ *               (T = 0: accept iff x_k = argmax t_k);
+ *   first rejection j: y ~ max(p_j - q_j, 0) by inverse CDF with u' from
+ *               stream 2 (T = 0: y = argmax t_j);
+ *   all accepted: y ~ p_{ell+1} the same way (the bonus token).
+ * Outputs: n_accept[b], tokens[b][0..gamma] = x_1..x_n, y, then -1;
+ * diag[b][k-1] = (p_k(x_k), min(1, p_k(x_k)/q_k(x_k))) for tested positions
+ * (NaN elsewhere); resid_mass[b] = S at a sampled rejection (-1 otherwise);
+ * accept_margin[b][k-1] = |u - p/q| (T > 0) or the top-two target gap
+ * (T = 0) for tested positions (NaN elsewhere); pick_margin[b] = the
+ * inverse-CDF margin of y (T > 0) or the top-two gap of t_j (T = 0). */
+int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
+               const float *U, const float *W1, const float *W2,
+               const int32_t *anchor, const int32_t *x, const float *temperature,
+               const int32_t *req_ids, int B, int gamma, int V, int r,
+               uint64_t seed, uint64_t round_id,
+               int32_t *n_accept, int32_t *tokens, double *diag, double *resid_mass,
+               double *accept_margin, double *pick_margin)
+{
+    if (B < 0 || gamma < 1 || V < 1 || r < 1) return ORC_ERR_ARG;
+    if (!target || !ell || !U || !W1 || !W2 || !anchor || !x || !temperature) return ORC_ERR_ARG;
+    if (!n_accept || !tokens) return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (ell[b] < 0 || ell[b] > gamma) return ORC_ERR_ARG;
+    int64_t *row0 = (int64_t *)malloc((size_t)(B > 0 ? B : 1) * sizeof(int64_t));
+    if (!row0) return ORC_ERR_ARG;
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+        row0[b] = off ? (int64_t)off[b] : acc;
+        acc += 1 + ell[b];
+    }
+    const double nan = NAN;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        double *zq = (double *)malloc((size_t)V * sizeof(double));
+        double *zt = (double *)malloc((size_t)V * sizeof(double));
+        double *mass = (double *)malloc((size_t)V * sizeof(double));
+        if (!zq || !zt || !mass) { status = ORC_ERR_ARG; free(zq); free(zt); free(mass); continue; }
+        int req = req_ids ? req_ids[b] : b;
+        double T = (double)temperature[b];
+        int L = ell[b];
+        const int32_t *xb = x + (size_t)b * (size_t)gamma;
+        for (int k = 0; k < gamma; ++k) {
+            if (diag) {
+                diag[((size_t)b * (size_t)(gamma + 1) + k) * 2 + 0] = nan;
+                diag[((size_t)b * (size_t)(gamma + 1) + k) * 2 + 1] = nan;
+            }
+            if (accept_margin) accept_margin[(size_t)b * (size_t)gamma + k] = nan;
+        }
+        if (diag) {
+            diag[((size_t)b * (size_t)(gamma + 1) + gamma) * 2 + 0] = nan;
+            diag[((size_t)b * (size_t)(gamma + 1) + gamma) * 2 + 1] = nan;
+        }
+        int n = 0;
+        int rejected = 0;
+        for (int k = 1; k <= L; ++k) {
+            const float *tk = target + (size_t)(row0[b] + k - 1) * (size_t)V;
+            int xk = xb[k - 1];
+            int accept;
+            double pk, ratio, margin;
+            if (T > 0.0) {
+                for (int v = 0; v < V; ++v) zt[v] = (double)tk[v] / T;
+                double lse_t = orc_logsumexp(zt, V);
+                pk = exp(zt[xk] - lse_t);
+                int prev = (k == 1) ? anchor[b] : xb[k - 2];
+                const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
+                orc_logits(Uk, W1, W2, prev, T, V, r, zq);
+                double lse_q = orc_logsumexp(zq, V);
+                double qk = exp(zq[xk] - lse_q);
+                double u = orc_u01(orc_random_word(seed, round_id, 1, k, req, 0));
+                accept = (u * qk < pk);
+                ratio = (qk > 0.0) ? fmin(1.0, pk / qk) : 1.0;
+                margin = (qk > 0.0) ? fabs(u - pk / qk) : INFINITY;
+            } else {
+                for (int v = 0; v < V; ++v) zt[v] = (double)tk[v];
+                int am = orc_argmax(zt, V, &margin);
+                accept = (xk == am);
+                pk = accept ? 1.0 : 0.0;
+                ratio = pk;
+            }
+            if (diag) {
+                diag[((size_t)b * (size_t)(gamma + 1) + (k - 1)) * 2 + 0] = pk;
+                diag[((size_t)b * (size_t)(gamma + 1) + (k - 1)) * 2 + 1] = ratio;
+            }
+            if (accept_margin) accept_margin[(size_t)b * (size_t)gamma + (k - 1)] = margin;
+            if (!accept) { rejected = 1; break; }
+            n = k;
+        }
+        /* position of the emitted non-draft token */
+        int j = n + 1;
+        const float *tj = target + (size_t)(row0[b] + j - 1) * (size_t)V;
+        int y;
+        double pmargin = 0.0, S = -1.0;
+        if (T > 0.0) {
+            for (int v = 0; v < V; ++v) zt[v] = (double)tj[v] / T;
+            double lse_t = orc_logsumexp(zt, V);
+            for (int v = 0; v < V; ++v) mass[v] = exp(zt[v] - lse_t);
+            if (rejected) {
+                int prev = (j == 1) ? anchor[b] : xb[j - 2];
+                const float *Uj = U + ((size_t)b * (size_t)gamma + (size_t)(j - 1)) * (size_t)V;
+                orc_logits(Uj, W1, W2, prev, T, V, r, zq);
+                double lse_q = orc_logsumexp(zq, V);
+                double tot = 0.0;
+                for (int v = 0; v < V; ++v) {
+                    double d = mass[v] - exp(zq[v] - lse_q);
+                    zq[v] = d > 0.0 ? d : 0.0; /* residual, reusing the buffer */
+                    tot += zq[v];
+                }
+                S = tot;
+                if (tot > 0.0)
+                    memcpy(mass, zq, (size_t)V * sizeof(double));
+                /* tot == 0: fall back to p_j, already in mass */
+            }
+            double u = orc_u01(orc_random_word(seed, round_id, 2, j, req, 0));
+            y = orc_inverse_cdf(mass, V, u, &pmargin);
+        } else {
+            for (int v = 0; v < V; ++v) zt[v] = (double)tj[v];
+            y = orc_argmax(zt, V, &pmargin);
+        }
+        n_accept[b] = n;
+        int32_t *tb = tokens + (size_t)b * (size_t)(gamma + 1);
+        for (int i = 0; i <= gamma; ++i) tb[i] = -1;
+        for (int i = 0; i < n; ++i) tb[i] = xb[i];
+        tb[n] = y;
+        if (resid_mass) resid_mass[b] = (T > 0.0 && rejected) ? S : -1.0;
+        if (pick_margin) pick_margin[b] = pmargin;
+        free(zq); free(zt); free(mass);
+    }
+    free(row0);
+    return status;
+}
+
+/* ------------------------------------------------------------------ */
+/* Host scheduler: confidence-scheduled prefix lengths                 */
+/* ------------------------------------------------------------------ */
+
+typedef struct { double a; int r; int j; } orc_cand;
+
+static int orc_cand_cmp(const void *pa, const void *pb)
+{
+    const orc_cand *x = (const orc_cand *)pa, *y = (const orc_cand *)pb;
+    if (x->a > y->a) return -1;
+    if (x->a < y->a) return 1;
+    if (x->r != y->r) return x->r < y->r ? -1 : 1;
+    if (x->j != y->j) return x->j < y->j ? -1 : 1;
+    return 0;
+}
+
+static double orc_sps(const double *sps, int sps_len, int64_t B)
+{
+    return (B >= 0 && B < sps_len) ? sps[B] : 0.0;
+}
+
+/* [MG] 4.3 and [CE] 04: a_{r,j} = prod_{i<=j} c_{r,i}; start from ell = 0,
+ * B = tau = R, best Theta = R * SPS(R); walk all (r, j) with a > 0 in
+ * descending a (ties: lower r, then lower j), extend only when j equals the
+ * current length of request r, B += 1, tau += a, Theta = tau * SPS(B); keep
+ * the lengths while Theta strictly improves, stop at the first step that
+ * does not improve.  j here is 0-based (position j+1). */
+int orc_schedule(const double *c, int R, int gamma, const double *sps, int sps_len,
+                 int32_t *ell_out, double *theta_out, double *tau_out, int32_t *B_out)
+{
+    if (R < 0 || gamma < 1 || !c || !sps || !ell_out) return ORC_ERR_ARG;
+    if (sps_len <= R) return ORC_ERR_ARG;
+    size_t ncand_max = (size_t)R * (size_t)gamma;
+    orc_cand *cand = (orc_cand *)malloc((ncand_max ? ncand_max : 1) * sizeof(orc_cand));
+    int32_t *len = (int32_t *)calloc((size_t)(R ? R : 1), sizeof(int32_t));
+    if (!cand || !len) { free(cand); free(len); return ORC_ERR_ARG; }
+    size_t n = 0;
+    for (int r = 0; r < R; ++r) {
+        double a = 1.0;
+        for (int j = 0; j < gamma; ++j) {
+            a *= c[(size_t)r * (size_t)gamma + j];
+            if (a > 0.0) {
+                cand[n].a = a; cand[n].r = r; cand[n].j = j;
+                ++n;
+            }
+        }
+    }
+    qsort(cand, n, sizeof(orc_cand), orc_cand_cmp);
+    int64_t B = R;
+    double tau = (double)R;
+    double best_theta = tau * orc_sps(sps, sps_len, B);
+    double best_tau = tau;
+    int64_t best_B = B;
+    size_t taken = 0; /* candidates consumed at the best point */
+    size_t walked = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const orc_cand *cd = &cand[i];
+        if (cd->j != len[cd->r]) continue;
+        len[cd->r] += 1;
+        B += 1;
+        tau += cd->a;
+        ++walked;
+        double theta = tau * orc_sps(sps, sps_len, B);
+        if (theta > best_theta) {
+            best_theta = theta;
+            best_tau = tau;
+            best_B = B;
+            taken = walked;
+        } else {
+            break;
+        }
+    }
+    /* the best lengths are those after the first `taken` extensions */
+    memset(len, 0, (size_t)(R ? R : 1) * sizeof(int32_t));
+    size_t used = 0;
+    for (size_t i = 0; i < n && used < taken; ++i) {
+        const orc_cand *cd = &cand[i];
+        if (cd->j != len[cd->r]) continue;
+        len[cd->r] += 1;
+        ++used;
+    }
+    for (int r = 0; r < R; ++r) ell_out[r] = len[r];
+    if (theta_out) *theta_out = best_theta;
+    if (tau_out) *tau_out = best_tau;
+    if (B_out) *B_out = (int32_t)best_B;
+    free(cand);
+    free(len);
+    return ORC_OK;
+}
