@@ -30,15 +30,18 @@
  *  - The draft sampler is Gumbel-max on z = (U_k + B_k)/T with Philox
  *    uniforms; the pages sample with a multinomial draw, which has the same
  *    distribution.  Temperature 0 means greedy: lowest index wins ties.
- *  - Philox counter: word0 = (stream << 24) | k, word1 = v >> 2 for the draft
- *    stream (0 otherwise), word2 = request index, word3 = low 32 bits of the
- *    round id; key = (seed low 32, seed high 32).  The draft stream takes
- *    output word (v & 3); the accept stream (1) and the resample stream (2)
- *    take word 0.  Uniform: u = ((w >> 8) + 0.5) * 2^-24, never 0 or 1.
- *  - Accept iff u * q(x) < p(x).  Resample by inverse CDF: the smallest v
- *    with C(v) > u' * S (C the running sum of the mass, S its total); if
- *    rounding leaves no such v, the last v with positive mass.  S = 0 on a
- *    rejection (only possible through rounding) falls back to p_j.
+ *  - Philox counter: word0 = (stream << 24) | k, word1 = v >> 2 for the
+ *    per-vocabulary streams (0: draft noise, 2: resample noise; 0 for the
+ *    accept stream 1), word2 = request index, word3 = low 32 bits of the
+ *    round id; key = (seed low 32, seed high 32).  Per-vocabulary streams
+ *    take output word (v & 3), the accept stream word 0.
+ *    Uniform: u = ((w >> 8) + 0.5) * 2^-24, never 0 or 1.
+ *  - Accept iff u * q(x) < p(x).  The pages give the resample distribution
+ *    r(v) = max(p - q, 0) / sum(...) (and p for the bonus token) but not how
+ *    to draw from it; the draw here is Gumbel-max over log r(v) with stream-2
+ *    noise, an exact sampler whose decision is an argmax with a margin.
+ *    Entries of zero mass never win.  S = 0 on a rejection (only possible
+ *    through rounding) falls back to p_j.
  *  - ell_r drafts are verified; ell_r = 0 still emits one token drawn from p_1.
  *  - Scheduler candidates are ordered by (-a, r, j); improvement must be
  *    strict; SPS beyond the table is 0; candidates with a = 0 are dropped.
@@ -91,18 +94,27 @@ double orc_u01(uint32_t w)
 
 /* One 32-bit random word of the round's streams.
  * stream 0: Gumbel noise for vocabulary entry v at draft position k;
- * stream 1: accept uniform at position k; stream 2: resample uniform at j. */
+ * stream 1: accept uniform at position k (v ignored);
+ * stream 2: Gumbel noise for vocabulary entry v of the resample / bonus
+ *           draw at position j. */
 uint32_t orc_random_word(uint64_t seed, uint64_t round_id, int stream, int k, int req, int v)
 {
     uint32_t ctr[4], key[2], out[4];
+    int per_vocab = (stream == 0 || stream == 2);
     ctr[0] = ((uint32_t)stream << 24) | (uint32_t)k;
-    ctr[1] = (stream == 0) ? ((uint32_t)v >> 2) : 0u;
+    ctr[1] = per_vocab ? ((uint32_t)v >> 2) : 0u;
     ctr[2] = (uint32_t)req;
     ctr[3] = (uint32_t)round_id;
     key[0] = (uint32_t)seed;
     key[1] = (uint32_t)(seed >> 32);
     orc_philox4x32_10(ctr, key, out);
-    return (stream == 0) ? out[v & 3] : out[0];
+    return per_vocab ? out[v & 3] : out[0];
+}
+
+/* Gumbel noise -log(-log u) of stream word w. */
+static double orc_gumbel(uint32_t w)
+{
+    return -log(-log(orc_u01(w)));
 }
 
 /* ------------------------------------------------------------------ */
@@ -152,33 +164,27 @@ static int orc_argmax(const double *z, int V, double *gap)
     return best;
 }
 
-/* Inverse-CDF draw from an unnormalised non-negative mass: the smallest v with
- * C(v) > u * S, where C is the running sum and S = C(V-1); the last entry of
- * positive mass if rounding leaves no such v.  *margin receives the distance
- * of u*S to the two CDF values that bracket the pick, divided by S. */
-static int orc_inverse_cdf(const double *mass, int V, double u, double *margin)
+/* Gumbel-max draw from an unnormalised non-negative mass: the v with mass > 0
+ * maximising log(mass(v)) + G(v), G from stream 2 at position j (lowest index
+ * among equal scores); *margin receives the gap to the runner-up. */
+static int orc_gumbel_pick(const double *mass, int V, uint64_t seed, uint64_t round_id, int j, int req,
+                           double *margin)
 {
-    double S = 0.0;
-    for (int v = 0; v < V; ++v) S += mass[v];
-    double target = u * S;
-    double below = 0.0, c = 0.0;
     int pick = -1;
+    double best = -INFINITY, second = -INFINITY;
     for (int v = 0; v < V; ++v) {
-        below = c;
-        c += mass[v];
-        if (c > target) { pick = v; break; }
+        if (!(mass[v] > 0.0)) continue;
+        double score = log(mass[v]) + orc_gumbel(orc_random_word(seed, round_id, 2, j, req, v));
+        if (pick < 0 || score > best) {
+            second = best;
+            best = score;
+            pick = v;
+        } else if (score > second) {
+            second = score;
+        }
     }
-    if (pick < 0) {
-        for (int v = V - 1; v >= 0; --v)
-            if (mass[v] > 0.0) { pick = v; break; }
-        if (pick < 0) pick = V - 1;
-        if (margin) *margin = 0.0;
-        return pick;
-    }
-    if (margin) {
-        double lo = target - below, hi = c - target;
-        *margin = (S > 0.0) ? fmin(lo, hi) / S : 0.0;
-    }
+    if (pick < 0) pick = 0;
+    if (margin) *margin = best - second;
     return pick;
 }
 
@@ -261,15 +267,16 @@ int orc_draft(const float *U, const float *W1, const float *W2,
  *   q_k = softmax(z_k) recomputed from U_k, W1[x_{k-1}], W2 as in the draft;
  *   k = 1..ell: u from stream 1, accept iff u * q_k(x_k) < p_k(x_k)
  *               (T = 0: accept iff x_k = argmax t_k);
- *   first rejection j: y ~ max(p_j - q_j, 0) by inverse CDF with u' from
- *               stream 2 (T = 0: y = argmax t_j);
+ *   first rejection j: y ~ max(p_j - q_j, 0) by Gumbel-max with stream-2
+ *               noise at position j (T = 0: y = argmax t_j);
  *   all accepted: y ~ p_{ell+1} the same way (the bonus token).
  * Outputs: n_accept[b], tokens[b][0..gamma] = x_1..x_n, y, then -1;
  * diag[b][k-1] = (p_k(x_k), min(1, p_k(x_k)/q_k(x_k))) for tested positions
  * (NaN elsewhere); resid_mass[b] = S at a sampled rejection (-1 otherwise);
  * accept_margin[b][k-1] = |u - p/q| (T > 0) or the top-two target gap
- * (T = 0) for tested positions (NaN elsewhere); pick_margin[b] = the
- * inverse-CDF margin of y (T > 0) or the top-two gap of t_j (T = 0). */
+ * (T = 0) for tested positions (NaN elsewhere); pick_margin[b] = the gap
+ * between the best and second-best Gumbel score of the draw of y (T > 0) or
+ * the top-two gap of t_j (T = 0). */
 int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
                const float *U, const float *W1, const float *W2,
                const int32_t *anchor, const int32_t *x, const float *temperature,
@@ -373,8 +380,7 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
                     memcpy(mass, zq, (size_t)V * sizeof(double));
                 /* tot == 0: fall back to p_j, already in mass */
             }
-            double u = orc_u01(orc_random_word(seed, round_id, 2, j, req, 0));
-            y = orc_inverse_cdf(mass, V, u, &pmargin);
+            y = orc_gumbel_pick(mass, V, seed, round_id, j, req, &pmargin);
         } else {
             for (int v = 0; v < V; ++v) zt[v] = (double)tj[v];
             y = orc_argmax(zt, V, &pmargin);

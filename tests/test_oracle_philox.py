@@ -88,12 +88,13 @@ def test_uniform_mapping_bounds():
 def test_counter_layout_streams_are_distinct():
     # the draft stream uses word (v & 3) of the block at counter word1 = v >> 2
     seed, rnd = 0x0123456789ABCDEF, 7
-    for v in range(8):
-        blk = oracle.philox4x32_10([(0 << 24) | 3, v >> 2, 5, rnd], [seed & 0xFFFFFFFF, seed >> 32])
-        assert oracle.random_word(seed, rnd, 0, 3, 5, v) == blk[v & 3]
-    for stream in (1, 2):
-        blk = oracle.philox4x32_10([(stream << 24) | 3, 0, 5, rnd], [seed & 0xFFFFFFFF, seed >> 32])
-        assert oracle.random_word(seed, rnd, stream, 3, 5, 0) == blk[0]
+    for stream in (0, 2):  # per-vocabulary streams: word (v & 3) of block v >> 2
+        for v in range(8):
+            blk = oracle.philox4x32_10([(stream << 24) | 3, v >> 2, 5, rnd], [seed & 0xFFFFFFFF, seed >> 32])
+            assert oracle.random_word(seed, rnd, stream, 3, 5, v) == blk[v & 3]
+    blk = oracle.philox4x32_10([(1 << 24) | 3, 0, 5, rnd], [seed & 0xFFFFFFFF, seed >> 32])
+    assert oracle.random_word(seed, rnd, 1, 3, 5, 0) == blk[0]
+    assert oracle.random_word(seed, rnd, 1, 3, 5, 77) == blk[0]  # accept stream ignores v
     words = {oracle.random_word(seed, rnd, s, 3, 5, 0) for s in range(3)}
     assert len(words) == 3
 

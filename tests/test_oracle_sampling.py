@@ -305,9 +305,9 @@ def test_ell_zero_emits_one_token_from_p1():
     assert chi2 < _chi2_crit(dof)
 
 
-def test_inverse_cdf_skips_zero_mass_tokens():
-    """Zero-probability tokens are never drawn by the bonus/resample search,
-    and the draw frequencies follow the mass (inverse-CDF sampling)."""
+def test_bonus_draw_skips_zero_mass_tokens():
+    """Zero-probability tokens are never drawn by the bonus / resample draw,
+    and the draw frequencies follow the mass."""
     logits = np.array([NEG, 0.0, NEG, NEG, 1.0, NEG, -0.5, NEG], np.float32)
     p = np.exp(np.where(np.isinf(logits), -np.inf, logits).astype(np.float64))
     p /= p.sum()
@@ -324,13 +324,14 @@ def test_inverse_cdf_skips_zero_mass_tokens():
     assert chi2 < _chi2_crit(dof)
 
 
-def test_inverse_cdf_brute_force_small_vocab():
-    """For tiny V, every pick is the first v whose running mass exceeds u' * S,
-    checked by a direct linear scan over the same uniform."""
+def test_bonus_draw_brute_force_small_vocab():
+    """For tiny V, every bonus token is the entry maximising log p(v) + G(v)
+    with G = -log(-log u) of the stream-2 word of (position 1, request, v),
+    recomputed here with numpy from the raw Philox words."""
     rng = np.random.default_rng(77)
     for V in (1, 2, 3, 5, 16):
         logits = rng.standard_normal(V).astype(np.float32)
-        B = 2000
+        B = 500
         W = np.zeros((V, 1), np.float32)
         U = _broadcast_draft_inputs([np.zeros(V, np.float32)], B)
         temp = np.ones(B, np.float32)
@@ -340,19 +341,25 @@ def test_inverse_cdf_brute_force_small_vocab():
         v = oracle.verify(target, np.zeros(B, np.int32), U, W, W, np.zeros(B, np.int32), d["x"], temp,
                           seed=seed, round_id=4)
         z = logits.astype(np.float64)
-        m = z.max()
-        lse = m + math.log(sum(math.exp(t - m) for t in z))
-        mass = [math.exp(t - lse) for t in z]
-        S = sum(mass)
         for b in range(B):
-            u = oracle.u01(oracle.random_word(seed, 4, 2, 1, b, 0))
-            c, pick = 0.0, None
-            for i, w in enumerate(mass):
-                c += w
-                if c > u * S:
-                    pick = i
-                    break
-            assert v["tokens"][b, 0] == pick
+            words = np.array([oracle.random_word(seed, 4, 2, 1, b, i) for i in range(V)], np.uint64)
+            u = ((words >> np.uint64(8)).astype(np.float64) + 0.5) / 2.0 ** 24
+            assert v["tokens"][b, 0] == int(np.argmax(z - np.log(-np.log(u))))
+
+
+def test_residual_draw_uses_position_of_rejection():
+    """The resample noise is drawn at the rejected position j: two requests
+    that differ only in where they reject get independent draws, and the
+    residual draw at j never returns a token with p_j <= q_j."""
+    q = np.array([0.70, 0.18, 0.12])
+    p = np.array([0.50, 0.30, 0.20])
+    B = 20000
+    d, v = _toy_verify(q, p, B, gamma=3, seed=8)
+    n = v["n"]
+    for j in (1, 2, 3):
+        rej = n == j - 1
+        y = v["tokens"][rej, j - 1]
+        assert np.all(y != 0)  # token 0 has p < q: no residual mass
 
 
 def test_greedy_verify_is_longest_matching_prefix():
