@@ -1,0 +1,321 @@
+"""Python binding of libdspark.so, the MI355X (gfx950) library for one DSpark
+draft-and-verify round.
+
+Argument marshalling only: every step of the round runs in the library's HIP
+kernels (or, for the scheduler, its host C++).  Device arrays are torch
+tensors on the current HIP device, passed by pointer together with torch's
+current stream; host arrays (scheduler) are numpy arrays.  The functions
+carry the C entry points' names.  A missing or unloadable library raises
+immediately: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "DSparkError", "load_library", "DSPARK_BF16", "DSPARK_F32",
+    "dspark_version", "dspark_status_string",
+    "dspark_draft_workspace_size", "dspark_draft_sample",
+    "dspark_verify_workspace_size", "dspark_verify", "dspark_verify_check",
+    "dspark_schedule", "dspark_debug_random_words", "dspark_debug_gumbel",
+    "dspark_profile_enable", "dspark_profile_collect", "dspark_profile_read", "dspark_profile_reset",
+]
+
+DSPARK_OK = 0
+DSPARK_ERR_ARG = -1
+DSPARK_ERR_UNSUPPORTED = -2
+DSPARK_ERR_WORKSPACE = -3
+DSPARK_ERR_HIP = -4
+DSPARK_ERR_DEVICE_INPUT = -5
+DSPARK_BF16 = 0
+DSPARK_F32 = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_u64 = ctypes.c_uint64
+_c_size = ctypes.c_size_t
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+_lib = None
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {dspark_status_string(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdspark.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libdspark.so not built at {path}; run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "dspark_version": ([], _c_int),
+        "dspark_status_string": ([_c_int], ctypes.c_char_p),
+        "dspark_draft_workspace_size": ([_c_int] * 4, _c_size),
+        "dspark_draft_sample": ([_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                 _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_verify_workspace_size": ([_c_int] * 4, _c_size),
+        "dspark_verify": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
+                           _c_void_p, _c_void_p, _c_void_p, _c_int,
+                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
+                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_verify_check": ([_c_void_p, _c_void_p], _c_int),
+        "dspark_schedule": ([_f64p, _c_int, _c_int, _f64p, _c_int, _i32p, _f64p, _f64p, _i32p], _c_int),
+        "dspark_debug_random_words": ([_c_u64, _c_u64, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_void_p, _c_void_p], _c_int),
+        "dspark_debug_gumbel": ([_c_void_p, _c_int, _c_void_p, _c_void_p], _c_int),
+        "dspark_profile_enable": ([_c_int], _c_int),
+        "dspark_profile_collect": ([], _c_int),
+        "dspark_profile_count": ([], _c_int),
+        "dspark_profile_get": ([_c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
+                                _f64p], _c_int),
+        "dspark_profile_reset": ([], _c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != DSPARK_OK:
+        raise DSparkError(status, where)
+
+
+def dspark_version() -> int:
+    return load_library().dspark_version()
+
+
+def dspark_status_string(status: int) -> str:
+    return load_library().dspark_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _weights(W1, W2, device):
+    torch = _torch()
+    if W1.dtype == torch.bfloat16 and W2.dtype == torch.bfloat16:
+        wdt = DSPARK_BF16
+    elif W1.dtype == torch.float32 and W2.dtype == torch.float32:
+        wdt = DSPARK_F32
+    else:
+        raise TypeError("W1/W2: both bfloat16 or both float32")
+    if W1.shape != W2.shape or W1.dim() != 2:
+        raise ValueError("W1/W2: equal [V, r] shapes")
+    for n, t in (("W1", W1), ("W2", W2)):
+        _need(t, n, t.dtype, None, device)
+    return wdt
+
+
+def dspark_draft_workspace_size(B: int, gamma: int, V: int, r: int) -> int:
+    return load_library().dspark_draft_workspace_size(B, gamma, V, r)
+
+
+def dspark_verify_workspace_size(B: int, gamma: int, V: int, r: int) -> int:
+    return load_library().dspark_verify_workspace_size(B, gamma, V, r)
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def dspark_draft_sample(U, W1, W2, anchor, temperature, seed: int, round_id: int, *,
+                        margin: bool = False, out: dict | None = None, workspace=None, stream=None) -> dict:
+    """Draft half of a round.  U [B, gamma, V] float32, W1/W2 [V, r] bf16 or
+    float32, anchor [B] int32, temperature [B] float32 -- all on one HIP device.
+    Returns {"x", "lse", "qx"[, "margin"], "workspace"}; pass ``out`` (a
+    previous result) to reuse its buffers."""
+    torch = _torch()
+    lib = load_library()
+    dev = U.device
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    _need(U, "U", torch.float32, (B, gamma, V), dev)
+    wdt = _weights(W1, W2, dev)
+    if W1.shape[0] != V:
+        raise ValueError("W1/W2: first dimension must be V")
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    if out is None:
+        out = {"x": torch.empty((B, gamma), dtype=torch.int32, device=dev),
+               "lse": torch.empty((B, gamma), dtype=torch.float32, device=dev),
+               "qx": torch.empty((B, gamma), dtype=torch.float32, device=dev)}
+        if margin:
+            out["margin"] = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    nbytes = lib.dspark_draft_workspace_size(B, gamma, V, r)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_draft_workspace_size")
+    ws = _workspace(nbytes, dev, workspace if workspace is not None else out.get("workspace"))
+    out["workspace"] = ws
+    st = lib.dspark_draft_sample(_ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(temperature),
+                                 B, gamma, V, r, int(seed), int(round_id),
+                                 _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")),
+                                 _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_draft_sample")
+    return out
+
+
+def dspark_verify(target, ell, U, W1, W2, anchor, x, lse_q, qx, temperature, seed: int, round_id: int, *,
+                  row_offsets=None, diag: bool = False, resid: bool = False, out_offsets: bool = True,
+                  out: dict | None = None, workspace=None, stream=None) -> dict:
+    """Verify half of a round.  target [rows, V] float32 packed per request
+    (rows off_b .. off_b + ell_b), ell [B] int32, and the draft's inputs and
+    outputs.  Returns {"n", "tokens"[, "offsets", "diag", "resid"], "workspace"}."""
+    torch = _torch()
+    lib = load_library()
+    dev = U.device
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    _need(U, "U", torch.float32, (B, gamma, V), dev)
+    wdt = _weights(W1, W2, dev)
+    if target.dim() != 2 or target.shape[1] != V:
+        raise ValueError("target: [rows, V]")
+    _need(target, "target", torch.float32, None, dev)
+    _need(ell, "ell", torch.int32, (B,), dev)
+    if row_offsets is not None:
+        _need(row_offsets, "row_offsets", torch.int32, (B + 1,), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(x, "x", torch.int32, (B, gamma), dev)
+    _need(lse_q, "lse_q", torch.float32, (B, gamma), dev)
+    _need(qx, "qx", torch.float32, (B, gamma), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    if out is None:
+        out = {"n": torch.empty(B, dtype=torch.int32, device=dev),
+               "tokens": torch.empty((B, gamma + 1), dtype=torch.int32, device=dev)}
+        if out_offsets:
+            out["offsets"] = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        if diag:
+            out["diag"] = torch.empty((B, gamma + 1, 2), dtype=torch.float32, device=dev)
+        if resid:
+            out["resid"] = torch.empty(B, dtype=torch.float32, device=dev)
+    nbytes = lib.dspark_verify_workspace_size(B, gamma, V, r)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_verify_workspace_size")
+    ws = _workspace(nbytes, dev, workspace if workspace is not None else out.get("workspace"))
+    out["workspace"] = ws
+    st = lib.dspark_verify(_ptr(target), target.shape[0], _ptr(ell), _ptr(row_offsets),
+                           _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q), _ptr(qx),
+                           _ptr(temperature), B, gamma, V, r, int(seed), int(round_id),
+                           _ptr(out["n"]), _ptr(out["tokens"]), _ptr(out.get("offsets")),
+                           _ptr(out.get("diag")), _ptr(out.get("resid")),
+                           _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_verify")
+    return out
+
+
+def dspark_verify_check(workspace, stream=None) -> int:
+    """Synchronise and return the device-side input status of the last verify."""
+    return load_library().dspark_verify_check(_ptr(workspace), _stream_ptr(stream))
+
+
+def dspark_schedule(c, sps):
+    """Host scheduler.  c [R, gamma] float64 in [0, 1], sps [sps_len] float64.
+    Returns (ell [R] int32, theta, tau, B)."""
+    lib = load_library()
+    c = np.ascontiguousarray(c, dtype=np.float64)
+    sps = np.ascontiguousarray(sps, dtype=np.float64)
+    if c.ndim != 2:
+        raise ValueError("c: [R, gamma]")
+    R, gamma = c.shape
+    ell = np.zeros(R, np.int32)
+    theta = ctypes.c_double()
+    tau = ctypes.c_double()
+    Bo = ctypes.c_int32()
+    st = lib.dspark_schedule(c.ctypes.data_as(_f64p), R, gamma, sps.ctypes.data_as(_f64p), len(sps),
+                             ell.ctypes.data_as(_i32p), ctypes.byref(theta), ctypes.byref(tau), ctypes.byref(Bo))
+    _check(st, "dspark_schedule")
+    return ell, theta.value, tau.value, Bo.value
+
+
+def dspark_debug_random_words(seed, round_id, stream_id, k, req, v0, n, device="cuda", stream=None):
+    torch = _torch()
+    out = torch.empty(n, dtype=torch.int32, device=device)
+    st = load_library().dspark_debug_random_words(int(seed), int(round_id), stream_id, k, req, v0, n,
+                                                  _ptr(out), _stream_ptr(stream))
+    _check(st, "dspark_debug_random_words")
+    return out
+
+
+def dspark_debug_gumbel(words, stream=None):
+    torch = _torch()
+    _need(words, "words", torch.int32, None, words.device)
+    out = torch.empty(words.numel(), dtype=torch.float32, device=words.device)
+    st = load_library().dspark_debug_gumbel(_ptr(words), words.numel(), _ptr(out), _stream_ptr(stream))
+    _check(st, "dspark_debug_gumbel")
+    return out
+
+
+def dspark_profile_enable(enable: bool = True):
+    _check(load_library().dspark_profile_enable(1 if enable else 0), "dspark_profile_enable")
+
+
+def dspark_profile_collect():
+    _check(load_library().dspark_profile_collect(), "dspark_profile_collect")
+
+
+def dspark_profile_reset():
+    _check(load_library().dspark_profile_reset(), "dspark_profile_reset")
+
+
+def dspark_profile_read() -> dict:
+    """{kernel name: (launches, total milliseconds)} accumulated so far."""
+    lib = load_library()
+    out = {}
+    for i in range(lib.dspark_profile_count()):
+        name = ctypes.c_char_p()
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(lib.dspark_profile_get(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
+               "dspark_profile_get")
+        out[name.value.decode()] = (n.value, ms.value)
+    return out

@@ -1,0 +1,301 @@
+// api.cpp -- the extern "C" entry points of libdspark.so: argument
+// validation, workspace layout, kernel sequencing and per-kernel profiling.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dspark.h"
+#include "internal.hpp"
+
+namespace dspark {
+
+// ------------------------------------------------------------------ profiling
+
+namespace {
+
+struct ProfEntry {
+    std::string name;
+    int64_t launches = 0;
+    double total_ms = 0.0;
+};
+
+struct Pending {
+    int entry;
+    hipEvent_t start, stop;
+};
+
+struct Profiler {
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<ProfEntry> entries;
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> pool;
+
+    int entry_for(const char *name) {
+        for (size_t i = 0; i < entries.size(); ++i)
+            if (entries[i].name == name) return int(i);
+        entries.push_back(ProfEntry{name});
+        return int(entries.size() - 1);
+    }
+    hipEvent_t take_event() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+};
+
+Profiler &prof() {
+    static Profiler p;
+    return p;
+}
+
+}  // namespace
+
+int prof_begin(const char *name, hipStream_t s) {
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (!p.enabled) return -1;
+    Pending pd{p.entry_for(name), p.take_event(), p.take_event()};
+    if (!pd.start || !pd.stop) return -1;
+    (void)hipEventRecord(pd.start, s);
+    p.pending.push_back(pd);
+    return int(p.pending.size() - 1);
+}
+
+void prof_end(int token, hipStream_t s) {
+    if (token < 0) return;
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (token < int(p.pending.size())) (void)hipEventRecord(p.pending[size_t(token)].stop, s);
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+namespace {
+
+bool rank_supported(int wdtype, int r) {
+    if (wdtype == DSPARK_BF16) return r == 16 || r == 32 || r == 64 || r == 128 || r == 256;
+    if (wdtype == DSPARK_F32) return r == 16 || r == 32 || r == 64 || r == 128;
+    return false;
+}
+
+bool sizes_ok(int B, int gamma, int V, int r) {
+    return B >= 1 && B <= DSPARK_MAX_BATCH && gamma >= 1 && gamma <= DSPARK_MAX_GAMMA && V >= 1 &&
+           V <= DSPARK_MAX_VOCAB && r >= 1;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t draft_bytes(int B, int V) {
+    const DraftPlan p = draft_plan(B, V);
+    size_t bytes = 0;
+    draft_carve(nullptr, B, p, &bytes);
+    return bytes;
+}
+
+size_t verify_bytes(int B, int gamma, int V) {
+    const VerifyPlan p = verify_plan(B, gamma, V);
+    size_t bytes = 0;
+    verify_carve(nullptr, B, gamma, V, p, &bytes);
+    return bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_version(void) { return 10000; }
+
+const char *dspark_status_string(int status) {
+    switch (status) {
+        case DSPARK_OK: return "ok";
+        case DSPARK_ERR_ARG: return "invalid argument";
+        case DSPARK_ERR_UNSUPPORTED: return "unsupported size or type";
+        case DSPARK_ERR_WORKSPACE: return "workspace missing or too small";
+        case DSPARK_ERR_HIP: return "HIP runtime error";
+        case DSPARK_ERR_DEVICE_INPUT: return "device-side input check failed";
+        default: return "unknown status";
+    }
+}
+
+size_t dspark_draft_workspace_size(int B, int gamma, int V, int r) {
+    if (!sizes_ok(B, gamma, V, r)) return 0;
+    return draft_bytes(B, V);
+}
+
+int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                        const float *temperature, int B, int gamma, int V, int r, uint64_t seed,
+                        uint64_t round_id, int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (!U || !W1 || !W2 || !anchor || !temperature || !x_out || !lse_out || !qx_out) return DSPARK_ERR_ARG;
+    if (!sizes_ok(B, gamma, V, r)) return DSPARK_ERR_ARG;
+    if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
+    if (!rank_supported(wdtype, r)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(W1) || !aligned16(W2)) return DSPARK_ERR_ARG;
+    const DraftPlan plan = draft_plan(B, V);
+    size_t need = 0;
+    draft_carve(nullptr, B, plan, &need);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+    const DraftWork w = draft_carve(workspace, B, plan, nullptr);
+    DraftArgs a{};
+    a.U = U;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.wdtype = wdtype;
+    a.anchor = anchor;
+    a.temperature = temperature;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.r = r;
+    a.key0 = uint32_t(seed);
+    a.key1 = uint32_t(seed >> 32);
+    a.round32 = uint32_t(round_id);
+    a.x_out = x_out;
+    a.lse_out = lse_out;
+    a.qx_out = qx_out;
+    a.margin_out = margin_out;
+    const hipError_t e = launch_draft(a, plan, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+size_t dspark_verify_workspace_size(int B, int gamma, int V, int r) {
+    if (!sizes_ok(B, gamma, V, r)) return 0;
+    return verify_bytes(B, gamma, V);
+}
+
+int dspark_verify(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                  const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                  const int32_t *x, const float *lse_q, const float *qx, const float *temperature, int B,
+                  int gamma, int V, int r, uint64_t seed, uint64_t round_id, int32_t *n_accept_out,
+                  int32_t *tokens_out, int32_t *out_offsets, float *diag_out, float *resid_out,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    if (!target || !ell || !U || !W1 || !W2 || !anchor || !x || !lse_q || !qx || !temperature ||
+        !n_accept_out || !tokens_out)
+        return DSPARK_ERR_ARG;
+    if (!sizes_ok(B, gamma, V, r) || n_target_rows < 1) return DSPARK_ERR_ARG;
+    if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
+    if (!rank_supported(wdtype, r)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(W1) || !aligned16(W2)) return DSPARK_ERR_ARG;
+    const VerifyPlan plan = verify_plan(B, gamma, V);
+    size_t need = 0;
+    verify_carve(nullptr, B, gamma, V, plan, &need);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+    const VerifyWork w = verify_carve(workspace, B, gamma, V, plan, nullptr);
+    VerifyArgs a{};
+    a.target = target;
+    a.n_target_rows = n_target_rows;
+    a.ell = ell;
+    a.row_offsets = row_offsets;
+    a.U = U;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.wdtype = wdtype;
+    a.anchor = anchor;
+    a.x = x;
+    a.lse_q = lse_q;
+    a.qx = qx;
+    a.temperature = temperature;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.r = r;
+    a.key0 = uint32_t(seed);
+    a.key1 = uint32_t(seed >> 32);
+    a.round32 = uint32_t(round_id);
+    a.n_accept_out = n_accept_out;
+    a.tokens_out = tokens_out;
+    a.out_offsets = out_offsets;
+    a.diag_out = diag_out;
+    a.resid_out = resid_out;
+    const hipError_t e = launch_verify(a, plan, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+int dspark_verify_check(const void *workspace, void *stream) {
+    if (!workspace) return DSPARK_ERR_ARG;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return DSPARK_ERR_HIP;
+    int32_t st = 0;
+    // the status word is the first region of the verify workspace
+    if (hipMemcpy(&st, workspace, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return DSPARK_ERR_HIP;
+    return st == 0 ? DSPARK_OK : DSPARK_ERR_DEVICE_INPUT;
+}
+
+int dspark_debug_random_words(uint64_t seed, uint64_t round_id, int stream_id, int k, int req, int v0, int n,
+                              uint32_t *out, void *stream) {
+    if (!out || n < 0 || stream_id < 0 || stream_id > 2 || k < 0 || k >= (1 << 24) || v0 < 0) return DSPARK_ERR_ARG;
+    const hipError_t e = launch_debug_words(uint32_t(seed), uint32_t(seed >> 32), uint32_t(round_id), stream_id,
+                                            k, req, v0, n, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+int dspark_debug_gumbel(const uint32_t *words, int n, float *out, void *stream) {
+    if (!words || !out || n < 0) return DSPARK_ERR_ARG;
+    const hipError_t e = launch_debug_gumbel(words, n, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+int dspark_profile_enable(int enable) {
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.enabled = enable != 0;
+    return DSPARK_OK;
+}
+
+int dspark_profile_collect(void) {
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    int status = DSPARK_OK;
+    for (const Pending &pd : p.pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(pd.stop) != hipSuccess || hipEventElapsedTime(&ms, pd.start, pd.stop) != hipSuccess) {
+            status = DSPARK_ERR_HIP;
+        } else {
+            p.entries[size_t(pd.entry)].launches += 1;
+            p.entries[size_t(pd.entry)].total_ms += ms;
+        }
+        p.pool.push_back(pd.start);
+        p.pool.push_back(pd.stop);
+    }
+    p.pending.clear();
+    return status;
+}
+
+int dspark_profile_count(void) {
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    return int(p.entries.size());
+}
+
+int dspark_profile_get(int i, const char **name, int64_t *launches, double *total_ms) {
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    if (i < 0 || i >= int(p.entries.size())) return DSPARK_ERR_ARG;
+    if (name) *name = p.entries[size_t(i)].name.c_str();
+    if (launches) *launches = p.entries[size_t(i)].launches;
+    if (total_ms) *total_ms = p.entries[size_t(i)].total_ms;
+    return DSPARK_OK;
+}
+
+int dspark_profile_reset(void) {
+    Profiler &p = prof();
+    std::lock_guard<std::mutex> g(p.mu);
+    for (ProfEntry &e : p.entries) {
+        e.launches = 0;
+        e.total_ms = 0.0;
+    }
+    return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// internal.hpp -- declarations shared by the host entry points (api.cpp) and
+// the kernel translation units (draft.hip, verify.hip, debug.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dspark {
+
+// Per-launch profiling hooks (api.cpp).  prof_begin returns a token that
+// prof_end closes on the same stream; both are no-ops while profiling is off.
+int prof_begin(const char *name, hipStream_t s);
+void prof_end(int token, hipStream_t s);
+
+// Bump allocator over the caller's workspace: every region 256-byte aligned.
+struct Carve {
+    char *base;
+    size_t off = 0;
+    explicit Carve(void *p) : base(static_cast<char *>(p)) {}
+    template <typename T>
+    T *take(size_t n) {
+        off = (off + 255) & ~size_t(255);
+        T *p = reinterpret_cast<T *>(base ? base + off : nullptr);
+        off += n * sizeof(T);
+        return p;
+    }
+};
+
+// ---- draft -----------------------------------------------------------
+
+struct DraftPlan {
+    int nbb;              // batch blocks of 32 rows
+    int ntiles;           // 32-column vocabulary tiles
+    int tiles_per_chunk;  // tiles one wave walks
+    int nchunk;           // vocabulary chunks = ceil(ntiles / tiles_per_chunk)
+    int total_waves;      // nbb * nchunk
+    int blocks;           // workgroups of 4 waves
+};
+DraftPlan draft_plan(int B, int V);
+
+struct DraftWork {
+    float *pm, *ps, *pb, *p2;  // [B, nchunk] partial max, sum, best score, second score
+    int32_t *pi;               // [B, nchunk] partial best index
+};
+DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes);
+
+struct DraftArgs {
+    const float *U;
+    const void *W1, *W2;
+    int wdtype;
+    const int32_t *anchor;
+    const float *temperature;
+    int B, gamma, V, r;
+    uint32_t key0, key1, round32;
+    int32_t *x_out;
+    float *lse_out, *qx_out, *margin_out;
+};
+hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork &w, hipStream_t s);
+
+// ---- verify ----------------------------------------------------------
+
+constexpr int kRowChunk = 2048;  // vocabulary chunk of the target-row statistics pass
+
+struct VerifyPlan {
+    int rows_max;     // B * (gamma + 1)
+    int nrchunk;      // ceil(V / kRowChunk)
+    int nbb;          // ceil(B / 32)
+    DraftPlan tile;   // vocabulary walk of the resample / bonus draw
+    int draw_blocks;  // workgroups of the draw kernel (room for both lists)
+};
+VerifyPlan verify_plan(int B, int gamma, int V);
+
+struct VerifyWork {
+    int32_t *status;     // [4] device status flags, rows_total, n_resid, n_bonus
+    int32_t *off;        // [B + 1] packed row offsets in use
+    int32_t *row_req;    // [rows_max] request of each packed row (-1: none)
+    int32_t *row_pos;    // [rows_max] position k (1-based)
+    float *row_lse2;     // [rows_max] logsumexp of t*s in log2 units
+    int32_t *row_amax;   // [rows_max] lowest-index argmax
+    float *row_tx2;      // [rows_max] t(x_k)*s (log2 units) for tested rows
+    int32_t *mode;       // [B] 0 done (greedy), 1 residual draw, 2 bonus draw, -1 invalid
+    int32_t *jpos;       // [B] position of the emitted non-draft token
+    int32_t *resid_list; // [B] requests taking the residual draw, ascending
+    int32_t *bonus_list; // [B] sampled requests taking the bonus draw, ascending
+    // draw partials per (list slot, vocabulary chunk); residual slots [0, B), bonus slots [B, 2B)
+    float *dw_sum;       // residual mass
+    float *dw_br;        // best Gumbel score of the residual
+    float *dw_bp;        // best Gumbel score of p
+    int32_t *dw_ir, *dw_ip;
+};
+VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, size_t *bytes);
+
+struct VerifyArgs {
+    const float *target;
+    int n_target_rows;
+    const int32_t *ell, *row_offsets;
+    const float *U;
+    const void *W1, *W2;
+    int wdtype;
+    const int32_t *anchor, *x;
+    const float *lse_q, *qx, *temperature;
+    int B, gamma, V, r;
+    uint32_t key0, key1, round32;
+    int32_t *n_accept_out, *tokens_out, *out_offsets;
+    float *diag_out, *resid_out;
+};
+hipError_t launch_verify(const VerifyArgs &a, const VerifyPlan &p, const VerifyWork &w, hipStream_t s);
+
+// ---- diagnostics -----------------------------------------------------
+
+hipError_t launch_debug_words(uint32_t key0, uint32_t key1, uint32_t round32, int stream_id, int k,
+                              int req, int v0, int n, uint32_t *out, hipStream_t s);
+hipError_t launch_debug_gumbel(const uint32_t *words, int n, float *out, hipStream_t s);
+
+}  // namespace dspark

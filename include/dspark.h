@@ -1,0 +1,228 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) library for one DSpark
+ * draft-and-verify round over vocabulary-sized logits.
+ *
+ * Sources (page title -- section):
+ *  [MG] "DSpark：DeepSeek 线上跑的投机解码，半自回归 + 置信度调度怎么做到的"
+ *       (marsggbo.github.io): 3.2 Sequential Stage -- Markov head
+ *       B_k = W2(W1[x_{k-1}]) and the left-to-right sampling loop;
+ *       4.3 Hardware-Aware Prefix Scheduler -- a_{r,j}, B, tau, Theta, greedy
+ *       extension in descending a with early stop.
+ *  [CE] "DeepSeek DSpark explained" (share.concentrate1.com): section 02 --
+ *       the first rejection truncates the suffix, a bonus token follows when
+ *       every draft passes; section 03 -- q_k = softmax(U_k + B_k); section
+ *       04 -- a_j, tau, Theta = tau * SPS(B); section 05 -- accept with
+ *       min(1, p/q), resample from max(p - q, 0) normalised.
+ *
+ * Conventions shared by every entry point:
+ *  - Arrays are row-major and densely packed.  "device" pointers are HIP
+ *    device memory (or memory the device can read at full speed); "host"
+ *    pointers are ordinary CPU memory.
+ *  - The caller owns every buffer.  The library never allocates or frees
+ *    device memory: scratch space is the caller's `workspace`, sized by the
+ *    matching *_workspace_size query.  Workspace contents need no
+ *    initialisation and are not meaningful between calls, except that
+ *    dspark_verify_check reads the status the last dspark_verify left there.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Device entry
+ *    points only enqueue work on it and return; results are ready when the
+ *    stream is.  Two calls that share a workspace must be ordered on one
+ *    stream.  dspark_schedule is synchronous host code.
+ *  - Every entry point returns a dspark_status.  Arguments are validated on
+ *    the host before anything is enqueued; on an error nothing is enqueued
+ *    and no output is written.
+ *  - Random numbers come from Philox4x32-10 (Salmon et al., SC'11), keyed by
+ *    `seed` and addressed by the counter (stream << 24 | position, vocabulary
+ *    quad v >> 2 or 0, request index, low 32 bits of round_id).  Streams:
+ *    0 = draft Gumbel noise, 1 = accept uniforms, 2 = Gumbel noise of the
+ *    resample / bonus draw.  Entry v of a per-vocabulary stream uses output
+ *    word v & 3; uniforms are ((w >> 8) + 0.5) * 2^-24.  Outputs are a pure
+ *    function of the inputs, seed and round_id: two identical calls give
+ *    identical bits.
+ *  - Logits may be -inf (probability 0).  NaN inputs give undefined values
+ *    but never out-of-bounds accesses or hangs.
+ */
+#ifndef DSPARK_H_
+#define DSPARK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dspark_status {
+    DSPARK_OK = 0,
+    DSPARK_ERR_ARG = -1,          /* null required pointer or size out of range */
+    DSPARK_ERR_UNSUPPORTED = -2,  /* valid arguments this build has no kernel for */
+    DSPARK_ERR_WORKSPACE = -3,    /* workspace missing or smaller than queried */
+    DSPARK_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+    DSPARK_ERR_DEVICE_INPUT = -5  /* device-resident input failed its check */
+} dspark_status;
+
+/* Element type of the Markov factors W1 and W2. */
+typedef enum dspark_dtype {
+    DSPARK_BF16 = 0, /* bfloat16 bit patterns (uint16_t) */
+    DSPARK_F32 = 1   /* IEEE float32 */
+} dspark_dtype;
+
+/* Size limits checked by every entry point. */
+#define DSPARK_MAX_GAMMA 32
+#define DSPARK_MAX_BATCH 65536
+#define DSPARK_MAX_VOCAB 16777215
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dspark_version(void);
+
+/* Static text for a dspark_status value (never NULL). */
+const char *dspark_status_string(int status);
+
+/* ------------------------------------------------------------------ */
+/* Draft half ([MG] 3.2; [CE] 03)                                      */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of device workspace dspark_draft_sample needs for these sizes;
+ * 0 when the sizes are invalid. */
+size_t dspark_draft_workspace_size(int B, int gamma, int V, int r);
+
+/* Markov-head draft sampling for B requests over block positions k = 1..gamma.
+ * For every request b and k, with x_0 = anchor[b]:
+ *   z_k = (U[b, k-1, :] + W1[x_{k-1}, :] . W2^T) / T_b
+ *   T_b > 0: x_k = argmax_v z_k(v) + Gumbel noise(b, k, v)   (a draw from
+ *            q_k = softmax(z_k)); T_b = 0: x_k = argmax_v z_k(v), lowest
+ *            index first among equal values.
+ * The [B, V] bias W1[x_{k-1}] W2^T is never written to memory.
+ *
+ *   U           device [B, gamma, V] float32   base logits U_k of the parallel stage
+ *   W1, W2      device [V, r] of `wdtype`      Markov factors (W1: embedding rows,
+ *                                              W2: output projection rows)
+ *   anchor      device [B] int32 in [0, V)     x_0 of each request
+ *   temperature device [B] float32 >= 0        T_b (0 = greedy)
+ *   B in [1, DSPARK_MAX_BATCH], gamma in [1, DSPARK_MAX_GAMMA],
+ *   V in [1, DSPARK_MAX_VOCAB], r in {16, 32, 64, 128, 256} (bf16) or
+ *   {16, 32, 64, 128} (f32), otherwise DSPARK_ERR_UNSUPPORTED.
+ *   seed, round_id                             Philox key and round counter
+ *   x_out       device [B, gamma] int32        sampled drafts x_1..x_gamma
+ *   lse_out     device [B, gamma] float32      logsumexp(z_k), so q_k = exp(z_k - lse);
+ *                                              for T_b = 0 the largest logit
+ *   qx_out      device [B, gamma] float32      q_k(x_k) (1 for T_b = 0)
+ *   margin_out  device [B, gamma] float32 or NULL   gap between the best and the
+ *                                              second-best score (Gumbel-perturbed
+ *                                              z for T_b > 0, logits for T_b = 0)
+ *   workspace   device, >= dspark_draft_workspace_size bytes
+ * Anchors outside [0, V) are clamped into range on the device. */
+int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdtype,
+                        const int32_t *anchor, const float *temperature,
+                        int B, int gamma, int V, int r,
+                        uint64_t seed, uint64_t round_id,
+                        int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Verify half ([CE] 02, 05; [MG] 1, 4.1)                              */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of device workspace dspark_verify needs; 0 for invalid sizes. */
+size_t dspark_verify_workspace_size(int B, int gamma, int V, int r);
+
+/* Exact rejection-sampling verification with per-request verify lengths.
+ * Request b verifies its first ell[b] drafts against packed target rows
+ * off_b .. off_b + ell[b] (row off_b + k - 1 = target logits for position
+ * k; the last one feeds the bonus token).  With p_k = softmax(t_k / T_b)
+ * and q_k the draft distribution recomputed from U, W1, W2 and lse_q:
+ *   k = 1..ell[b]: accept x_k iff u_k * q_k(x_k) < p_k(x_k), u_k a Philox
+ *                  uniform (T_b = 0: iff x_k = argmax t_k);
+ *   first rejection j: y drawn from r = max(p_j - q_j, 0) / S, S = sum of
+ *                  the residual (T_b = 0: y = argmax t_j); S = 0 falls back
+ *                  to p_j;
+ *   every draft accepted: y drawn from p_{ell+1} (the bonus token).
+ * The draws are Gumbel-max: y = argmax_v log r(v) + G_v with stream-2 noise
+ * at position j (entries of zero mass never win), an exact sampler of r.
+ * Request b emits n_b + 1 tokens: x_1..x_{n_b}, y.
+ *
+ *   target        device [n_target_rows, V] float32   packed target logits
+ *   n_target_rows rows in `target`; a request whose rows fall outside it is
+ *                 not verified (outputs -1, device status set)
+ *   ell           device [B] int32 in [0, gamma]
+ *   row_offsets   device [B + 1] int32 or NULL: off_b, the exclusive scan of
+ *                 (1 + ell); NULL = computed on the device
+ *   U, W1, W2, wdtype, temperature, B, gamma, V, r: as for dspark_draft_sample
+ *   anchor, x     device [B] and [B, gamma] int32: x_0 and the drafts
+ *   lse_q, qx     device [B, gamma] float32: lse_out and qx_out of the draft
+ *   seed, round_id  same values as the draft call of this round
+ *   n_accept_out  device [B] int32: n_b (-1 for a request that failed its check)
+ *   tokens_out    device [B, gamma + 1] int32: x_1..x_n, y, then -1
+ *   out_offsets   device [B + 1] int32 or NULL: exclusive scan of (n_b + 1)
+ *   diag_out      device [B, gamma + 1, 2] float32 or NULL: for tested
+ *                 positions (p_k(x_k), min(1, p_k(x_k) / q_k(x_k))), NaN elsewhere
+ *   resid_out     device [B] float32 or NULL: residual mass S at a sampled
+ *                 rejection, -1 otherwise
+ *   workspace     device, >= dspark_verify_workspace_size bytes
+ * Invalid ell / row_offsets values are device-resident, so they are found on
+ * the device: the affected request outputs -1 and dspark_verify_check
+ * reports DSPARK_ERR_DEVICE_INPUT. */
+int dspark_verify(const float *target, int n_target_rows, const int32_t *ell,
+                  const int32_t *row_offsets,
+                  const float *U, const void *W1, const void *W2, int wdtype,
+                  const int32_t *anchor, const int32_t *x, const float *lse_q, const float *qx,
+                  const float *temperature, int B, int gamma, int V, int r,
+                  uint64_t seed, uint64_t round_id,
+                  int32_t *n_accept_out, int32_t *tokens_out, int32_t *out_offsets,
+                  float *diag_out, float *resid_out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Waits for `stream`, then returns DSPARK_OK or DSPARK_ERR_DEVICE_INPUT for
+ * the device-side input checks of the last dspark_verify that used
+ * `workspace` (DSPARK_ERR_HIP if the copy fails). */
+int dspark_verify_check(const void *workspace, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Host scheduler ([MG] 4.3; [CE] 04)                                  */
+/* ------------------------------------------------------------------ */
+
+/* Confidence-scheduled prefix lengths.  Synchronous, host memory only.
+ *   c         host [R, gamma] double in [0, 1]: calibrated confidences c_{r,j}
+ *   sps       host [sps_len] double: SPS(B) for B = 0..sps_len-1; B beyond the
+ *             table counts as 0.  sps_len must exceed R.
+ *   ell_out   host [R] int32: chosen verify lengths
+ *   theta_out, tau_out, B_out  (each may be NULL): Theta, tau and B of the choice
+ * a_{r,j} = prod_{i<=j} c_{r,i}; starting from ell = 0 (B = tau = R), the
+ * candidates with a > 0 are taken in descending a (ties: lower r, then lower
+ * j); each extends its request by one (B += 1, tau += a) and is kept while
+ * Theta = tau * SPS(B) strictly improves; the first step that does not
+ * improve ends the search.  R = 0 is valid and returns Theta = 0. */
+int dspark_schedule(const double *c, int R, int gamma, const double *sps, int sps_len,
+                    int32_t *ell_out, double *theta_out, double *tau_out, int32_t *B_out);
+
+/* ------------------------------------------------------------------ */
+/* Diagnostics                                                         */
+/* ------------------------------------------------------------------ */
+
+/* Writes the library's 32-bit Philox words for vocabulary entries
+ * v0 .. v0 + n - 1 of random stream `stream_id` (0: draft noise, 1: accept
+ * uniforms, 2: resample noise; v is ignored for stream 1) at position k of
+ * request `req` to device [n] uint32 `out`. */
+int dspark_debug_random_words(uint64_t seed, uint64_t round_id, int stream_id, int k, int req,
+                              int v0, int n, uint32_t *out, void *stream);
+
+/* Applies the library's device Gumbel transform to n device words:
+ * out[i] = -log2(-log2(u_i)), u_i = ((w_i >> 8) + 0.5) * 2^-24. */
+int dspark_debug_gumbel(const uint32_t *words, int n, float *out, void *stream);
+
+/* Per-kernel timing with HIP events on the launch stream.  While enabled,
+ * every kernel the library enqueues is bracketed by an event pair; calling
+ * dspark_profile_collect waits for the recorded events and adds their
+ * durations to per-kernel totals.  Not for concurrent use from several
+ * threads. */
+int dspark_profile_enable(int enable);
+int dspark_profile_collect(void);
+/* Number of kernel names with totals, and the totals of entry i. */
+int dspark_profile_count(void);
+int dspark_profile_get(int i, const char **name, int64_t *launches, double *total_ms);
+int dspark_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H_ */

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded
+inputs and the same Philox streams, through the C ABI.
+
+Token indices and accepted lengths must be identical for every request whose
+decisions all clear their margins (draft and resample Gumbel top-two gaps
+> 1e-3, accept tests |u - p/q| > 1e-4; greedy decisions need a top-two logit
+gap > 1e-3); probabilities agree within 1e-4.  The rest are counted and
+reported.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as S
+from roundkit import (compare_draft, compare_verify, gpu_draft, gpu_verify, np_of, oracle_round, packed_subset,
+                      to_device)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import draft_sampling_verification_02_amd as ds  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- random streams
+
+@pytest.mark.parametrize("seed", [0, 1, 0xDEADBEEFCAFEF00D])
+def test_device_philox_words_match_oracle(seed):
+    for stream, k, req, v0, n in [(0, 1, 0, 0, 4096), (0, 5, 255, 129000, 280), (0, 16, 63, 7, 93),
+                                  (1, 3, 17, 0, 1), (2, 6, 1023, 0, 1)]:
+        got = np_of(ds.dspark_debug_random_words(seed, 12345, stream, k, req, v0, n)).view(np.uint32)
+        want = np.array([oracle.random_word(seed, 12345, stream, k, req, v0 + i) for i in range(n)], np.uint32)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_device_gumbel_transform_accuracy():
+    # every uniform grid point near both ends, and a random sample between
+    w = np.concatenate([np.arange(0, 1 << 14, dtype=np.uint64) << 8,
+                        (np.uint64(0xFFFFFFFF) - (np.arange(0, 1 << 14, dtype=np.uint64) << 8)),
+                        np.random.default_rng(0).integers(0, 2**32, 200000, dtype=np.uint64)]).astype(np.uint32)
+    g = np_of(ds.dspark_debug_gumbel(torch.from_numpy(w.view(np.int32)).cuda())).astype(np.float64)
+    u = ((w >> 8).astype(np.float64) + 0.5) * 2.0 ** -24
+    want = -np.log2(-np.log2(u))
+    err = np.abs(g - want)
+    _say(f"[gumbel] max error {err.max() * math.log(2):.3g} (natural units) at word {w[np.argmax(err)]:#x}")
+    # in natural units the score error is ln2 * err; it must stay far below the 1e-3 draft margin
+    assert err.max() * math.log(2) < 2e-5, (err.max(), w[np.argmax(err)])
+
+
+# ---------------------------------------------------------------- full rounds
+
+_CACHE = {}
+
+
+def _round(name, rows=None):
+    if name not in _CACHE:
+        cfg = S.CONFIGS[name]
+        rnd = S.make_round(cfg)
+        ell = np.full(cfg.B, cfg.gamma, np.int32)
+        target = rnd.target_packed(ell)
+        _CACHE[name] = (rnd, ell, target)
+    return _CACHE[name]
+
+
+def _run_config(name, oracle_rows=None, round_id=0):
+    rnd, ell, target = _round(name)
+    cfg = rnd.cfg
+    _say(f"[{name}] B={cfg.B} gamma={cfg.gamma} V={cfg.V} r={cfg.r} round={round_id}")
+    dev = to_device(rnd)
+    td = torch.from_numpy(target).cuda()
+    ed = torch.from_numpy(ell).cuda()
+    d = gpu_draft(dev, cfg.seed, round_id)
+    v = gpu_verify(dev, td, ed, d, cfg.seed, round_id)
+    torch.cuda.synchronize()
+    assert ds.dspark_verify_check(v["workspace"]) == 0
+    gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+    gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
+    rows = oracle_rows
+    if rows is None:
+        od, ov = oracle_round(rnd, target, ell, cfg.seed, round_id)
+        temp, ellr = rnd.temperature, ell
+    else:
+        od, ov = oracle_round(rnd, packed_subset(target, ell, rows), ell, cfg.seed, round_id, rows=rows)
+        temp, ellr = rnd.temperature[rows], ell[rows]
+    cd = compare_draft(gd, od, rows=rows)
+    _say(f"[{name}] draft:  {cd.report()}")
+    cv = compare_verify(gv, od, ov, temp, ellr, rows=rows)
+    _say(f"[{name}] verify: {cv.report()}")
+    # structural checks on every request
+    n, tok, off = gv["n"], gv["tokens"], gv["offsets"]
+    assert np.all((n >= 0) & (n <= ell))
+    for b in range(cfg.B):
+        assert np.all(tok[b, :n[b]] == gd["x"][b, :n[b]])
+        assert 0 <= tok[b, n[b]] < cfg.V
+        assert np.all(tok[b, n[b] + 1:] == -1)
+    np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(n + 1)]))
+    return cd, cv, gd, gv
+
+
+def test_tiny_config_parity():
+    for rid in (0, 1, 2):
+        _run_config("tiny", round_id=rid)
+
+
+def test_tiny_config_many_rounds():
+    """Tiny over many rounds: every eligible round matches the oracle."""
+    rnd, ell, target = _round("tiny")
+    cfg = rnd.cfg
+    dev = to_device(rnd)
+    td = torch.from_numpy(target).cuda()
+    ed = torch.from_numpy(ell).cuda()
+    mism = inel = 0
+    rounds = 300
+    for rid in range(rounds):
+        d = gpu_draft(dev, cfg.seed, rid)
+        v = gpu_verify(dev, td, ed, d, cfg.seed, rid)
+        od, ov = oracle_round(rnd, target, ell, cfg.seed, rid)
+        gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+        gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
+        compare_draft(gd, od)
+        cv = compare_verify(gv, od, ov, rnd.temperature, ell)
+        inel += int((~cv.eligible).sum())
+        mism += int(cv.mismatch[~cv.eligible].sum())
+    _say(f"[tiny x{rounds}] ineligible rounds={inel} mismatching among them={mism}")
+    assert inel <= rounds * 0.05
+
+
+def test_dspark5_config_parity():
+    cd, cv, *_ = _run_config("dspark5")
+    assert cd.ineligible_rate < 0.2
+
+
+def test_large_batch_config_parity():
+    cd, cv, gd, gv = _run_config("large")
+    assert cd.ineligible_rate < 0.2
+    # greedy requests (r % 10 == 0) have q one-hot
+    rnd, *_ = _round("large")
+    greedy = rnd.temperature == 0
+    assert np.all(gd["qx"][greedy] == 1.0)
+
+
+def test_long_block_config_parity():
+    cd, cv, *_ = _run_config("long")
+    assert cd.ineligible_rate < 0.3
+
+
+def test_scheduled_config_sampled_parity():
+    """Batch 1024: the scheduler's literal choice is ell = 0 everywhere; the
+    GPU verifies all 1024 bonus rows, the oracle checks a sample of requests."""
+    cfg = S.CONFIGS["sched"]
+    rnd = S.make_round(cfg)
+    sps = S.sps_table_toy(0.2, cfg.B * (1 + cfg.gamma) + 1)
+    ell, *_ = ds.dspark_schedule(rnd.c, sps)
+    assert np.all(ell == 0)
+    # supplement: 256 groups of 4 requests scheduled independently
+    ell_g = np.concatenate([ds.dspark_schedule(rnd.c[4 * g:4 * g + 4], S.sps_table_toy(0.2, 25))[0]
+                            for g in range(cfg.B // 4)]).astype(np.int32)
+    dev = to_device(rnd)
+    rows = np.arange(0, cfg.B, 16)
+    for tag, e in (("literal", ell.astype(np.int32)), ("groups-of-4", ell_g)):
+        target = rnd.target_packed(e)
+        _say(f"[sched {tag}] rows={target.shape[0]}")
+        td = torch.from_numpy(target).cuda()
+        ed = torch.from_numpy(e).cuda()
+        d = gpu_draft(dev, cfg.seed, 0)
+        v = gpu_verify(dev, td, ed, d, cfg.seed, 0)
+        gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+        gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
+        od, ov = oracle_round(rnd, packed_subset(target, e, rows), e, cfg.seed, 0, rows=rows)
+        cd = compare_draft(gd, od, rows=rows)
+        cv = compare_verify(gv, od, ov, rnd.temperature[rows], e[rows], rows=rows)
+        _say(f"[sched {tag}] draft {cd.report()} | verify {cv.report()}")
+        assert np.all(gv["n"] <= e)
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _custom_round(B, gamma, V, r, wdtype, seed, greedy_every=0, ell=None, neg_inf_frac=0.0, u_std=3.0,
+                  w_std=0.05):
+    cfg = S.Config("custom", B=B, gamma=gamma, V=V, r=r, wdtype=wdtype, w_std=w_std, u_std=u_std,
+                   noise_std=1.0, seed=seed, greedy_every=greedy_every)
+    rnd = S.make_round(cfg)
+    if neg_inf_frac > 0:
+        mask = np.random.default_rng(seed + 99).uniform(size=rnd.U.shape) < neg_inf_frac
+        rnd.U[mask] = -np.inf
+    if ell is None:
+        ell = np.random.default_rng(seed + 7).integers(0, gamma + 1, B).astype(np.int32)
+    target = rnd.target_packed(ell)
+    if neg_inf_frac > 0:
+        mask = np.random.default_rng(seed + 98).uniform(size=target.shape) < neg_inf_frac
+        target[mask] = -np.inf
+    return rnd, np.asarray(ell, np.int32), target
+
+
+@pytest.mark.parametrize("B,gamma,V,r,wdtype,greedy", [
+    (1, 1, 3, 16, "f32", 0),          # three-token vocabulary, one position
+    (5, 3, 17, 16, "bf16", 0),        # vocabulary inside one tile
+    (33, 4, 1003, 32, "bf16", 3),     # ragged batch and vocabulary, greedy mix
+    (70, 6, 4099, 64, "f32", 5),      # f32 weights, several tiles and chunks
+    (40, 2, 2048 * 3 + 5, 128, "bf16", 0),
+    (3, 32, 300, 256, "bf16", 2),     # longest block
+])
+def test_edge_shapes_parity(B, gamma, V, r, wdtype, greedy):
+    rnd, ell, target = _custom_round(B, gamma, V, r, wdtype, seed=B * 31 + V, greedy_every=greedy)
+    _say(f"[edge] B={B} gamma={gamma} V={V} r={r} {wdtype} greedy_every={greedy} ell={ell.tolist()[:8]}")
+    dev = to_device(rnd)
+    td = torch.from_numpy(target).cuda()
+    ed = torch.from_numpy(ell).cuda()
+    d = gpu_draft(dev, 77, 3)
+    v = gpu_verify(dev, td, ed, d, 77, 3)
+    assert ds.dspark_verify_check(v["workspace"]) == 0
+    gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+    gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
+    od, ov = oracle_round(rnd, target, ell, 77, 3)
+    cd = compare_draft(gd, od)
+    cv = compare_verify(gv, od, ov, rnd.temperature, ell)
+    _say(f"[edge] draft {cd.report()} | verify {cv.report()}")
+    assert cv.eligible.sum() >= 0.5 * B
+
+
+def test_neg_inf_logits_parity():
+    rnd, ell, target = _custom_round(40, 4, 777, 16, "bf16", seed=5, neg_inf_frac=0.3)
+    dev = to_device(rnd)
+    d = gpu_draft(dev, 3, 0)
+    v = gpu_verify(dev, torch.from_numpy(target).cuda(), torch.from_numpy(ell).cuda(), d, 3, 0)
+    gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+    gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
+    od, ov = oracle_round(rnd, target, ell, 3, 0)
+    compare_draft(gd, od)
+    compare_verify(gv, od, ov, rnd.temperature, ell)
+    # no draft and no emitted token lands on a -inf logit
+    for b in range(40):
+        for k in range(4):
+            assert np.isfinite(rnd.U[b, k, gd["x"][b, k]])
+
+
+def test_row_offsets_given_equal_computed_and_bad_ell_flagged():
+    rnd, ell, target = _custom_round(24, 3, 500, 16, "bf16", seed=9)
+    dev = to_device(rnd)
+    td = torch.from_numpy(target).cuda()
+    d = gpu_draft(dev, 1, 1)
+    v1 = gpu_verify(dev, td, torch.from_numpy(ell).cuda(), d, 1, 1)
+    off = torch.from_numpy(S.pack_offsets(ell)).cuda()
+    v2 = gpu_verify(dev, td, torch.from_numpy(ell).cuda(), d, 1, 1, row_offsets=off)
+    assert torch.equal(v1["tokens"], v2["tokens"]) and torch.equal(v1["n"], v2["n"])
+    bad = ell.copy()
+    bad[5] = 9  # beyond gamma: that request is not verified, the others are
+    v3 = gpu_verify(dev, td, torch.from_numpy(bad).cuda(), d, 1, 1)
+    assert ds.dspark_verify_check(v3["workspace"]) == ds.DSPARK_ERR_DEVICE_INPUT
+    assert int(v3["n"][5]) == -1
+    assert np.all(np_of(v3["tokens"][5]) == -1)
+
+
+def test_bitwise_determinism():
+    rnd, ell, target = _round("dspark5")
+    dev = to_device(rnd)
+    td = torch.from_numpy(target).cuda()
+    ed = torch.from_numpy(ell).cuda()
+    outs = []
+    for _ in range(2):
+        d = gpu_draft(dev, 1, 42)
+        v = gpu_verify(dev, td, ed, d, 1, 42)
+        outs.append({k: t.clone() for k, t in list(d.items()) + [("n", v["n"]), ("tokens", v["tokens"]),
+                                                                  ("diag", v["diag"]), ("resid", v["resid"])]
+                     if k != "workspace"})
+    for k in outs[0]:
+        a, b = outs[0][k], outs[1][k]
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), k
+
+
+# ---------------------------------------------------------------- statistics
+
+def test_worked_example_section05_on_gpu():
+    """q = (0.70, 0.18, 0.12), p = (0.50, 0.30, 0.20) through the GPU kernels
+    (U = ln q, W2 = 0, target = ln p): acceptance 0.80, residual (0, 0.6, 0.4),
+    emitted tokens distributed as p (chi-square, 2 dof, 13.82 at alpha 1e-3)."""
+    q = np.array([0.70, 0.18, 0.12])
+    p = np.array([0.50, 0.30, 0.20])
+    B, rounds = 50000, 20
+    V, r = 3, 16
+    U = torch.from_numpy(np.broadcast_to(np.log(q).astype(np.float32), (B, 1, V)).copy()).cuda()
+    W = torch.zeros((V, r), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.zeros(B, dtype=torch.int32, device="cuda")
+    temp = torch.ones(B, dtype=torch.float32, device="cuda")
+    ell = torch.ones(B, dtype=torch.int32, device="cuda")
+    target = torch.from_numpy(np.broadcast_to(np.log(p).astype(np.float32), (2 * B, V)).copy()).cuda()
+    acc = 0
+    counts = np.zeros(3)
+    rcounts = np.zeros(3)
+    for rid in range(rounds):
+        d = ds.dspark_draft_sample(U, W, W, anchor, temp, 2024, rid)
+        v = ds.dspark_verify(target, ell, U, W, W, anchor, d["x"], d["lse"], d["qx"], temp, 2024, rid, resid=True)
+        n = np_of(v["n"])
+        y = np_of(v["tokens"][:, 0])
+        acc += int((n == 1).sum())
+        counts += np.bincount(y, minlength=3)
+        rcounts += np.bincount(y[n == 0], minlength=3)
+        res = np_of(v["resid"])[n == 0]
+        np.testing.assert_allclose(res, 0.2, atol=1e-5)
+    N = B * rounds
+    rate = acc / N
+    assert abs(rate - 0.8) < 3 * math.sqrt(0.16 / N), rate
+    chi2 = (((counts - N * p) ** 2) / (N * p)).sum()
+    assert chi2 < 13.82, chi2
+    assert rcounts[0] == 0
+    rp = np.array([0.6, 0.4])
+    chi2r = (((rcounts[1:] - rcounts.sum() * rp) ** 2) / (rcounts.sum() * rp)).sum()
+    assert chi2r < 10.83, chi2r
+    _say(f"[worked example] acceptance={rate:.5f} chi2(p)={chi2:.2f} chi2(residual)={chi2r:.2f}")
+
+
+def test_q_equals_p_accepts_all_on_gpu():
+    V, r, B, gamma = 5, 16, 4096, 3
+    logits = np.log(np.array([0.1, 0.2, 0.3, 0.15, 0.25])).astype(np.float32)
+    U = torch.from_numpy(np.broadcast_to(logits, (B, gamma, V)).copy()).cuda()
+    W = torch.zeros((V, r), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.zeros(B, dtype=torch.int32, device="cuda")
+    temp = torch.ones(B, dtype=torch.float32, device="cuda")
+    ell = torch.full((B,), gamma, dtype=torch.int32, device="cuda")
+    target = torch.from_numpy(np.broadcast_to(logits, (B * (gamma + 1), V)).copy()).cuda()
+    full = total = 0
+    for rid in range(5):
+        d = ds.dspark_draft_sample(U, W, W, anchor, temp, 5, rid)
+        v = ds.dspark_verify(target, ell, U, W, W, anchor, d["x"], d["lse"], d["qx"], temp, 5, rid)
+        full += int((v["n"] == gamma).sum())
+        total += B
+    # p/q = 1 up to float32 rounding: only a uniform within ~1e-7 of 1 can fail
+    assert total - full <= 2, (total, full)
