@@ -36,12 +36,15 @@
  *    round id; key = (seed low 32, seed high 32).  Per-vocabulary streams
  *    take output word (v & 3), the accept stream word 0.
  *    Uniform: u = ((w >> 8) + 0.5) * 2^-24, never 0 or 1.
- *  - Accept iff u * q(x) < p(x).  The pages give the resample distribution
- *    r(v) = max(p - q, 0) / sum(...) (and p for the bonus token) but not how
- *    to draw from it; the draw here is Gumbel-max over log r(v) with stream-2
- *    noise, an exact sampler whose decision is an argmax with a margin.
- *    Entries of zero mass never win.  S = 0 on a rejection (only possible
- *    through rounding) falls back to p_j.
+ *  - Every sampled draw (x_k ~ q_k; y ~ r or p_{ell+1}) is a two-level
+ *    Gumbel-max: a Gumbel race over the logsumexp of 32-entry vocabulary
+ *    tiles, then one over the entries of the winning tile.  The pages fix the
+ *    distributions (q_k = softmax(U_k + B_k); r(v) = max(p - q, 0) / sum;
+ *    p for the bonus), not the sampler; this one is exact and its decisions
+ *    are argmaxes with margins.  Noise: tiles from stream 3 (draft) / 4
+ *    (resample), entries from stream 0 / 2.  Entries of zero mass never win.
+ *  - Accept iff u * q(x) < p(x).  S = 0 on a rejection (only possible through
+ *    rounding) falls back to p_j.
  *  - ell_r drafts are verified; ell_r = 0 still emits one token drawn from p_1.
  *  - Scheduler candidates are ordered by (-a, r, j); improvement must be
  *    strict; SPS beyond the table is 0; candidates with a = 0 are dropped.
@@ -92,15 +95,17 @@ double orc_u01(uint32_t w)
     return ((double)(w >> 8) + 0.5) * (1.0 / 16777216.0);
 }
 
-/* One 32-bit random word of the round's streams.
- * stream 0: Gumbel noise for vocabulary entry v at draft position k;
+/* One 32-bit random word of the round's streams.  v indexes a vocabulary
+ * entry (streams 0, 2) or a 32-entry tile (streams 3, 4).
+ * stream 0: Gumbel noise of entry v at draft position k;
  * stream 1: accept uniform at position k (v ignored);
- * stream 2: Gumbel noise for vocabulary entry v of the resample / bonus
- *           draw at position j. */
+ * stream 2: Gumbel noise of entry v of the resample / bonus draw at position j;
+ * stream 3: Gumbel noise of tile v at draft position k;
+ * stream 4: Gumbel noise of tile v of the resample / bonus draw at position j. */
 uint32_t orc_random_word(uint64_t seed, uint64_t round_id, int stream, int k, int req, int v)
 {
     uint32_t ctr[4], key[2], out[4];
-    int per_vocab = (stream == 0 || stream == 2);
+    int per_vocab = (stream != 1);
     ctr[0] = ((uint32_t)stream << 24) | (uint32_t)k;
     ctr[1] = per_vocab ? ((uint32_t)v >> 2) : 0u;
     ctr[2] = (uint32_t)req;
@@ -164,27 +169,58 @@ static int orc_argmax(const double *z, int V, double *gap)
     return best;
 }
 
-/* Gumbel-max draw from an unnormalised non-negative mass: the v with mass > 0
- * maximising log(mass(v)) + G(v), G from stream 2 at position j (lowest index
- * among equal scores); *margin receives the gap to the runner-up. */
-static int orc_gumbel_pick(const double *mass, int V, uint64_t seed, uint64_t round_id, int j, int req,
-                           double *margin)
+#define ORC_TILE 32 /* vocabulary entries per tile of the two-level draw */
+
+/* Two-level Gumbel-max draw over log-masses s(v) (-inf: excluded):
+ * level 1 picks the tile t = v / 32 maximising logsumexp_{v in t} s(v) + G_t
+ * (noise from tile_stream at index t), level 2 the entry v of that tile
+ * maximising s(v) + G_v (noise from entry_stream at index v); lowest index
+ * wins ties.  P(v) = exp(s(v)) / sum exp(s): an exact draw.  *margin receives
+ * the smaller of the two top-two score gaps (+inf where a level has one
+ * candidate).  Returns 0 when no entry has finite log-mass. */
+static int orc_two_level_draw(const double *s, int V, uint64_t seed, uint64_t round_id, int tile_stream,
+                              int entry_stream, int k, int req, double *margin)
 {
-    int pick = -1;
-    double best = -INFINITY, second = -INFINITY;
-    for (int v = 0; v < V; ++v) {
-        if (!(mass[v] > 0.0)) continue;
-        double score = log(mass[v]) + orc_gumbel(orc_random_word(seed, round_id, 2, j, req, v));
-        if (pick < 0 || score > best) {
-            second = best;
-            best = score;
-            pick = v;
-        } else if (score > second) {
-            second = score;
+    int ntile = (V + ORC_TILE - 1) / ORC_TILE;
+    int tbest = -1;
+    double b1 = -INFINITY, s1 = -INFINITY;
+    for (int t = 0; t < ntile; ++t) {
+        int v0 = t * ORC_TILE, v1 = v0 + ORC_TILE < V ? v0 + ORC_TILE : V;
+        double m = -INFINITY;
+        for (int v = v0; v < v1; ++v)
+            if (s[v] > m) m = s[v];
+        if (m == -INFINITY) continue;
+        double acc = 0.0;
+        for (int v = v0; v < v1; ++v)
+            acc += exp(s[v] - m);
+        double score = m + log(acc) + orc_gumbel(orc_random_word(seed, round_id, tile_stream, k, req, t));
+        if (tbest < 0 || score > b1) {
+            s1 = b1;
+            b1 = score;
+            tbest = t;
+        } else if (score > s1) {
+            s1 = score;
         }
     }
-    if (pick < 0) pick = 0;
-    if (margin) *margin = best - second;
+    if (tbest < 0) {
+        if (margin) *margin = 0.0;
+        return 0;
+    }
+    int pick = -1;
+    double b2 = -INFINITY, s2 = -INFINITY;
+    int v0 = tbest * ORC_TILE, v1 = v0 + ORC_TILE < V ? v0 + ORC_TILE : V;
+    for (int v = v0; v < v1; ++v) {
+        if (s[v] == -INFINITY) continue;
+        double score = s[v] + orc_gumbel(orc_random_word(seed, round_id, entry_stream, k, req, v));
+        if (pick < 0 || score > b2) {
+            s2 = b2;
+            b2 = score;
+            pick = v;
+        } else if (score > s2) {
+            s2 = score;
+        }
+    }
+    if (margin) *margin = fmin(b1 - s1, b2 - s2);
     return pick;
 }
 
@@ -195,10 +231,12 @@ static int orc_gumbel_pick(const double *mass, int V, uint64_t seed, uint64_t ro
 /* For each request b and k = 1..gamma ([MG] 3.2, [CE] 03):
  *   z = (U_k + W1[x_{k-1}] W2^T) / T,  x_0 = anchor,
  *   lse = logsumexp(z),  q_k(v) = exp(z(v) - lse),
- *   T > 0: x_k = argmax_v z(v) + G(v),  G = -log(-log u), u from stream 0;
+ *   T > 0: x_k = the two-level Gumbel-max draw from softmax(z) (tiles:
+ *          stream 3, entries: stream 0), G = -log(-log u);
  *   T = 0: x_k = argmax_v z(v) (lowest index wins), q_k one-hot.
  * Outputs per (b, k): x, lse (the max logit for T = 0), q_k(x_k) (1 for
- * T = 0), and the gap between the two best scores.
+ * T = 0), and the smaller of the draw's two top-two score gaps (the top-two
+ * logit gap for T = 0).
  * req_ids (nullable) gives the request index used in the Philox counter. */
 int orc_draft(const float *U, const float *W1, const float *W2,
               const int32_t *anchor, const float *temperature, const int32_t *req_ids,
@@ -222,21 +260,8 @@ int orc_draft(const float *U, const float *W1, const float *W2,
             double lse, qx, margin;
             if (T > 0.0) {
                 lse = orc_logsumexp(z, V);
-                double best = -INFINITY, second = -INFINITY;
-                x = 0;
-                for (int v = 0; v < V; ++v) {
-                    double u = orc_u01(orc_random_word(seed, round_id, 0, k, req, v));
-                    double score = z[v] - log(-log(u));
-                    if (v == 0 || score > best) {
-                        if (v > 0) second = best;
-                        best = score;
-                        x = v;
-                    } else if (score > second) {
-                        second = score;
-                    }
-                }
+                x = orc_two_level_draw(z, V, seed, round_id, 3, 0, k, req, &margin);
                 qx = exp(z[x] - lse);
-                margin = best - second;
             } else {
                 x = orc_argmax(z, V, &margin);
                 lse = z[x];
@@ -267,16 +292,17 @@ int orc_draft(const float *U, const float *W1, const float *W2,
  *   q_k = softmax(z_k) recomputed from U_k, W1[x_{k-1}], W2 as in the draft;
  *   k = 1..ell: u from stream 1, accept iff u * q_k(x_k) < p_k(x_k)
  *               (T = 0: accept iff x_k = argmax t_k);
- *   first rejection j: y ~ max(p_j - q_j, 0) by Gumbel-max with stream-2
- *               noise at position j (T = 0: y = argmax t_j);
+ *   first rejection j: y ~ max(p_j - q_j, 0) by the two-level Gumbel-max
+ *               draw at position j (tiles: stream 4, entries: stream 2)
+ *               (T = 0: y = argmax t_j);
  *   all accepted: y ~ p_{ell+1} the same way (the bonus token).
  * Outputs: n_accept[b], tokens[b][0..gamma] = x_1..x_n, y, then -1;
  * diag[b][k-1] = (p_k(x_k), min(1, p_k(x_k)/q_k(x_k))) for tested positions
  * (NaN elsewhere); resid_mass[b] = S at a sampled rejection (-1 otherwise);
  * accept_margin[b][k-1] = |u - p/q| (T > 0) or the top-two target gap
- * (T = 0) for tested positions (NaN elsewhere); pick_margin[b] = the gap
- * between the best and second-best Gumbel score of the draw of y (T > 0) or
- * the top-two gap of t_j (T = 0). */
+ * (T = 0) for tested positions (NaN elsewhere); pick_margin[b] = the
+ * smaller top-two score gap of the two-level draw of y (T > 0) or the
+ * top-two gap of t_j (T = 0). */
 int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
                const float *U, const float *W1, const float *W2,
                const int32_t *anchor, const int32_t *x, const float *temperature,
@@ -361,9 +387,10 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
         int y;
         double pmargin = 0.0, S = -1.0;
         if (T > 0.0) {
+            /* log-mass of the draw: log p_j, or log max(p_j - q_j, 0) after a rejection */
             for (int v = 0; v < V; ++v) zt[v] = (double)tj[v] / T;
             double lse_t = orc_logsumexp(zt, V);
-            for (int v = 0; v < V; ++v) mass[v] = exp(zt[v] - lse_t);
+            for (int v = 0; v < V; ++v) mass[v] = zt[v] - lse_t;
             if (rejected) {
                 int prev = (j == 1) ? anchor[b] : xb[j - 2];
                 const float *Uj = U + ((size_t)b * (size_t)gamma + (size_t)(j - 1)) * (size_t)V;
@@ -371,16 +398,16 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
                 double lse_q = orc_logsumexp(zq, V);
                 double tot = 0.0;
                 for (int v = 0; v < V; ++v) {
-                    double d = mass[v] - exp(zq[v] - lse_q);
-                    zq[v] = d > 0.0 ? d : 0.0; /* residual, reusing the buffer */
-                    tot += zq[v];
+                    double d = exp(zt[v] - lse_t) - exp(zq[v] - lse_q);
+                    zq[v] = d > 0.0 ? log(d) : -INFINITY; /* residual log-mass, reusing the buffer */
+                    tot += d > 0.0 ? d : 0.0;
                 }
                 S = tot;
                 if (tot > 0.0)
                     memcpy(mass, zq, (size_t)V * sizeof(double));
                 /* tot == 0: fall back to p_j, already in mass */
             }
-            y = orc_gumbel_pick(mass, V, seed, round_id, j, req, &pmargin);
+            y = orc_two_level_draw(mass, V, seed, round_id, 4, 2, j, req, &pmargin);
         } else {
             for (int v = 0; v < V; ++v) zt[v] = (double)tj[v];
             y = orc_argmax(zt, V, &pmargin);

@@ -101,6 +101,65 @@ def test_gumbel_max_matches_softmax():
     np.testing.assert_allclose(out["qx"][:, 0], p[out["x"][:, 0]], rtol=1e-13)
 
 
+def test_two_level_draw_matches_softmax_across_tiles():
+    """The draft sampler (a Gumbel race over 32-entry tile logsumexps, then
+    over the entries of the winning tile) is an exact draw from softmax(z):
+    chi-square over a vocabulary spanning several tiles and a ragged tail,
+    with -inf entries that must never come out."""
+    rng = np.random.default_rng(12)
+    V = 75  # tiles of 32, 32, 11
+    z = (rng.standard_normal(V) * 1.2).astype(np.float32)
+    z[[3, 40, 74]] = -np.inf
+    B = 400_000
+    U = _broadcast_draft_inputs([z], B)
+    W = np.zeros((V, 1), np.float32)
+    out = oracle.draft(U, W, W, np.zeros(B), np.ones(B, np.float32), seed=6, round_id=2)
+    zz = z.astype(np.float64)
+    p = np.exp(zz - zz[np.isfinite(zz)].max())
+    p /= p.sum()
+    counts = np.bincount(out["x"][:, 0], minlength=V)
+    assert counts[3] == counts[40] == counts[74] == 0
+    # merge bins with expected count < 5
+    exp_ = B * p
+    keep = exp_ >= 5
+    c2 = (((counts[keep] - exp_[keep]) ** 2) / exp_[keep]).sum()
+    rest_c, rest_e = counts[~keep].sum(), exp_[~keep].sum()
+    if rest_e > 0:
+        c2 += (rest_c - rest_e) ** 2 / rest_e
+    assert c2 < _chi2_crit(int(keep.sum()))
+
+
+def test_two_level_draw_brute_force():
+    """Each sampled draft equals the two-level argmax recomputed here from the
+    raw Philox words with numpy: tile t maximising logsumexp(z over t) plus
+    tile noise (stream 3, index t), then the entry of t maximising z plus
+    entry noise (stream 0, index v); the reported margin is the smaller
+    top-two gap of the two levels."""
+    rng = np.random.default_rng(21)
+    V, B, seed, rid, k = 70, 300, 17, 5, 1
+    z = (rng.standard_normal((B, 1, V)) * 2).astype(np.float32)
+    W = np.zeros((V, 1), np.float32)
+    out = oracle.draft(z, W, W, np.zeros(B), np.ones(B, np.float32), seed=seed, round_id=rid)
+
+    def g(stream, b, i):
+        w = np.array([oracle.random_word(seed, rid, stream, k, b, j) for j in i], np.uint64)
+        u = ((w >> np.uint64(8)).astype(np.float64) + 0.5) / 2.0 ** 24
+        return -np.log(-np.log(u))
+
+    tiles = [(t * 32, min(V, t * 32 + 32)) for t in range((V + 31) // 32)]
+    for b in range(B):
+        zb = z[b, 0].astype(np.float64)
+        lse_t = np.array([np.log(np.exp(zb[a:c]).sum()) for a, c in tiles])
+        s1 = lse_t + g(3, b, range(len(tiles)))
+        t = int(np.argmax(s1))
+        a, c = tiles[t]
+        s2 = zb[a:c] + g(0, b, range(a, c))
+        assert out["x"][b, 0] == a + int(np.argmax(s2))
+        gap1 = np.sort(s1)[-1] - np.sort(s1)[-2]
+        gap2 = np.sort(s2)[-1] - np.sort(s2)[-2]
+        assert out["margin"][b, 0] == pytest.approx(min(gap1, gap2), abs=1e-9)
+
+
 def test_temperature_scales_logits():
     """T = 0.5 samples from softmax(2 z); lse is logsumexp(z / T)."""
     z = np.array([0.0, 0.5, -0.5, 1.0], np.float32)
@@ -307,8 +366,9 @@ def test_ell_zero_emits_one_token_from_p1():
 
 def test_bonus_draw_skips_zero_mass_tokens():
     """Zero-probability tokens are never drawn by the bonus / resample draw,
-    and the draw frequencies follow the mass."""
-    logits = np.array([NEG, 0.0, NEG, NEG, 1.0, NEG, -0.5, NEG], np.float32)
+    and the draw frequencies follow the mass, across tile boundaries."""
+    logits = np.full(70, NEG, np.float32)
+    logits[[1, 4, 6, 31, 32, 50, 69]] = [0.0, 1.0, -0.5, 0.3, -1.0, 0.7, 0.1]
     p = np.exp(np.where(np.isinf(logits), -np.inf, logits).astype(np.float64))
     p /= p.sum()
     B = 200_000
@@ -325,9 +385,9 @@ def test_bonus_draw_skips_zero_mass_tokens():
 
 
 def test_bonus_draw_brute_force_small_vocab():
-    """For tiny V, every bonus token is the entry maximising log p(v) + G(v)
-    with G = -log(-log u) of the stream-2 word of (position 1, request, v),
-    recomputed here with numpy from the raw Philox words."""
+    """For V <= 32 (one tile), every bonus token is the entry maximising
+    log p(v) + G(v) with G = -log(-log u) of the stream-2 word of
+    (position 1, request, v), recomputed here with numpy from the raw words."""
     rng = np.random.default_rng(77)
     for V in (1, 2, 3, 5, 16):
         logits = rng.standard_normal(V).astype(np.float32)
@@ -345,6 +405,36 @@ def test_bonus_draw_brute_force_small_vocab():
             words = np.array([oracle.random_word(seed, 4, 2, 1, b, i) for i in range(V)], np.uint64)
             u = ((words >> np.uint64(8)).astype(np.float64) + 0.5) / 2.0 ** 24
             assert v["tokens"][b, 0] == int(np.argmax(z - np.log(-np.log(u))))
+
+
+def test_residual_draw_follows_residual_across_tiles():
+    """After a rejection, y follows r = max(p - q, 0) / sum(...) over a
+    vocabulary of several tiles (chi-square), and every emitted first token
+    follows p."""
+    rng = np.random.default_rng(31)
+    V = 80
+    q = rng.dirichlet(np.ones(V))
+    p = rng.dirichlet(np.ones(V))
+    B = 400_000
+    d, v = _toy_verify(q, p, B, seed=13)
+    qf = np.exp(np.log(q).astype(np.float32).astype(np.float64))
+    qf /= qf.sum()
+    pf = np.exp(np.log(p).astype(np.float32).astype(np.float64))
+    pf /= pf.sum()
+    r = np.maximum(pf - qf, 0)
+    r /= r.sum()
+    rej = v["n"] == 0
+    counts = np.bincount(v["tokens"][rej, 0], minlength=V)
+    assert np.all(counts[r == 0] == 0)
+    e = rej.sum() * r
+    keep = e >= 5
+    c2 = (((counts[keep] - e[keep]) ** 2) / e[keep]).sum()
+    assert c2 < _chi2_crit(int(keep.sum()) - 1)
+    counts = np.bincount(v["tokens"][:, 0], minlength=V)
+    e = B * pf
+    keep = e >= 5
+    c2 = (((counts[keep] - e[keep]) ** 2) / e[keep]).sum()
+    assert c2 < _chi2_crit(int(keep.sum()) - 1)
 
 
 def test_residual_draw_uses_position_of_rejection():
