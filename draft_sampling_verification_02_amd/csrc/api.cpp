@@ -234,7 +234,7 @@ int dspark_verify_check(const void *workspace, void *stream) {
 
 int dspark_debug_random_words(uint64_t seed, uint64_t round_id, int stream_id, int k, int req, int v0, int n,
                               uint32_t *out, void *stream) {
-    if (!out || n < 0 || stream_id < 0 || stream_id > 2 || k < 0 || k >= (1 << 24) || v0 < 0) return DSPARK_ERR_ARG;
+    if (!out || n < 0 || stream_id < 0 || stream_id > 4 || k < 0 || k >= (1 << 24) || v0 < 0) return DSPARK_ERR_ARG;
     const hipError_t e = launch_debug_words(uint32_t(seed), uint32_t(seed >> 32), uint32_t(round_id), stream_id,
                                             k, req, v0, n, out, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;

@@ -11,10 +11,8 @@ __global__ void debug_words_kernel(uint32_t k0, uint32_t k1, uint32_t round32, i
                                    int v0, int n, uint32_t *out) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    if (stream_id == kStreamDraft || stream_id == kStreamResample) {
-        const int v = v0 + i;
-        const uint4 w = noise_block(stream_id, k, uint32_t(v) >> 2, uint32_t(req), round32, k0, k1);
-        out[i] = u4get(w, v & 3);
+    if (stream_id != kStreamAccept) {
+        out[i] = noise_word(stream_id, k, uint32_t(v0 + i), uint32_t(req), round32, k0, k1);
     } else {
         out[i] = scalar_word(stream_id, k, uint32_t(req), round32, k0, k1);
     }

@@ -6,16 +6,23 @@
 // (share.concentrate1.com), section 03): with x_0 the anchor,
 //   B_k = W1[x_{k-1}] W2^T,   q_k = softmax((U_k + B_k) / T),   x_k ~ q_k,
 // one position after another, each step reading the token the previous one
-// sampled.  The draw is Gumbel-max with Philox noise; T = 0 is greedy.
+// sampled.  T = 0 is greedy.  The draw is a two-level Gumbel-max: a Gumbel
+// race over the logsumexp of 32-entry vocabulary tiles (Philox stream 3),
+// then one over the entries of the winning tile (stream 0) -- an exact draw
+// from q_k that needs per-entry noise for a single tile only.
 //
 // Per position k the work is one pass over the [B, V] plane:
-//   draft_step    one wave per (32 requests x vocabulary chunk): the bias
-//                 tile on MFMA (bf16 32x32x16, or f32 32x32x2), + U_k, the
-//                 temperature, an online max / sum of exp2 (base-2 softmax
-//                 statistics) and the Gumbel-perturbed best score, all in
-//                 registers; per (request, chunk) partials go to the workspace.
-//   draft_reduce  one wave per request: merges the chunk partials into x_k,
-//                 lse_k, q_k(x_k) and the top-two gap.
+//   draft_step    a workgroup of up to 4 waves (32 requests each) walks the
+//                 vocabulary tiles of one chunk; the W2 tile is staged in LDS
+//                 by direct loads (double buffered, shared by the waves) and
+//                 the U_k tile is prefetched into registers one tile ahead.
+//                 The bias tile comes from MFMA (bf16 32x32x16, or f32
+//                 32x32x2); + U_k and 1/T give the tile's base-2 logsumexp,
+//                 which feeds both the running softmax sum and the tile race.
+//   draft_reduce  one wave per request: merges the chunk partials (row
+//                 logsumexp, best tile), recomputes the winning tile's 32
+//                 logits on the vector ALUs and races their entry noise:
+//                 x_k, lse_k, q_k(x_k) and the draw's margin.
 // The bias plane is never stored; HBM traffic per step is U_k, W2 and the
 // gathered W1 rows.
 #include "device_common.hpp"
@@ -36,7 +43,7 @@ struct StepParams {
     const float *temperature;
     int B, V, k;
     uint32_t key0, key1, round32;
-    int nbb, tiles_per_chunk, nchunk, total_waves;
+    int nbb, nw, nbg, ntiles, tiles_per_chunk, nchunk;
     int vec;  // U rows allow aligned 16-byte loads
     float *pm, *ps, *pb, *p2;
     int32_t *pi;
@@ -44,85 +51,95 @@ struct StepParams {
 
 template <typename WT, int R, bool TRACK2>
 __global__ __launch_bounds__(256) void draft_step_kernel(StepParams p) {
-    const int lane = threadIdx.x & 63;
-    const int gw = xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
-    if (gw >= p.total_waves) return;
-    const int bb = gw % p.nbb;
-    const int chunk = gw / p.nbb;
+    using L = TileLDS<WT, R>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::BYTES];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nthreads = p.nw * 64;
+    const int lg = xcd_remap(blockIdx.x, gridDim.x);
+    const int chunk = lg / p.nbg, bg = lg % p.nbg;
+    const int bb = bg * p.nw + wave;
+    const bool wave_ok = bb < p.nbb;  // uniform across the wave
     const int n = lane & 31, h = lane >> 5;
     const int b = bb * 32 + n;
-    const bool row_ok = b < p.B;
-    const int bc = row_ok ? b : p.B - 1;
+    const bool row_ok = wave_ok && b < p.B;
+    const int bc = min(b, p.B - 1);
 
     int prev = p.xprev[size_t(bc) * p.xprev_stride];
     prev = min(max(prev, 0), p.V - 1);
     const float T = p.temperature[bc];
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;  // base-2 logits; greedy keeps raw logits
-    const float gm = sampled ? 1.0f : 0.0f;        // greedy rows ignore the noise
 
-    const WT *W1 = static_cast<const WT *>(p.W1);
     const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
-    ef.load(W1 + size_t(prev) * R, h);
+    ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
     const float *urow = p.U + size_t(bc) * p.u_stride;
     const bool vec = p.vec != 0;
 
-    const int v_begin = chunk * p.tiles_per_chunk * 32;
-    const int v_end = min(p.V, v_begin + p.tiles_per_chunk * 32);
+    const int t_begin = chunk * p.tiles_per_chunk;
+    const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
     float m_run = kNegInf, s_run = 0.f;
     float best = kNegInf, second = kNegInf;
-    int bidx = v_begin + 4 * h;  // lowest entry of this lane: wins if everything is -inf
+    int bt = t_begin;
+    uint4 tw = make_uint4(0u, 0u, 0u, 0u);
 
-    for (int v0 = v_begin; v0 < v_end; v0 += 32) {
-        const int vrow = min(v0 + n, p.V - 1);
-        const f32x16_t acc = bias_tile(ef, W2 + size_t(vrow) * R, h);
-        float z[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 u = load4_masked(urow, v0 + 8 * i + 4 * h, p.V, vec);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) z[4 * i + j] = (f4get(u, j) + acc[4 * i + j]) * sc;
+    tile_issue<WT, R>(W2, t_begin * kTile, p.V, lds, nthreads);
+    float4 ucur[4];
+    load_tile_row(urow, t_begin, h, p.V, vec, ucur);
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t (LDS and U) have landed
+        __syncthreads();                // ... and every thread's; the other buffer is free again
+        float4 unext[4];
+        if (t + 1 < t_end) {
+            tile_issue<WT, R>(W2, (t + 1) * kTile, p.V, lds + (buf ^ 1) * L::BYTES, nthreads);
+            load_tile_row(urow, t + 1, h, p.V, vec, unext);
         }
-        float mt = z[0];
+        if (wave_ok) {
+            const f32x16_t acc = bias_tile_lds(ef, lds + buf * L::BYTES, lane);
+            float tv[16];
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, z[e]);
-        const float mn = fmaxf(m_run, mt);
-        const float ms = (mn == kNegInf) ? 0.f : mn;
-        float add = 0.f;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) add += fast_exp2(z[e] - ms);
-        s_run = s_run * fast_exp2(m_run - ms) + add;
-        m_run = mn;
+                for (int j = 0; j < 4; ++j) tv[4 * i + j] = f4get(ucur[i], j) + acc[4 * i + j];
+            float mx = tv[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 w = draft_noise_block(p.k, uint32_t(v0 >> 2) + uint32_t(2 * i + h), uint32_t(b),
-                                              p.round32, p.key0, p.key1);
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, tv[e]);
+            // this half's share of the tile: max and sum of exp2 in base-2 units
+            const float mh = mx * sc;
+            const float nmh = (mh == kNegInf) ? 0.f : -mh;
+            float sh = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float score = __builtin_fmaf(gumbel2(u4get(w, j)), gm, z[4 * i + j]);
-                if (TRACK2) second = fmaxf(second, fminf(score, best));
-                if (score > best) {
-                    best = score;
-                    bidx = v0 + 8 * i + 4 * h + j;
-                }
+            for (int e = 0; e < 16; ++e) sh += fast_exp2(__builtin_fmaf(tv[e], sc, nmh));
+            // the whole tile: merge with the other half of the lane pair
+            const float mo = __shfl_xor(mh, 32), so = __shfl_xor(sh, 32);
+            const float mt = fmaxf(mh, mo);
+            const float mts = (mt == kNegInf) ? 0.f : mt;
+            const float st = sh * fast_exp2(mh - mts) + so * fast_exp2(mo - mts);
+            // tile race: logsumexp + tile noise (greedy: the tile's largest logit)
+            if (t == t_begin || (t & 3) == 0)
+                tw = noise_block(kStreamDraftTile, p.k, uint32_t(t) >> 2, uint32_t(b), p.round32, p.key0, p.key1);
+            const float g = gumbel2(u4get(tw, t & 3));
+            const float Lt = sampled ? mt + fast_log2(st) + g : mt;
+            if (TRACK2) second = fmaxf(second, fminf(Lt, best));
+            if (Lt > best) {
+                best = Lt;
+                bt = t;
             }
+            lse_merge(m_run, s_run, mt, st);
+        }
+        if (t + 1 < t_end) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ucur[i] = unext[i];
         }
     }
-    // merge the two lane halves that share a request
-    {
-        const float m2 = __shfl_xor(m_run, 32), s2 = __shfl_xor(s_run, 32);
-        const float b2 = __shfl_xor(best, 32), c2 = __shfl_xor(second, 32);
-        const int i2 = __shfl_xor(bidx, 32);
-        lse_merge(m_run, s_run, m2, s2);
-        best_merge(best, bidx, second, b2, i2, c2);
-    }
+    // both lane halves hold the same request state
     if (h == 0 && row_ok) {
         const size_t o = size_t(b) * p.nchunk + chunk;
         p.pm[o] = m_run;
         p.ps[o] = s_run;
         p.pb[o] = best;
-        p.pi[o] = bidx;
+        p.pi[o] = bt;
         if (TRACK2) p.p2[o] = second;
     }
 }
@@ -134,7 +151,8 @@ struct ReduceParams {
     const int32_t *xprev;
     int xprev_stride;
     const float *temperature;
-    int B, V, k, gamma, nchunk;
+    int B, V, k, gamma, nchunk, ntiles;
+    uint32_t key0, key1, round32;
     const float *pm, *ps, *pb, *p2;
     const int32_t *pi;
     int32_t *x_out;
@@ -147,56 +165,64 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= p.B) return;
     const bool track2 = p.margin_out != nullptr;
+    // level 1: row logsumexp and the winning tile
     float m = kNegInf, s = 0.f, best = kNegInf, second = kNegInf;
-    int idx = 0x7fffffff;
+    int bt = 0x7fffffff;
     for (int c = lane; c < p.nchunk; c += 64) {
         const size_t o = size_t(b) * p.nchunk + c;
         lse_merge(m, s, p.pm[o], p.ps[o]);
-        best_merge(best, idx, second, p.pb[o], p.pi[o], track2 ? p.p2[o] : kNegInf);
+        best_merge(best, bt, second, p.pb[o], p.pi[o], track2 ? p.p2[o] : kNegInf);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
         const float b2 = __shfl_xor(best, off), c2 = __shfl_xor(second, off);
-        const int i2 = __shfl_xor(idx, off);
+        const int i2 = __shfl_xor(bt, off);
         lse_merge(m, s, m2, s2);
-        best_merge(best, idx, second, b2, i2, c2);
+        best_merge(best, bt, second, b2, i2, c2);
     }
-    const int x = min(max(idx, 0), p.V - 1);
+    const int tile = min(max(bt, 0), p.ntiles - 1);
+    // level 2: the winning tile's logits on the vector ALUs, then the entry race
     int prev = p.xprev[size_t(b) * p.xprev_stride];
     prev = min(max(prev, 0), p.V - 1);
-    // z(x_k): recompute the one bias entry the sample landed on
+    const float T = p.temperature[b];
+    const bool sampled = T > 0.f;
+    const float sc = sampled ? kLog2e / T : 1.0f;
+    const int i = lane & 31, h = lane >> 5;
+    const int v = tile * kTile + i;
+    const bool valid = v < p.V;
+    const int vc = min(v, p.V - 1);
     const WT *W1 = static_cast<const WT *>(p.W1);
     const WT *W2 = static_cast<const WT *>(p.W2);
-    float d = 0.f;
-    for (int i = lane; i < R; i += 64) {
-        float a, w;
-        if constexpr (sizeof(WT) == 2) {
-            a = __uint_as_float(uint32_t(W1[size_t(prev) * R + i]) << 16);
-            w = __uint_as_float(uint32_t(W2[size_t(x) * R + i]) << 16);
-        } else {
-            a = W1[size_t(prev) * R + i];
-            w = W2[size_t(x) * R + i];
-        }
-        d = __builtin_fmaf(a, w, d);
-    }
+    const float d = bias_entry<WT, R>(W1 + size_t(prev) * R, W2 + size_t(vc) * R, h);
+    const float logit = valid ? p.U[size_t(b) * p.u_stride + vc] + d : kNegInf;
+    const float z2 = logit * sc;
+    float score = logit;
+    if (sampled) score = z2 + gumbel2(noise_word(kStreamDraft, p.k, uint32_t(vc), uint32_t(b), p.round32, p.key0, p.key1));
+    if (h != 0) score = kNegInf;  // the upper half duplicates the lower half
+    float s1 = score, s2 = kNegInf;
+    int xi = v;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+    for (int off = 1; off < 64; off <<= 1) {
+        const float b2 = __shfl_xor(s1, off), c2 = __shfl_xor(s2, off);
+        const int i2 = __shfl_xor(xi, off);
+        best_merge(s1, xi, s2, b2, i2, c2);
+    }
+    const int x = min(max(xi, tile * kTile), p.V - 1);
+    const float z2x = __shfl(z2, x - tile * kTile);
     if (lane == 0) {
-        const float T = p.temperature[b];
         const size_t o = size_t(b) * p.gamma + (p.k - 1);
         p.x_out[o] = x;
-        if (T > 0.f) {
-            const float sc = kLog2e / T;
-            const float z2x = (p.U[size_t(b) * p.u_stride + x] + d) * sc;
+        const float gap = fminf(best - second, s1 - s2);
+        if (sampled) {
             const float lse2 = m + fast_log2(s);
             p.lse_out[o] = lse2 * kLn2;
             p.qx_out[o] = fast_exp2(z2x - lse2);
-            if (track2) p.margin_out[o] = (best - second) * kLn2;
+            if (track2) p.margin_out[o] = gap * kLn2;
         } else {
             p.lse_out[o] = m;
             p.qx_out[o] = 1.0f;
-            if (track2) p.margin_out[o] = best - second;
+            if (track2) p.margin_out[o] = gap;
         }
     }
 }
@@ -221,9 +247,11 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         sp.key1 = a.key1;
         sp.round32 = a.round32;
         sp.nbb = pl.nbb;
+        sp.nw = pl.nw;
+        sp.nbg = pl.nbg;
+        sp.ntiles = pl.ntiles;
         sp.tiles_per_chunk = pl.tiles_per_chunk;
         sp.nchunk = pl.nchunk;
-        sp.total_waves = pl.total_waves;
         sp.vec = vec;
         sp.pm = w.pm;
         sp.ps = w.ps;
@@ -232,9 +260,9 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         sp.pi = w.pi;
         int t = prof_begin("draft_step", s);
         if (track2)
-            hipLaunchKernelGGL((draft_step_kernel<WT, R, true>), dim3(pl.blocks), dim3(256), 0, s, sp);
+            hipLaunchKernelGGL((draft_step_kernel<WT, R, true>), dim3(pl.blocks), dim3(64 * pl.nw), 0, s, sp);
         else
-            hipLaunchKernelGGL((draft_step_kernel<WT, R, false>), dim3(pl.blocks), dim3(256), 0, s, sp);
+            hipLaunchKernelGGL((draft_step_kernel<WT, R, false>), dim3(pl.blocks), dim3(64 * pl.nw), 0, s, sp);
         prof_end(t, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -252,6 +280,10 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         rp.k = k;
         rp.gamma = a.gamma;
         rp.nchunk = pl.nchunk;
+        rp.ntiles = pl.ntiles;
+        rp.key0 = a.key0;
+        rp.key1 = a.key1;
+        rp.round32 = a.round32;
         rp.pm = w.pm;
         rp.ps = w.ps;
         rp.pb = w.pb;
@@ -275,14 +307,17 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
 DraftPlan draft_plan(int B, int V) {
     DraftPlan p{};
     p.nbb = (B + 31) / 32;
-    p.ntiles = (V + 31) / 32;
-    // aim for ~4096 waves (16 per CU) so every SIMD keeps several waves
+    p.nw = std::min(4, p.nbb);
+    p.nbg = (p.nbb + p.nw - 1) / p.nw;
+    p.ntiles = (V + kTile - 1) / kTile;
+    // about 2048 waves in flight over the 1024 SIMDs; chunks of a multiple of
+    // 4 tiles share the tile-noise Philox blocks
     const long long work = 1LL * p.nbb * p.ntiles;
-    const long long target = 4096;
-    p.tiles_per_chunk = int(std::max<long long>(1, (work + target - 1) / target));
+    long long tpc = std::max<long long>(1, (work + 2047) / 2048);
+    if (tpc > 2) tpc = (tpc + 3) / 4 * 4;
+    p.tiles_per_chunk = int(std::min<long long>(tpc, p.ntiles));
     p.nchunk = (p.ntiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk;
-    p.total_waves = p.nbb * p.nchunk;
-    p.blocks = (p.total_waves + 3) / 4;
+    p.blocks = p.nchunk * p.nbg;
     return p;
 }
 

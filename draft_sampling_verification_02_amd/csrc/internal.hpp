@@ -30,13 +30,17 @@ struct Carve {
 
 // ---- draft -----------------------------------------------------------
 
+// Vocabulary walk of the MFMA tile kernels: a workgroup of `nw` waves (one
+// 32-row block of requests each) streams the W2 tiles of one vocabulary chunk
+// through LDS; `nbg` workgroups cover the request blocks of a chunk.
 struct DraftPlan {
-    int nbb;              // batch blocks of 32 rows
-    int ntiles;           // 32-column vocabulary tiles
-    int tiles_per_chunk;  // tiles one wave walks
+    int nbb;              // request blocks of 32 rows
+    int nw;               // waves per workgroup = min(4, nbb)
+    int nbg;              // workgroups per vocabulary chunk = ceil(nbb / nw)
+    int ntiles;           // 32-entry vocabulary tiles
+    int tiles_per_chunk;  // tiles one workgroup walks
     int nchunk;           // vocabulary chunks = ceil(ntiles / tiles_per_chunk)
-    int total_waves;      // nbb * nchunk
-    int blocks;           // workgroups of 4 waves
+    int blocks;           // workgroups = nchunk * nbg
 };
 DraftPlan draft_plan(int B, int V);
 
@@ -61,14 +65,12 @@ hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork 
 
 // ---- verify ----------------------------------------------------------
 
-constexpr int kRowChunk = 2048;  // vocabulary chunk of the target-row statistics pass
-
 struct VerifyPlan {
     int rows_max;     // B * (gamma + 1)
-    int nrchunk;      // ceil(V / kRowChunk)
     int nbb;          // ceil(B / 32)
     DraftPlan tile;   // vocabulary walk of the resample / bonus draw
-    int draw_blocks;  // workgroups of the draw kernel (room for both lists)
+    int draw_nbg;     // workgroups per chunk of the draw (room for both lists)
+    int draw_blocks;  // workgroups of the draw kernel
 };
 VerifyPlan verify_plan(int B, int gamma, int V);
 
@@ -86,9 +88,8 @@ struct VerifyWork {
     int32_t *bonus_list; // [B] sampled requests taking the bonus draw, ascending
     // draw partials per (list slot, vocabulary chunk); residual slots [0, B), bonus slots [B, 2B)
     float *dw_sum;       // residual mass
-    float *dw_br;        // best Gumbel score of the residual
-    float *dw_bp;        // best Gumbel score of p
-    int32_t *dw_ir, *dw_ip;
+    float *dw_bl;        // best tile score of the level-1 race
+    int32_t *dw_bt;      // its tile
 };
 VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, size_t *bytes);
 

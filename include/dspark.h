@@ -31,13 +31,18 @@
  *    the host before anything is enqueued; on an error nothing is enqueued
  *    and no output is written.
  *  - Random numbers come from Philox4x32-10 (Salmon et al., SC'11), keyed by
- *    `seed` and addressed by the counter (stream << 24 | position, vocabulary
- *    quad v >> 2 or 0, request index, low 32 bits of round_id).  Streams:
- *    0 = draft Gumbel noise, 1 = accept uniforms, 2 = Gumbel noise of the
- *    resample / bonus draw.  Entry v of a per-vocabulary stream uses output
- *    word v & 3; uniforms are ((w >> 8) + 0.5) * 2^-24.  Outputs are a pure
- *    function of the inputs, seed and round_id: two identical calls give
- *    identical bits.
+ *    `seed` and addressed by the counter (stream << 24 | position, i >> 2 or
+ *    0, request index, low 32 bits of round_id), output word i & 3, where i
+ *    is a vocabulary entry (streams 0 and 2) or a 32-entry vocabulary tile
+ *    (streams 3 and 4).  Streams: 0 = draft entry noise, 1 = accept uniforms
+ *    (word 0 of counter word1 = 0), 2 = resample / bonus entry noise, 3 =
+ *    draft tile noise, 4 = resample / bonus tile noise.  Uniforms are
+ *    ((w >> 8) + 0.5) * 2^-24, Gumbel noise -ln(-ln u).  Every sampled draw is
+ *    a two-level Gumbel-max: tile t = v / 32 wins the race of
+ *    logsumexp_{v in t} log-mass + tile noise, then entry v of that tile wins
+ *    log-mass(v) + entry noise -- an exact draw from the normalised mass.
+ *    Outputs are a pure function of the inputs, seed and round_id: two
+ *    identical calls give identical bits.
  *  - Logits may be -inf (probability 0).  NaN inputs give undefined values
  *    but never out-of-bounds accesses or hangs.
  */
@@ -88,9 +93,9 @@ size_t dspark_draft_workspace_size(int B, int gamma, int V, int r);
 /* Markov-head draft sampling for B requests over block positions k = 1..gamma.
  * For every request b and k, with x_0 = anchor[b]:
  *   z_k = (U[b, k-1, :] + W1[x_{k-1}, :] . W2^T) / T_b
- *   T_b > 0: x_k = argmax_v z_k(v) + Gumbel noise(b, k, v)   (a draw from
- *            q_k = softmax(z_k)); T_b = 0: x_k = argmax_v z_k(v), lowest
- *            index first among equal values.
+ *   T_b > 0: x_k = the two-level Gumbel-max draw from q_k = softmax(z_k)
+ *            (tile noise stream 3, entry noise stream 0, position k);
+ *   T_b = 0: x_k = argmax_v z_k(v), lowest index first among equal values.
  * The [B, V] bias W1[x_{k-1}] W2^T is never written to memory.
  *
  *   U           device [B, gamma, V] float32   base logits U_k of the parallel stage
@@ -106,9 +111,9 @@ size_t dspark_draft_workspace_size(int B, int gamma, int V, int r);
  *   lse_out     device [B, gamma] float32      logsumexp(z_k), so q_k = exp(z_k - lse);
  *                                              for T_b = 0 the largest logit
  *   qx_out      device [B, gamma] float32      q_k(x_k) (1 for T_b = 0)
- *   margin_out  device [B, gamma] float32 or NULL   gap between the best and the
- *                                              second-best score (Gumbel-perturbed
- *                                              z for T_b > 0, logits for T_b = 0)
+ *   margin_out  device [B, gamma] float32 or NULL   the smaller of the draw's two
+ *                                              top-two score gaps (tile race and
+ *                                              entry race; logits for T_b = 0)
  *   workspace   device, >= dspark_draft_workspace_size bytes
  * Anchors outside [0, V) are clamped into range on the device. */
 int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdtype,
@@ -136,8 +141,8 @@ size_t dspark_verify_workspace_size(int B, int gamma, int V, int r);
  *                  the residual (T_b = 0: y = argmax t_j); S = 0 falls back
  *                  to p_j;
  *   every draft accepted: y drawn from p_{ell+1} (the bonus token).
- * The draws are Gumbel-max: y = argmax_v log r(v) + G_v with stream-2 noise
- * at position j (entries of zero mass never win), an exact sampler of r.
+ * The draws are two-level Gumbel-max draws at position j (tile noise stream
+ * 4, entry noise stream 2); entries of zero mass never win.
  * Request b emits n_b + 1 tokens: x_1..x_{n_b}, y.
  *
  *   target        device [n_target_rows, V] float32   packed target logits
@@ -198,10 +203,10 @@ int dspark_schedule(const double *c, int R, int gamma, const double *sps, int sp
 /* Diagnostics                                                         */
 /* ------------------------------------------------------------------ */
 
-/* Writes the library's 32-bit Philox words for vocabulary entries
- * v0 .. v0 + n - 1 of random stream `stream_id` (0: draft noise, 1: accept
- * uniforms, 2: resample noise; v is ignored for stream 1) at position k of
- * request `req` to device [n] uint32 `out`. */
+/* Writes the library's 32-bit Philox words for indices v0 .. v0 + n - 1
+ * (entries for streams 0 and 2, tiles for 3 and 4; ignored for stream 1) of
+ * random stream `stream_id` in [0, 4] at position k of request `req` to
+ * device [n] uint32 `out`. */
 int dspark_debug_random_words(uint64_t seed, uint64_t round_id, int stream_id, int k, int req,
                               int v0, int n, uint32_t *out, void *stream);
 

@@ -36,7 +36,8 @@ def _say(msg):
 @pytest.mark.parametrize("seed", [0, 1, 0xDEADBEEFCAFEF00D])
 def test_device_philox_words_match_oracle(seed):
     for stream, k, req, v0, n in [(0, 1, 0, 0, 4096), (0, 5, 255, 129000, 280), (0, 16, 63, 7, 93),
-                                  (1, 3, 17, 0, 1), (2, 6, 1023, 0, 1)]:
+                                  (1, 3, 17, 0, 1), (2, 6, 1023, 0, 300), (3, 2, 9, 0, 4040),
+                                  (4, 6, 200, 100, 77)]:
         got = np_of(ds.dspark_debug_random_words(seed, 12345, stream, k, req, v0, n)).view(np.uint32)
         want = np.array([oracle.random_word(seed, 12345, stream, k, req, v0 + i) for i in range(n)], np.uint32)
         np.testing.assert_array_equal(got, want)
