@@ -67,10 +67,10 @@ def main():
     if args.copy_probe:
         import torch
         n = args.copy_probe << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+        src = torch.full((n // 4,), 7.0, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)  # an elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
         return

@@ -95,6 +95,14 @@ __device__ __forceinline__ float gumbel2(uint32_t w) {
     return -__builtin_amdgcn_logf(e2);
 }
 
+// v_max3_f32, without the NaN-quieting self-max that IEEE mode makes the
+// compiler put in front of every fmaxf of a loaded or exchanged value.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -190,7 +198,11 @@ struct TileLDS {
     static constexpr int CPR = RB / 16;
     static constexpr int BYTES = kTile * RB;
     static constexpr int SLOTS = kTile * CPR;
+    static constexpr int SW = CPR < 16 ? CPR : 16;  // chunks per swizzle group
     static_assert((CPR & (CPR - 1)) == 0 && SLOTS % 64 == 0, "tile layout");
+    // physical 16-byte chunk of logical chunk c of row m: the low bits of c are
+    // XORed with the row, so the rows that one LDS cycle serves hit distinct banks
+    __device__ static __forceinline__ int chunk(int m, int c) { return (c & ~(SW - 1)) | ((c ^ m) & (SW - 1)); }
 };
 
 // Issue the loads of W2 rows v0 .. v0 + 31 (clamped to V - 1) into `buf`;
@@ -202,7 +214,7 @@ __device__ __forceinline__ void tile_issue(const WT *W2, int v0, int V, uint8_t 
     for (int s0 = wave * 64; s0 < L::SLOTS; s0 += nthreads) {
         const int slot = s0 + lane;
         const int m = slot / L::CPR;
-        const int c = (slot % L::CPR) ^ (m & (L::CPR - 1));
+        const int c = L::chunk(m, slot % L::CPR);
         const int vrow = min(v0 + m, V - 1);
         const uint8_t *g = reinterpret_cast<const uint8_t *>(W2) + size_t(vrow) * L::RB + c * 16;
         __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(buf + s0 * 16),
@@ -212,15 +224,14 @@ __device__ __forceinline__ void tile_issue(const WT *W2, int v0, int V, uint8_t 
 
 // The Markov-bias MFMA tile with the A operand (W2 rows) read from an LDS tile.
 template <int R>
-__device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<uint16_t, R> &ef, const uint8_t *buf, int lane) {
+__device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<uint16_t, R> &ef, const uint8_t *buf, int lane,
+                                                  f32x16_t acc = {}) {
     using L = TileLDS<uint16_t, R>;
     const int m = lane & 31, h = lane >> 5;
     const uint8_t *row = buf + m * L::RB;
-    f32x16_t acc = {};
 #pragma unroll
     for (int s = 0; s < EFrags<uint16_t, R>::S; ++s) {
-        const int c = (2 * s + h) ^ (m & (L::CPR - 1));
-        const uint4 a = *reinterpret_cast<const uint4 *>(row + c * 16);
+        const uint4 a = *reinterpret_cast<const uint4 *>(row + L::chunk(m, 2 * s + h) * 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                       __builtin_bit_cast(bf16x8_t, ef.e[s]), acc, 0, 0, 0);
     }
@@ -228,15 +239,14 @@ __device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<uint16_t, R> &ef,
 }
 
 template <int R>
-__device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<float, R> &ef, const uint8_t *buf, int lane) {
+__device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<float, R> &ef, const uint8_t *buf, int lane,
+                                                  f32x16_t acc = {}) {
     using L = TileLDS<float, R>;
     const int m = lane & 31, h = lane >> 5;
     const uint8_t *row = buf + m * L::RB;
-    f32x16_t acc = {};
 #pragma unroll
     for (int q = 0; q < EFrags<float, R>::Q; ++q) {
-        const int c = (2 * q + h) ^ (m & (L::CPR - 1));
-        const float4 a = *reinterpret_cast<const float4 *>(row + c * 16);
+        const float4 a = *reinterpret_cast<const float4 *>(row + L::chunk(m, 2 * q + h) * 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, ef.e[q].x, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, ef.e[q].y, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, ef.e[q].z, acc, 0, 0, 0);
@@ -300,6 +310,129 @@ __device__ __forceinline__ void load_tile_row(const float *row, int t, int h, in
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) out[i] = load4_masked(row, v0 + 8 * i + 4 * h, V, vec);
+    }
+}
+
+// Two C-initialised MFMA chains over the two 32-row tiles of a stage (buf and
+// buf + one tile), sharing the E fragments; the A fragments are read from LDS
+// a few K-steps ahead of their MFMAs.
+template <int R>
+__device__ __forceinline__ void bias_pair_lds(const EFrags<uint16_t, R> &ef, const uint8_t *buf, int lane,
+                                              f32x16_t &c0, f32x16_t &c1) {
+    using L = TileLDS<uint16_t, R>;
+    constexpr int S = EFrags<uint16_t, R>::S;
+    constexpr int D = S < 3 ? S : 3;  // K-steps in flight
+    const int m = lane & 31, h = lane >> 5;
+    const uint8_t *row = buf + m * L::RB;
+    uint4 a0[D], a1[D];
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+        a0[s] = *reinterpret_cast<const uint4 *>(row + L::chunk(m, 2 * s + h) * 16);
+        a1[s] = *reinterpret_cast<const uint4 *>(row + L::BYTES + L::chunk(m, 2 * s + h) * 16);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint4 x0 = a0[s % D], x1 = a1[s % D];
+        if (s + D < S) {
+            a0[s % D] = *reinterpret_cast<const uint4 *>(row + L::chunk(m, 2 * (s + D) + h) * 16);
+            a1[s % D] = *reinterpret_cast<const uint4 *>(row + L::BYTES + L::chunk(m, 2 * (s + D) + h) * 16);
+        }
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x0),
+                                                     __builtin_bit_cast(bf16x8_t, ef.e[s]), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x1),
+                                                     __builtin_bit_cast(bf16x8_t, ef.e[s]), c1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads D steps ahead of their MFMAs
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void bias_pair_lds(const EFrags<float, R> &ef, const uint8_t *buf, int lane,
+                                              f32x16_t &c0, f32x16_t &c1) {
+    using L = TileLDS<float, R>;
+    constexpr int Q = EFrags<float, R>::Q;
+    constexpr int D = Q < 3 ? Q : 3;
+    const int m = lane & 31, h = lane >> 5;
+    const uint8_t *row = buf + m * L::RB;
+    float4 a0[D], a1[D];
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+        a0[q] = *reinterpret_cast<const float4 *>(row + L::chunk(m, 2 * q + h) * 16);
+        a1[q] = *reinterpret_cast<const float4 *>(row + L::BYTES + L::chunk(m, 2 * q + h) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const float4 x0 = a0[q % D], x1 = a1[q % D];
+        if (q + D < Q) {
+            a0[q % D] = *reinterpret_cast<const float4 *>(row + L::chunk(m, 2 * (q + D) + h) * 16);
+            a1[q % D] = *reinterpret_cast<const float4 *>(row + L::BYTES + L::chunk(m, 2 * (q + D) + h) * 16);
+        }
+        const float4 e = ef.e[q];
+        c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.x, e.x, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.x, e.x, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.y, e.y, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.y, e.y, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.z, e.z, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.z, e.z, c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x0.w, e.w, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.w, e.w, c1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// One 32-entry tile of a logit row in the accumulator layout of the 32x32
+// MFMA: value 4i+j of lane (n, h) is entry v0 + 8i + 4h + j.  Entries at or
+// beyond V read as -inf, so a tile that starts past the row end is all -inf.
+// VEC: the row allows aligned 16-byte loads (V % 4 == 0, 16-byte aligned rows).
+template <bool VEC>
+__device__ __forceinline__ f32x16_t load_acc_tile(const float *row, int v0, int h, int V, bool tail) {
+    f32x16_t c;
+    if (!tail) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 x;
+            if constexpr (VEC) {
+                x = *reinterpret_cast<const float4 *>(row + v0 + 8 * i + 4 * h);
+            } else {
+                const float *q = row + v0 + 8 * i + 4 * h;
+                x = make_float4(q[0], q[1], q[2], q[3]);
+            }
+            c[4 * i] = x.x;
+            c[4 * i + 1] = x.y;
+            c[4 * i + 2] = x.z;
+            c[4 * i + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int v = v0 + 8 * i + 4 * h;
+            if constexpr (VEC) {
+                // V % 4 == 0: a 4-entry group is either wholly inside the row or wholly past it
+                float4 x = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+                if (v < V) x = *reinterpret_cast<const float4 *>(row + v);
+                c[4 * i] = x.x;
+                c[4 * i + 1] = x.y;
+                c[4 * i + 2] = x.z;
+                c[4 * i + 3] = x.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) c[4 * i + j] = (v + j < V) ? row[v + j] : kNegInf;
+            }
+        }
+    }
+    return c;
+}
+
+// Exchange the lane halves of two accumulator tiles (v_permlane32_swap, which
+// swaps lanes 32..63 of its first operand with lanes 0..31 of its second).
+// Before: lane (n, h) holds rows 8i+4h+j of tile a in a and of tile b in b.
+// After: lanes 0..31 hold every row of tile a (a: rows 8i+j, b: rows 8i+4+j)
+// and lanes 32..63 every row of tile b, in the same arrangement.
+__device__ __forceinline__ void swap_halves(f32x16_t &a, f32x16_t &b) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[e]), __float_as_uint(b[e]), false, false);
+        a[e] = __uint_as_float(r[0]);
+        b[e] = __uint_as_float(r[1]);
     }
 }
 

@@ -49,15 +49,173 @@ struct StepParams {
     int32_t *pi;
 };
 
-template <typename WT, int R, bool TRACK2>
-__global__ __launch_bounds__(256) void draft_step_kernel(StepParams p) {
+// Race state of one lane over the tiles it owns: running base-2 logsumexp as
+// (max, sum of 2^(z - max)), and the best and second tile scores.
+struct TileRace {
+    float m, s, best, second;
+    int bt;
+};
+
+// Scores one 32-entry tile held by this lane in (a, b) (logits U + B, -inf past
+// the row end).  Sampled: the tile's logsumexp of z = logit * sc plus its
+// Gumbel noise g; greedy: the tile's largest logit.  The sum is taken against
+// the running maximum, so one rescale per tile keeps the row total.
+template <bool TRACK2>
+__device__ __forceinline__ void race_tile(TileRace &st, const f32x16_t &a, const f32x16_t &b, float sc, bool sampled,
+                                          int t, float g) {
+    float ma = max3f(a[0], a[1], a[2]), mb = max3f(b[0], b[1], b[2]);
+#pragma unroll
+    for (int e = 3; e < 15; e += 2) {
+        ma = max3f(ma, a[e], a[e + 1]);
+        mb = max3f(mb, b[e], b[e + 1]);
+    }
+    const float mx = max3f(max3f(ma, a[15], b[15]), mb, mb);
+    const float mt = mx * sc;
+    const float mn = fmaxf(st.m, mt);
+    const float mg = (mn == kNegInf) ? 0.f : mn;
+    const float nmg = -mg;
+    float s0 = fast_exp2(__builtin_fmaf(a[0], sc, nmg)), s1 = fast_exp2(__builtin_fmaf(a[1], sc, nmg));
+    float s2 = fast_exp2(__builtin_fmaf(b[0], sc, nmg)), s3 = fast_exp2(__builtin_fmaf(b[1], sc, nmg));
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) {
+        s0 += fast_exp2(__builtin_fmaf(a[e], sc, nmg));
+        s1 += fast_exp2(__builtin_fmaf(a[e + 1], sc, nmg));
+        s2 += fast_exp2(__builtin_fmaf(b[e], sc, nmg));
+        s3 += fast_exp2(__builtin_fmaf(b[e + 1], sc, nmg));
+    }
+    const float sum = (s0 + s1) + (s2 + s3);
+    st.s = __builtin_fmaf(st.s, fast_exp2(st.m - mg), sum);
+    st.m = mn;
+    const float Lt = sampled ? mg + fast_log2(sum) + g : mt;
+    if (TRACK2) st.second = fmaxf(st.second, fminf(Lt, st.best));
+    if (Lt > st.best) {
+        st.best = Lt;
+        st.bt = t;
+    }
+}
+
+constexpr int kStepThreads = 512;  // 8 waves: one 32-request block each
+
+// Direct-to-LDS loads of one two-tile stage (64 W2 rows) by the workgroup's
+// 512 threads.  Each thread's slots are fixed, so their source offsets are
+// computed once.
+template <typename WT, int R>
+struct StageDMA {
     using L = TileLDS<WT, R>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::BYTES];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nthreads = p.nw * 64;
+    static constexpr int SLOTS = 2 * L::SLOTS;  // 16-byte slots of a stage
+    static constexpr int J = (SLOTS + kStepThreads - 1) / kStepThreads;
+    uint32_t goff[J];  // byte offset of the slot's source from the stage's first row
+    int row[J];        // stage row (0..63) the slot belongs to
+
+    __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int slot = tid + j * kStepThreads;
+            const int m = slot / L::CPR;
+            row[j] = m;
+            goff[j] = uint32_t(m * L::RB + L::chunk(m, slot % L::CPR) * 16);
+        }
+    }
+    // rows v0 .. v0 + 63; CLAMP repeats row V - 1 for rows past the vocabulary
+    template <bool CLAMP>
+    __device__ __forceinline__ void issue(const WT *W2, int v0, int V, uint8_t *buf, int wave) const {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(W2) + size_t(v0) * L::RB;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int s0 = wave * 64 + j * kStepThreads;  // slot of lane 0, uniform
+            if (J * kStepThreads > SLOTS && s0 >= SLOTS) break;
+            const uint8_t *g = src + goff[j];
+            if (CLAMP) {
+                const int vrow = min(v0 + row[j], V - 1);
+                g = reinterpret_cast<const uint8_t *>(W2) + size_t(vrow) * L::RB + (goff[j] - uint32_t(row[j] * L::RB));
+            }
+            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(buf + s0 * 16), 16, 0, 0);
+        }
+    }
+};
+
+// The U_k entries of a two-tile stage for one wave's 32 requests: 32 rows of
+// 64 floats, staged in a wave-private LDS region by direct loads so that each
+// load instruction covers whole 256-byte row segments, then read back in the
+// MFMA accumulator layout.  In LDS the 16-byte chunk c of row r sits at chunk
+// c ^ (r & 15).  VEC moves 16 bytes a lane (rows allow aligned 16-byte
+// loads), else 4 bytes.
+template <bool VEC>
+struct StageU {
+    static constexpr int ROWB = 2 * kTile * 4;          // bytes of a row segment
+    static constexpr int BYTES = 32 * ROWB;             // one wave's region
+    static constexpr int NI = VEC ? BYTES / 1024 : BYTES / 256;  // load instructions a stage
+    const float *rowp[NI];  // source row of each instruction's lane
+    int col[NI];            // first column of the lane's 16 (or 4) bytes, relative to v0
+
+    __device__ __forceinline__ void init(const float *U, size_t u_stride, int row0, int B, int lane) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            int r, c;
+            if (VEC) {
+                r = 4 * j + (lane >> 4);
+                c = 4 * ((lane & 15) ^ (r & 15));
+            } else {
+                r = j;
+                c = 4 * (((lane >> 2) ^ r) & 15) + (lane & 3);
+            }
+            rowp[j] = U + size_t(min(row0 + r, B - 1)) * u_stride;
+            col[j] = c;
+        }
+    }
+    template <bool CLAMP>
+    __device__ __forceinline__ void issue(int v0, int V, uint8_t *region) const {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            int v = v0 + col[j];
+            if (CLAMP) v = min(v, V - (VEC ? 4 : 1));
+            const void *g = rowp[j] + v;
+            if constexpr (VEC)
+                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 256), 4, 0, 0);
+        }
+    }
+    // accumulator layout: value 4i+j of lane (n, h) is entry 32q + 8i + 4h + j
+    __device__ __forceinline__ void read(const uint8_t *region, int lane, f32x16_t &c0, f32x16_t &c1) const {
+        const int n = lane & 31, h = lane >> 5;
+        const uint8_t *row = region + n * ROWB;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            f32x16_t &c = q ? c1 : c0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = (8 * q + 2 * i + h) ^ (n & 15);
+                const float4 x = *reinterpret_cast<const float4 *>(row + ch * 16);
+                c[4 * i] = x.x;
+                c[4 * i + 1] = x.y;
+                c[4 * i + 2] = x.z;
+                c[4 * i + 3] = x.w;
+            }
+        }
+    }
+};
+
+// One workgroup of 8 waves walks the tiles [t_begin, t_end) of one vocabulary
+// chunk, two tiles per stage: the pair's 64 W2 rows are staged in LDS by
+// direct loads (two named buffers, so that the wait for one stage never waits
+// for the next) and so are the pair's U_k entries (one region per wave,
+// refilled as soon as the wave has read it); the U_k entries seed the MFMA
+// accumulators, and after the two MFMA chains a lane-half swap hands the
+// first tile of the pair to lanes 0..31 and the second to lanes 32..63.  A
+// last stage that runs past the vocabulary is done on its own, after the loop.
+template <typename WT, int R, bool TRACK2, bool VEC>
+__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void draft_step_kernel(StepParams p) {
+    using L = TileLDS<WT, R>;
+    using SU = StageU<VEC>;
+    __shared__ __attribute__((aligned(16))) uint8_t ldsA[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsB[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsU[(kStepThreads / 64) * SU::BYTES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
     const int chunk = lg / p.nbg, bg = lg % p.nbg;
-    const int bb = bg * p.nw + wave;
+    const int bb = bg * (kStepThreads / 64) + wave;
     const bool wave_ok = bb < p.nbb;  // uniform across the wave
     const int n = lane & 31, h = lane >> 5;
     const int b = bb * 32 + n;
@@ -72,75 +230,89 @@ __global__ __launch_bounds__(256) void draft_step_kernel(StepParams p) {
 
     const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
-    ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
-    const float *urow = p.U + size_t(bc) * p.u_stride;
-    const bool vec = p.vec != 0;
+    if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    StageDMA<WT, R> dma;
+    dma.init(tid);
+    SU su;
+    if (wave_ok) su.init(p.U, p.u_stride, bb * 32, p.B, lane);
+    uint8_t *uregion = ldsU + wave * SU::BYTES;
 
     const int t_begin = chunk * p.tiles_per_chunk;
     const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
-    float m_run = kNegInf, s_run = 0.f;
-    float best = kNegInf, second = kNegInf;
-    int bt = t_begin;
+    const int nst = (t_end - t_begin + 1) >> 1;  // stages of two tiles
+    const bool tail = (t_begin + 2 * nst) * kTile > p.V;
+    const int nfull = nst - (tail ? 1 : 0);
+    TileRace st{kNegInf, 0.f, kNegInf, kNegInf, t_begin};
     uint4 tw = make_uint4(0u, 0u, 0u, 0u);
 
-    tile_issue<WT, R>(W2, t_begin * kTile, p.V, lds, nthreads);
-    float4 ucur[4];
-    load_tile_row(urow, t_begin, h, p.V, vec, ucur);
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t (LDS and U) have landed
-        __syncthreads();                // ... and every thread's; the other buffer is free again
-        float4 unext[4];
-        if (t + 1 < t_end) {
-            tile_issue<WT, R>(W2, (t + 1) * kTile, p.V, lds + (buf ^ 1) * L::BYTES, nthreads);
-            load_tile_row(urow, t + 1, h, p.V, vec, unext);
+    // stage at tile t0 (even): U_k from the wave's region, W2 from buf; next_v0
+    // >= 0 refills the region with the next stage's U_k once it has been read
+    auto stage = [&](const uint8_t *buf, int t0, int next_v0, bool masked) __device__ {
+        f32x16_t c0, c1;
+        su.read(uregion, lane, c0, c1);
+        if (next_v0 >= 0) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the region has been read
+            su.template issue<false>(next_v0, p.V, uregion);
         }
-        if (wave_ok) {
-            const f32x16_t acc = bias_tile_lds(ef, lds + buf * L::BYTES, lane);
-            float tv[16];
+        bias_pair_lds(ef, buf, lane, c0, c1);
+        swap_halves(c0, c1);
+        if (masked) {
+            const int vb = (t0 + h) * kTile;  // this lane's tile: c0 rows 8i+j, c1 rows 8i+4+j
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) tv[4 * i + j] = f4get(ucur[i], j) + acc[4 * i + j];
-            float mx = tv[0];
-#pragma unroll
-            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, tv[e]);
-            // this half's share of the tile: max and sum of exp2 in base-2 units
-            const float mh = mx * sc;
-            const float nmh = (mh == kNegInf) ? 0.f : -mh;
-            float sh = 0.f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sh += fast_exp2(__builtin_fmaf(tv[e], sc, nmh));
-            // the whole tile: merge with the other half of the lane pair
-            const float mo = __shfl_xor(mh, 32), so = __shfl_xor(sh, 32);
-            const float mt = fmaxf(mh, mo);
-            const float mts = (mt == kNegInf) ? 0.f : mt;
-            const float st = sh * fast_exp2(mh - mts) + so * fast_exp2(mo - mts);
-            // tile race: logsumexp + tile noise (greedy: the tile's largest logit)
-            if (t == t_begin || (t & 3) == 0)
-                tw = noise_block(kStreamDraftTile, p.k, uint32_t(t) >> 2, uint32_t(b), p.round32, p.key0, p.key1);
-            const float g = gumbel2(u4get(tw, t & 3));
-            const float Lt = sampled ? mt + fast_log2(st) + g : mt;
-            if (TRACK2) second = fmaxf(second, fminf(Lt, best));
-            if (Lt > best) {
-                best = Lt;
-                bt = t;
-            }
-            lse_merge(m_run, s_run, mt, st);
+                for (int j = 0; j < 4; ++j) {
+                    if (vb + 8 * i + j >= p.V) c0[4 * i + j] = kNegInf;
+                    if (vb + 8 * i + 4 + j >= p.V) c1[4 * i + j] = kNegInf;
+                }
         }
-        if (t + 1 < t_end) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ucur[i] = unext[i];
-        }
+        // t0 is even, so both tiles of the pair share one noise block; tile
+        // t0 + h takes word (t0 & 3) + h
+        if (t0 == t_begin || (t0 & 3) == 0)
+            tw = noise_block(kStreamDraftTile, p.k, uint32_t(t0) >> 2, uint32_t(b), p.round32, p.key0, p.key1);
+        const uint32_t w_lo = (t0 & 2) ? tw.z : tw.x, w_hi = (t0 & 2) ? tw.w : tw.y;
+        race_tile<TRACK2>(st, c0, c1, sc, sampled, t0 + h, gumbel2(h ? w_hi : w_lo));
+    };
+    auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
+
+    if (nfull > 0) {
+        dma.template issue<false>(W2, v0_of(0), p.V, ldsA, wave);
+        if (wave_ok) su.template issue<false>(v0_of(0), p.V, uregion);
     }
-    // both lane halves hold the same request state
+    for (int i = 0; i < nfull; i += 2) {
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage i have landed
+        __syncthreads();                // ... and every thread's; ldsB is free again
+        if (i + 1 < nfull) dma.template issue<false>(W2, v0_of(i + 1), p.V, ldsB, wave);
+        if (wave_ok) stage(ldsA, t_begin + 2 * i, i + 1 < nfull ? v0_of(i + 1) : -1, false);
+        if (i + 1 >= nfull) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // stage i + 1 has landed; ldsA is free again
+        if (i + 2 < nfull) dma.template issue<false>(W2, v0_of(i + 2), p.V, ldsA, wave);
+        if (wave_ok) stage(ldsB, t_begin + 2 * (i + 1), i + 2 < nfull ? v0_of(i + 2) : -1, false);
+    }
+    if (tail) {
+        __syncthreads();  // every wave is done with both W2 buffers and its region
+        dma.template issue<true>(W2, v0_of(nfull), p.V, ldsA, wave);
+        if (wave_ok) su.template issue<true>(v0_of(nfull), p.V, uregion);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave_ok) stage(ldsA, t_begin + 2 * nfull, -1, true);
+    }
+    // the two lane halves raced alternate tiles of the same request
+    {
+        const float m2 = __shfl_xor(st.m, 32), s2 = __shfl_xor(st.s, 32);
+        const float b2 = __shfl_xor(st.best, 32), c2 = __shfl_xor(st.second, 32);
+        const int i2 = __shfl_xor(st.bt, 32);
+        lse_merge(st.m, st.s, m2, s2);
+        best_merge(st.best, st.bt, st.second, b2, i2, TRACK2 ? c2 : kNegInf);
+    }
     if (h == 0 && row_ok) {
         const size_t o = size_t(b) * p.nchunk + chunk;
-        p.pm[o] = m_run;
-        p.ps[o] = s_run;
-        p.pb[o] = best;
-        p.pi[o] = bt;
-        if (TRACK2) p.p2[o] = second;
+        p.pm[o] = st.m;
+        p.ps[o] = st.s;
+        p.pb[o] = st.best;
+        p.pi[o] = st.bt;
+        if (TRACK2) p.p2[o] = st.second;
     }
 }
 
@@ -259,10 +431,18 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         sp.p2 = w.p2;
         sp.pi = w.pi;
         int t = prof_begin("draft_step", s);
-        if (track2)
-            hipLaunchKernelGGL((draft_step_kernel<WT, R, true>), dim3(pl.blocks), dim3(64 * pl.nw), 0, s, sp);
-        else
-            hipLaunchKernelGGL((draft_step_kernel<WT, R, false>), dim3(pl.blocks), dim3(64 * pl.nw), 0, s, sp);
+        const dim3 grid(pl.blocks), block(kStepThreads);
+        if (track2) {
+            if (vec)
+                hipLaunchKernelGGL((draft_step_kernel<WT, R, true, true>), grid, block, 0, s, sp);
+            else
+                hipLaunchKernelGGL((draft_step_kernel<WT, R, true, false>), grid, block, 0, s, sp);
+        } else {
+            if (vec)
+                hipLaunchKernelGGL((draft_step_kernel<WT, R, false, true>), grid, block, 0, s, sp);
+            else
+                hipLaunchKernelGGL((draft_step_kernel<WT, R, false, false>), grid, block, 0, s, sp);
+        }
         prof_end(t, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -304,21 +484,25 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
 
 }  // namespace
 
-DraftPlan draft_plan(int B, int V) {
+DraftPlan tile_walk_plan(int B, int V, int nw_max, long long target_blocks, int align) {
     DraftPlan p{};
     p.nbb = (B + 31) / 32;
-    p.nw = std::min(4, p.nbb);
+    p.nw = std::min(nw_max, p.nbb);
     p.nbg = (p.nbb + p.nw - 1) / p.nw;
     p.ntiles = (V + kTile - 1) / kTile;
-    // about 2048 waves in flight over the 1024 SIMDs; chunks of a multiple of
-    // 4 tiles share the tile-noise Philox blocks
-    const long long work = 1LL * p.nbb * p.ntiles;
-    long long tpc = std::max<long long>(1, (work + 2047) / 2048);
-    if (tpc > 2) tpc = (tpc + 3) / 4 * 4;
-    p.tiles_per_chunk = int(std::min<long long>(tpc, p.ntiles));
+    long long tpc = std::max<long long>(1, (1LL * p.ntiles * p.nbg + target_blocks - 1) / target_blocks);
+    tpc = (tpc + align - 1) / align * align;
+    p.tiles_per_chunk = int(std::min<long long>(tpc, (p.ntiles + align - 1) / align * align));
     p.nchunk = (p.ntiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk;
     p.blocks = p.nchunk * p.nbg;
     return p;
+}
+
+DraftPlan draft_plan(int B, int V) {
+    // 8-wave workgroups holding two 2-tile LDS stages (64 KB at bf16 rank 256)
+    // and up to 256 registers a lane: one workgroup per CU, so about 256
+    // workgroups; chunks are whole 2-tile stages
+    return tile_walk_plan(B, V, kStepThreads / 64, 256, 2);
 }
 
 DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes) {

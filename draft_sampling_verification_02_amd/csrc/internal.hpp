@@ -35,7 +35,7 @@ struct Carve {
 // through LDS; `nbg` workgroups cover the request blocks of a chunk.
 struct DraftPlan {
     int nbb;              // request blocks of 32 rows
-    int nw;               // waves per workgroup = min(4, nbb)
+    int nw;               // waves per workgroup
     int nbg;              // workgroups per vocabulary chunk = ceil(nbb / nw)
     int ntiles;           // 32-entry vocabulary tiles
     int tiles_per_chunk;  // tiles one workgroup walks
@@ -43,6 +43,9 @@ struct DraftPlan {
     int blocks;           // workgroups = nchunk * nbg
 };
 DraftPlan draft_plan(int B, int V);
+// Walk of up to nw_max waves per workgroup, sized for about target_blocks
+// workgroups; tiles_per_chunk is a multiple of `align`.
+DraftPlan tile_walk_plan(int B, int V, int nw_max, long long target_blocks, int align);
 
 struct DraftWork {
     float *pm, *ps, *pb, *p2;  // [B, nchunk] partial max, sum, best score, second score

@@ -760,7 +760,10 @@ VerifyPlan verify_plan(int B, int gamma, int V) {
     VerifyPlan p{};
     p.rows_max = B * (gamma + 1);
     p.nbb = (B + 31) / 32;
-    p.tile = draft_plan(B, V);
+    // about 2048 waves of up to 4 over the 1024 SIMDs; chunks of a multiple of
+    // 4 tiles share the tile-noise Philox blocks
+    const long long nbb = (B + 31) / 32, nw = std::min<long long>(4, nbb);
+    p.tile = tile_walk_plan(B, V, 4, std::max<long long>(1, 2048 / nw), 4);
     // the residual and bonus lists hold at most B requests but each rounds up to 32
     p.draw_nbg = (p.nbb + 1 + p.tile.nw - 1) / p.tile.nw;
     p.draw_blocks = p.tile.nchunk * p.draw_nbg;
