@@ -69,7 +69,8 @@ hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork 
 // ---- verify ----------------------------------------------------------
 
 struct VerifyPlan {
-    int rows_max;     // B * (gamma + 1)
+    int nseg;         // vocabulary segments a target row is split into by the position passes
+    int seg_len;      // entries per segment (a multiple of 4)
     int nbb;          // ceil(B / 32)
     DraftPlan tile;   // vocabulary walk of the resample / bonus draw
     int draw_nbg;     // workgroups per chunk of the draw (room for both lists)
@@ -78,17 +79,20 @@ struct VerifyPlan {
 VerifyPlan verify_plan(int B, int gamma, int V);
 
 struct VerifyWork {
-    int32_t *status;     // [4] device status flags, rows_total, n_resid, n_bonus
+    int32_t *status;     // [4] device status flags, -, n_resid, n_bonus
     int32_t *off;        // [B + 1] packed row offsets in use
-    int32_t *row_req;    // [rows_max] request of each packed row (-1: none)
-    int32_t *row_pos;    // [rows_max] position k (1-based)
-    float *row_lse2;     // [rows_max] logsumexp of t*s in log2 units
-    int32_t *row_amax;   // [rows_max] lowest-index argmax
-    float *row_tx2;      // [rows_max] t(x_k)*s (log2 units) for tested rows
-    int32_t *mode;       // [B] 0 done (greedy), 1 residual draw, 2 bonus draw, -1 invalid
+    // position passes, double buffered by pass parity: pass j reads the half
+    // pass j - 1 wrote
+    int32_t *act;        // [2, B] 1: the request's row of that pass was reduced
+    float *seg_m, *seg_s, *seg_v;  // [2, B, nseg] per-segment max, sum of 2^(z - max), best value
+    int32_t *seg_i;      // [2, B, nseg] per-segment lowest-index argmax
+    float *seg_tx;       // [2, B] t(x_j) / T in log2 units for the accept test
+    float *fin_lse2;     // [B] logsumexp (log2 units) of the row the draw uses
+    int32_t *mode;       // [B] 0 done, 1 residual draw, 2 bonus draw, -1 invalid
     int32_t *jpos;       // [B] position of the emitted non-draft token
-    int32_t *resid_list; // [B] requests taking the residual draw, ascending
-    int32_t *bonus_list; // [B] sampled requests taking the bonus draw, ascending
+    int32_t *slot;       // [B] draw slot: list index, + B for the bonus list
+    int32_t *resid_list; // [B] requests taking the residual draw, in arrival order
+    int32_t *bonus_list; // [B] sampled requests taking the bonus draw, in arrival order
     // draw partials per (list slot, vocabulary chunk); residual slots [0, B), bonus slots [B, 2B)
     float *dw_sum;       // residual mass
     float *dw_bl;        // best tile score of the level-1 race

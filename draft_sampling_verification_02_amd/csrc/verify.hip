@@ -15,14 +15,14 @@
 //
 // Kernels, in launch order:
 //   verify_prep      1 workgroup: packed row offsets (scan of 1 + ell, or the
-//                    caller's, checked), row -> (request, position) map.
-//   verify_rowstats  1 workgroup per packed target row: one coalesced
-//                    streaming pass for logsumexp(t / T) in base 2, the
-//                    lowest-index argmax and t(x_k).
-//   verify_accept    1 workgroup: per request the accept tests u*q < p in
-//                    order, n = leading accepts, greedy outputs, the output
-//                    offsets and the ascending lists of residual and bonus
-//                    requests.
+//                    caller's, checked), output defaults, pass state.
+//   verify_pass      once per position j = 1..gamma+1, over the requests
+//                    still testing at j: the row's vocabulary is split into
+//                    segments, one workgroup streams each for logsumexp(t / T)
+//                    in base 2 and the lowest-index argmax, and the last
+//                    segment to finish merges them and runs the accept test
+//                    u*q < p at j (or takes the bonus row).  A request stops
+//                    at its first rejection, so rows past it are never read.
 //   verify_draw      level 1: waves of 32 listed requests walk vocabulary
 //                    chunks; residual rows recompute q_j with the draft's
 //                    LDS-staged MFMA bias tile and sum max(p_j - q_j, 0) per
@@ -30,7 +30,8 @@
 //                    race with their noise.
 //   verify_finish    level 2: one wave per drawing request merges the chunk
 //                    partials, recomputes the winning tile's 32 entries and
-//                    races them; writes the emitted token and S.
+//                    races them; writes the emitted token and S.  One more
+//                    workgroup scans the emitted counts into out_offsets.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -95,8 +96,10 @@ __device__ int block_exclusive_scan(int v, int *lds, int *total) {
 
 struct PrepParams {
     const int32_t *ell, *row_offsets;
-    int B, gamma, rows_max, n_target_rows;
-    int32_t *status, *off, *row_req, *row_pos, *mode;
+    int B, gamma, n_target_rows;
+    int32_t *status, *off, *mode;
+    int32_t *n_accept_out, *tokens_out;
+    float *diag_out, *resid_out;
 };
 
 __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
@@ -104,10 +107,7 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
     const int t = threadIdx.x;
     const int seg = (p.B + 1023) / 1024;
     const int b0 = min(p.B, t * seg), b1 = min(p.B, b0 + seg);
-    for (int i = t; i < p.rows_max; i += 1024) {
-        p.row_req[i] = -1;
-        p.row_pos[i] = 0;
-    }
+    const float nan = __builtin_nanf("");
     int flags = 0;
     int local = 0;
     for (int b = b0; b < b1; ++b) {
@@ -134,12 +134,18 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
                 flags |= kStatusBadOffsets;
             }
         }
-        if (ok && (o + e + 1 > p.n_target_rows || o + e + 1 > p.rows_max)) {
+        if (ok && o + e + 1 > p.n_target_rows) {
             ok = false;
             flags |= kStatusRowsOutOfRange;
         }
         p.off[b] = ok ? o : 0;
         p.mode[b] = ok ? kModeDone : -1;
+        p.n_accept_out[b] = -1;  // set by the pass that ends the request
+        int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
+        for (int i = 0; i <= p.gamma; ++i) tok[i] = -1;
+        if (p.diag_out)
+            for (int i = 0; i < 2 * (p.gamma + 1); ++i) p.diag_out[size_t(b) * 2 * (p.gamma + 1) + i] = nan;
+        if (p.resid_out) p.resid_out[b] = -1.f;
         base += 1 + e;
     }
     if (t == 1023) p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : total;
@@ -152,58 +158,155 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
     }
     if (t == 0) {
         p.status[0] = lds[0];
-        p.status[1] = min(p.rows_max, p.row_offsets ? max(0, p.row_offsets[p.B]) : total);
+        p.status[1] = 0;
         p.status[2] = 0;
         p.status[3] = 0;
     }
-    __syncthreads();  // every row_req entry is initialised before the fill below
-    for (int b = b0; b < b1; ++b) {
-        if (p.mode[b] < 0) continue;
-        const int e = p.ell[b];
-        const int o = p.off[b];
-        for (int i = 0; i <= e; ++i) {
-            p.row_req[o + i] = b;
-            p.row_pos[o + i] = i + 1;
-        }
-    }
 }
 
-// ------------------------------------------------------------------ rowstats
+// ------------------------------------------------------------------ position pass
 
-struct RowStatsParams {
+struct PassParams {
     const float *target;
     const int32_t *x, *ell;
-    const float *temperature;
-    int V, gamma, vec;
-    const int32_t *status, *row_req, *row_pos;
-    float *row_lse2, *row_tx2;
-    int32_t *row_amax;
+    const float *qx, *temperature;
+    int B, gamma, V, j, nseg, seg_len, vec;
+    uint32_t key0, key1, round32;
+    const int32_t *off;
+    // pass j reads what pass j - 1 left (row j - 1 of every request it reduced)
+    // and writes its own row j into the other half of each double buffer
+    const int32_t *act_in;  // [B] 1: row j - 1 was reduced
+    const float *pm_in, *ps_in, *pv_in, *tx_in;
+    const int32_t *pi_in;
+    int32_t *act_out;
+    float *pm_out, *ps_out, *pv_out, *tx_out;
+    int32_t *pi_out;
+    int32_t *status, *mode, *jpos, *slot, *resid_list, *bonus_list;
+    float *fin_lse2;
+    int32_t *n_accept_out, *tokens_out;
+    float *diag_out;
 };
 
-// One workgroup streams one packed target row: every thread keeps its own
-// running max / sum of exp2 (base 2) and argmax over batches of eight float4
-// loads, and the workgroup merges the 256 states at the end.
-__global__ __launch_bounds__(256) void verify_rowstats_kernel(RowStatsParams p) {
-    const int row = blockIdx.x;
-    if (row >= p.status[1]) return;
-    const int req = p.row_req[row];
-    if (req < 0) return;
+// Position k = j - 1 of request b, from its merged row statistics: the accept
+// test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
+// request takes the same decision; only `writer` stores it.  Returns whether
+// the request goes on to position j.
+__device__ bool pass_decide(const PassParams &p, int b, int k, bool sampled, float lse2, int amax, float tx2,
+                            bool writer) {
+    const int L = p.ell[b];
+    int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
+    bool bonus = false;
+    if (k <= L) {
+        const int xk = p.x[size_t(b) * p.gamma + k - 1];
+        bool acc;
+        float pk, ratio;
+        if (sampled) {
+            pk = fast_exp2(tx2 - lse2);
+            const float qk = p.qx[size_t(b) * p.gamma + k - 1];
+            const float u = uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
+            acc = u * qk < pk;
+            ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
+        } else {
+            acc = (xk == amax);
+            pk = acc ? 1.f : 0.f;
+            ratio = pk;
+        }
+        if (writer && p.diag_out) {
+            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = pk;
+            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = ratio;
+        }
+        if (acc) {
+            if (writer) tok[k - 1] = xk;
+            return true;
+        }
+        if (writer) p.n_accept_out[b] = k - 1;
+    } else {
+        if (writer) p.n_accept_out[b] = L;
+        bonus = true;
+    }
+    if (!writer) return false;
+    p.jpos[b] = k;
+    if (!sampled) {
+        tok[k - 1] = amax;
+        p.mode[b] = kModeDone;
+        return false;
+    }
+    p.fin_lse2[b] = lse2;
+    if (bonus) {
+        const int e = atomicAdd(&p.status[3], 1);
+        p.bonus_list[e] = b;
+        p.slot[b] = p.B + e;
+        p.mode[b] = kModeBonus;
+    } else {
+        const int e = atomicAdd(&p.status[2], 1);
+        p.resid_list[e] = b;
+        p.slot[b] = e;
+        p.mode[b] = kModeResidual;
+    }
+    return false;
+}
+
+// Pass j = 1..gamma+2, one workgroup per (request, vocabulary segment).
+// First the request's position j - 1 is decided from the segment statistics
+// pass j - 1 wrote; a request that goes on streams segment sg of its row j:
+// every thread keeps its own running max / sum of exp2 and argmax over
+// batches of eight float4 loads, and the workgroup merges them.
+__global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
+    const int b = blockIdx.x / p.nseg, sg = blockIdx.x % p.nseg;
+    const int j = p.j;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float T = p.temperature[req];
-    const float sc = T > 0.f ? kLog2e / T : 1.0f;
-    const float *trow = p.target + size_t(row) * p.V;
+    const bool writer = sg == 0;
+    if (p.mode[b] < 0 || (j > 1 && p.act_in[b] == 0)) {
+        if (writer && tid == 0) p.act_out[b] = 0;
+        return;
+    }
+    const float T = p.temperature[b];
+    const bool sampled = T > 0.f;
+    const float sc = sampled ? kLog2e / T : 1.0f;
+    __shared__ int go_on;
+    if (j > 1) {
+        if (wave == 0) {
+            float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
+            int i2 = 0x7fffffff;
+            for (int c = lane; c < p.nseg; c += 64) {
+                const size_t o = size_t(b) * p.nseg + c;
+                lse_merge(mm, s2, p.pm_in[o], p.ps_in[o]);
+                argmax_merge(v2, i2, p.pv_in[o], p.pi_in[o]);
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                lse_merge(mm, s2, __shfl_xor(mm, o), __shfl_xor(s2, o));
+                argmax_merge(v2, i2, __shfl_xor(v2, o), __shfl_xor(i2, o));
+            }
+            if (lane == 0) {
+                const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(s2);
+                go_on = pass_decide(p, b, j - 1, sampled, lse2, min(max(i2, 0), p.V - 1), p.tx_in[b], writer);
+            }
+        }
+        __syncthreads();
+        if (!go_on) {
+            if (writer && tid == 0) p.act_out[b] = 0;
+            return;
+        }
+    }
+    if (j > p.ell[b] + 1) {  // nothing left to reduce (the decision above ended it)
+        if (writer && tid == 0) p.act_out[b] = 0;
+        return;
+    }
+    const float *trow = p.target + size_t(p.off[b] + j - 1) * p.V;
+    const int v_lo = sg * p.seg_len, v_hi = min(p.V, v_lo + p.seg_len);
     float m = kNegInf, s = 0.f, av = kNegInf;
     int ai = 0x7fffffff;
     if (p.vec) {
         const float4 *r4 = reinterpret_cast<const float4 *>(trow);
-        const int nq = p.V >> 2;
+        const int q_hi = v_hi >> 2;
         constexpr int U = 8;
-        for (int q0 = tid; q0 < nq; q0 += 256 * U) {
+        for (int q0 = (v_lo >> 2) + tid; q0 < q_hi; q0 += 256 * U) {
             float4 xs[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int q = q0 + 256 * u;
-                xs[u] = q < nq ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+                xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
             }
             float bm = kNegInf;
 #pragma unroll
@@ -228,17 +331,17 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(RowStatsParams p) 
             for (int u = 0; u < U; ++u) {
                 const int v = 4 * (q0 + 256 * u);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float xv = f4get(xs[u], j);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float xv = f4get(xs[u], jj);
                     if (xv > av) {
                         av = xv;
-                        ai = v + j;
+                        ai = v + jj;
                     }
                 }
             }
         }
     } else {
-        for (int v = tid; v < p.V; v += 256) {
+        for (int v = v_lo + tid; v < v_hi; v += 256) {
             const float xv = trow[v] * sc;
             const float mn = fmaxf(m, xv);
             if (mn != kNegInf) {
@@ -267,120 +370,21 @@ __global__ __launch_bounds__(256) void verify_rowstats_kernel(RowStatsParams p) 
     }
     __syncthreads();
     if (tid == 0) {
-        float mm = sm[0], s2 = ss[0], v2 = sv[0];
-        int i2 = si[0];
         for (int w = 1; w < 4; ++w) {
-            lse_merge(mm, s2, sm[w], ss[w]);
-            argmax_merge(v2, i2, sv[w], si[w]);
+            lse_merge(sm[0], ss[0], sm[w], ss[w]);
+            argmax_merge(sv[0], si[0], sv[w], si[w]);
         }
-        p.row_lse2[row] = (mm == kNegInf) ? kNegInf : mm + fast_log2(s2);
-        p.row_amax[row] = min(max(i2, 0), p.V - 1);
-        const int pos = p.row_pos[row];
-        if (pos <= p.ell[req]) {
-            int xk = p.x[size_t(req) * p.gamma + pos - 1];
-            xk = min(max(xk, 0), p.V - 1);
-            p.row_tx2[row] = trow[xk] * sc;
-        } else {
-            p.row_tx2[row] = kNegInf;
+        const size_t o = size_t(b) * p.nseg + sg;
+        p.pm_out[o] = sm[0];
+        p.ps_out[o] = ss[0];
+        p.pv_out[o] = sv[0];
+        p.pi_out[o] = si[0];
+        if (writer) p.act_out[b] = 1;
+        // t(x_j) for the accept test at j, from the segment that holds x_j
+        if (sampled && j <= p.ell[b]) {
+            const int xk = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
+            if (xk >= v_lo && xk < v_hi) p.tx_out[b] = trow[xk] * sc;
         }
-    }
-}
-
-// ------------------------------------------------------------------ accept
-
-struct AcceptParams {
-    const int32_t *ell, *x;
-    const float *qx, *temperature;
-    int B, gamma;
-    uint32_t key0, key1, round32;
-    int32_t *status;
-    const int32_t *off;
-    const float *row_lse2, *row_tx2;
-    const int32_t *row_amax;
-    int32_t *mode, *jpos, *resid_list, *bonus_list;
-    int32_t *n_accept_out, *tokens_out, *out_offsets;
-    float *diag_out, *resid_out;
-};
-
-__global__ __launch_bounds__(1024) void verify_accept_kernel(AcceptParams p) {
-    __shared__ int lds[1024];
-    const int t = threadIdx.x;
-    const int seg = (p.B + 1023) / 1024;
-    const int b0 = min(p.B, t * seg), b1 = min(p.B, b0 + seg);
-    const float nan = __builtin_nanf("");
-    int emitted = 0, nres = 0, nbon = 0;
-    for (int b = b0; b < b1; ++b) {
-        int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
-        for (int i = 0; i <= p.gamma; ++i) tok[i] = -1;
-        if (p.diag_out)
-            for (int i = 0; i < 2 * (p.gamma + 1); ++i) p.diag_out[size_t(b) * 2 * (p.gamma + 1) + i] = nan;
-        if (p.resid_out) p.resid_out[b] = -1.f;
-        if (p.mode[b] < 0) {
-            p.n_accept_out[b] = -1;
-            continue;
-        }
-        const int L = p.ell[b];
-        const int o = p.off[b];
-        const bool sampled = p.temperature[b] > 0.f;
-        int n = 0;
-        bool rejected = false;
-        for (int k = 1; k <= L; ++k) {
-            const int row = o + k - 1;
-            const int xk = p.x[size_t(b) * p.gamma + k - 1];
-            bool acc;
-            float pk, ratio;
-            if (sampled) {
-                pk = fast_exp2(p.row_tx2[row] - p.row_lse2[row]);
-                const float qk = p.qx[size_t(b) * p.gamma + k - 1];
-                const float u =
-                    uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
-                acc = u * qk < pk;
-                ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
-            } else {
-                acc = (xk == p.row_amax[row]);
-                pk = acc ? 1.f : 0.f;
-                ratio = pk;
-            }
-            if (p.diag_out) {
-                p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = pk;
-                p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = ratio;
-            }
-            if (!acc) {
-                rejected = true;
-                break;
-            }
-            tok[k - 1] = xk;
-            n = k;
-        }
-        p.n_accept_out[b] = n;
-        p.jpos[b] = n + 1;
-        emitted += n + 1;
-        if (!sampled) {
-            tok[n] = p.row_amax[o + n];
-            p.mode[b] = kModeDone;
-        } else if (rejected) {
-            p.mode[b] = kModeResidual;
-            ++nres;
-        } else {
-            p.mode[b] = kModeBonus;
-            ++nbon;
-        }
-    }
-    int tot_emit = 0, tot_res = 0, tot_bon = 0;
-    const int base_emit = block_exclusive_scan<1024>(emitted, lds, &tot_emit);
-    const int base_res = block_exclusive_scan<1024>(nres, lds, &tot_res);
-    const int base_bon = block_exclusive_scan<1024>(nbon, lds, &tot_bon);
-    int e = base_emit, r = base_res, q = base_bon;
-    for (int b = b0; b < b1; ++b) {
-        if (p.out_offsets) p.out_offsets[b] = e;
-        if (p.mode[b] >= 0) e += p.n_accept_out[b] + 1;
-        if (p.mode[b] == kModeResidual) p.resid_list[r++] = b;
-        if (p.mode[b] == kModeBonus) p.bonus_list[q++] = b;
-    }
-    if (t == 0) {
-        if (p.out_offsets) p.out_offsets[p.B] = tot_emit;
-        p.status[2] = tot_res;
-        p.status[3] = tot_bon;
     }
 }
 
@@ -396,7 +400,7 @@ struct DrawParams {
     int vec_u, vec_t;
     uint32_t key0, key1, round32;
     const int32_t *status, *resid_list, *bonus_list, *jpos, *off;
-    const float *row_lse2;
+    const float *fin_lse2;
     float *dw_sum, *dw_bl;
     int32_t *dw_bt;
 };
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(DrawParams p) {
     const float sc = wave_ok ? kLog2e / p.temperature[req] : 1.0f;
     const int trow_i = wave_ok ? p.off[req] + j - 1 : 0;
     const float *trow = p.target + size_t(trow_i) * p.V;
-    const float lse2t = wave_ok ? p.row_lse2[trow_i] : 0.f;
+    const float lse2t = wave_ok ? p.fin_lse2[req] : 0.f;
     const bool vec_t = p.vec_t != 0, vec_u = p.vec_u != 0;
 
     const WT *W2 = static_cast<const WT *>(p.W2);
@@ -543,25 +547,13 @@ struct FinishParams {
     const float *lse_q, *temperature;
     int B, gamma, V, nchunk, ntiles;
     uint32_t key0, key1, round32;
-    const int32_t *status, *mode, *n_accept, *resid_list, *bonus_list, *off;
-    const float *row_lse2;
+    const int32_t *status, *mode, *n_accept, *slot, *off;
+    const float *fin_lse2;
     const float *dw_sum, *dw_bl;
     const int32_t *dw_bt;
-    int32_t *tokens_out;
+    int32_t *tokens_out, *out_offsets;
     float *resid_out;
 };
-
-__device__ int list_position(const int32_t *list, int n, int b) {
-    int lo = 0, hi = n - 1;
-    while (lo <= hi) {
-        const int mid = (lo + hi) >> 1;
-        const int v = list[mid];
-        if (v == b) return mid;
-        if (v < b) lo = mid + 1;
-        else hi = mid - 1;
-    }
-    return 0;
-}
 
 // Winner of an entry race held by the 32 lower lanes of the wave.
 __device__ __forceinline__ int wave_race(float score, int v) {
@@ -573,15 +565,37 @@ __device__ __forceinline__ int wave_race(float score, int v) {
 }
 
 // Level 2 of the draws, and the emitted token: one wave per drawing request.
+// Exclusive scan of the emitted counts n_b + 1 (0 for a request that failed
+// its check) into out_offsets, by one workgroup of 256 threads.
+__device__ void scan_out_offsets(const FinishParams &p) {
+    __shared__ int lds[256];
+    const int t = threadIdx.x;
+    const int seg = (p.B + 255) / 256;
+    const int b0 = min(p.B, t * seg), b1 = min(p.B, b0 + seg);
+    int local = 0;
+    for (int b = b0; b < b1; ++b)
+        if (p.mode[b] >= 0) local += p.n_accept[b] + 1;
+    int total = 0;
+    int e = block_exclusive_scan<256>(local, lds, &total);
+    for (int b = b0; b < b1; ++b) {
+        p.out_offsets[b] = e;
+        if (p.mode[b] >= 0) e += p.n_accept[b] + 1;
+    }
+    if (t == 0) p.out_offsets[p.B] = total;
+}
+
 template <typename WT, int R>
 __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
+    if (blockIdx.x == gridDim.x - 1) {  // the extra workgroup
+        if (p.out_offsets) scan_out_offsets(p);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= p.B) return;
     const int mode = p.mode[b];
     if (mode != kModeResidual && mode != kModeBonus) return;
-    const int slot = (mode == kModeResidual) ? list_position(p.resid_list, p.status[2], b)
-                                             : p.B + list_position(p.bonus_list, p.status[3], b);
+    const int slot = p.slot[b];
     float S = 0.f, bl = kNegInf;
     int tile = 0x7fffffff;
     for (int c = lane; c < p.nchunk; c += 64) {
@@ -597,7 +611,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     const float sc = kLog2e / p.temperature[b];
     const int trow_i = p.off[b] + j - 1;
     const float *trow = p.target + size_t(trow_i) * p.V;
-    const float lse2t = p.row_lse2[trow_i];
+    const float lse2t = p.fin_lse2[b];
     const int i = lane & 31, h = lane >> 5;
     const bool use_res = mode == kModeResidual && S > 0.f && bl > kNegInf;
     if (mode == kModeResidual && !use_res) {
@@ -653,8 +667,8 @@ template <typename WT, int R>
 hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyWork &w, hipStream_t s) {
     hipError_t e;
     {
-        PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, pl.rows_max, a.n_target_rows,
-                      w.status, w.off, w.row_req, w.row_pos, w.mode};
+        PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, a.n_target_rows, w.status, w.off,
+                      w.mode, a.n_accept_out, a.tokens_out, a.diag_out, a.resid_out};
         int t = prof_begin("verify_prep", s);
         hipLaunchKernelGGL(verify_prep_kernel, dim3(1), dim3(1024), 0, s, pp);
         prof_end(t, s);
@@ -662,20 +676,52 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
-    {
-        RowStatsParams rp{a.target, a.x, a.ell, a.temperature, a.V, a.gamma, vec_t,
-                          w.status, w.row_req, w.row_pos, w.row_lse2, w.row_tx2, w.row_amax};
-        int t = prof_begin("verify_rowstats", s);
-        hipLaunchKernelGGL(verify_rowstats_kernel, dim3(pl.rows_max), dim3(256), 0, s, rp);
-        prof_end(t, s);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
-        AcceptParams ap{a.ell, a.x, a.qx, a.temperature, a.B, a.gamma, a.key0, a.key1, a.round32,
-                        w.status, w.off, w.row_lse2, w.row_tx2, w.row_amax, w.mode, w.jpos, w.resid_list,
-                        w.bonus_list, a.n_accept_out, a.tokens_out, a.out_offsets, a.diag_out, a.resid_out};
-        int t = prof_begin("verify_accept", s);
-        hipLaunchKernelGGL(verify_accept_kernel, dim3(1), dim3(1024), 0, s, ap);
+    for (int j = 1; j <= a.gamma + 2; ++j) {
+        const int in = (j - 1) & 1, out = j & 1;  // double-buffer halves
+        const size_t ns = size_t(a.B) * pl.nseg;
+        PassParams pp{};
+        pp.target = a.target;
+        pp.x = a.x;
+        pp.ell = a.ell;
+        pp.qx = a.qx;
+        pp.temperature = a.temperature;
+        pp.B = a.B;
+        pp.gamma = a.gamma;
+        pp.V = a.V;
+        pp.j = j;
+        pp.nseg = pl.nseg;
+        pp.seg_len = pl.seg_len;
+        pp.vec = vec_t;
+        pp.key0 = a.key0;
+        pp.key1 = a.key1;
+        pp.round32 = a.round32;
+        pp.off = w.off;
+        pp.act_in = w.act + size_t(in) * a.B;
+        pp.pm_in = w.seg_m + in * ns;
+        pp.ps_in = w.seg_s + in * ns;
+        pp.pv_in = w.seg_v + in * ns;
+        pp.pi_in = w.seg_i + in * ns;
+        pp.tx_in = w.seg_tx + size_t(in) * a.B;
+        pp.act_out = w.act + size_t(out) * a.B;
+        pp.pm_out = w.seg_m + out * ns;
+        pp.ps_out = w.seg_s + out * ns;
+        pp.pv_out = w.seg_v + out * ns;
+        pp.pi_out = w.seg_i + out * ns;
+        pp.tx_out = w.seg_tx + size_t(out) * a.B;
+        pp.status = w.status;
+        pp.mode = w.mode;
+        pp.jpos = w.jpos;
+        pp.slot = w.slot;
+        pp.resid_list = w.resid_list;
+        pp.bonus_list = w.bonus_list;
+        pp.fin_lse2 = w.fin_lse2;
+        pp.n_accept_out = a.n_accept_out;
+        pp.tokens_out = a.tokens_out;
+        pp.diag_out = a.diag_out;
+        static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
+                                            "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
+        int t = prof_begin(names[std::min(j, 8) - 1], s);
+        hipLaunchKernelGGL(verify_pass_kernel, dim3(size_t(a.B) * pl.nseg), dim3(256), 0, s, pp);
         prof_end(t, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -707,7 +753,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.bonus_list = w.bonus_list;
         dp.jpos = w.jpos;
         dp.off = w.off;
-        dp.row_lse2 = w.row_lse2;
+        dp.fin_lse2 = w.fin_lse2;
         dp.dw_sum = w.dw_sum;
         dp.dw_bl = w.dw_bl;
         dp.dw_bt = w.dw_bt;
@@ -737,17 +783,17 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         fp.status = w.status;
         fp.mode = w.mode;
         fp.n_accept = a.n_accept_out;
-        fp.resid_list = w.resid_list;
-        fp.bonus_list = w.bonus_list;
+        fp.slot = w.slot;
         fp.off = w.off;
-        fp.row_lse2 = w.row_lse2;
+        fp.fin_lse2 = w.fin_lse2;
         fp.dw_sum = w.dw_sum;
         fp.dw_bl = w.dw_bl;
         fp.dw_bt = w.dw_bt;
         fp.tokens_out = a.tokens_out;
+        fp.out_offsets = a.out_offsets;
         fp.resid_out = a.resid_out;
         int t = prof_begin("verify_finish", s);
-        hipLaunchKernelGGL((verify_finish_kernel<WT, R>), dim3((a.B + 3) / 4), dim3(256), 0, s, fp);
+        hipLaunchKernelGGL((verify_finish_kernel<WT, R>), dim3((a.B + 3) / 4 + 1), dim3(256), 0, s, fp);
         prof_end(t, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -757,8 +803,12 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
 }  // namespace
 
 VerifyPlan verify_plan(int B, int gamma, int V) {
+    (void)gamma;
     VerifyPlan p{};
-    p.rows_max = B * (gamma + 1);
+    // at most 16 segments a row, each a whole number of float4 groups
+    const int n4 = (V + 3) / 4;
+    p.seg_len = 4 * ((n4 + 15) / 16);
+    p.nseg = (V + p.seg_len - 1) / p.seg_len;
     p.nbb = (B + 31) / 32;
     // about 2048 waves of up to 4 over the 1024 SIMDs; chunks of a multiple of
     // 4 tiles share the tile-noise Philox blocks
@@ -777,13 +827,17 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     VerifyWork w{};
     w.status = c.take<int32_t>(4);
     w.off = c.take<int32_t>(size_t(B) + 1);
-    w.row_req = c.take<int32_t>(p.rows_max);
-    w.row_pos = c.take<int32_t>(p.rows_max);
-    w.row_lse2 = c.take<float>(p.rows_max);
-    w.row_amax = c.take<int32_t>(p.rows_max);
-    w.row_tx2 = c.take<float>(p.rows_max);
+    w.act = c.take<int32_t>(size_t(2) * B);
+    const size_t ns = size_t(2) * B * p.nseg;
+    w.seg_m = c.take<float>(ns);
+    w.seg_s = c.take<float>(ns);
+    w.seg_v = c.take<float>(ns);
+    w.seg_i = c.take<int32_t>(ns);
+    w.seg_tx = c.take<float>(size_t(2) * B);
+    w.fin_lse2 = c.take<float>(B);
     w.mode = c.take<int32_t>(B);
     w.jpos = c.take<int32_t>(B);
+    w.slot = c.take<int32_t>(B);
     w.resid_list = c.take<int32_t>(B);
     w.bonus_list = c.take<int32_t>(B);
     const size_t nd = size_t(2) * B * p.tile.nchunk;
