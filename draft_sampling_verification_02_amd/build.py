@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "schedule.cpp", "draft.hip", "verify.hip", "debug.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
-    "-Wno-unused-parameter",
+    "-Wno-unused-parameter", "-Wno-cuda-compat",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]

@@ -27,6 +27,7 @@
 // gathered W1 rows.
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "stage.hpp"
 
 #include <algorithm>
 
@@ -49,152 +50,7 @@ struct StepParams {
     int32_t *pi;
 };
 
-// Race state of one lane over the tiles it owns: running base-2 logsumexp as
-// (max, sum of 2^(z - max)), and the best and second tile scores.
-struct TileRace {
-    float m, s, best, second;
-    int bt;
-};
-
-// Scores one 32-entry tile held by this lane in (a, b) (logits U + B, -inf past
-// the row end).  Sampled: the tile's logsumexp of z = logit * sc plus its
-// Gumbel noise g; greedy: the tile's largest logit.  The sum is taken against
-// the running maximum, so one rescale per tile keeps the row total.
-template <bool TRACK2>
-__device__ __forceinline__ void race_tile(TileRace &st, const f32x16_t &a, const f32x16_t &b, float sc, bool sampled,
-                                          int t, float g) {
-    float ma = max3f(a[0], a[1], a[2]), mb = max3f(b[0], b[1], b[2]);
-#pragma unroll
-    for (int e = 3; e < 15; e += 2) {
-        ma = max3f(ma, a[e], a[e + 1]);
-        mb = max3f(mb, b[e], b[e + 1]);
-    }
-    const float mx = max3f(max3f(ma, a[15], b[15]), mb, mb);
-    const float mt = mx * sc;
-    const float mn = fmaxf(st.m, mt);
-    const float mg = (mn == kNegInf) ? 0.f : mn;
-    const float nmg = -mg;
-    float s0 = fast_exp2(__builtin_fmaf(a[0], sc, nmg)), s1 = fast_exp2(__builtin_fmaf(a[1], sc, nmg));
-    float s2 = fast_exp2(__builtin_fmaf(b[0], sc, nmg)), s3 = fast_exp2(__builtin_fmaf(b[1], sc, nmg));
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) {
-        s0 += fast_exp2(__builtin_fmaf(a[e], sc, nmg));
-        s1 += fast_exp2(__builtin_fmaf(a[e + 1], sc, nmg));
-        s2 += fast_exp2(__builtin_fmaf(b[e], sc, nmg));
-        s3 += fast_exp2(__builtin_fmaf(b[e + 1], sc, nmg));
-    }
-    const float sum = (s0 + s1) + (s2 + s3);
-    st.s = __builtin_fmaf(st.s, fast_exp2(st.m - mg), sum);
-    st.m = mn;
-    const float Lt = sampled ? mg + fast_log2(sum) + g : mt;
-    if (TRACK2) st.second = fmaxf(st.second, fminf(Lt, st.best));
-    if (Lt > st.best) {
-        st.best = Lt;
-        st.bt = t;
-    }
-}
-
 constexpr int kStepThreads = 512;  // 8 waves: one 32-request block each
-
-// Direct-to-LDS loads of one two-tile stage (64 W2 rows) by the workgroup's
-// 512 threads.  Each thread's slots are fixed, so their source offsets are
-// computed once.
-template <typename WT, int R>
-struct StageDMA {
-    using L = TileLDS<WT, R>;
-    static constexpr int SLOTS = 2 * L::SLOTS;  // 16-byte slots of a stage
-    static constexpr int J = (SLOTS + kStepThreads - 1) / kStepThreads;
-    uint32_t goff[J];  // byte offset of the slot's source from the stage's first row
-    int row[J];        // stage row (0..63) the slot belongs to
-
-    __device__ __forceinline__ void init(int tid) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int slot = tid + j * kStepThreads;
-            const int m = slot / L::CPR;
-            row[j] = m;
-            goff[j] = uint32_t(m * L::RB + L::chunk(m, slot % L::CPR) * 16);
-        }
-    }
-    // rows v0 .. v0 + 63; CLAMP repeats row V - 1 for rows past the vocabulary
-    template <bool CLAMP>
-    __device__ __forceinline__ void issue(const WT *W2, int v0, int V, uint8_t *buf, int wave) const {
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(W2) + size_t(v0) * L::RB;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int s0 = wave * 64 + j * kStepThreads;  // slot of lane 0, uniform
-            if (J * kStepThreads > SLOTS && s0 >= SLOTS) break;
-            const uint8_t *g = src + goff[j];
-            if (CLAMP) {
-                const int vrow = min(v0 + row[j], V - 1);
-                g = reinterpret_cast<const uint8_t *>(W2) + size_t(vrow) * L::RB + (goff[j] - uint32_t(row[j] * L::RB));
-            }
-            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(buf + s0 * 16), 16, 0, 0);
-        }
-    }
-};
-
-// The U_k entries of a two-tile stage for one wave's 32 requests: 32 rows of
-// 64 floats, staged in a wave-private LDS region by direct loads so that each
-// load instruction covers whole 256-byte row segments, then read back in the
-// MFMA accumulator layout.  In LDS the 16-byte chunk c of row r sits at chunk
-// c ^ (r & 15).  VEC moves 16 bytes a lane (rows allow aligned 16-byte
-// loads), else 4 bytes.
-template <bool VEC>
-struct StageU {
-    static constexpr int ROWB = 2 * kTile * 4;          // bytes of a row segment
-    static constexpr int BYTES = 32 * ROWB;             // one wave's region
-    static constexpr int NI = VEC ? BYTES / 1024 : BYTES / 256;  // load instructions a stage
-    const float *rowp[NI];  // source row of each instruction's lane
-    int col[NI];            // first column of the lane's 16 (or 4) bytes, relative to v0
-
-    __device__ __forceinline__ void init(const float *U, size_t u_stride, int row0, int B, int lane) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            int r, c;
-            if (VEC) {
-                r = 4 * j + (lane >> 4);
-                c = 4 * ((lane & 15) ^ (r & 15));
-            } else {
-                r = j;
-                c = 4 * (((lane >> 2) ^ r) & 15) + (lane & 3);
-            }
-            rowp[j] = U + size_t(min(row0 + r, B - 1)) * u_stride;
-            col[j] = c;
-        }
-    }
-    template <bool CLAMP>
-    __device__ __forceinline__ void issue(int v0, int V, uint8_t *region) const {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            int v = v0 + col[j];
-            if (CLAMP) v = min(v, V - (VEC ? 4 : 1));
-            const void *g = rowp[j] + v;
-            if constexpr (VEC)
-                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 1024), 16, 0, 0);
-            else
-                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 256), 4, 0, 0);
-        }
-    }
-    // accumulator layout: value 4i+j of lane (n, h) is entry 32q + 8i + 4h + j
-    __device__ __forceinline__ void read(const uint8_t *region, int lane, f32x16_t &c0, f32x16_t &c1) const {
-        const int n = lane & 31, h = lane >> 5;
-        const uint8_t *row = region + n * ROWB;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            f32x16_t &c = q ? c1 : c0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = (8 * q + 2 * i + h) ^ (n & 15);
-                const float4 x = *reinterpret_cast<const float4 *>(row + ch * 16);
-                c[4 * i] = x.x;
-                c[4 * i + 1] = x.y;
-                c[4 * i + 2] = x.z;
-                c[4 * i + 3] = x.w;
-            }
-        }
-    }
-};
 
 // One workgroup of 8 waves walks the tiles [t_begin, t_end) of one vocabulary
 // chunk, two tiles per stage: the pair's 64 W2 rows are staged in LDS by
@@ -207,7 +63,7 @@ struct StageU {
 template <typename WT, int R, bool TRACK2, bool VEC>
 __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void draft_step_kernel(StepParams p) {
     using L = TileLDS<WT, R>;
-    using SU = StageU<VEC>;
+    using SU = StageRows<VEC>;
     __shared__ __attribute__((aligned(16))) uint8_t ldsA[2 * L::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsB[2 * L::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsU[(kStepThreads / 64) * SU::BYTES];
@@ -231,10 +87,10 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
     if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
-    StageDMA<WT, R> dma;
+    StageDMA<WT, R, kStepThreads> dma;
     dma.init(tid);
     SU su;
-    if (wave_ok) su.init(p.U, p.u_stride, bb * 32, p.B, lane);
+    if (wave_ok) su.init(lane, p.U, p.u_stride, [&](int r) { return min(bb * 32 + r, p.B - 1); });
     uint8_t *uregion = ldsU + wave * SU::BYTES;
 
     const int t_begin = chunk * p.tiles_per_chunk;
@@ -252,7 +108,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
         su.read(uregion, lane, c0, c1);
         if (next_v0 >= 0) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the region has been read
-            su.template issue<false>(next_v0, p.V, uregion);
+            su.template issue<false>(next_v0, p.V, uregion, lane);
         }
         bias_pair_lds(ef, buf, lane, c0, c1);
         swap_halves(c0, c1);
@@ -277,7 +133,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
 
     if (nfull > 0) {
         dma.template issue<false>(W2, v0_of(0), p.V, ldsA, wave);
-        if (wave_ok) su.template issue<false>(v0_of(0), p.V, uregion);
+        if (wave_ok) su.template issue<false>(v0_of(0), p.V, uregion, lane);
     }
     for (int i = 0; i < nfull; i += 2) {
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage i have landed
@@ -293,7 +149,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     if (tail) {
         __syncthreads();  // every wave is done with both W2 buffers and its region
         dma.template issue<true>(W2, v0_of(nfull), p.V, ldsA, wave);
-        if (wave_ok) su.template issue<true>(v0_of(nfull), p.V, uregion);
+        if (wave_ok) su.template issue<true>(v0_of(nfull), p.V, uregion, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (wave_ok) stage(ldsA, t_begin + 2 * nfull, -1, true);

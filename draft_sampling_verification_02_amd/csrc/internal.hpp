@@ -69,8 +69,9 @@ hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork 
 // ---- verify ----------------------------------------------------------
 
 struct VerifyPlan {
-    int nseg;         // vocabulary segments a target row is split into by the position passes
-    int seg_len;      // entries per segment (a multiple of 4)
+    int nseg_first, seg_len_first;  // segments of a target row in the first position pass, entries each
+    int nseg, seg_len;              // the same for the later passes (entries a multiple of 4)
+    int nseg_max;                   // partials kept per request
     int nbb;          // ceil(B / 32)
     DraftPlan tile;   // vocabulary walk of the resample / bonus draw
     int draw_nbg;     // workgroups per chunk of the draw (room for both lists)

@@ -34,6 +34,7 @@
 //                    workgroup scans the emitted counts into out_offsets.
 #include "device_common.hpp"
 #include "internal.hpp"
+#include "stage.hpp"
 
 #include <algorithm>
 
@@ -170,7 +171,10 @@ struct PassParams {
     const float *target;
     const int32_t *x, *ell;
     const float *qx, *temperature;
-    int B, gamma, V, j, nseg, seg_len, vec;
+    int B, gamma, V, j, vec;
+    int nseg, seg_len;  // this pass's segments of a row
+    int nseg_in;        // the previous pass's
+    int seg_stride;     // partials per request in the buffers
     uint32_t key0, key1, round32;
     const int32_t *off;
     // pass j reads what pass j - 1 left (row j - 1 of every request it reduced)
@@ -246,51 +250,51 @@ __device__ bool pass_decide(const PassParams &p, int b, int k, bool sampled, flo
     return false;
 }
 
-// Pass j = 1..gamma+2, one workgroup per (request, vocabulary segment).
-// First the request's position j - 1 is decided from the segment statistics
-// pass j - 1 wrote; a request that goes on streams segment sg of its row j:
-// every thread keeps its own running max / sum of exp2 and argmax over
-// batches of eight float4 loads, and the workgroup merges them.
+// Pass j = 1..gamma+2, one wave per (request, vocabulary segment), four
+// requests to a workgroup.  First the request's position j - 1 is decided
+// from the segment statistics pass j - 1 wrote; a request that goes on
+// streams segment sg of its row j: every lane keeps its own running max / sum
+// of exp2 and argmax over batches of eight float4 loads, and the wave merges
+// them.  The waves never wait for one another.
 __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
-    const int b = blockIdx.x / p.nseg, sg = blockIdx.x % p.nseg;
+    const int sg = blockIdx.x % p.nseg;
+    const int b = (blockIdx.x / p.nseg) * 4 + (threadIdx.x >> 6);
     const int j = p.j;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    if (b >= p.B) return;
     const bool writer = sg == 0;
     if (p.mode[b] < 0 || (j > 1 && p.act_in[b] == 0)) {
-        if (writer && tid == 0) p.act_out[b] = 0;
+        if (writer && lane == 0) p.act_out[b] = 0;
         return;
     }
     const float T = p.temperature[b];
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    __shared__ int go_on;
     if (j > 1) {
-        if (wave == 0) {
-            float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
-            int i2 = 0x7fffffff;
-            for (int c = lane; c < p.nseg; c += 64) {
-                const size_t o = size_t(b) * p.nseg + c;
-                lse_merge(mm, s2, p.pm_in[o], p.ps_in[o]);
-                argmax_merge(v2, i2, p.pv_in[o], p.pi_in[o]);
-            }
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                lse_merge(mm, s2, __shfl_xor(mm, o), __shfl_xor(s2, o));
-                argmax_merge(v2, i2, __shfl_xor(v2, o), __shfl_xor(i2, o));
-            }
-            if (lane == 0) {
-                const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(s2);
-                go_on = pass_decide(p, b, j - 1, sampled, lse2, min(max(i2, 0), p.V - 1), p.tx_in[b], writer);
-            }
+        float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
+        int i2 = 0x7fffffff;
+        for (int c = lane; c < p.nseg_in; c += 64) {
+            const size_t o = size_t(b) * p.seg_stride + c;
+            lse_merge(mm, s2, p.pm_in[o], p.ps_in[o]);
+            argmax_merge(v2, i2, p.pv_in[o], p.pi_in[o]);
         }
-        __syncthreads();
-        if (!go_on) {
-            if (writer && tid == 0) p.act_out[b] = 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            lse_merge(mm, s2, __shfl_xor(mm, o), __shfl_xor(s2, o));
+            argmax_merge(v2, i2, __shfl_xor(v2, o), __shfl_xor(i2, o));
+        }
+        int go_on = 0;
+        if (lane == 0) {
+            const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(s2);
+            go_on = pass_decide(p, b, j - 1, sampled, lse2, min(max(i2, 0), p.V - 1), p.tx_in[b], writer);
+        }
+        if (!__shfl(go_on, 0)) {
+            if (writer && lane == 0) p.act_out[b] = 0;
             return;
         }
     }
     if (j > p.ell[b] + 1) {  // nothing left to reduce (the decision above ended it)
-        if (writer && tid == 0) p.act_out[b] = 0;
+        if (writer && lane == 0) p.act_out[b] = 0;
         return;
     }
     const float *trow = p.target + size_t(p.off[b] + j - 1) * p.V;
@@ -301,11 +305,11 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         const float4 *r4 = reinterpret_cast<const float4 *>(trow);
         const int q_hi = v_hi >> 2;
         constexpr int U = 8;
-        for (int q0 = (v_lo >> 2) + tid; q0 < q_hi; q0 += 256 * U) {
+        for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
             float4 xs[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int q = q0 + 256 * u;
+                const int q = q0 + 64 * u;
                 xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
             }
             float bm = kNegInf;
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int v = 4 * (q0 + 256 * u);
+                const int v = 4 * (q0 + 64 * u);
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const float xv = f4get(xs[u], jj);
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             }
         }
     } else {
-        for (int v = v_lo + tid; v < v_hi; v += 256) {
+        for (int v = v_lo + lane; v < v_hi; v += 64) {
             const float xv = trow[v] * sc;
             const float mn = fmaxf(m, xv);
             if (mn != kNegInf) {
@@ -354,31 +358,17 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             }
         }
     }
-    // merge the 256 thread states: within the wave, then across the 4 waves
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         lse_merge(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
         argmax_merge(av, ai, __shfl_xor(av, o), __shfl_xor(ai, o));
     }
-    __shared__ float sm[4], ss[4], sv[4];
-    __shared__ int si[4];
     if (lane == 0) {
-        sm[wave] = m;
-        ss[wave] = s;
-        sv[wave] = av;
-        si[wave] = ai;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < 4; ++w) {
-            lse_merge(sm[0], ss[0], sm[w], ss[w]);
-            argmax_merge(sv[0], si[0], sv[w], si[w]);
-        }
-        const size_t o = size_t(b) * p.nseg + sg;
-        p.pm_out[o] = sm[0];
-        p.ps_out[o] = ss[0];
-        p.pv_out[o] = sv[0];
-        p.pi_out[o] = si[0];
+        const size_t o = size_t(b) * p.seg_stride + sg;
+        p.pm_out[o] = m;
+        p.ps_out[o] = s;
+        p.pv_out[o] = av;
+        p.pi_out[o] = ai;
         if (writer) p.act_out[b] = 1;
         // t(x_j) for the accept test at j, from the segment that holds x_j
         if (sampled && j <= p.ell[b]) {
@@ -396,8 +386,7 @@ struct DrawParams {
     const int32_t *anchor, *x;
     const float *lse_q, *temperature;
     int B, gamma, V;
-    int nw, nbg, ntiles, tiles_per_chunk, nchunk;
-    int vec_u, vec_t;
+    int nbg, ntiles, tiles_per_chunk, nchunk;
     uint32_t key0, key1, round32;
     const int32_t *status, *resid_list, *bonus_list, *jpos, *off;
     const float *fin_lse2;
@@ -405,136 +394,186 @@ struct DrawParams {
     int32_t *dw_bt;
 };
 
-// Level 1 of the resample / bonus draws.  A workgroup of up to 4 waves walks
-// the tiles of one vocabulary chunk; each wave holds 32 listed requests.
-// Residual waves recompute q_j from the W2 tile (staged in LDS as in the
-// draft) and sum max(p_j - q_j, 0) per tile; bonus waves take the tile
-// logsumexp of p.  Either way the tile enters a Gumbel race (stream 4).
-template <typename WT, int R>
-__global__ __launch_bounds__(256) void verify_draw_kernel(DrawParams p) {
+constexpr int kDrawThreads = 512;  // 8 waves: one block of 32 listed requests each
+
+// Level 1 of the resample / bonus draws.  A workgroup of 8 waves walks the
+// tiles of one vocabulary chunk, two tiles per stage, each wave holding 32
+// listed requests.  The target rows p_j of its requests (and, for residual
+// waves, the U_j rows) are staged in wave-private LDS regions by direct loads;
+// residual waves recompute q_j = softmax(U_j + B_j) from the stage's W2 rows
+// (one LDS stage shared by the workgroup, refilled once every wave has run
+// its MFMAs) with the draft's MFMA tiles and lane-half swap, and sum
+// max(p_j - q_j, 0) over each tile; bonus waves race the tile logsumexps of p.
+// Either way the tile score takes its noise from stream 4.
+template <typename WT, int R, bool VEC>
+__global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_draw_kernel(
+    DrawParams p) {
     using L = TileLDS<WT, R>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::BYTES];
+    using SR = StageRows<VEC>;
+    __shared__ __attribute__((aligned(16))) uint8_t ldsW[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsU[(kDrawThreads / 64) * SR::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsT[(kDrawThreads / 64) * SR::BYTES];
     const int nres = p.status[2], nbon = p.status[3];
     const int nblk_r = (nres + 31) / 32, nblk = nblk_r + (nbon + 31) / 32;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nthreads = p.nw * 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
     const int chunk = lg / p.nbg, bg = lg % p.nbg;
-    const int lb0 = bg * p.nw;
-    if (lb0 >= nblk) return;                   // the whole workgroup is idle
-    const bool need_tiles = lb0 < nblk_r;      // uniform across the workgroup
+    const int lb0 = bg * (kDrawThreads / 64);
+    if (lb0 >= nblk) return;               // the whole workgroup is idle
+    const bool need_w2 = lb0 < nblk_r;     // uniform across the workgroup
     const int lb = lb0 + wave;
-    const bool wave_ok = lb < nblk;            // uniform across the wave
-    const bool resid = lb < nblk_r;            // uniform across the wave
+    const bool wave_ok = lb < nblk;        // uniform across the wave
+    const bool resid = lb < nblk_r;        // uniform across the wave
     const int n = lane & 31, h = lane >> 5;
-    int e = 0, req = 0, slot = 0;
+    int req = 0, slot = 0;
     bool ok = false;
     if (resid) {
-        e = lb * 32 + n;
+        const int e = lb * 32 + n;
         ok = e < nres;
         req = p.resid_list[ok ? e : nres - 1];
         slot = e;
     } else if (wave_ok) {
-        e = (lb - nblk_r) * 32 + n;
+        const int e = (lb - nblk_r) * 32 + n;
         ok = e < nbon;
         req = p.bonus_list[ok ? e : nbon - 1];
         slot = p.B + e;
     }
     const int j = wave_ok ? p.jpos[req] : 1;
     const float sc = wave_ok ? kLog2e / p.temperature[req] : 1.0f;
-    const int trow_i = wave_ok ? p.off[req] + j - 1 : 0;
-    const float *trow = p.target + size_t(trow_i) * p.V;
     const float lse2t = wave_ok ? p.fin_lse2[req] : 0.f;
-    const bool vec_t = p.vec_t != 0, vec_u = p.vec_u != 0;
+    const int trow_i = ok ? p.off[req] + j - 1 : -1;  // packed target row
 
     const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
-    const float *urow = p.U;
+    int urow_i = -1;  // row of U
     float lse2q = 0.f;
     if (resid) {
         int prev = (j == 1) ? p.anchor[req] : p.x[size_t(req) * p.gamma + j - 2];
         prev = min(max(prev, 0), p.V - 1);
         ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
-        urow = p.U + (size_t(req) * p.gamma + j - 1) * p.V;
+        if (ok) urow_i = req * p.gamma + j - 1;
         lse2q = p.lse_q[size_t(req) * p.gamma + j - 1] * kLog2e;
     }
+    StageDMA<WT, R, kDrawThreads> dma;
+    if (need_w2) dma.init(tid);
+    SR su, stg;
+    if (wave_ok) stg.init(lane, p.target, size_t(p.V), [&](int r) { return __shfl(trow_i, r); });
+    if (resid) su.init(lane, p.U, size_t(p.V), [&](int r) { return __shfl(urow_i, r); });
+    uint8_t *uregion = ldsU + wave * SR::BYTES;
+    uint8_t *tregion = ldsT + wave * SR::BYTES;
 
     const int t_begin = chunk * p.tiles_per_chunk;
     const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
-    float S = 0.f, best = kNegInf;
-    int bt = t_begin;
+    const int nst = (t_end - t_begin + 1) >> 1;  // stages of two tiles
+    const bool tail = (t_begin + 2 * nst) * kTile > p.V;
+    const int nfull = nst - (tail ? 1 : 0);
+    float S = 0.f;  // residual mass of this lane's tiles
+    TileRace st{kNegInf, 0.f, kNegInf, kNegInf, t_begin};
     uint4 tw = make_uint4(0u, 0u, 0u, 0u);
-    if (need_tiles) tile_issue<WT, R>(W2, t_begin * kTile, p.V, lds, nthreads);
-    float4 tcur[4], ucur[4];
-    if (wave_ok) load_tile_row(trow, t_begin, h, p.V, vec_t, tcur);
-    if (resid) load_tile_row(urow, t_begin, h, p.V, vec_u, ucur);
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        __builtin_amdgcn_s_waitcnt(0);
-        if (need_tiles) __syncthreads();
-        const bool more = t + 1 < t_end;
-        float4 tnext[4], unext[4];
-        if (more) {
-            if (need_tiles) tile_issue<WT, R>(W2, (t + 1) * kTile, p.V, lds + (buf ^ 1) * L::BYTES, nthreads);
-            if (wave_ok) load_tile_row(trow, t + 1, h, p.V, vec_t, tnext);
-            if (resid) load_tile_row(urow, t + 1, h, p.V, vec_u, unext);
+    auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
+
+    // the rest of a stage once its MFMAs are done: lane (n, h) scores tile t0 + h
+    auto score = [&](f32x16_t &p0, f32x16_t &p1, f32x16_t &c0, f32x16_t &c1, int t0, bool masked) __device__ {
+        if (resid) swap_halves(c0, c1);
+        if (masked) {
+            const int vb = (t0 + h) * kTile;  // this lane's tile: rows 8i+j, then rows 8i+4+j
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    if (vb + 8 * i + jj >= p.V) p0[4 * i + jj] = c0[4 * i + jj] = kNegInf;
+                    if (vb + 8 * i + 4 + jj >= p.V) p1[4 * i + jj] = c1[4 * i + jj] = kNegInf;
+                }
         }
+        // t0 is even, so both tiles of the pair share one noise block; tile
+        // t0 + h takes word (t0 & 3) + h
+        if (t0 == t_begin || (t0 & 3) == 0)
+            tw = noise_block(kStreamResampleTile, j, uint32_t(t0) >> 2, uint32_t(req), p.round32, p.key0, p.key1);
+        const uint32_t w_lo = (t0 & 2) ? tw.z : tw.x, w_hi = (t0 & 2) ? tw.w : tw.y;
+        const float g = gumbel2(h ? w_hi : w_lo);
+        if (resid) {
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                r0 += fmaxf(fast_exp2(__builtin_fmaf(p0[e], sc, -lse2t)) - fast_exp2(__builtin_fmaf(c0[e], sc, -lse2q)),
+                            0.f);
+                r1 += fmaxf(fast_exp2(__builtin_fmaf(p1[e], sc, -lse2t)) - fast_exp2(__builtin_fmaf(c1[e], sc, -lse2q)),
+                            0.f);
+            }
+            const float rt = r0 + r1;
+            S += rt;
+            const float Lt = rt > 0.f ? fast_log2(rt) + g : kNegInf;
+            if (Lt > st.best) {
+                st.best = Lt;
+                st.bt = t0 + h;
+            }
+        } else {
+            race_tile<false>(st, p0, p1, sc, true, t0 + h, g);
+        }
+    };
+
+    if (nfull > 0) {
+        if (need_w2) dma.template issue<false>(W2, v0_of(0), p.V, ldsW, wave);
+        if (wave_ok) stg.template issue<false>(v0_of(0), p.V, tregion, lane);
+        if (resid) su.template issue<false>(v0_of(0), p.V, uregion, lane);
+    }
+    for (int i = 0; i < nfull; ++i) {
+        const bool more = i + 1 < nfull;
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage i have landed
+        __syncthreads();                // ... and every thread's
+        f32x16_t p0, p1, c0, c1;
         if (wave_ok) {
-            if (t == t_begin || (t & 3) == 0)
-                tw = noise_block(kStreamResampleTile, j, uint32_t(t) >> 2, uint32_t(req), p.round32, p.key0, p.key1);
-            const float g = gumbel2(u4get(tw, t & 3));
-            float Lt;
+            // U first (it seeds the MFMAs), the target rows after the MFMAs;
+            // each region is refilled with the next stage once it has been read
             if (resid) {
-                const f32x16_t acc = bias_tile_lds(ef, lds + buf * L::BYTES, lane);
-                float sh = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float q = fast_exp2(__builtin_fmaf(f4get(ucur[i], jj) + acc[4 * i + jj], sc, -lse2q));
-                        const float pv = fast_exp2(__builtin_fmaf(f4get(tcur[i], jj), sc, -lse2t));
-                        sh += fmaxf(pv - q, 0.f);
-                    }
-                const float st = sh + __shfl_xor(sh, 32);
-                S += st;
-                Lt = st > 0.f ? fast_log2(st) + g : kNegInf;
-            } else {
-                float tv[16];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) tv[4 * i + jj] = f4get(tcur[i], jj) * sc;
-                float mh = tv[0];
-#pragma unroll
-                for (int q = 1; q < 16; ++q) mh = fmaxf(mh, tv[q]);
-                const float mhs = (mh == kNegInf) ? 0.f : mh;
-                float sh = 0.f;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) sh += fast_exp2(tv[q] - mhs);
-                const float mo = __shfl_xor(mh, 32), so = __shfl_xor(sh, 32);
-                const float mt = fmaxf(mh, mo);
-                const float mts = (mt == kNegInf) ? 0.f : mt;
-                const float st = sh * fast_exp2(mh - mts) + so * fast_exp2(mo - mts);
-                Lt = mt + fast_log2(st) + g;
+                su.read(uregion, lane, c0, c1);
+                if (more) {
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    su.template issue<false>(v0_of(i + 1), p.V, uregion, lane);
+                }
+                bias_pair_lds(ef, ldsW, lane, c0, c1);
             }
-            if (Lt > best) {
-                best = Lt;
-                bt = t;
+            stg.read_swapped(tregion, lane, p0, p1);
+            if (more) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                stg.template issue<false>(v0_of(i + 1), p.V, tregion, lane);
             }
         }
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                tcur[i] = tnext[i];
-                ucur[i] = unext[i];
+        __syncthreads();  // every wave is done with ldsW
+        if (need_w2 && more) dma.template issue<false>(W2, v0_of(i + 1), p.V, ldsW, wave);
+        if (wave_ok) score(p0, p1, c0, c1, t_begin + 2 * i, false);
+    }
+    if (tail) {
+        __syncthreads();  // every wave is done with ldsW and its regions
+        if (need_w2) dma.template issue<true>(W2, v0_of(nfull), p.V, ldsW, wave);
+        if (wave_ok) stg.template issue<true>(v0_of(nfull), p.V, tregion, lane);
+        if (resid) su.template issue<true>(v0_of(nfull), p.V, uregion, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave_ok) {
+            f32x16_t p0, p1, c0, c1;
+            stg.read_swapped(tregion, lane, p0, p1);
+            if (resid) {
+                su.read(uregion, lane, c0, c1);
+                bias_pair_lds(ef, ldsW, lane, c0, c1);
             }
+            score(p0, p1, c0, c1, t_begin + 2 * nfull, true);
         }
+    }
+    // the two lane halves raced alternate tiles of the same request
+    S += __shfl_xor(S, 32);
+    {
+        const float b2 = __shfl_xor(st.best, 32);
+        const int i2 = __shfl_xor(st.bt, 32);
+        float sec = kNegInf;
+        best_merge(st.best, st.bt, sec, b2, i2, kNegInf);
     }
     if (h == 0 && ok) {
         const size_t o = size_t(slot) * p.nchunk + chunk;
         p.dw_sum[o] = S;
-        p.dw_bl[o] = best;
-        p.dw_bt[o] = bt;
+        p.dw_bl[o] = st.best;
+        p.dw_bt[o] = st.bt;
     }
 }
 
@@ -678,7 +717,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
     for (int j = 1; j <= a.gamma + 2; ++j) {
         const int in = (j - 1) & 1, out = j & 1;  // double-buffer halves
-        const size_t ns = size_t(a.B) * pl.nseg;
+        const size_t ns = size_t(a.B) * pl.nseg_max;
+        const int nseg = (j == 1) ? pl.nseg_first : pl.nseg;
         PassParams pp{};
         pp.target = a.target;
         pp.x = a.x;
@@ -689,8 +729,10 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.gamma = a.gamma;
         pp.V = a.V;
         pp.j = j;
-        pp.nseg = pl.nseg;
-        pp.seg_len = pl.seg_len;
+        pp.nseg = nseg;
+        pp.seg_len = (j == 1) ? pl.seg_len_first : pl.seg_len;
+        pp.nseg_in = (j == 2) ? pl.nseg_first : pl.nseg;
+        pp.seg_stride = pl.nseg_max;
         pp.vec = vec_t;
         pp.key0 = a.key0;
         pp.key1 = a.key1;
@@ -721,7 +763,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
                                             "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
         int t = prof_begin(names[std::min(j, 8) - 1], s);
-        hipLaunchKernelGGL(verify_pass_kernel, dim3(size_t(a.B) * pl.nseg), dim3(256), 0, s, pp);
+        hipLaunchKernelGGL(verify_pass_kernel, dim3(size_t((a.B + 3) / 4) * nseg), dim3(256), 0, s, pp);
         prof_end(t, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -738,13 +780,10 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.B = a.B;
         dp.gamma = a.gamma;
         dp.V = a.V;
-        dp.nw = pl.tile.nw;
         dp.nbg = pl.draw_nbg;
         dp.ntiles = pl.tile.ntiles;
         dp.tiles_per_chunk = pl.tile.tiles_per_chunk;
         dp.nchunk = pl.tile.nchunk;
-        dp.vec_u = vec_u;
-        dp.vec_t = vec_t;
         dp.key0 = a.key0;
         dp.key1 = a.key1;
         dp.round32 = a.round32;
@@ -758,7 +797,10 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.dw_bl = w.dw_bl;
         dp.dw_bt = w.dw_bt;
         int t = prof_begin("verify_draw", s);
-        hipLaunchKernelGGL((verify_draw_kernel<WT, R>), dim3(pl.draw_blocks), dim3(64 * pl.tile.nw), 0, s, dp);
+        if (vec_u && vec_t)
+            hipLaunchKernelGGL((verify_draw_kernel<WT, R, true>), dim3(pl.draw_blocks), dim3(kDrawThreads), 0, s, dp);
+        else
+            hipLaunchKernelGGL((verify_draw_kernel<WT, R, false>), dim3(pl.draw_blocks), dim3(kDrawThreads), 0, s, dp);
         prof_end(t, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -805,17 +847,25 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
 VerifyPlan verify_plan(int B, int gamma, int V) {
     (void)gamma;
     VerifyPlan p{};
-    // at most 16 segments a row, each a whole number of float4 groups
+    // Position passes split a row into segments of whole float4 groups: the
+    // first pass, which reads every request's row, in a few long ones (long
+    // streams per workgroup), the later ones, which read fewer and fewer rows,
+    // in up to 16 short ones (more workgroups per row).
     const int n4 = (V + 3) / 4;
-    p.seg_len = 4 * ((n4 + 15) / 16);
-    p.nseg = (V + p.seg_len - 1) / p.seg_len;
+    auto split = [&](int k, int &nseg, int &len) {
+        len = 4 * ((n4 + k - 1) / k);
+        nseg = (V + len - 1) / len;
+    };
+    split(4, p.nseg_first, p.seg_len_first);
+    split(16, p.nseg, p.seg_len);
+    p.nseg_max = std::max(p.nseg_first, p.nseg);
     p.nbb = (B + 31) / 32;
-    // about 2048 waves of up to 4 over the 1024 SIMDs; chunks of a multiple of
-    // 4 tiles share the tile-noise Philox blocks
-    const long long nbb = (B + 31) / 32, nw = std::min<long long>(4, nbb);
-    p.tile = tile_walk_plan(B, V, 4, std::max<long long>(1, 2048 / nw), 4);
+    // 8-wave workgroups holding one 2-tile W2 stage and the wave regions
+    // (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them for the
+    // requests; chunks are whole 2-tile stages
+    p.tile = tile_walk_plan(B, V, kDrawThreads / 64, 256, 2);
     // the residual and bonus lists hold at most B requests but each rounds up to 32
-    p.draw_nbg = (p.nbb + 1 + p.tile.nw - 1) / p.tile.nw;
+    p.draw_nbg = (p.nbb + 1 + kDrawThreads / 64 - 1) / (kDrawThreads / 64);
     p.draw_blocks = p.tile.nchunk * p.draw_nbg;
     return p;
 }
@@ -828,7 +878,7 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     w.status = c.take<int32_t>(4);
     w.off = c.take<int32_t>(size_t(B) + 1);
     w.act = c.take<int32_t>(size_t(2) * B);
-    const size_t ns = size_t(2) * B * p.nseg;
+    const size_t ns = size_t(2) * B * p.nseg_max;
     w.seg_m = c.take<float>(ns);
     w.seg_s = c.take<float>(ns);
     w.seg_v = c.take<float>(ns);
