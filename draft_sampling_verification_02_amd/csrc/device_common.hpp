@@ -422,6 +422,17 @@ __device__ __forceinline__ f32x16_t load_acc_tile(const float *row, int v0, int 
     return c;
 }
 
+// x of lane n plus (or max with) x of lane n ^ 32, in every lane: one
+// v_permlane32_swap of x with itself hands each half the other half's x.
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Exchange the lane halves of two accumulator tiles (v_permlane32_swap, which
 // swaps lanes 32..63 of its first operand with lanes 0..31 of its second).
 // Before: lane (n, h) holds rows 8i+4h+j of tile a in a and of tile b in b.

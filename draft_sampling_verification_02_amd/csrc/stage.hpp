@@ -170,4 +170,97 @@ struct StageRows {
     }
 };
 
+// The logit rows of a one-tile stage for one wave's 32 requests: 32 rows of
+// 32 floats in a wave-private LDS region, loaded by direct loads (each load
+// instruction covers whole 128-byte row segments) and read back in the MFMA
+// accumulator layout.  In LDS the 16-byte chunk c of row r sits at chunk
+// c ^ (r & 7).  VEC moves 16 bytes a lane, else 4 bytes.
+template <bool VEC>
+struct TileRows {
+    static constexpr int ROWB = kTile * 4;                      // bytes of a row segment
+    static constexpr int BYTES = 32 * ROWB;                     // one wave's region
+    static constexpr int NI = VEC ? BYTES / 1024 : BYTES / 256;  // load instructions a stage
+    const float *base;  // region row r reads base + idx * stride
+    size_t stride;
+    int idx[NI];        // source row of each instruction's lane, -1 for none
+
+    __device__ static __forceinline__ int region_row(int j, int lane) { return VEC ? 8 * j + (lane >> 3) : 2 * j + (lane >> 5); }
+    __device__ static __forceinline__ int region_col(int j, int lane) {
+        const int r = region_row(j, lane);
+        return VEC ? 4 * ((lane & 7) ^ (r & 7)) : 4 * (((lane >> 2) & 7) ^ (r & 7)) + (lane & 3);
+    }
+    template <typename RowFn>
+    __device__ __forceinline__ void init(int lane, const float *base_, size_t stride_, RowFn row) {
+        base = base_;
+        stride = stride_;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) idx[j] = row(region_row(j, lane));
+    }
+    // rows without a source are skipped (their region rows keep stale data)
+    template <bool CLAMP>
+    __device__ __forceinline__ void issue(int v0, int V, uint8_t *region, int lane) const {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            int v = v0 + region_col(j, lane);
+            if (CLAMP) v = min(v, V - (VEC ? 4 : 1));
+            if (idx[j] < 0) continue;
+            const void *g = base + size_t(idx[j]) * stride + v;
+            if constexpr (VEC)
+                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 1024), 16, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 256), 4, 0, 0);
+        }
+    }
+    // accumulator layout: value 4i+j of lane (n, h) is entry 8i + 4h + j
+    __device__ __forceinline__ f32x16_t read(const uint8_t *region, int lane) const {
+        const int n = lane & 31, h = lane >> 5;
+        const uint8_t *row = region + n * ROWB;
+        f32x16_t c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 x = *reinterpret_cast<const float4 *>(row + (((2 * i + h) ^ (n & 7)) * 16));
+            c[4 * i] = x.x;
+            c[4 * i + 1] = x.y;
+            c[4 * i + 2] = x.z;
+            c[4 * i + 3] = x.w;
+        }
+        return c;
+    }
+};
+
+// Direct-to-LDS loads of one tile (32 W2 rows) by the workgroup's NT threads,
+// with the per-thread source offsets computed once.
+template <typename WT, int R, int NT>
+struct TileDMA {
+    using L = TileLDS<WT, R>;
+    static constexpr int J = (L::SLOTS + NT - 1) / NT;
+    uint32_t goff[J];
+    int row[J];
+
+    __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int slot = tid + j * NT;
+            const int m = slot / L::CPR;
+            row[j] = m;
+            goff[j] = uint32_t(m * L::RB + L::chunk(m, slot % L::CPR) * 16);
+        }
+    }
+    template <bool CLAMP>
+    __device__ __forceinline__ void issue(const WT *W2, int v0, int V, uint8_t *buf, int wave) const {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(W2) + size_t(v0) * L::RB;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int s0 = wave * 64 + j * NT;  // slot of lane 0, uniform
+            if (J * NT > L::SLOTS && s0 >= L::SLOTS) break;
+            const uint8_t *g = src + goff[j];
+            if (CLAMP) {
+                const int vrow = min(v0 + row[j], V - 1);
+                g = reinterpret_cast<const uint8_t *>(W2) + size_t(vrow) * L::RB + (goff[j] - uint32_t(row[j] * L::RB));
+            }
+            __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(buf + s0 * 16), 16, 0, 0);
+        }
+    }
+};
+
 }  // namespace dspark

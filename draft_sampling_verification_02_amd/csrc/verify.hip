@@ -37,6 +37,7 @@
 #include "stage.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dspark {
 
@@ -195,18 +196,16 @@ struct PassParams {
 // test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
 // request takes the same decision; only `writer` stores it.  Returns whether
 // the request goes on to position j.
-__device__ bool pass_decide(const PassParams &p, int b, int k, bool sampled, float lse2, int amax, float tx2,
-                            bool writer) {
-    const int L = p.ell[b];
+// xk, qk: x_k and q_k(x_k) (any value when k > ell).
+__device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampled, float lse2, int amax, float tx2,
+                            int xk, float qk, bool writer) {
     int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
     bool bonus = false;
     if (k <= L) {
-        const int xk = p.x[size_t(b) * p.gamma + k - 1];
         bool acc;
         float pk, ratio;
         if (sampled) {
             pk = fast_exp2(tx2 - lse2);
-            const float qk = p.qx[size_t(b) * p.gamma + k - 1];
             const float u = uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
             acc = u * qk < pk;
             ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
@@ -263,21 +262,35 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     const int lane = threadIdx.x & 63;
     if (b >= p.B) return;
     const bool writer = sg == 0;
-    if (p.mode[b] < 0 || (j > 1 && p.act_in[b] == 0)) {
+    // every load the decision needs, issued together: the previous pass's
+    // segment statistics (one per lane) are read whatever the request's state
+    const int mode = p.mode[b];
+    const int act = j > 1 ? p.act_in[b] : 1;
+    const float T = p.temperature[b];
+    const int L = p.ell[b];
+    float mm = kNegInf, s2 = 0.f, v2 = kNegInf, tx2 = 0.f, qk = 0.f;
+    int i2 = 0x7fffffff, xk = 0;
+    if (j > 1) {
+        if (lane < p.nseg_in) {
+            const size_t o = size_t(b) * p.seg_stride + lane;
+            mm = p.pm_in[o];
+            s2 = p.ps_in[o];
+            v2 = p.pv_in[o];
+            i2 = p.pi_in[o];
+        }
+        tx2 = p.tx_in[b];
+        if (j - 1 <= p.gamma) {
+            xk = p.x[size_t(b) * p.gamma + j - 2];
+            qk = p.qx[size_t(b) * p.gamma + j - 2];
+        }
+    }
+    if (mode < 0 || act == 0) {
         if (writer && lane == 0) p.act_out[b] = 0;
         return;
     }
-    const float T = p.temperature[b];
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
     if (j > 1) {
-        float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
-        int i2 = 0x7fffffff;
-        for (int c = lane; c < p.nseg_in; c += 64) {
-            const size_t o = size_t(b) * p.seg_stride + c;
-            lse_merge(mm, s2, p.pm_in[o], p.ps_in[o]);
-            argmax_merge(v2, i2, p.pv_in[o], p.pi_in[o]);
-        }
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             lse_merge(mm, s2, __shfl_xor(mm, o), __shfl_xor(s2, o));
@@ -286,14 +299,14 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         int go_on = 0;
         if (lane == 0) {
             const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(s2);
-            go_on = pass_decide(p, b, j - 1, sampled, lse2, min(max(i2, 0), p.V - 1), p.tx_in[b], writer);
+            go_on = pass_decide(p, b, L, j - 1, sampled, lse2, min(max(i2, 0), p.V - 1), tx2, xk, qk, writer);
         }
         if (!__shfl(go_on, 0)) {
             if (writer && lane == 0) p.act_out[b] = 0;
             return;
         }
     }
-    if (j > p.ell[b] + 1) {  // nothing left to reduce (the decision above ended it)
+    if (j > L + 1) {  // nothing left to reduce (the decision above ended it)
         if (writer && lane == 0) p.act_out[b] = 0;
         return;
     }
@@ -371,9 +384,9 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         p.pi_out[o] = ai;
         if (writer) p.act_out[b] = 1;
         // t(x_j) for the accept test at j, from the segment that holds x_j
-        if (sampled && j <= p.ell[b]) {
-            const int xk = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
-            if (xk >= v_lo && xk < v_hi) p.tx_out[b] = trow[xk] * sc;
+        if (sampled && j <= L) {
+            const int xj = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
+            if (xj >= v_lo && xj < v_hi) p.tx_out[b] = trow[xj] * sc;
         }
     }
 }
@@ -397,29 +410,34 @@ struct DrawParams {
 constexpr int kDrawThreads = 512;  // 8 waves: one block of 32 listed requests each
 
 // Level 1 of the resample / bonus draws.  A workgroup of 8 waves walks the
-// tiles of one vocabulary chunk, two tiles per stage, each wave holding 32
-// listed requests.  The target rows p_j of its requests (and, for residual
-// waves, the U_j rows) are staged in wave-private LDS regions by direct loads;
-// residual waves recompute q_j = softmax(U_j + B_j) from the stage's W2 rows
-// (one LDS stage shared by the workgroup, refilled once every wave has run
-// its MFMAs) with the draft's MFMA tiles and lane-half swap, and sum
-// max(p_j - q_j, 0) over each tile; bonus waves race the tile logsumexps of p.
-// Either way the tile score takes its noise from stream 4.
+// tiles of one vocabulary chunk, one tile per stage, each wave holding 32
+// listed requests.  Every stage is double buffered in LDS and loaded by
+// direct loads one stage ahead: the tile's W2 rows (shared by the workgroup)
+// and, in wave-private regions, the requests' target rows p_j and (residual
+// waves) U_j rows.  Residual waves recompute the q_j logits U_j + B_j of the
+// tile with the draft's MFMA tile and sum max(p_j - q_j, 0) over it; bonus
+// waves take the tile logsumexp of p.  Either way the tile score takes its
+// noise from stream 4.  The two halves of a wave hold the two halves of the
+// tile and combine their sums with one lane-half exchange.
 template <typename WT, int R, bool VEC>
 __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_draw_kernel(
     DrawParams p) {
     using L = TileLDS<WT, R>;
-    using SR = StageRows<VEC>;
-    __shared__ __attribute__((aligned(16))) uint8_t ldsW[2 * L::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t ldsU[(kDrawThreads / 64) * SR::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t ldsT[(kDrawThreads / 64) * SR::BYTES];
+    using TR = TileRows<VEC>;
+    constexpr int NWV = kDrawThreads / 64;
+    __shared__ __attribute__((aligned(16))) uint8_t ldsW0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsW1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsU0[NWV * TR::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsU1[NWV * TR::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsT0[NWV * TR::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsT1[NWV * TR::BYTES];
     const int nres = p.status[2], nbon = p.status[3];
     const int nblk_r = (nres + 31) / 32, nblk = nblk_r + (nbon + 31) / 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
     const int chunk = lg / p.nbg, bg = lg % p.nbg;
-    const int lb0 = bg * (kDrawThreads / 64);
+    const int lb0 = bg * NWV;
     if (lb0 >= nblk) return;               // the whole workgroup is idle
     const bool need_w2 = lb0 < nblk_r;     // uniform across the workgroup
     const int lb = lb0 + wave;
@@ -455,125 +473,103 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
         if (ok) urow_i = req * p.gamma + j - 1;
         lse2q = p.lse_q[size_t(req) * p.gamma + j - 1] * kLog2e;
     }
-    StageDMA<WT, R, kDrawThreads> dma;
+    TileDMA<WT, R, kDrawThreads> dma;
     if (need_w2) dma.init(tid);
-    SR su, stg;
+    TR su, stg;
     if (wave_ok) stg.init(lane, p.target, size_t(p.V), [&](int r) { return __shfl(trow_i, r); });
     if (resid) su.init(lane, p.U, size_t(p.V), [&](int r) { return __shfl(urow_i, r); });
-    uint8_t *uregion = ldsU + wave * SR::BYTES;
-    uint8_t *tregion = ldsT + wave * SR::BYTES;
+    const int roff = wave * TR::BYTES;  // this wave's region in each region buffer
 
     const int t_begin = chunk * p.tiles_per_chunk;
     const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
-    const int nst = (t_end - t_begin + 1) >> 1;  // stages of two tiles
-    const bool tail = (t_begin + 2 * nst) * kTile > p.V;
-    const int nfull = nst - (tail ? 1 : 0);
-    float S = 0.f;  // residual mass of this lane's tiles
-    TileRace st{kNegInf, 0.f, kNegInf, kNegInf, t_begin};
+    const bool tail = t_end * kTile > p.V;  // the chunk's last tile runs past the vocabulary
+    const int nfull = (t_end - t_begin) - (tail ? 1 : 0);
+    float S = 0.f;  // residual mass (both halves hold the same sum)
+    float best = kNegInf;
+    int bt = t_begin;
     uint4 tw = make_uint4(0u, 0u, 0u, 0u);
-    auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
 
-    // the rest of a stage once its MFMAs are done: lane (n, h) scores tile t0 + h
-    auto score = [&](f32x16_t &p0, f32x16_t &p1, f32x16_t &c0, f32x16_t &c1, int t0, bool masked) __device__ {
-        if (resid) swap_halves(c0, c1);
+    auto issue = [&](int t, uint8_t *w, uint8_t *ur, uint8_t *tr, auto clamp) __device__ {
+        constexpr bool C = decltype(clamp)::value;
+        if (need_w2) dma.template issue<C>(W2, t * kTile, p.V, w, wave);
+        if (wave_ok) stg.template issue<C>(t * kTile, p.V, tr + roff, lane);
+        if (resid) su.template issue<C>(t * kTile, p.V, ur + roff, lane);
+    };
+    auto stage = [&](int t, const uint8_t *w, const uint8_t *ur, const uint8_t *tr, bool masked) __device__ {
+        f32x16_t pv = stg.read(tr + roff, lane);
+        f32x16_t c;
+        if (resid) c = bias_tile_lds(ef, w, lane, su.read(ur + roff, lane));
         if (masked) {
-            const int vb = (t0 + h) * kTile;  // this lane's tile: rows 8i+j, then rows 8i+4+j
+            // value 4i+jj of lane (n, h) is entry 8i + 4h + jj of the tile
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    if (vb + 8 * i + jj >= p.V) p0[4 * i + jj] = c0[4 * i + jj] = kNegInf;
-                    if (vb + 8 * i + 4 + jj >= p.V) p1[4 * i + jj] = c1[4 * i + jj] = kNegInf;
-                }
+                for (int jj = 0; jj < 4; ++jj)
+                    if (t * kTile + 8 * i + 4 * h + jj >= p.V) pv[4 * i + jj] = c[4 * i + jj] = kNegInf;
         }
-        // t0 is even, so both tiles of the pair share one noise block; tile
-        // t0 + h takes word (t0 & 3) + h
-        if (t0 == t_begin || (t0 & 3) == 0)
-            tw = noise_block(kStreamResampleTile, j, uint32_t(t0) >> 2, uint32_t(req), p.round32, p.key0, p.key1);
-        const uint32_t w_lo = (t0 & 2) ? tw.z : tw.x, w_hi = (t0 & 2) ? tw.w : tw.y;
-        const float g = gumbel2(h ? w_hi : w_lo);
+        if (t == t_begin || (t & 3) == 0)
+            tw = noise_block(kStreamResampleTile, j, uint32_t(t) >> 2, uint32_t(req), p.round32, p.key0, p.key1);
+        const float g = gumbel2(u4get(tw, t & 3));
+        float Lt;
         if (resid) {
             float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                r0 += fmaxf(fast_exp2(__builtin_fmaf(p0[e], sc, -lse2t)) - fast_exp2(__builtin_fmaf(c0[e], sc, -lse2q)),
+            for (int e = 0; e < 16; e += 2) {
+                r0 += fmaxf(fast_exp2(__builtin_fmaf(pv[e], sc, -lse2t)) - fast_exp2(__builtin_fmaf(c[e], sc, -lse2q)),
                             0.f);
-                r1 += fmaxf(fast_exp2(__builtin_fmaf(p1[e], sc, -lse2t)) - fast_exp2(__builtin_fmaf(c1[e], sc, -lse2q)),
+                r1 += fmaxf(fast_exp2(__builtin_fmaf(pv[e + 1], sc, -lse2t)) -
+                                fast_exp2(__builtin_fmaf(c[e + 1], sc, -lse2q)),
                             0.f);
             }
-            const float rt = r0 + r1;
+            const float rt = half_sum(r0 + r1);
             S += rt;
-            const float Lt = rt > 0.f ? fast_log2(rt) + g : kNegInf;
-            if (Lt > st.best) {
-                st.best = Lt;
-                st.bt = t0 + h;
-            }
+            Lt = rt > 0.f ? fast_log2(rt) + g : kNegInf;
         } else {
-            race_tile<false>(st, p0, p1, sc, true, t0 + h, g);
+            float mh = max3f(pv[0], pv[1], pv[2]);
+#pragma unroll
+            for (int e = 3; e < 15; e += 2) mh = max3f(mh, pv[e], pv[e + 1]);
+            mh = max3f(mh, pv[15], pv[15]) * sc;
+            const float mt = half_max(mh);
+            const float mg = (mt == kNegInf) ? 0.f : mt;
+            float sh = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sh += fast_exp2(__builtin_fmaf(pv[e], sc, -mg));
+            const float st = half_sum(sh);
+            Lt = mg + fast_log2(st) + g;
+        }
+        if (Lt > best) {
+            best = Lt;
+            bt = t;
         }
     };
 
-    if (nfull > 0) {
-        if (need_w2) dma.template issue<false>(W2, v0_of(0), p.V, ldsW, wave);
-        if (wave_ok) stg.template issue<false>(v0_of(0), p.V, tregion, lane);
-        if (resid) su.template issue<false>(v0_of(0), p.V, uregion, lane);
-    }
-    for (int i = 0; i < nfull; ++i) {
-        const bool more = i + 1 < nfull;
+    using NoClamp = std::integral_constant<bool, false>;
+    using Clamp = std::integral_constant<bool, true>;
+    if (nfull > 0) issue(t_begin, ldsW0, ldsU0, ldsT0, NoClamp{});
+    for (int i = 0; i < nfull; i += 2) {
+        const int t = t_begin + i;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage i have landed
-        __syncthreads();                // ... and every thread's
-        f32x16_t p0, p1, c0, c1;
-        if (wave_ok) {
-            // U first (it seeds the MFMAs), the target rows after the MFMAs;
-            // each region is refilled with the next stage once it has been read
-            if (resid) {
-                su.read(uregion, lane, c0, c1);
-                if (more) {
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                    su.template issue<false>(v0_of(i + 1), p.V, uregion, lane);
-                }
-                bias_pair_lds(ef, ldsW, lane, c0, c1);
-            }
-            stg.read_swapped(tregion, lane, p0, p1);
-            if (more) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                stg.template issue<false>(v0_of(i + 1), p.V, tregion, lane);
-            }
-        }
-        __syncthreads();  // every wave is done with ldsW
-        if (need_w2 && more) dma.template issue<false>(W2, v0_of(i + 1), p.V, ldsW, wave);
-        if (wave_ok) score(p0, p1, c0, c1, t_begin + 2 * i, false);
+        __syncthreads();                // ... and every thread's; the 1-buffers are free again
+        if (i + 1 < nfull) issue(t + 1, ldsW1, ldsU1, ldsT1, NoClamp{});
+        if (wave_ok) stage(t, ldsW0, ldsU0, ldsT0, false);
+        if (i + 1 >= nfull) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // stage i + 1 has landed; the 0-buffers are free again
+        if (i + 2 < nfull) issue(t + 2, ldsW0, ldsU0, ldsT0, NoClamp{});
+        if (wave_ok) stage(t + 1, ldsW1, ldsU1, ldsT1, false);
     }
     if (tail) {
-        __syncthreads();  // every wave is done with ldsW and its regions
-        if (need_w2) dma.template issue<true>(W2, v0_of(nfull), p.V, ldsW, wave);
-        if (wave_ok) stg.template issue<true>(v0_of(nfull), p.V, tregion, lane);
-        if (resid) su.template issue<true>(v0_of(nfull), p.V, uregion, lane);
+        __syncthreads();  // every wave is done with every buffer
+        issue(t_end - 1, ldsW0, ldsU0, ldsT0, Clamp{});
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (wave_ok) {
-            f32x16_t p0, p1, c0, c1;
-            stg.read_swapped(tregion, lane, p0, p1);
-            if (resid) {
-                su.read(uregion, lane, c0, c1);
-                bias_pair_lds(ef, ldsW, lane, c0, c1);
-            }
-            score(p0, p1, c0, c1, t_begin + 2 * nfull, true);
-        }
-    }
-    // the two lane halves raced alternate tiles of the same request
-    S += __shfl_xor(S, 32);
-    {
-        const float b2 = __shfl_xor(st.best, 32);
-        const int i2 = __shfl_xor(st.bt, 32);
-        float sec = kNegInf;
-        best_merge(st.best, st.bt, sec, b2, i2, kNegInf);
+        if (wave_ok) stage(t_end - 1, ldsW0, ldsU0, ldsT0, true);
     }
     if (h == 0 && ok) {
         const size_t o = size_t(slot) * p.nchunk + chunk;
         p.dw_sum[o] = S;
-        p.dw_bl[o] = st.best;
-        p.dw_bt[o] = st.bt;
+        p.dw_bl[o] = best;
+        p.dw_bt[o] = bt;
     }
 }
 
@@ -850,20 +846,20 @@ VerifyPlan verify_plan(int B, int gamma, int V) {
     // Position passes split a row into segments of whole float4 groups: the
     // first pass, which reads every request's row, in a few long ones (long
     // streams per workgroup), the later ones, which read fewer and fewer rows,
-    // in up to 16 short ones (more workgroups per row).
+    // in up to 32 short ones (more waves per row).
     const int n4 = (V + 3) / 4;
     auto split = [&](int k, int &nseg, int &len) {
         len = 4 * ((n4 + k - 1) / k);
         nseg = (V + len - 1) / len;
     };
     split(4, p.nseg_first, p.seg_len_first);
-    split(16, p.nseg, p.seg_len);
+    split(32, p.nseg, p.seg_len);
     p.nseg_max = std::max(p.nseg_first, p.nseg);
     p.nbb = (B + 31) / 32;
-    // 8-wave workgroups holding one 2-tile W2 stage and the wave regions
-    // (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them for the
-    // requests; chunks are whole 2-tile stages
-    p.tile = tile_walk_plan(B, V, kDrawThreads / 64, 256, 2);
+    // 8-wave workgroups holding two one-tile stages of W2 rows and wave
+    // regions (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them
+    // for the requests
+    p.tile = tile_walk_plan(B, V, kDrawThreads / 64, 256, 1);
     // the residual and bonus lists hold at most B requests but each rounds up to 32
     p.draw_nbg = (p.nbb + 1 + kDrawThreads / 64 - 1) / (kDrawThreads / 64);
     p.draw_blocks = p.tile.nchunk * p.draw_nbg;
