@@ -30,6 +30,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 KERNEL_SOURCES = ["draft_sampling_verification_02_amd/csrc/draft.hip",
+                  "draft_sampling_verification_02_amd/csrc/stage.hpp",
                   "draft_sampling_verification_02_amd/csrc/device_common.hpp"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "draft_step_large_batch_counters.md")
 
@@ -67,7 +68,7 @@ def main():
     if args.copy_probe:
         import torch
         n = args.copy_probe << 20
-        src = torch.full((n // 4,), 7.0, dtype=torch.float32, device="cuda")
+        src = torch.empty(n // 4, dtype=torch.float32, device="cuda").uniform_()  # not an elementwise kernel
         dst = torch.empty_like(src)
         for _ in range(5):
             torch.mul(src, 1.0, out=dst)  # an elementwise kernel: reads n bytes, writes n bytes
