@@ -159,39 +159,14 @@ struct EFrags<float, R> {
     }
 };
 
-template <int R>
-__device__ __forceinline__ f32x16_t bias_tile(const EFrags<uint16_t, R> &ef, const uint16_t *w2row, int h) {
-    f32x16_t acc = {};
-#pragma unroll
-    for (int s = 0; s < EFrags<uint16_t, R>::S; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4 *>(w2row + 16 * s + 8 * h);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                      __builtin_bit_cast(bf16x8_t, ef.e[s]), acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-template <int R>
-__device__ __forceinline__ f32x16_t bias_tile(const EFrags<float, R> &ef, const float *w2row, int h) {
-    f32x16_t acc = {};
-#pragma unroll
-    for (int q = 0; q < EFrags<float, R>::Q; ++q) {
-        const float4 a = *reinterpret_cast<const float4 *>(w2row + 8 * q + 4 * h);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, ef.e[q].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, ef.e[q].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, ef.e[q].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, ef.e[q].w, acc, 0, 0, 0);
-    }
-    return acc;
-}
-
 // W2 tile staged in LDS.  A tile is the 32 rows v0 .. v0 + 31 of W2, RB bytes
 // each (RB = r * element size), split into CPR = RB / 16 chunks of 16 bytes.
-// Row m's logical chunk c sits in physical chunk c ^ (m & (CPR - 1)), so the
-// 32 rows an MFMA fragment read touches at one chunk index fall in distinct
-// banks.  The tile is filled by direct global-to-LDS loads: each wave
-// instruction writes 64 consecutive 16-byte slots, lane i the i-th, and every
-// lane fetches the global chunk that belongs in its slot.
+// Within each group of SW = min(CPR, 16) chunks, row m's logical chunk c sits
+// at c ^ (m & (SW - 1)), so the rows an MFMA fragment read touches at one
+// chunk index fall in distinct banks.  The tile is filled by direct
+// global-to-LDS loads: each wave instruction writes 64 consecutive 16-byte
+// slots, lane i the i-th, and every lane fetches the global chunk that
+// belongs in its slot.
 template <typename WT, int R>
 struct TileLDS {
     static constexpr int RB = R * int(sizeof(WT));
@@ -204,23 +179,6 @@ struct TileLDS {
     // XORed with the row, so the rows that one LDS cycle serves hit distinct banks
     __device__ static __forceinline__ int chunk(int m, int c) { return (c & ~(SW - 1)) | ((c ^ m) & (SW - 1)); }
 };
-
-// Issue the loads of W2 rows v0 .. v0 + 31 (clamped to V - 1) into `buf`;
-// `nthreads` threads of the workgroup take part.
-template <typename WT, int R>
-__device__ __forceinline__ void tile_issue(const WT *W2, int v0, int V, uint8_t *buf, int nthreads) {
-    using L = TileLDS<WT, R>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int s0 = wave * 64; s0 < L::SLOTS; s0 += nthreads) {
-        const int slot = s0 + lane;
-        const int m = slot / L::CPR;
-        const int c = L::chunk(m, slot % L::CPR);
-        const int vrow = min(v0 + m, V - 1);
-        const uint8_t *g = reinterpret_cast<const uint8_t *>(W2) + size_t(vrow) * L::RB + c * 16;
-        __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(buf + s0 * 16),
-                                         16, 0, 0);
-    }
-}
 
 // The Markov-bias MFMA tile with the A operand (W2 rows) read from an LDS tile.
 template <int R>
@@ -255,63 +213,41 @@ __device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<float, R> &ef, co
     return acc;
 }
 
-// One Markov-bias entry sum_i W1[prev][i] W2[v][i] on the vector ALUs, split
-// over the two lane halves: half h sums i in [h R/2, (h+1) R/2); the halves'
-// sums are added with a lane swap.  Used for the within-tile second level.
+// One lane half's share of a W1 row (entries [h * R/2, (h + 1) * R/2)) held
+// in registers, and its dot product with the same share of a W2 row.
 template <typename WT, int R>
-__device__ __forceinline__ float bias_entry(const WT *W1row, const WT *W2row, int h) {
-    float d = 0.f;
-    constexpr int HALF = R / 2;
-    if constexpr (sizeof(WT) == 2) {
+struct RowHalf {
+    static constexpr int HALF = R / 2;
+    static constexpr int N = HALF * int(sizeof(WT)) / 16;  // 16-byte pieces
+    uint4 w[N];
+    __device__ __forceinline__ void load(const WT *row, int h) {
+        const uint4 *q = reinterpret_cast<const uint4 *>(row + h * HALF);
 #pragma unroll
-        for (int q = 0; q < HALF / 8; ++q) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(W1row + h * HALF + 8 * q);
-            const uint4 w = *reinterpret_cast<const uint4 *>(W2row + h * HALF + 8 * q);
-            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, wv[4] = {w.x, w.y, w.z, w.w};
+        for (int i = 0; i < N; ++i) w[i] = q[i];
+    }
+    // the full dot product W1row . W2row, summed over the two lane halves
+    __device__ __forceinline__ float dot(const WT *W2row, int h) const {
+        const uint4 *q = reinterpret_cast<const uint4 *>(W2row + h * HALF);
+        uint4 x[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = q[i];
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t av[4] = {w[i].x, w[i].y, w[i].z, w[i].w}, xv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                d = __builtin_fmaf(__uint_as_float(av[e] << 16), __uint_as_float(wv[e] << 16), d);
-                d = __builtin_fmaf(__uint_as_float(av[e] & 0xFFFF0000u), __uint_as_float(wv[e] & 0xFFFF0000u), d);
+                if constexpr (sizeof(WT) == 2) {
+                    d = __builtin_fmaf(__uint_as_float(av[e] << 16), __uint_as_float(xv[e] << 16), d);
+                    d = __builtin_fmaf(__uint_as_float(av[e] & 0xFFFF0000u), __uint_as_float(xv[e] & 0xFFFF0000u), d);
+                } else {
+                    d = __builtin_fmaf(__uint_as_float(av[e]), __uint_as_float(xv[e]), d);
+                }
             }
         }
-    } else {
-#pragma unroll
-        for (int q = 0; q < HALF / 4; ++q) {
-            const float4 a = *reinterpret_cast<const float4 *>(W1row + h * HALF + 4 * q);
-            const float4 w = *reinterpret_cast<const float4 *>(W2row + h * HALF + 4 * q);
-            d = __builtin_fmaf(a.x, w.x, d);
-            d = __builtin_fmaf(a.y, w.y, d);
-            d = __builtin_fmaf(a.z, w.z, d);
-            d = __builtin_fmaf(a.w, w.w, d);
-        }
+        return d + __shfl_xor(d, 32);
     }
-    return d + __shfl_xor(d, 32);
-}
-
-// Four consecutive logits starting at v (v % 4 == 0); entries at or past V read
-// as -inf.  `vec` says the row allows aligned 16-byte loads.
-__device__ __forceinline__ float4 load4_masked(const float *row, int v, int V, bool vec) {
-    if (vec && v + 3 < V) return *reinterpret_cast<const float4 *>(row + v);
-    float4 r;
-    r.x = (v + 0 < V) ? row[v + 0] : kNegInf;
-    r.y = (v + 1 < V) ? row[v + 1] : kNegInf;
-    r.z = (v + 2 < V) ? row[v + 2] : kNegInf;
-    r.w = (v + 3 < V) ? row[v + 3] : kNegInf;
-    return r;
-}
-
-// The 16 entries of a row that lane half h holds in tile t: t*32 + 8i + 4h + j
-// (entries at or past V read as -inf).
-__device__ __forceinline__ void load_tile_row(const float *row, int t, int h, int V, bool vec, float4 out[4]) {
-    const int v0 = t * kTile;
-    if (vec && v0 + kTile <= V) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = *reinterpret_cast<const float4 *>(row + v0 + 8 * i + 4 * h);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = load4_masked(row, v0 + 8 * i + 4 * h, V, vec);
-    }
-}
+};
 
 // Two C-initialised MFMA chains over the two 32-row tiles of a stage (buf and
 // buf + one tile), sharing the E fragments; the A fragments are read from LDS
@@ -377,49 +313,6 @@ __device__ __forceinline__ void bias_pair_lds(const EFrags<float, R> &ef, const 
         c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x1.w, e.w, c1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-// One 32-entry tile of a logit row in the accumulator layout of the 32x32
-// MFMA: value 4i+j of lane (n, h) is entry v0 + 8i + 4h + j.  Entries at or
-// beyond V read as -inf, so a tile that starts past the row end is all -inf.
-// VEC: the row allows aligned 16-byte loads (V % 4 == 0, 16-byte aligned rows).
-template <bool VEC>
-__device__ __forceinline__ f32x16_t load_acc_tile(const float *row, int v0, int h, int V, bool tail) {
-    f32x16_t c;
-    if (!tail) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float4 x;
-            if constexpr (VEC) {
-                x = *reinterpret_cast<const float4 *>(row + v0 + 8 * i + 4 * h);
-            } else {
-                const float *q = row + v0 + 8 * i + 4 * h;
-                x = make_float4(q[0], q[1], q[2], q[3]);
-            }
-            c[4 * i] = x.x;
-            c[4 * i + 1] = x.y;
-            c[4 * i + 2] = x.z;
-            c[4 * i + 3] = x.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int v = v0 + 8 * i + 4 * h;
-            if constexpr (VEC) {
-                // V % 4 == 0: a 4-entry group is either wholly inside the row or wholly past it
-                float4 x = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-                if (v < V) x = *reinterpret_cast<const float4 *>(row + v);
-                c[4 * i] = x.x;
-                c[4 * i + 1] = x.y;
-                c[4 * i + 2] = x.z;
-                c[4 * i + 3] = x.w;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) c[4 * i + j] = (v + j < V) ? row[v + j] : kNegInf;
-            }
-        }
-    }
-    return c;
 }
 
 // x of lane n plus (or max with) x of lane n ^ 32, in every lane: one

@@ -187,19 +187,44 @@ struct ReduceParams {
     float *lse_out, *qx_out, *margin_out;
 };
 
+// One wave per request.  The loads that do not depend on the winning tile
+// (the W1 row, the chunk partials) go out together; the winning tile's W2
+// rows and U entries go out together once it is known.
 template <typename WT, int R>
 __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= p.B) return;
     const bool track2 = p.margin_out != nullptr;
-    // level 1: row logsumexp and the winning tile
+    const int i = lane & 31, h = lane >> 5;
+    int prev = p.xprev[size_t(b) * p.xprev_stride];
+    prev = min(max(prev, 0), p.V - 1);
+    const float T = p.temperature[b];
+    RowHalf<WT, R> w1;
+    w1.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    // level 1: row logsumexp and the winning tile, four chunks a lane per batch
     float m = kNegInf, s = 0.f, best = kNegInf, second = kNegInf;
     int bt = 0x7fffffff;
-    for (int c = lane; c < p.nchunk; c += 64) {
-        const size_t o = size_t(b) * p.nchunk + c;
-        lse_merge(m, s, p.pm[o], p.ps[o]);
-        best_merge(best, bt, second, p.pb[o], p.pi[o], track2 ? p.p2[o] : kNegInf);
+    constexpr int PC = 4;
+    for (int c0 = 0; c0 < p.nchunk; c0 += 64 * PC) {
+        float cm[PC], cs[PC], cb[PC], c2[PC];
+        int ci[PC];
+#pragma unroll
+        for (int u = 0; u < PC; ++u) {
+            const int c = c0 + lane + 64 * u;
+            const bool in = c < p.nchunk;
+            const size_t o = size_t(b) * p.nchunk + (in ? c : 0);
+            cm[u] = in ? p.pm[o] : kNegInf;
+            cs[u] = in ? p.ps[o] : 0.f;
+            cb[u] = in ? p.pb[o] : kNegInf;
+            ci[u] = in ? p.pi[o] : 0x7fffffff;
+            c2[u] = (in && track2) ? p.p2[o] : kNegInf;
+        }
+#pragma unroll
+        for (int u = 0; u < PC; ++u) {
+            lse_merge(m, s, cm[u], cs[u]);
+            best_merge(best, bt, second, cb[u], ci[u], c2[u]);
+        }
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -211,19 +236,14 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     }
     const int tile = min(max(bt, 0), p.ntiles - 1);
     // level 2: the winning tile's logits on the vector ALUs, then the entry race
-    int prev = p.xprev[size_t(b) * p.xprev_stride];
-    prev = min(max(prev, 0), p.V - 1);
-    const float T = p.temperature[b];
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    const int i = lane & 31, h = lane >> 5;
     const int v = tile * kTile + i;
     const bool valid = v < p.V;
     const int vc = min(v, p.V - 1);
-    const WT *W1 = static_cast<const WT *>(p.W1);
-    const WT *W2 = static_cast<const WT *>(p.W2);
-    const float d = bias_entry<WT, R>(W1 + size_t(prev) * R, W2 + size_t(vc) * R, h);
-    const float logit = valid ? p.U[size_t(b) * p.u_stride + vc] + d : kNegInf;
+    const float u_v = p.U[size_t(b) * p.u_stride + vc];
+    const float d = w1.dot(static_cast<const WT *>(p.W2) + size_t(vc) * R, h);
+    const float logit = valid ? u_v + d : kNegInf;
     const float z2 = logit * sc;
     float score = logit;
     if (sampled) score = z2 + gumbel2(noise_word(kStreamDraft, p.k, uint32_t(vc), uint32_t(b), p.round32, p.key0, p.key1));

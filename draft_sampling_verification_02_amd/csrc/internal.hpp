@@ -89,6 +89,8 @@ struct VerifyWork {
     int32_t *seg_i;      // [2, B, nseg] per-segment lowest-index argmax
     float *seg_tx;       // [2, B] t(x_j) / T in log2 units for the accept test
     float *fin_lse2;     // [B] logsumexp (log2 units) of the row the draw uses
+    int32_t *prev;       // [B] x_{j-1} of a residual draw at position j (the anchor for j = 1)
+    float *lse2q;        // [B] log2-unit logsumexp of q_j for a residual draw
     int32_t *mode;       // [B] 0 done, 1 residual draw, 2 bonus draw, -1 invalid
     int32_t *jpos;       // [B] position of the emitted non-draft token
     int32_t *slot;       // [B] draw slot: list index, + B for the bonus list

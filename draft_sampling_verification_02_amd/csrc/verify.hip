@@ -186,8 +186,10 @@ struct PassParams {
     int32_t *act_out;
     float *pm_out, *ps_out, *pv_out, *tx_out;
     int32_t *pi_out;
-    int32_t *status, *mode, *jpos, *slot, *resid_list, *bonus_list;
-    float *fin_lse2;
+    int32_t *status, *mode, *jpos, *slot, *resid_list, *bonus_list, *prev;
+    float *fin_lse2, *lse2q;
+    const int32_t *anchor;
+    const float *lse_q;
     int32_t *n_accept_out, *tokens_out;
     float *diag_out;
 };
@@ -245,6 +247,9 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
         p.resid_list[e] = b;
         p.slot[b] = e;
         p.mode[b] = kModeResidual;
+        // what the residual draw needs to rebuild q_k
+        p.prev[b] = min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
+        p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + k - 1] * kLog2e;
     }
     return false;
 }
@@ -401,8 +406,8 @@ struct DrawParams {
     int B, gamma, V;
     int nbg, ntiles, tiles_per_chunk, nchunk;
     uint32_t key0, key1, round32;
-    const int32_t *status, *resid_list, *bonus_list, *jpos, *off;
-    const float *fin_lse2;
+    const int32_t *status, *resid_list, *bonus_list, *jpos, *off, *prev;
+    const float *fin_lse2, *lse2q;
     float *dw_sum, *dw_bl;
     int32_t *dw_bt;
 };
@@ -467,11 +472,9 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
     int urow_i = -1;  // row of U
     float lse2q = 0.f;
     if (resid) {
-        int prev = (j == 1) ? p.anchor[req] : p.x[size_t(req) * p.gamma + j - 2];
-        prev = min(max(prev, 0), p.V - 1);
-        ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+        ef.load(static_cast<const WT *>(p.W1) + size_t(p.prev[req]) * R, h);
         if (ok) urow_i = req * p.gamma + j - 1;
-        lse2q = p.lse_q[size_t(req) * p.gamma + j - 1] * kLog2e;
+        lse2q = p.lse2q[req];
     }
     TileDMA<WT, R, kDrawThreads> dma;
     if (need_w2) dma.init(tid);
@@ -582,8 +585,8 @@ struct FinishParams {
     const float *lse_q, *temperature;
     int B, gamma, V, nchunk, ntiles;
     uint32_t key0, key1, round32;
-    const int32_t *status, *mode, *n_accept, *slot, *off;
-    const float *fin_lse2;
+    const int32_t *status, *mode, *n_accept, *slot, *off, *jpos, *prev;
+    const float *fin_lse2, *lse2q;
     const float *dw_sum, *dw_bl;
     const int32_t *dw_bt;
     int32_t *tokens_out, *out_offsets;
@@ -630,23 +633,43 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     if (b >= p.B) return;
     const int mode = p.mode[b];
     if (mode != kModeResidual && mode != kModeBonus) return;
-    const int slot = p.slot[b];
+    // loads that do not depend on the winning tile, in two rounds
+    const int slot = p.slot[b], j = p.jpos[b];
+    const float sc = kLog2e / p.temperature[b];
+    const float lse2t = p.fin_lse2[b];
+    const int trow_i = p.off[b] + j - 1;
+    const float *trow = p.target + size_t(trow_i) * p.V;
+    RowHalf<WT, R> w1;
+    float lse2q = 0.f;
+    if (mode == kModeResidual) {
+        w1.load(static_cast<const WT *>(p.W1) + size_t(p.prev[b]) * R, lane >> 5);
+        lse2q = p.lse2q[b];
+    }
     float S = 0.f, bl = kNegInf;
     int tile = 0x7fffffff;
-    for (int c = lane; c < p.nchunk; c += 64) {
-        const size_t o = size_t(slot) * p.nchunk + c;
-        S += p.dw_sum[o];
-        argmax_merge(bl, tile, p.dw_bl[o], p.dw_bt[o]);
+    constexpr int PC = 4;
+    for (int c0 = 0; c0 < p.nchunk; c0 += 64 * PC) {
+        float cs[PC], cb[PC];
+        int ct[PC];
+#pragma unroll
+        for (int u = 0; u < PC; ++u) {
+            const int c = c0 + lane + 64 * u;
+            const bool in = c < p.nchunk;
+            const size_t o = size_t(slot) * p.nchunk + (in ? c : 0);
+            cs[u] = in ? p.dw_sum[o] : 0.f;
+            cb[u] = in ? p.dw_bl[o] : kNegInf;
+            ct[u] = in ? p.dw_bt[o] : 0x7fffffff;
+        }
+#pragma unroll
+        for (int u = 0; u < PC; ++u) {
+            S += cs[u];
+            argmax_merge(bl, tile, cb[u], ct[u]);
+        }
     }
     S = wave_sum(S);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) argmax_merge(bl, tile, __shfl_xor(bl, o), __shfl_xor(tile, o));
 
-    const int j = p.n_accept[b] + 1;
-    const float sc = kLog2e / p.temperature[b];
-    const int trow_i = p.off[b] + j - 1;
-    const float *trow = p.target + size_t(trow_i) * p.V;
-    const float lse2t = p.fin_lse2[b];
     const int i = lane & 31, h = lane >> 5;
     const bool use_res = mode == kModeResidual && S > 0.f && bl > kNegInf;
     if (mode == kModeResidual && !use_res) {
@@ -676,13 +699,9 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     const float tt = trow[vc] * sc;
     float score;
     if (use_res) {
-        int prev = (j == 1) ? p.anchor[b] : p.x[size_t(b) * p.gamma + j - 2];
-        prev = min(max(prev, 0), p.V - 1);
-        const WT *W1 = static_cast<const WT *>(p.W1);
-        const WT *W2 = static_cast<const WT *>(p.W2);
-        const float d = bias_entry<WT, R>(W1 + size_t(prev) * R, W2 + size_t(vc) * R, h);
-        const float lse2q = p.lse_q[size_t(b) * p.gamma + j - 1] * kLog2e;
-        const float logit = p.U[(size_t(b) * p.gamma + j - 1) * p.V + vc] + d;
+        const float u_v = p.U[(size_t(b) * p.gamma + j - 1) * p.V + vc];
+        const float d = w1.dot(static_cast<const WT *>(p.W2) + size_t(vc) * R, h);
+        const float logit = u_v + d;
         const float q = fast_exp2(__builtin_fmaf(logit, sc, -lse2q));
         const float pv = fast_exp2(tt - lse2t);
         const float res = fmaxf(pv - q, 0.f);
@@ -753,6 +772,10 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.resid_list = w.resid_list;
         pp.bonus_list = w.bonus_list;
         pp.fin_lse2 = w.fin_lse2;
+        pp.prev = w.prev;
+        pp.lse2q = w.lse2q;
+        pp.anchor = a.anchor;
+        pp.lse_q = a.lse_q;
         pp.n_accept_out = a.n_accept_out;
         pp.tokens_out = a.tokens_out;
         pp.diag_out = a.diag_out;
@@ -789,6 +812,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.jpos = w.jpos;
         dp.off = w.off;
         dp.fin_lse2 = w.fin_lse2;
+        dp.prev = w.prev;
+        dp.lse2q = w.lse2q;
         dp.dw_sum = w.dw_sum;
         dp.dw_bl = w.dw_bl;
         dp.dw_bt = w.dw_bt;
@@ -824,6 +849,9 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         fp.slot = w.slot;
         fp.off = w.off;
         fp.fin_lse2 = w.fin_lse2;
+        fp.jpos = w.jpos;
+        fp.prev = w.prev;
+        fp.lse2q = w.lse2q;
         fp.dw_sum = w.dw_sum;
         fp.dw_bl = w.dw_bl;
         fp.dw_bt = w.dw_bt;
@@ -881,6 +909,8 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     w.seg_i = c.take<int32_t>(ns);
     w.seg_tx = c.take<float>(size_t(2) * B);
     w.fin_lse2 = c.take<float>(B);
+    w.prev = c.take<int32_t>(B);
+    w.lse2q = c.take<float>(B);
     w.mode = c.take<int32_t>(B);
     w.jpos = c.take<int32_t>(B);
     w.slot = c.take<int32_t>(B);
