@@ -82,12 +82,12 @@ VerifyPlan verify_plan(int B, int gamma, int V);
 struct VerifyWork {
     int32_t *status;     // [4] device status flags, -, n_resid, n_bonus
     int32_t *off;        // [B + 1] packed row offsets in use
-    // position passes, double buffered by pass parity: pass j reads the half
-    // pass j - 1 wrote
-    int32_t *act;        // [2, B] 1: the request's row of that pass was reduced
-    float *seg_m, *seg_s, *seg_v;  // [2, B, nseg] per-segment max, sum of 2^(z - max), best value
-    int32_t *seg_i;      // [2, B, nseg] per-segment lowest-index argmax
-    float *seg_tx;       // [2, B] t(x_j) / T in log2 units for the accept test
+    // position passes, double buffered by pass parity (pass p reads the half
+    // pass p - 1 wrote), one slot per row a pass reduces
+    int32_t *act;        // [2, B] 1: the request's rows of that pass were reduced
+    float *seg_m, *seg_s, *seg_v;  // [2, rows, B, nseg] per-segment max, sum of 2^(z - max), best value
+    int32_t *seg_i;      // [2, rows, B, nseg] per-segment lowest-index argmax
+    float *seg_tx;       // [2, rows, B] t(x_j) / T in log2 units for the accept test
     float *fin_lse2;     // [B] logsumexp (log2 units) of the row the draw uses
     int32_t *prev;       // [B] x_{j-1} of a residual draw at position j (the anchor for j = 1)
     float *lse2q;        // [B] log2-unit logsumexp of q_j for a residual draw

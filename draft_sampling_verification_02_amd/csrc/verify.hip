@@ -168,19 +168,28 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
 
 // ------------------------------------------------------------------ position pass
 
+// Rows a position pass reduces: pass p reduces positions (p-1)*D+1 .. p*D of
+// the requests still testing and decides the D positions pass p - 1 reduced.
+// With D = 2 a request that rejects at the first of a pair has the second row
+// read for nothing, in exchange for (gamma + 1) / 2 + 1 passes instead of
+// gamma + 2; at the headline size the extra bytes cost more than the passes
+// they save, so one row a pass it is.
+constexpr int kPassRows = 1;
+
 struct PassParams {
     const float *target;
     const int32_t *x, *ell;
     const float *qx, *temperature;
-    int B, gamma, V, j, vec;
+    int B, gamma, V, j0, vec;  // j0: first position this pass reduces
     int nseg, seg_len;  // this pass's segments of a row
     int nseg_in;        // the previous pass's
     int seg_stride;     // partials per request in the buffers
+    size_t row_stride;  // partials per row slot of a pass (B * seg_stride)
     uint32_t key0, key1, round32;
     const int32_t *off;
-    // pass j reads what pass j - 1 left (row j - 1 of every request it reduced)
-    // and writes its own row j into the other half of each double buffer
-    const int32_t *act_in;  // [B] 1: row j - 1 was reduced
+    // pass p reads what pass p - 1 left and writes into the other half of
+    // each double buffer; slot q holds the pass's q-th row
+    const int32_t *act_in;  // [B] 1: the request's rows of the previous pass were reduced
     const float *pm_in, *ps_in, *pv_in, *tx_in;
     const int32_t *pi_in;
     int32_t *act_out;
@@ -254,39 +263,52 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
     return false;
 }
 
-// Pass j = 1..gamma+2, one wave per (request, vocabulary segment), four
-// requests to a workgroup.  First the request's position j - 1 is decided
-// from the segment statistics pass j - 1 wrote; a request that goes on
-// streams segment sg of its row j: every lane keeps its own running max / sum
-// of exp2 and argmax over batches of eight float4 loads, and the wave merges
-// them.  The waves never wait for one another.
+// Pass p, one wave per (request, row slot q, vocabulary segment), four
+// requests to a workgroup.  First the request's previous D positions are
+// decided, in order, from the segment statistics pass p - 1 wrote; a request
+// that goes on streams segment sg of its row j0 + q: every lane keeps its own
+// running max / sum of exp2 and argmax over batches of eight float4 loads,
+// and the wave merges them.  The waves never wait for one another.
 __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
+    constexpr int D = kPassRows;
+    static_assert(D <= 2, "two row slots fit the two lane halves");
     const int sg = blockIdx.x % p.nseg;
-    const int b = (blockIdx.x / p.nseg) * 4 + (threadIdx.x >> 6);
-    const int j = p.j;
+    const int q = (blockIdx.x / p.nseg) % D;
+    const int b = (blockIdx.x / (p.nseg * D)) * 4 + (threadIdx.x >> 6);
+    const int j0 = p.j0, j = j0 + q;
     const int lane = threadIdx.x & 63;
     if (b >= p.B) return;
-    const bool writer = sg == 0;
-    // every load the decision needs, issued together: the previous pass's
-    // segment statistics (one per lane) are read whatever the request's state
+    const bool writer = sg == 0 && q == 0;
+    // every load the decisions need, issued together: lane half h holds the
+    // segment statistics of the previous pass's row slot h, read whatever the
+    // request's state
     const int mode = p.mode[b];
-    const int act = j > 1 ? p.act_in[b] : 1;
+    const int act = j0 > 1 ? p.act_in[b] : 1;
     const float T = p.temperature[b];
     const int L = p.ell[b];
-    float mm = kNegInf, s2 = 0.f, v2 = kNegInf, tx2 = 0.f, qk = 0.f;
-    int i2 = 0x7fffffff, xk = 0;
-    if (j > 1) {
-        if (lane < p.nseg_in) {
-            const size_t o = size_t(b) * p.seg_stride + lane;
+    float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
+    int i2 = 0x7fffffff;
+    float tx2[D], qk[D];
+    int xk[D];
+    if (j0 > 1) {
+        const int hq = lane >> 5, c = lane & 31;
+        if (hq < D && c < p.nseg_in) {
+            const size_t o = hq * p.row_stride + size_t(b) * p.seg_stride + c;
             mm = p.pm_in[o];
             s2 = p.ps_in[o];
             v2 = p.pv_in[o];
             i2 = p.pi_in[o];
         }
-        tx2 = p.tx_in[b];
-        if (j - 1 <= p.gamma) {
-            xk = p.x[size_t(b) * p.gamma + j - 2];
-            qk = p.qx[size_t(b) * p.gamma + j - 2];
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int k = j0 - D + u;  // position decided from slot u
+            tx2[u] = p.tx_in[size_t(u) * p.B + b];
+            xk[u] = 0;
+            qk[u] = 0.f;
+            if (k <= p.gamma) {
+                xk[u] = p.x[size_t(b) * p.gamma + k - 1];
+                qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
+            }
         }
     }
     if (mode < 0 || act == 0) {
@@ -295,23 +317,36 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     }
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    if (j > 1) {
+    if (j0 > 1) {
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
+        for (int o = 1; o < 32; o <<= 1) {  // within each lane half
             lse_merge(mm, s2, __shfl_xor(mm, o), __shfl_xor(s2, o));
             argmax_merge(v2, i2, __shfl_xor(v2, o), __shfl_xor(i2, o));
         }
+        float lse2[D];
+        int amax[D];
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const float mu = __shfl(mm, 32 * u), su = __shfl(s2, 32 * u);
+            lse2[u] = (mu == kNegInf) ? kNegInf : mu + fast_log2(su);
+            amax[u] = min(max(__shfl(i2, 32 * u), 0), p.V - 1);
+        }
         int go_on = 0;
         if (lane == 0) {
-            const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(s2);
-            go_on = pass_decide(p, b, L, j - 1, sampled, lse2, min(max(i2, 0), p.V - 1), tx2, xk, qk, writer);
+            go_on = 1;
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                const int k = j0 - D + u;
+                if (!go_on || k > L + 1) break;
+                go_on = pass_decide(p, b, L, k, sampled, lse2[u], amax[u], tx2[u], xk[u], qk[u], writer);
+            }
         }
         if (!__shfl(go_on, 0)) {
             if (writer && lane == 0) p.act_out[b] = 0;
             return;
         }
     }
-    if (j > L + 1) {  // nothing left to reduce (the decision above ended it)
+    if (j > L + 1) {  // no row at this slot (slot 0 always has one once the request goes on)
         if (writer && lane == 0) p.act_out[b] = 0;
         return;
     }
@@ -382,7 +417,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         argmax_merge(av, ai, __shfl_xor(av, o), __shfl_xor(ai, o));
     }
     if (lane == 0) {
-        const size_t o = size_t(b) * p.seg_stride + sg;
+        const size_t o = q * p.row_stride + size_t(b) * p.seg_stride + sg;
         p.pm_out[o] = m;
         p.ps_out[o] = s;
         p.pv_out[o] = av;
@@ -391,7 +426,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         // t(x_j) for the accept test at j, from the segment that holds x_j
         if (sampled && j <= L) {
             const int xj = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
-            if (xj >= v_lo && xj < v_hi) p.tx_out[b] = trow[xj] * sc;
+            if (xj >= v_lo && xj < v_hi) p.tx_out[size_t(q) * p.B + b] = trow[xj] * sc;
         }
     }
 }
@@ -730,10 +765,12 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
-    for (int j = 1; j <= a.gamma + 2; ++j) {
-        const int in = (j - 1) & 1, out = j & 1;  // double-buffer halves
-        const size_t ns = size_t(a.B) * pl.nseg_max;
-        const int nseg = (j == 1) ? pl.nseg_first : pl.nseg;
+    const int npass = (a.gamma + 1 + kPassRows - 1) / kPassRows + 1;
+    for (int pass = 1; pass <= npass; ++pass) {
+        const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
+        const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
+        const size_t half = rs * kPassRows;
+        const int nseg = (pass == 1) ? pl.nseg_first : pl.nseg;
         PassParams pp{};
         pp.target = a.target;
         pp.x = a.x;
@@ -743,28 +780,29 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.B = a.B;
         pp.gamma = a.gamma;
         pp.V = a.V;
-        pp.j = j;
-        pp.nseg = nseg;
-        pp.seg_len = (j == 1) ? pl.seg_len_first : pl.seg_len;
-        pp.nseg_in = (j == 2) ? pl.nseg_first : pl.nseg;
-        pp.seg_stride = pl.nseg_max;
+        pp.j0 = (pass - 1) * kPassRows + 1;
         pp.vec = vec_t;
+        pp.nseg = nseg;
+        pp.seg_len = (pass == 1) ? pl.seg_len_first : pl.seg_len;
+        pp.nseg_in = (pass == 2) ? pl.nseg_first : pl.nseg;
+        pp.seg_stride = pl.nseg_max;
+        pp.row_stride = rs;
         pp.key0 = a.key0;
         pp.key1 = a.key1;
         pp.round32 = a.round32;
         pp.off = w.off;
         pp.act_in = w.act + size_t(in) * a.B;
-        pp.pm_in = w.seg_m + in * ns;
-        pp.ps_in = w.seg_s + in * ns;
-        pp.pv_in = w.seg_v + in * ns;
-        pp.pi_in = w.seg_i + in * ns;
-        pp.tx_in = w.seg_tx + size_t(in) * a.B;
+        pp.pm_in = w.seg_m + in * half;
+        pp.ps_in = w.seg_s + in * half;
+        pp.pv_in = w.seg_v + in * half;
+        pp.pi_in = w.seg_i + in * half;
+        pp.tx_in = w.seg_tx + size_t(in) * kPassRows * a.B;
         pp.act_out = w.act + size_t(out) * a.B;
-        pp.pm_out = w.seg_m + out * ns;
-        pp.ps_out = w.seg_s + out * ns;
-        pp.pv_out = w.seg_v + out * ns;
-        pp.pi_out = w.seg_i + out * ns;
-        pp.tx_out = w.seg_tx + size_t(out) * a.B;
+        pp.pm_out = w.seg_m + out * half;
+        pp.ps_out = w.seg_s + out * half;
+        pp.pv_out = w.seg_v + out * half;
+        pp.pi_out = w.seg_i + out * half;
+        pp.tx_out = w.seg_tx + size_t(out) * kPassRows * a.B;
         pp.status = w.status;
         pp.mode = w.mode;
         pp.jpos = w.jpos;
@@ -781,8 +819,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.diag_out = a.diag_out;
         static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
                                             "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
-        int t = prof_begin(names[std::min(j, 8) - 1], s);
-        hipLaunchKernelGGL(verify_pass_kernel, dim3(size_t((a.B + 3) / 4) * nseg), dim3(256), 0, s, pp);
+        int t = prof_begin(names[std::min(pass, 8) - 1], s);
+        hipLaunchKernelGGL(verify_pass_kernel, dim3(size_t((a.B + 3) / 4) * nseg * kPassRows), dim3(256), 0, s, pp);
         prof_end(t, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -902,12 +940,12 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     w.status = c.take<int32_t>(4);
     w.off = c.take<int32_t>(size_t(B) + 1);
     w.act = c.take<int32_t>(size_t(2) * B);
-    const size_t ns = size_t(2) * B * p.nseg_max;
+    const size_t ns = size_t(2) * kPassRows * B * p.nseg_max;
     w.seg_m = c.take<float>(ns);
     w.seg_s = c.take<float>(ns);
     w.seg_v = c.take<float>(ns);
     w.seg_i = c.take<int32_t>(ns);
-    w.seg_tx = c.take<float>(size_t(2) * B);
+    w.seg_tx = c.take<float>(size_t(2) * kPassRows * B);
     w.fin_lse2 = c.take<float>(B);
     w.prev = c.take<int32_t>(B);
     w.lse2q = c.take<float>(B);
