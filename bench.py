@@ -12,6 +12,10 @@ The printed JSON line carries the headline throughput (drafted positions per
 second), the dominant kernel's roofline figures measured with HIP events on
 the launch stream, and the CPU oracle timed on this host on one full round of
 the same workload (which also gates parity: eligible requests must match).
+Secondary figures: the distribution of single-round times over --rounds
+rounds, the bias product alone (the draft step's MFMA tiling without U_k or
+sampling) with W2 warm in the last-level cache and after a 512 MiB flush, the
+host scheduler's time on a 1024-request batch, and the oracle on one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -56,12 +60,96 @@ def _traffic_from_counters(launch_bytes):
     return float(t.group(1))
 
 
+def _round_distribution(torch, step, n, base):
+    """Single-round times (HIP events on the launch stream around each round,
+    rounds queued back to back): p10 / p50 / p90 in milliseconds."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        step(base + i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"rounds": n, "p10": round(float(np.percentile(t, 10)), 5), "p50": round(float(np.median(t)), 5),
+            "p90": round(float(np.percentile(t, 90)), 5)}
+
+
+def _bias_gemm_alone(torch, ds, dev, B, V, r, reps=30):
+    """The bias product B = W1[idx] . W2^T of one draft step with the step's
+    tiling and a running maximum as its only epilogue.  Warm: launches back to
+    back, so W2 (V*r*2 bytes) stays in the last-level cache; cold: a 512 MiB
+    write between launches evicts it.  Times are HIP events around the kernel
+    alone, on the launch stream."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    idx = torch.randint(0, V, (B,), generator=g, dtype=torch.int32).cuda()
+    out = ds.dspark_debug_bias_gemm(dev["W1"], dev["W2"], idx)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flops = 2.0 * B * r * V
+    res = {"flops_per_launch": flops, "w2_bytes": V * r * 2}
+    for mode in ("warm", "cold"):
+        torch.cuda.synchronize()
+        ds.dspark_profile_reset()
+        ds.dspark_profile_enable(True)
+        for i in range(reps):
+            if mode == "cold":
+                flush.fill_(i & 255)
+            ds.dspark_debug_bias_gemm(dev["W1"], dev["W2"], idx, out=out)
+        torch.cuda.synchronize()
+        ds.dspark_profile_collect()
+        ds.dspark_profile_enable(False)
+        n, ms = ds.dspark_profile_read()["bias_gemm"]
+        us = 1e3 * ms / n
+        tf = flops / (us * 1e-6) / 1e12
+        res[mode] = {"avg_us": round(us, 2), "tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "w2_gbs": round(V * r * 2 / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
+def _schedule_time(ds, S, reps=400):
+    """Host scheduler on the scheduled-batch workload (1024 requests, gamma 5,
+    confidences ~ Beta(8, 2), SPS(B) tabulated for every batch size): median
+    and p90 microseconds per call, including the ctypes call."""
+    import numpy as np
+    cfg = S.CONFIGS["sched"]
+    c = np.random.default_rng((cfg.seed, 5)).beta(8.0, 2.0, size=(cfg.B, cfg.gamma))
+    sps = S.sps_table_toy(0.5, cfg.B * (1 + cfg.gamma) + 1)
+    ds.dspark_schedule(c, sps)
+    t = []
+    for _ in range(reps):
+        t0 = time.perf_counter_ns()
+        ds.dspark_schedule(c, sps)
+        t.append((time.perf_counter_ns() - t0) / 1e3)
+    t = np.array(t)
+    return {"requests": cfg.B, "gamma": cfg.gamma, "sps_len": len(sps), "p50_us": round(float(np.median(t)), 2),
+            "p90_us": round(float(np.percentile(t, 90)), 2)}
+
+
+def _oracle_one_thread(rnd, target, ell, seed, gamma, oracle_round, rows=128):
+    """The oracle restricted to one OpenMP thread on the first `rows` requests
+    of the same round (a bounded sample of a few seconds)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from roundkit import packed_subset
+    sel = np.arange(rows)
+    tgt = packed_subset(target, ell, sel)
+    with threadpool_limits(limits=1):
+        omp = [i for i in threadpool_info() if i.get("user_api") == "openmp"]
+        threads = max([i["num_threads"] for i in omp], default=1)
+        t0 = time.time()
+        oracle_round(rnd, tgt, ell, seed, 0, rows=sel)
+        dt = time.time() - t0
+    return {"value": round(rows * gamma / dt, 2), "unit": "drafted positions/s", "cores": threads,
+            "sample": f"requests 0..{rows - 1} of the same round: fp64 draft + verify, {dt:.1f}s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg (and the parity gate)")
+    ap.add_argument("--rounds", type=int, default=60, help="rounds timed one by one for the round-time distribution")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte device buffer 5 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -143,6 +231,10 @@ def main():
     prof = ds.dspark_profile_read()
     phases = {k: {"launches": n, "avg_us": 1e3 * ms / max(1, n)} for k, (n, ms) in prof.items()}
 
+    round_dist = _round_distribution(torch, step, args.rounds, 3000)
+    gemm = _bias_gemm_alone(torch, ds, dev, B, V, r)
+    sched = _schedule_time(ds, S)
+
     drafted = B * gamma
     value = drafted / (ms_step * 1e-3)
     # dominant kernel: draft_step (gamma launches per step)
@@ -176,7 +268,10 @@ def main():
                    "parallelism": "single-gpu"},
         "secondary": {"verified_positions_per_s": round(B * (gamma + 1) / (ms_step * 1e-3), 1),
                       "emitted_tokens_per_s": round(emitted / (ms_step * 1e-3), 1),
-                      "phases_us": {k: round(p["avg_us"], 2) for k, p in phases.items()}},
+                      "phases_us": {k: round(p["avg_us"], 2) for k, p in phases.items()},
+                      "round_ms": round_dist,
+                      "bias_gemm_alone": gemm,
+                      "schedule": sched},
         "roofline": roofline,
     }
 
@@ -197,6 +292,7 @@ def main():
                                   "cores": cores, "kind": "oracle",
                                   "sample": f"one full round of the same workload (B={B}, gamma={gamma}, "
                                             f"V={V}): fp64 draft + verify, {cpu_s:.1f}s"}
+        result["cpu_baseline"]["one_thread"] = _oracle_one_thread(rnd, target, ell, seed, gamma, oracle_round)
         result["parity"] = {"draft": cd.report(), "verify": cv.report(),
                             "eligible_mismatches": int(cv.mismatch[cv.eligible].sum()) + int(cd.mismatch[cd.eligible].sum())}
         if cv.mismatch[cv.eligible].any() or cd.mismatch[cd.eligible].any():

@@ -20,7 +20,7 @@ __all__ = [
     "dspark_version", "dspark_status_string",
     "dspark_draft_workspace_size", "dspark_draft_sample",
     "dspark_verify_workspace_size", "dspark_verify", "dspark_verify_check",
-    "dspark_schedule", "dspark_debug_random_words", "dspark_debug_gumbel",
+    "dspark_schedule", "dspark_debug_random_words", "dspark_debug_gumbel", "dspark_debug_bias_gemm",
     "dspark_profile_enable", "dspark_profile_collect", "dspark_profile_read", "dspark_profile_reset",
 ]
 
@@ -79,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "dspark_debug_random_words": ([_c_u64, _c_u64, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_void_p, _c_void_p], _c_int),
         "dspark_debug_gumbel": ([_c_void_p, _c_int, _c_void_p, _c_void_p], _c_int),
+        "dspark_debug_bias_gemm": ([_c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_void_p,
+                                    _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_profile_enable": ([_c_int], _c_int),
         "dspark_profile_collect": ([], _c_int),
         "dspark_profile_count": ([], _c_int),
@@ -292,6 +294,29 @@ def dspark_debug_gumbel(words, stream=None):
     out = torch.empty(words.numel(), dtype=torch.float32, device=words.device)
     st = load_library().dspark_debug_gumbel(_ptr(words), words.numel(), _ptr(out), _stream_ptr(stream))
     _check(st, "dspark_debug_gumbel")
+    return out
+
+
+def dspark_debug_bias_gemm(W1, W2, idx, *, out=None, workspace=None, stream=None) -> dict:
+    """The Markov-bias product alone: rowmax[b] = max_v W1[idx[b]] . W2[v], with
+    the draft step's tiling and no sampling.  Returns {"rowmax", "workspace"}."""
+    torch = _torch()
+    lib = load_library()
+    dev = W1.device
+    V, r = W1.shape
+    wdt = _weights(W1, W2, dev)
+    B = idx.numel()
+    _need(idx, "idx", torch.int32, (B,), dev)
+    if out is None:
+        out = {"rowmax": torch.empty(B, dtype=torch.float32, device=dev)}
+    nbytes = lib.dspark_draft_workspace_size(B, 1, V, r)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_draft_workspace_size")
+    ws = _workspace(nbytes, dev, workspace if workspace is not None else out.get("workspace"))
+    out["workspace"] = ws
+    st = lib.dspark_debug_bias_gemm(_ptr(W1), _ptr(W2), wdt, _ptr(idx), B, V, r, _ptr(out["rowmax"]),
+                                    _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_debug_bias_gemm")
     return out
 
 

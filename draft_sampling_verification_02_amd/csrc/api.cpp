@@ -240,6 +240,23 @@ int dspark_debug_random_words(uint64_t seed, uint64_t round_id, int stream_id, i
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
 }
 
+int dspark_debug_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,
+                           float *rowmax_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!W1 || !W2 || !idx || !rowmax_out) return DSPARK_ERR_ARG;
+    if (!sizes_ok(B, 1, V, r)) return DSPARK_ERR_ARG;
+    if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
+    if (!rank_supported(wdtype, r)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(W1) || !aligned16(W2)) return DSPARK_ERR_ARG;
+    const DraftPlan plan = draft_plan(B, V);
+    size_t need = 0;
+    draft_carve(nullptr, B, plan, &need);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+    const DraftWork w = draft_carve(workspace, B, plan, nullptr);
+    const hipError_t e =
+        launch_bias_gemm(W1, W2, wdtype, idx, B, V, r, plan, w, rowmax_out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
 int dspark_debug_gumbel(const uint32_t *words, int n, float *out, void *stream) {
     if (!words || !out || n < 0) return DSPARK_ERR_ARG;
     const hipError_t e = launch_debug_gumbel(words, n, out, static_cast<hipStream_t>(stream));

@@ -97,6 +97,9 @@ __device__ __forceinline__ float gumbel2(uint32_t w) {
 
 // v_max3_f32, without the NaN-quieting self-max that IEEE mode makes the
 // compiler put in front of every fmaxf of a loaded or exchanged value.
+// Inline asm is opaque to the compiler's hazard tracking, so its operands must
+// come from ordinary VALU or memory instructions, never straight from an MFMA
+// accumulator (the required wait states after the MFMA would be missing).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));

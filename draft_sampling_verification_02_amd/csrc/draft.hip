@@ -275,6 +275,122 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     }
 }
 
+// ---- the bias product alone (a diagnostic of the matrix-unit tiling)
+
+struct GemmParams {
+    const void *W1, *W2;
+    const int32_t *idx;
+    int B, V;
+    int nbb, nbg, ntiles, tiles_per_chunk, nchunk;
+    float *pm;  // [B, nchunk] per-chunk row maxima
+};
+
+// The draft step's walk with its epilogue cut down to a running maximum: the
+// same workgroups, W2 stages and MFMA tiles, no U_k read and no sampling.
+template <typename WT, int R>
+__global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bias_gemm_kernel(
+    GemmParams p) {
+    using L = TileLDS<WT, R>;
+    __shared__ __attribute__((aligned(16))) uint8_t ldsA[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ldsB[2 * L::BYTES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = xcd_remap(blockIdx.x, gridDim.x);
+    const int chunk = lg / p.nbg, bg = lg % p.nbg;
+    const int bb = bg * (kStepThreads / 64) + wave;
+    const bool wave_ok = bb < p.nbb;
+    const int n = lane & 31, h = lane >> 5;
+    const int b = bb * 32 + n;
+    const bool row_ok = wave_ok && b < p.B;
+    const int bc = min(b, p.B - 1);
+    const int prev = min(max(p.idx[bc], 0), p.V - 1);
+    const WT *W2 = static_cast<const WT *>(p.W2);
+    EFrags<WT, R> ef;
+    if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    StageDMA<WT, R, kStepThreads> dma;
+    dma.init(tid);
+    const int t_begin = chunk * p.tiles_per_chunk;
+    const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
+    const int nst = (t_end - t_begin + 1) >> 1;
+    const bool tail = (t_begin + 2 * nst) * kTile > p.V;
+    const int nfull = nst - (tail ? 1 : 0);
+    float mx = kNegInf;
+    auto stage = [&](const uint8_t *buf, int t0, bool masked) __device__ {
+        f32x16_t c0 = {}, c1 = {};
+        bias_pair_lds(ef, buf, lane, c0, c1);
+        if (masked) {
+            // value 4i+j of lane (n, h) is entry 8i + 4h + j of each tile
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (t0 * kTile + 8 * i + 4 * h + j >= p.V) c0[4 * i + j] = kNegInf;
+                    if ((t0 + 1) * kTile + 8 * i + 4 * h + j >= p.V) c1[4 * i + j] = kNegInf;
+                }
+        }
+        // the first level is an ordinary fmaxf, which the compiler orders
+        // after the MFMAs that produce c0 and c1; max3f is inline asm and
+        // must not read accumulators straight from the chain
+        float d[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) d[e] = fmaxf(c0[e], c1[e]);
+        float m0 = max3f(d[0], d[1], d[2]), m1 = max3f(d[3], d[4], d[5]);
+#pragma unroll
+        for (int e = 6; e < 14; e += 4) {
+            m0 = max3f(m0, d[e], d[e + 1]);
+            m1 = max3f(m1, d[e + 2], d[e + 3]);
+        }
+        mx = max3f(max3f(m0, d[14], d[15]), m1, mx);
+    };
+    auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
+    if (nfull > 0) dma.template issue<false>(W2, v0_of(0), p.V, ldsA, wave);
+    for (int i = 0; i < nfull; i += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (i + 1 < nfull) dma.template issue<false>(W2, v0_of(i + 1), p.V, ldsB, wave);
+        if (wave_ok) stage(ldsA, t_begin + 2 * i, false);
+        if (i + 1 >= nfull) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (i + 2 < nfull) dma.template issue<false>(W2, v0_of(i + 2), p.V, ldsA, wave);
+        if (wave_ok) stage(ldsB, t_begin + 2 * (i + 1), false);
+    }
+    if (tail) {
+        __syncthreads();
+        dma.template issue<true>(W2, v0_of(nfull), p.V, ldsA, wave);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave_ok) stage(ldsA, t_begin + 2 * nfull, true);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // the two lane halves held different rows of the same tiles
+    if (h == 0 && row_ok) p.pm[size_t(b) * p.nchunk + chunk] = mx;
+}
+
+// Row maxima from the per-chunk maxima: one wave per request.
+__global__ __launch_bounds__(256) void bias_rowmax_kernel(const float *pm, int B, int nchunk, float *out) {
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= B) return;
+    float m = kNegInf;
+    for (int c = lane; c < nchunk; c += 64) m = fmaxf(m, pm[size_t(b) * nchunk + c]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) out[b] = m;
+}
+
+template <typename WT, int R>
+hipError_t launch_gemm_typed(const void *W1, const void *W2, const int32_t *idx, int B, int V, const DraftPlan &pl,
+                             const DraftWork &w, float *rowmax, hipStream_t s) {
+    GemmParams gp{W1, W2, idx, B, V, pl.nbb, pl.nbg, pl.ntiles, pl.tiles_per_chunk, pl.nchunk, w.pm};
+    int t = prof_begin("bias_gemm", s);
+    hipLaunchKernelGGL((bias_gemm_kernel<WT, R>), dim3(pl.blocks), dim3(kStepThreads), 0, s, gp);
+    prof_end(t, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bias_rowmax_kernel, dim3((B + 3) / 4), dim3(256), 0, s, w.pm, B, pl.nchunk, rowmax);
+    return hipGetLastError();
+}
+
 template <typename WT, int R>
 hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork &w, hipStream_t s) {
     const bool track2 = a.margin_out != nullptr;
@@ -392,6 +508,27 @@ DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes) {
     w.pi = c.take<int32_t>(n);
     if (bytes) *bytes = c.off + 256;
     return w;
+}
+
+hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,
+                            const DraftPlan &p, const DraftWork &w, float *rowmax, hipStream_t s) {
+    if (wdtype == 0) {
+        switch (r) {
+            case 16: return launch_gemm_typed<uint16_t, 16>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 32: return launch_gemm_typed<uint16_t, 32>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 64: return launch_gemm_typed<uint16_t, 64>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 128: return launch_gemm_typed<uint16_t, 128>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 256: return launch_gemm_typed<uint16_t, 256>(W1, W2, idx, B, V, p, w, rowmax, s);
+        }
+    } else {
+        switch (r) {
+            case 16: return launch_gemm_typed<float, 16>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 32: return launch_gemm_typed<float, 32>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 64: return launch_gemm_typed<float, 64>(W1, W2, idx, B, V, p, w, rowmax, s);
+            case 128: return launch_gemm_typed<float, 128>(W1, W2, idx, B, V, p, w, rowmax, s);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork &w, hipStream_t s) {

@@ -65,6 +65,9 @@ struct DraftArgs {
     float *lse_out, *qx_out, *margin_out;
 };
 hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork &w, hipStream_t s);
+// The bias product alone: rowmax[b] = max_v W1[idx[b]] . W2[v] (diagnostic).
+hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,
+                            const DraftPlan &p, const DraftWork &w, float *rowmax, hipStream_t s);
 
 // ---- verify ----------------------------------------------------------
 

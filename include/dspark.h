@@ -214,6 +214,19 @@ int dspark_debug_random_words(uint64_t seed, uint64_t round_id, int stream_id, i
  * out[i] = -log2(-log2(u_i)), u_i = ((w_i >> 8) + 0.5) * 2^-24. */
 int dspark_debug_gumbel(const uint32_t *words, int n, float *out, void *stream);
 
+/* The Markov-bias product alone, to measure the matrix-unit tiling of the
+ * draft step ([MG] 3.2; [CE] 03: B_k = W1[x_{k-1}] W2^T) without the rest of
+ * the step: rowmax_out[b] = max_v sum_i W1[idx[b]][i] * W2[v][i], computed
+ * with the draft step's workgroups, LDS-staged W2 tiles and MFMA tiles, with
+ * no U_k read and no sampling.
+ *   W1, W2, wdtype, V, r  as for dspark_draft_sample
+ *   idx         device [B] int32: the W1 rows (clamped into [0, V))
+ *   rowmax_out  device [B] float32
+ *   workspace   device, >= dspark_draft_workspace_size(B, 1, V, r) bytes
+ * Same argument checks and error codes as dspark_draft_sample. */
+int dspark_debug_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,
+                           float *rowmax_out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Per-kernel timing with HIP events on the launch stream.  While enabled,
  * every kernel the library enqueues is bracketed by an event pair; calling
  * dspark_profile_collect waits for the recorded events and adds their

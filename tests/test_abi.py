@@ -108,3 +108,22 @@ def test_schedule_argument_errors():
     assert len(ell) == 0 and B == 0 and theta == 0.0
     st = lib.dspark_schedule(None, 2, 3, None, 0, None, None, None, None)
     assert st == ds.DSPARK_ERR_ARG
+
+
+def test_bias_gemm_argument_errors_need_no_gpu():
+    lib = ds.load_library()
+
+    def call(**kw):
+        a = dict(W1=_FAKE, W2=_FAKE, wdtype=0, idx=_FAKE, B=4, V=1000, r=16, out=_FAKE, ws=_FAKE,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.dspark_debug_bias_gemm(a["W1"], a["W2"], a["wdtype"], a["idx"], a["B"], a["V"], a["r"],
+                                          a["out"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(W1=None) == ds.DSPARK_ERR_ARG
+    assert call(out=None) == ds.DSPARK_ERR_ARG
+    assert call(B=0) == ds.DSPARK_ERR_ARG
+    assert call(wdtype=3) == ds.DSPARK_ERR_ARG
+    assert call(r=24) == ds.DSPARK_ERR_UNSUPPORTED
+    assert call(W1=ctypes.c_void_p(0x1004)) == ds.DSPARK_ERR_ARG
+    assert call(ws_bytes=16) == ds.DSPARK_ERR_WORKSPACE

@@ -336,3 +336,27 @@ def test_q_equals_p_accepts_all_on_gpu():
         total += B
     # p/q = 1 up to float32 rounding: only a uniform within ~1e-7 of 1 can fail
     assert total - full <= 2, (total, full)
+
+
+# ---------------------------------------------------------------- bias product alone
+
+@pytest.mark.parametrize("B,V,r,wdtype", [
+    (70, 4099, 64, "f32"),             # ragged batch and vocabulary, several chunks
+    (256, 2048 * 3 + 5, 256, "bf16"),  # headline rank, ragged tail tile
+    (33, 17, 16, "bf16"),              # vocabulary inside one tile
+])
+def test_bias_gemm_rowmax_matches_fp64(B, V, r, wdtype):
+    """The matrix-unit tiling of the draft step on its own: rowmax[b] =
+    max_v W1[idx_b] . W2[v] against the same sums in fp64.  The products of
+    exact bf16 / f32 values are summed in fp32, so each sum is within
+    r * 2^-24 * sum |terms| of the fp64 one (the classic bound, doubled)."""
+    rnd, _, _ = _custom_round(B, 1, V, r, wdtype, seed=B + V + r)
+    dev = to_device(rnd)
+    idx = np.random.default_rng(V).integers(0, V, B).astype(np.int32)
+    _say(f"[bias_gemm] B={B} V={V} r={r} {wdtype}")
+    out = ds.dspark_debug_bias_gemm(dev["W1"], dev["W2"], torch.from_numpy(idx).cuda())
+    got = np_of(out["rowmax"])
+    ref = (rnd.W1[idx].astype(np.float64) @ rnd.W2.astype(np.float64).T).max(axis=1)
+    scale = np.abs(rnd.W1[idx].astype(np.float64)) @ np.abs(rnd.W2.astype(np.float64)).T
+    tol = 2 * r * 2.0 ** -24 * scale.max(axis=1) + 1e-7
+    assert np.all(np.abs(got - ref) <= tol), np.max(np.abs(got - ref) / tol)
