@@ -96,9 +96,8 @@ struct VerifyWork {
     float *lse2q;        // [B] log2-unit logsumexp of q_j for a residual draw
     int32_t *mode;       // [B] 0 done, 1 residual draw, 2 bonus draw, -1 invalid
     int32_t *jpos;       // [B] position of the emitted non-draft token
-    int32_t *slot;       // [B] draw slot: list index, + B for the bonus list
-    int32_t *resid_list; // [B] requests taking the residual draw, in arrival order
-    int32_t *bonus_list; // [B] sampled requests taking the bonus draw, in arrival order
+    int32_t *slot;       // [B] draw slot: the request's entry in the draw list
+    int32_t *draw_list;  // [B] drawing requests: residual draws from the front, bonus draws from the back
     // draw partials per (list slot, vocabulary chunk); residual slots [0, B), bonus slots [B, 2B)
     float *dw_sum;       // residual mass
     float *dw_bl;        // best tile score of the level-1 race

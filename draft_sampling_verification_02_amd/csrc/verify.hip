@@ -195,7 +195,7 @@ struct PassParams {
     int32_t *act_out;
     float *pm_out, *ps_out, *pv_out, *tx_out;
     int32_t *pi_out;
-    int32_t *status, *mode, *jpos, *slot, *resid_list, *bonus_list, *prev;
+    int32_t *status, *mode, *jpos, *slot, *draw_list, *prev;
     float *fin_lse2, *lse2q;
     const int32_t *anchor;
     const float *lse_q;
@@ -247,13 +247,13 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
     }
     p.fin_lse2[b] = lse2;
     if (bonus) {
-        const int e = atomicAdd(&p.status[3], 1);
-        p.bonus_list[e] = b;
-        p.slot[b] = p.B + e;
+        const int e = p.B - 1 - atomicAdd(&p.status[3], 1);
+        p.draw_list[e] = b;
+        p.slot[b] = e;
         p.mode[b] = kModeBonus;
     } else {
         const int e = atomicAdd(&p.status[2], 1);
-        p.resid_list[e] = b;
+        p.draw_list[e] = b;
         p.slot[b] = e;
         p.mode[b] = kModeResidual;
         // what the residual draw needs to rebuild q_k
@@ -441,7 +441,7 @@ struct DrawParams {
     int B, gamma, V;
     int nbg, ntiles, tiles_per_chunk, nchunk;
     uint32_t key0, key1, round32;
-    const int32_t *status, *resid_list, *bonus_list, *jpos, *off, *prev;
+    const int32_t *status, *draw_list, *jpos, *off, *prev;
     const float *fin_lse2, *lse2q;
     float *dw_sum, *dw_bl;
     int32_t *dw_bt;
@@ -471,32 +471,27 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
     __shared__ __attribute__((aligned(16))) uint8_t ldsU1[NWV * TR::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsT0[NWV * TR::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsT1[NWV * TR::BYTES];
+    // entries [0, nres) of the draw list are residual draws, [B - nbon, B)
+    // bonus draws; the two never overlap, so at most one wave holds both kinds
     const int nres = p.status[2], nbon = p.status[3];
-    const int nblk_r = (nres + 31) / 32, nblk = nblk_r + (nbon + 31) / 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
     const int chunk = lg / p.nbg, bg = lg % p.nbg;
-    const int lb0 = bg * NWV;
-    if (lb0 >= nblk) return;               // the whole workgroup is idle
-    const bool need_w2 = lb0 < nblk_r;     // uniform across the workgroup
-    const int lb = lb0 + wave;
-    const bool wave_ok = lb < nblk;        // uniform across the wave
-    const bool resid = lb < nblk_r;        // uniform across the wave
+    const int e0 = bg * NWV * 32;  // first list entry of the workgroup
+    const int bon0 = p.B - nbon;   // first bonus entry
+    if (e0 >= nres && (nbon == 0 || e0 + NWV * 32 <= bon0 || e0 >= p.B)) return;  // the whole workgroup is idle
+    const bool need_w2 = e0 < nres;  // uniform across the workgroup
+    const int w0 = e0 + wave * 32;   // first entry of the wave
+    const bool wave_resid = w0 < nres;                          // uniform across the wave
+    const bool wave_bonus = w0 < p.B && w0 + 32 > bon0 && nbon > 0;  // uniform across the wave
+    const bool wave_ok = wave_resid || wave_bonus;
     const int n = lane & 31, h = lane >> 5;
-    int req = 0, slot = 0;
-    bool ok = false;
-    if (resid) {
-        const int e = lb * 32 + n;
-        ok = e < nres;
-        req = p.resid_list[ok ? e : nres - 1];
-        slot = e;
-    } else if (wave_ok) {
-        const int e = (lb - nblk_r) * 32 + n;
-        ok = e < nbon;
-        req = p.bonus_list[ok ? e : nbon - 1];
-        slot = p.B + e;
-    }
+    const int e = w0 + n;
+    const bool resid = e < nres;
+    const bool ok = resid || (e >= bon0 && e < p.B);
+    const int req = ok ? p.draw_list[e] : 0;
+    const int slot = e;
     const int j = wave_ok ? p.jpos[req] : 1;
     const float sc = wave_ok ? kLog2e / p.temperature[req] : 1.0f;
     const float lse2t = wave_ok ? p.fin_lse2[req] : 0.f;
@@ -506,16 +501,18 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
     EFrags<WT, R> ef;
     int urow_i = -1;  // row of U
     float lse2q = 0.f;
-    if (resid) {
-        ef.load(static_cast<const WT *>(p.W1) + size_t(p.prev[req]) * R, h);
-        if (ok) urow_i = req * p.gamma + j - 1;
-        lse2q = p.lse2q[req];
+    if (wave_resid) {
+        ef.load(static_cast<const WT *>(p.W1) + size_t(resid ? p.prev[req] : 0) * R, h);
+        if (resid) {
+            urow_i = req * p.gamma + j - 1;
+            lse2q = p.lse2q[req];
+        }
     }
     TileDMA<WT, R, kDrawThreads> dma;
     if (need_w2) dma.init(tid);
     TR su, stg;
     if (wave_ok) stg.init(lane, p.target, size_t(p.V), [&](int r) { return __shfl(trow_i, r); });
-    if (resid) su.init(lane, p.U, size_t(p.V), [&](int r) { return __shfl(urow_i, r); });
+    if (wave_resid) su.init(lane, p.U, size_t(p.V), [&](int r) { return __shfl(urow_i, r); });
     const int roff = wave * TR::BYTES;  // this wave's region in each region buffer
 
     const int t_begin = chunk * p.tiles_per_chunk;
@@ -531,12 +528,12 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
         constexpr bool C = decltype(clamp)::value;
         if (need_w2) dma.template issue<C>(W2, t * kTile, p.V, w, wave);
         if (wave_ok) stg.template issue<C>(t * kTile, p.V, tr + roff, lane);
-        if (resid) su.template issue<C>(t * kTile, p.V, ur + roff, lane);
+        if (wave_resid) su.template issue<C>(t * kTile, p.V, ur + roff, lane);
     };
     auto stage = [&](int t, const uint8_t *w, const uint8_t *ur, const uint8_t *tr, bool masked) __device__ {
         f32x16_t pv = stg.read(tr + roff, lane);
         f32x16_t c;
-        if (resid) c = bias_tile_lds(ef, w, lane, su.read(ur + roff, lane));
+        if (wave_resid) c = bias_tile_lds(ef, w, lane, su.read(ur + roff, lane));
         if (masked) {
             // value 4i+jj of lane (n, h) is entry 8i + 4h + jj of the tile
 #pragma unroll
@@ -548,8 +545,10 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
         if (t == t_begin || (t & 3) == 0)
             tw = noise_block(kStreamResampleTile, j, uint32_t(t) >> 2, uint32_t(req), p.round32, p.key0, p.key1);
         const float g = gumbel2(u4get(tw, t & 3));
-        float Lt;
-        if (resid) {
+        // a wave holding both kinds scores the tile both ways and each lane
+        // keeps its own, so the lane-half exchanges never run divergent
+        float Lt = kNegInf, rt = 0.f;
+        if (wave_resid) {
             float r0 = 0.f, r1 = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
@@ -559,10 +558,10 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
                                 fast_exp2(__builtin_fmaf(c[e + 1], sc, -lse2q)),
                             0.f);
             }
-            const float rt = half_sum(r0 + r1);
-            S += rt;
+            rt = half_sum(r0 + r1);
             Lt = rt > 0.f ? fast_log2(rt) + g : kNegInf;
-        } else {
+        }
+        if (wave_bonus) {
             float mh = max3f(pv[0], pv[1], pv[2]);
 #pragma unroll
             for (int e = 3; e < 15; e += 2) mh = max3f(mh, pv[e], pv[e + 1]);
@@ -573,8 +572,9 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
             for (int e = 0; e < 16; ++e) sh += fast_exp2(__builtin_fmaf(pv[e], sc, -mg));
             const float st = half_sum(sh);
-            Lt = mg + fast_log2(st) + g;
+            if (!resid) Lt = mg + fast_log2(st) + g;
         }
+        if (resid) S += rt;
         if (Lt > best) {
             best = Lt;
             bt = t;
@@ -807,8 +807,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.mode = w.mode;
         pp.jpos = w.jpos;
         pp.slot = w.slot;
-        pp.resid_list = w.resid_list;
-        pp.bonus_list = w.bonus_list;
+        pp.draw_list = w.draw_list;
         pp.fin_lse2 = w.fin_lse2;
         pp.prev = w.prev;
         pp.lse2q = w.lse2q;
@@ -845,8 +844,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.key1 = a.key1;
         dp.round32 = a.round32;
         dp.status = w.status;
-        dp.resid_list = w.resid_list;
-        dp.bonus_list = w.bonus_list;
+        dp.draw_list = w.draw_list;
         dp.jpos = w.jpos;
         dp.off = w.off;
         dp.fin_lse2 = w.fin_lse2;
@@ -926,8 +924,8 @@ VerifyPlan verify_plan(int B, int gamma, int V) {
     // regions (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them
     // for the requests
     p.tile = tile_walk_plan(B, V, kDrawThreads / 64, 256, 1);
-    // the residual and bonus lists hold at most B requests but each rounds up to 32
-    p.draw_nbg = (p.nbb + 1 + kDrawThreads / 64 - 1) / (kDrawThreads / 64);
+    // the draw list holds every drawing request in B entries
+    p.draw_nbg = (p.nbb + kDrawThreads / 64 - 1) / (kDrawThreads / 64);
     p.draw_blocks = p.tile.nchunk * p.draw_nbg;
     return p;
 }
@@ -952,9 +950,8 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     w.mode = c.take<int32_t>(B);
     w.jpos = c.take<int32_t>(B);
     w.slot = c.take<int32_t>(B);
-    w.resid_list = c.take<int32_t>(B);
-    w.bonus_list = c.take<int32_t>(B);
-    const size_t nd = size_t(2) * B * p.tile.nchunk;
+    w.draw_list = c.take<int32_t>(B);
+    const size_t nd = size_t(B) * p.tile.nchunk;
     w.dw_sum = c.take<float>(nd);
     w.dw_bl = c.take<float>(nd);
     w.dw_bt = c.take<int32_t>(nd);
