@@ -267,8 +267,11 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
 // requests to a workgroup.  First the request's previous D positions are
 // decided, in order, from the segment statistics pass p - 1 wrote; a request
 // that goes on streams segment sg of its row j0 + q: every lane keeps its own
-// running max / sum of exp2 and argmax over batches of eight float4 loads,
-// and the wave merges them.  The waves never wait for one another.
+// running max / sum of exp2 and argmax over batches of eight float4 loads
+// (PIPE: two batches, one in flight while the other is reduced, for the long
+// segments of the first pass), and the wave merges them.  The waves never
+// wait for one another.
+template <bool PIPE>
 __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     constexpr int D = kPassRows;
     static_assert(D <= 2, "two row slots fit the two lane halves");
@@ -355,44 +358,115 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     float m = kNegInf, s = 0.f, av = kNegInf;
     int ai = 0x7fffffff;
     if (p.vec) {
-        const float4 *r4 = reinterpret_cast<const float4 *>(trow);
-        const int q_hi = v_hi >> 2;
-        constexpr int U = 8;
-        for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
-            float4 xs[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int q = q0 + 64 * u;
-                xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        if constexpr (PIPE) {
+            // two batches of U float4 a lane, one in flight while the other is
+            // reduced
+            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
+            const int q_hi = v_hi >> 2;
+            constexpr int U = 8;
+            // loads past the segment re-read its last group and are masked when used
+            auto load = [&](float4(&xs)[U], int qb) __device__ {
+    #pragma unroll
+                for (int u = 0; u < U; ++u) xs[u] = r4[min(qb + lane + 64 * u, q_hi - 1)];
+            };
+            auto consume = [&](float4(&xs)[U], int qb) __device__ {
+                float bm = kNegInf;
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool in = qb + lane + 64 * u < q_hi;
+                    xs[u].x = in ? xs[u].x * sc : kNegInf;
+                    xs[u].y = in ? xs[u].y * sc : kNegInf;
+                    xs[u].z = in ? xs[u].z * sc : kNegInf;
+                    xs[u].w = in ? xs[u].w * sc : kNegInf;
+                    bm = fmaxf(fmaxf(bm, fmaxf(xs[u].x, xs[u].y)), fmaxf(xs[u].z, xs[u].w));
+                }
+                const float mn = fmaxf(m, bm);
+                if (mn != kNegInf) {
+                    float add = 0.f;
+    #pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        add += fast_exp2(xs[u].x - mn) + fast_exp2(xs[u].y - mn) + fast_exp2(xs[u].z - mn) +
+                               fast_exp2(xs[u].w - mn);
+                    s = s * fast_exp2(m - mn) + add;
+                    m = mn;
+                }
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int v = 4 * (qb + lane + 64 * u);
+    #pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float xv = f4get(xs[u], jj);
+                        if (xv > av) {
+                            av = xv;
+                            ai = v + jj;
+                        }
+                    }
+                }
+            };
+            // The loop body is straight-line, so that every consume sees the
+            // same loads in flight on every path into it; it runs while the
+            // batch after the pair exists, and the last one or two batches
+            // follow it.  The batch bounds are uniform across the wave.
+            constexpr int NB = 64 * U;  // float4 groups a batch
+            const int qs = v_lo >> 2;
+            float4 xa[U], xb[U];
+            load(xa, qs);
+            int qb = qs;
+            for (; qb + 2 * NB < q_hi; qb += 2 * NB) {
+                load(xb, qb + NB);
+                consume(xa, qb);
+                load(xa, qb + 2 * NB);
+                consume(xb, qb + NB);
             }
-            float bm = kNegInf;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                xs[u].x *= sc;
-                xs[u].y *= sc;
-                xs[u].z *= sc;
-                xs[u].w *= sc;
-                bm = fmaxf(fmaxf(bm, fmaxf(xs[u].x, xs[u].y)), fmaxf(xs[u].z, xs[u].w));
+            if (qb + NB < q_hi) {
+                load(xb, qb + NB);
+                consume(xa, qb);
+                consume(xb, qb + NB);
+            } else {
+                consume(xa, qb);
             }
-            const float mn = fmaxf(m, bm);
-            if (mn != kNegInf) {
-                float add = 0.f;
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    add += fast_exp2(xs[u].x - mn) + fast_exp2(xs[u].y - mn) + fast_exp2(xs[u].z - mn) +
-                           fast_exp2(xs[u].w - mn);
-                s = s * fast_exp2(m - mn) + add;
-                m = mn;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = 4 * (q0 + 64 * u);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const float xv = f4get(xs[u], jj);
-                    if (xv > av) {
-                        av = xv;
-                        ai = v + jj;
+        } else {
+            // one batch of U float4 a lane at a time: fewer registers, twice
+            // the waves a SIMD for the short segments of the later passes
+            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
+            const int q_hi = v_hi >> 2;
+            constexpr int U = 8;
+            for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
+                float4 xs[U];
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int q = q0 + 64 * u;
+                    xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+                }
+                float bm = kNegInf;
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    xs[u].x *= sc;
+                    xs[u].y *= sc;
+                    xs[u].z *= sc;
+                    xs[u].w *= sc;
+                    bm = fmaxf(fmaxf(bm, fmaxf(xs[u].x, xs[u].y)), fmaxf(xs[u].z, xs[u].w));
+                }
+                const float mn = fmaxf(m, bm);
+                if (mn != kNegInf) {
+                    float add = 0.f;
+    #pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        add += fast_exp2(xs[u].x - mn) + fast_exp2(xs[u].y - mn) + fast_exp2(xs[u].z - mn) +
+                               fast_exp2(xs[u].w - mn);
+                    s = s * fast_exp2(m - mn) + add;
+                    m = mn;
+                }
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int v = 4 * (q0 + 64 * u);
+    #pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float xv = f4get(xs[u], jj);
+                        if (xv > av) {
+                            av = xv;
+                            ai = v + jj;
+                        }
                     }
                 }
             }
@@ -770,7 +844,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
         const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
         const size_t half = rs * kPassRows;
-        const int nseg = (pass == 1) ? pl.nseg_first : pl.nseg;
+        // the last pass only decides: one wave a request
+        const int nseg = (pass == 1) ? pl.nseg_first : (pass == npass ? 1 : pl.nseg);
         PassParams pp{};
         pp.target = a.target;
         pp.x = a.x;
@@ -819,7 +894,11 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
                                             "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
         int t = prof_begin(names[std::min(pass, 8) - 1], s);
-        hipLaunchKernelGGL(verify_pass_kernel, dim3(size_t((a.B + 3) / 4) * nseg * kPassRows), dim3(256), 0, s, pp);
+        const dim3 grid(size_t((a.B + 3) / 4) * nseg * kPassRows);
+        if (pass == 1)
+            hipLaunchKernelGGL(verify_pass_kernel<true>, grid, dim3(256), 0, s, pp);
+        else
+            hipLaunchKernelGGL(verify_pass_kernel<false>, grid, dim3(256), 0, s, pp);
         prof_end(t, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
