@@ -14,6 +14,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- Philox
@@ -228,27 +229,30 @@ struct RowHalf {
 #pragma unroll
         for (int i = 0; i < N; ++i) w[i] = q[i];
     }
-    // the full dot product W1row . W2row, summed over the two lane halves
+    // the full dot product W1row . W2row, summed over the two lane halves:
+    // four independent accumulator chains, bf16 pairs through v_dot2 (each
+    // bf16 product is exact in fp32)
     __device__ __forceinline__ float dot(const WT *W2row, int h) const {
         const uint4 *q = reinterpret_cast<const uint4 *>(W2row + h * HALF);
         uint4 x[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) x[i] = q[i];
-        float d = 0.f;
+        float d[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const uint32_t av[4] = {w[i].x, w[i].y, w[i].z, w[i].w}, xv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if constexpr (sizeof(WT) == 2) {
-                    d = __builtin_fmaf(__uint_as_float(av[e] << 16), __uint_as_float(xv[e] << 16), d);
-                    d = __builtin_fmaf(__uint_as_float(av[e] & 0xFFFF0000u), __uint_as_float(xv[e] & 0xFFFF0000u), d);
+                    d[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[e]),
+                                                           __builtin_bit_cast(bf16x2_t, xv[e]), d[e], false);
                 } else {
-                    d = __builtin_fmaf(__uint_as_float(av[e]), __uint_as_float(xv[e]), d);
+                    d[e] = __builtin_fmaf(__uint_as_float(av[e]), __uint_as_float(xv[e]), d[e]);
                 }
             }
         }
-        return d + __shfl_xor(d, 32);
+        const float t = (d[0] + d[1]) + (d[2] + d[3]);
+        return t + __shfl_xor(t, 32);
     }
 };
 

@@ -197,33 +197,42 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     if (b >= p.B) return;
     const bool track2 = p.margin_out != nullptr;
     const int i = lane & 31, h = lane >> 5;
+    // level 1: row logsumexp and the winning tile, four chunks a lane per
+    // batch.  The loads go out first and unconditionally (an index past the
+    // chunks re-reads chunk 0 and is masked after), so that the first batch
+    // is in flight while x_{k-1} and its W1 row are fetched.
+    constexpr int PC = 4;
+    float cm[PC], cs[PC], cb[PC], c2[PC];
+    int ci[PC];
+    auto load_batch = [&](int c0) __device__ {
+#pragma unroll
+        for (int u = 0; u < PC; ++u) {
+            const int c = c0 + lane + 64 * u;
+            const size_t o = size_t(b) * p.nchunk + (c < p.nchunk ? c : 0);
+            cm[u] = p.pm[o];
+            cs[u] = p.ps[o];
+            cb[u] = p.pb[o];
+            ci[u] = p.pi[o];
+            c2[u] = p.p2[o];  // written only when the margin is tracked; masked below otherwise
+        }
+    };
+    load_batch(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch ahead of the dependent W1 fetch
     int prev = p.xprev[size_t(b) * p.xprev_stride];
     prev = min(max(prev, 0), p.V - 1);
     const float T = p.temperature[b];
     RowHalf<WT, R> w1;
     w1.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
-    // level 1: row logsumexp and the winning tile, four chunks a lane per batch
     float m = kNegInf, s = 0.f, best = kNegInf, second = kNegInf;
     int bt = 0x7fffffff;
-    constexpr int PC = 4;
     for (int c0 = 0; c0 < p.nchunk; c0 += 64 * PC) {
-        float cm[PC], cs[PC], cb[PC], c2[PC];
-        int ci[PC];
+        if (c0 > 0) load_batch(c0);
 #pragma unroll
         for (int u = 0; u < PC; ++u) {
-            const int c = c0 + lane + 64 * u;
-            const bool in = c < p.nchunk;
-            const size_t o = size_t(b) * p.nchunk + (in ? c : 0);
-            cm[u] = in ? p.pm[o] : kNegInf;
-            cs[u] = in ? p.ps[o] : 0.f;
-            cb[u] = in ? p.pb[o] : kNegInf;
-            ci[u] = in ? p.pi[o] : 0x7fffffff;
-            c2[u] = (in && track2) ? p.p2[o] : kNegInf;
-        }
-#pragma unroll
-        for (int u = 0; u < PC; ++u) {
-            lse_merge(m, s, cm[u], cs[u]);
-            best_merge(best, bt, second, cb[u], ci[u], c2[u]);
+            if (c0 + lane + 64 * u < p.nchunk) {
+                lse_merge(m, s, cm[u], cs[u]);
+                best_merge(best, bt, second, cb[u], ci[u], track2 ? c2[u] : kNegInf);
+            }
         }
     }
 #pragma unroll

@@ -740,39 +740,49 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= p.B) return;
+    // the request's state in one round of loads (read whatever the mode; used
+    // only by drawing requests), then the chunk partials ahead of the W1 row
     const int mode = p.mode[b];
+    const int slot = p.slot[b], j = p.jpos[b], off = p.off[b], prev = p.prev[b];
+    const float T = p.temperature[b], lse2t = p.fin_lse2[b], lse2q_in = p.lse2q[b];
+    // an empty use ahead of the branch keeps the compiler from sinking the
+    // loads after it, which would put a second round trip on the path
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(slot), "v"(j), "v"(off), "v"(prev), "v"(T), "v"(lse2t), "v"(lse2q_in));
     if (mode != kModeResidual && mode != kModeBonus) return;
-    // loads that do not depend on the winning tile, in two rounds
-    const int slot = p.slot[b], j = p.jpos[b];
-    const float sc = kLog2e / p.temperature[b];
-    const float lse2t = p.fin_lse2[b];
-    const int trow_i = p.off[b] + j - 1;
-    const float *trow = p.target + size_t(trow_i) * p.V;
+    const float sc = kLog2e / T;
+    const float *trow = p.target + size_t(off + j - 1) * p.V;
+    constexpr int PC = 4;
+    float cs[PC], cb[PC];
+    int ct[PC];
+    auto load_batch = [&](int c0) __device__ {
+#pragma unroll
+        for (int u = 0; u < PC; ++u) {
+            const int c = c0 + lane + 64 * u;  // past the chunks: re-reads chunk 0, masked below
+            const size_t o = size_t(slot) * p.nchunk + (c < p.nchunk ? c : 0);
+            cs[u] = p.dw_sum[o];
+            cb[u] = p.dw_bl[o];
+            ct[u] = p.dw_bt[o];
+        }
+    };
+    load_batch(0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch ahead of the W1 fetch
     RowHalf<WT, R> w1;
     float lse2q = 0.f;
     if (mode == kModeResidual) {
-        w1.load(static_cast<const WT *>(p.W1) + size_t(p.prev[b]) * R, lane >> 5);
-        lse2q = p.lse2q[b];
+        w1.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, lane >> 5);
+        lse2q = lse2q_in;
     }
     float S = 0.f, bl = kNegInf;
     int tile = 0x7fffffff;
-    constexpr int PC = 4;
     for (int c0 = 0; c0 < p.nchunk; c0 += 64 * PC) {
-        float cs[PC], cb[PC];
-        int ct[PC];
+        if (c0 > 0) load_batch(c0);
 #pragma unroll
         for (int u = 0; u < PC; ++u) {
-            const int c = c0 + lane + 64 * u;
-            const bool in = c < p.nchunk;
-            const size_t o = size_t(slot) * p.nchunk + (in ? c : 0);
-            cs[u] = in ? p.dw_sum[o] : 0.f;
-            cb[u] = in ? p.dw_bl[o] : kNegInf;
-            ct[u] = in ? p.dw_bt[o] : 0x7fffffff;
-        }
-#pragma unroll
-        for (int u = 0; u < PC; ++u) {
-            S += cs[u];
-            argmax_merge(bl, tile, cb[u], ct[u]);
+            if (c0 + lane + 64 * u < p.nchunk) {
+                S += cs[u];
+                argmax_merge(bl, tile, cb[u], ct[u]);
+            }
         }
     }
     S = wave_sum(S);
