@@ -282,37 +282,35 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     const int lane = threadIdx.x & 63;
     if (b >= p.B) return;
     const bool writer = sg == 0 && q == 0;
-    // every load the decisions need, issued together: lane half h holds the
-    // segment statistics of the previous pass's row slot h, read whatever the
-    // request's state
+    // every load the decisions need, issued together and unconditionally
+    // (clamped indices; what a case does not use is masked after): lane half
+    // h holds the segment statistics of the previous pass's row slot h, read
+    // whatever the request's state.  The first pass reads buffers it ignores.
+    const int hq = min(lane >> 5, D - 1), c = min(lane & 31, p.nseg_in - 1);
+    const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
     const int mode = p.mode[b];
-    const int act = j0 > 1 ? p.act_in[b] : 1;
+    const int act_raw = p.act_in[b];
     const float T = p.temperature[b];
     const int L = p.ell[b];
-    float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
-    int i2 = 0x7fffffff;
+    float mm = p.pm_in[o_in], s2 = p.ps_in[o_in], v2 = p.pv_in[o_in];
+    int i2 = p.pi_in[o_in];
     float tx2[D], qk[D];
     int xk[D];
-    if (j0 > 1) {
-        const int hq = lane >> 5, c = lane & 31;
-        if (hq < D && c < p.nseg_in) {
-            const size_t o = hq * p.row_stride + size_t(b) * p.seg_stride + c;
-            mm = p.pm_in[o];
-            s2 = p.ps_in[o];
-            v2 = p.pv_in[o];
-            i2 = p.pi_in[o];
-        }
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int k = j0 - D + u;  // position decided from slot u
-            tx2[u] = p.tx_in[size_t(u) * p.B + b];
-            xk[u] = 0;
-            qk[u] = 0.f;
-            if (k <= p.gamma) {
-                xk[u] = p.x[size_t(b) * p.gamma + k - 1];
-                qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
-            }
-        }
+    for (int u = 0; u < D; ++u) {
+        const int k = min(max(j0 - D + u, 1), p.gamma);  // position decided from slot u (clamped)
+        tx2[u] = p.tx_in[size_t(u) * p.B + b];
+        xk[u] = p.x[size_t(b) * p.gamma + k - 1];
+        qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(mode), "v"(act_raw), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
+    const int act = j0 > 1 ? act_raw : 1;
+    if (!((lane >> 5) < D && (lane & 31) < p.nseg_in)) {
+        mm = kNegInf;
+        s2 = 0.f;
+        v2 = kNegInf;
+        i2 = 0x7fffffff;
     }
     if (mode < 0 || act == 0) {
         if (writer && lane == 0) p.act_out[b] = 0;
