@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace dspark {
 
@@ -126,6 +127,53 @@ __device__ __forceinline__ void best_merge(float &b, int &i, float &sc, float b2
     if (b2 > b || (b2 == b && i2 < i)) {
         b = b2;
         i = i2;
+    }
+}
+
+// ---------------------------------------------------------------- butterflies
+// The partner value of a 64-lane all-reduce at step S, on the vector ALUs
+// (no round trip through the LDS crossbar).  Step 0 pairs lane i with i ^ 1
+// and step 1 with i ^ 2 (quad permutes), step 2 with 7 - i within its group
+// of 8 (row half mirror), step 3 with 15 - i within its row of 16 (row
+// mirror), step 4 with i ^ 16 and step 5 with i ^ 32 (v_permlane16_swap and
+// v_permlane32_swap of x with itself, which hand each row or half its
+// partner's copy).  Each step joins two groups that earlier steps have
+// already reduced, so after steps 0..3 every lane holds its row's result,
+// after step 4 its half's and after step 5 the wave's.  Every lane of the
+// wave must be active.
+template <int S>
+__device__ __forceinline__ uint32_t bfly_u32(uint32_t x) {
+    if constexpr (S == 0) {
+        return uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    } else if constexpr (S == 1) {
+        return uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    } else if constexpr (S == 2) {
+        return uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    } else if constexpr (S == 3) {
+        return uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+    } else if constexpr (S == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (threadIdx.x & 16) ? r[0] : r[1];
+    } else {
+        static_assert(S == 5, "six steps");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+}
+template <int S>
+__device__ __forceinline__ float bfly(float x) {
+    return __uint_as_float(bfly_u32<S>(__float_as_uint(x)));
+}
+template <int S>
+__device__ __forceinline__ int bfly(int x) {
+    return int(bfly_u32<S>(uint32_t(x)));
+}
+// f(std::integral_constant<int, S>) for S = S0 .. S1 - 1, in order
+template <int S0, int S1, class F>
+__device__ __forceinline__ void bfly_steps(F &&f) {
+    if constexpr (S0 < S1) {
+        f(std::integral_constant<int, S0>{});
+        bfly_steps<S0 + 1, S1>(f);
     }
 }
 
@@ -252,7 +300,7 @@ struct RowHalf {
             }
         }
         const float t = (d[0] + d[1]) + (d[2] + d[3]);
-        return t + __shfl_xor(t, 32);
+        return t + bfly<5>(t);
     }
 };
 

@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     }
     // the two lane halves raced alternate tiles of the same request
     {
-        const float m2 = __shfl_xor(st.m, 32), s2 = __shfl_xor(st.s, 32);
-        const float b2 = __shfl_xor(st.best, 32), c2 = __shfl_xor(st.second, 32);
-        const int i2 = __shfl_xor(st.bt, 32);
+        const float m2 = bfly<5>(st.m), s2 = bfly<5>(st.s);
+        const float b2 = bfly<5>(st.best), c2 = bfly<5>(st.second);
+        const int i2 = bfly<5>(st.bt);
         lse_merge(st.m, st.s, m2, s2);
         best_merge(st.best, st.bt, st.second, b2, i2, TRACK2 ? c2 : kNegInf);
     }
@@ -235,14 +235,13 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
             }
         }
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
-        const float b2 = __shfl_xor(best, off), c2 = __shfl_xor(second, off);
-        const int i2 = __shfl_xor(bt, off);
+    bfly_steps<0, 6>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float m2 = bfly<S>(m), s2 = bfly<S>(s), b2 = bfly<S>(best), c2 = bfly<S>(second);
+        const int i2 = bfly<S>(bt);
         lse_merge(m, s, m2, s2);
         best_merge(best, bt, second, b2, i2, c2);
-    }
+    });
     const int tile = min(max(bt, 0), p.ntiles - 1);
     // level 2: the winning tile's logits on the vector ALUs, then the entry race
     const bool sampled = T > 0.f;
@@ -259,12 +258,12 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     if (h != 0) score = kNegInf;  // the upper half duplicates the lower half
     float s1 = score, s2 = kNegInf;
     int xi = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float b2 = __shfl_xor(s1, off), c2 = __shfl_xor(s2, off);
-        const int i2 = __shfl_xor(xi, off);
+    bfly_steps<0, 6>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float b2 = bfly<S>(s1), c2 = bfly<S>(s2);
+        const int i2 = bfly<S>(xi);
         best_merge(s1, xi, s2, b2, i2, c2);
-    }
+    });
     const int x = min(max(xi, tile * kTile), p.V - 1);
     const float z2x = __shfl(z2, x - tile * kTile);
     if (lane == 0) {
@@ -371,7 +370,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
         __syncthreads();
         if (wave_ok) stage(ldsA, t_begin + 2 * nfull, true);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // the two lane halves held different rows of the same tiles
+    mx = fmaxf(mx, bfly<5>(mx));  // the two lane halves held different rows of the same tiles
     if (h == 0 && row_ok) p.pm[size_t(b) * p.nchunk + chunk] = mx;
 }
 
@@ -382,8 +381,7 @@ __global__ __launch_bounds__(256) void bias_rowmax_kernel(const float *pm, int B
     if (b >= B) return;
     float m = kNegInf;
     for (int c = lane; c < nchunk; c += 64) m = fmaxf(m, pm[size_t(b) * nchunk + c]);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    bfly_steps<0, 6>([&](auto st) { m = fmaxf(m, bfly<decltype(st)::value>(m)); });
     if (lane == 0) out[b] = m;
 }
 

@@ -52,14 +52,12 @@ constexpr int kModeResidual = 1;
 constexpr int kModeBonus = 2;
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    bfly_steps<0, 6>([&](auto st) { v = fmaxf(v, bfly<decltype(st)::value>(v)); });
     return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    bfly_steps<0, 6>([&](auto st) { v += bfly<decltype(st)::value>(v); });
     return v;
 }
 
@@ -72,8 +70,12 @@ __device__ __forceinline__ void argmax_merge(float &v, int &i, float v2, int i2)
 
 // value/index argmax across the wave: larger value, lower index on ties
 __device__ __forceinline__ void wave_argmax(float &v, int &i) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) argmax_merge(v, i, __shfl_xor(v, o), __shfl_xor(i, o));
+    bfly_steps<0, 6>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float v2 = bfly<S>(v);
+        const int i2 = bfly<S>(i);
+        argmax_merge(v, i, v2, i2);
+    });
 }
 
 // Exclusive scan over a workgroup of NT threads of one int per thread.
@@ -319,11 +321,13 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
     if (j0 > 1) {
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {  // within each lane half
-            lse_merge(mm, s2, __shfl_xor(mm, o), __shfl_xor(s2, o));
-            argmax_merge(v2, i2, __shfl_xor(v2, o), __shfl_xor(i2, o));
-        }
+        bfly_steps<0, 5>([&](auto st) {  // within each lane half
+            constexpr int S = decltype(st)::value;
+            const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
+            const int i_o = bfly<S>(i2);
+            lse_merge(mm, s2, m_o, s_o);
+            argmax_merge(v2, i2, v_o, i_o);
+        });
         float lse2[D];
         int amax[D];
 #pragma unroll
@@ -483,11 +487,13 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             }
         }
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        lse_merge(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
-        argmax_merge(av, ai, __shfl_xor(av, o), __shfl_xor(ai, o));
-    }
+    bfly_steps<0, 6>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float m_o = bfly<S>(m), s_o = bfly<S>(s), v_o = bfly<S>(av);
+        const int i_o = bfly<S>(ai);
+        lse_merge(m, s, m_o, s_o);
+        argmax_merge(av, ai, v_o, i_o);
+    });
     if (lane == 0) {
         const size_t o = q * p.row_stride + size_t(b) * p.seg_stride + sg;
         p.pm_out[o] = m;
@@ -704,8 +710,7 @@ struct FinishParams {
 __device__ __forceinline__ int wave_race(float score, int v) {
     float s = (threadIdx.x & 32) ? kNegInf : score;
     int i = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) argmax_merge(s, i, __shfl_xor(s, o), __shfl_xor(i, o));
+    wave_argmax(s, i);
     return i;
 }
 
@@ -784,8 +789,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
         }
     }
     S = wave_sum(S);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) argmax_merge(bl, tile, __shfl_xor(bl, o), __shfl_xor(tile, o));
+    wave_argmax(bl, tile);
 
     const int i = lane & 31, h = lane >> 5;
     const bool use_res = mode == kModeResidual && S > 0.f && bl > kNegInf;
@@ -804,8 +808,7 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
                 gumbel2(noise_word(kStreamResampleTile, j, uint32_t(t), uint32_t(b), p.round32, p.key0, p.key1));
             argmax_merge(b1, t1, mm + fast_log2(ss) + g, t);
         }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) argmax_merge(b1, t1, __shfl_xor(b1, o), __shfl_xor(t1, o));
+        wave_argmax(b1, t1);
         tile = t1;
     }
     tile = min(max(tile, 0), p.ntiles - 1);
