@@ -146,8 +146,10 @@ def _oracle_one_thread(rnd, target, ell, seed, gamma, oracle_round, rows=128):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # a round takes about 0.4 ms: a hundred warmup rounds bring the clocks to
+    # their sustained level (five leave the timed rounds about 5% slower)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg (and the parity gate)")
     ap.add_argument("--rounds", type=int, default=60, help="rounds timed one by one for the round-time distribution")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

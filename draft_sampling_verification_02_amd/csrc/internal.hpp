@@ -84,6 +84,7 @@ VerifyPlan verify_plan(int B, int gamma, int V);
 
 struct VerifyWork {
     int32_t *status;     // [4] device status flags, -, n_resid, n_bonus
+    int32_t *req_flags;  // [B] the status flags each request's inputs raise
     int32_t *off;        // [B + 1] packed row offsets in use
     // position passes, double buffered by pass parity (pass p reads the half
     // pass p - 1 wrote), one slot per row a pass reduces

@@ -50,6 +50,7 @@ constexpr int kStatusRowsOutOfRange = 4;
 constexpr int kModeDone = 0;
 constexpr int kModeResidual = 1;
 constexpr int kModeBonus = 2;
+constexpr int kPrepInPassMaxBatch = 512;
 
 __device__ __forceinline__ float wave_max(float v) {
     bfly_steps<0, 6>([&](auto st) { v = fmaxf(v, bfly<decltype(st)::value>(v)); });
@@ -57,6 +58,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
+    bfly_steps<0, 6>([&](auto st) { v += bfly<decltype(st)::value>(v); });
+    return v;
+}
+
+__device__ __forceinline__ int wave_isum(int v) {
     bfly_steps<0, 6>([&](auto st) { v += bfly<decltype(st)::value>(v); });
     return v;
 }
@@ -101,67 +107,68 @@ __device__ int block_exclusive_scan(int v, int *lds, int *total) {
 struct PrepParams {
     const int32_t *ell, *row_offsets;
     int B, gamma, n_target_rows;
-    int32_t *status, *off, *mode;
+    int32_t *status, *off, *mode, *req_flags;
     int32_t *n_accept_out, *tokens_out;
     float *diag_out, *resid_out;
 };
 
+// Checks one request's ell and row offset (o: the computed offset, replaced by
+// the caller's when given) and returns its input flags; *off_out gets the
+// offset to use (0 for a request that fails).
+__device__ __forceinline__ int check_request(const int32_t *ell, const int32_t *row_offsets, int b, int gamma,
+                                             int n_target_rows, int o, int *off_out) {
+    const int e_raw = ell[b];
+    const int e = min(max(e_raw, 0), gamma);
+    int f = (e_raw == e) ? 0 : kStatusBadEll;
+    if (row_offsets) {
+        o = row_offsets[b];
+        const int o1 = row_offsets[b + 1];
+        if (o < 0 || o1 - o != 1 + e_raw) f |= kStatusBadOffsets;
+    }
+    if (f == 0 && o + e + 1 > n_target_rows) f |= kStatusRowsOutOfRange;
+    *off_out = f == 0 ? o : 0;
+    return f;
+}
+
+// The output defaults of request b, shared by `stride` threads of which this
+// is number `lane`.
+__device__ __forceinline__ void output_defaults(int b, int gamma, int lane, int stride, int32_t *n_accept_out,
+                                                int32_t *tokens_out, float *diag_out, float *resid_out) {
+    int32_t *tok = tokens_out + size_t(b) * (gamma + 1);
+    for (int i = lane; i <= gamma; i += stride) tok[i] = -1;
+    if (diag_out)
+        for (int i = lane; i < 2 * (gamma + 1); i += stride)
+            diag_out[size_t(b) * 2 * (gamma + 1) + i] = __builtin_nanf("");
+    if (lane == 0) {
+        n_accept_out[b] = -1;  // set by the pass that ends the request
+        if (resid_out) resid_out[b] = -1.f;
+    }
+}
+
+// Input checks, row offsets and output defaults of a large batch, by one
+// workgroup (a small batch has them done by its first position pass).
 __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
     __shared__ int lds[1024];
     const int t = threadIdx.x;
     const int seg = (p.B + 1023) / 1024;
     const int b0 = min(p.B, t * seg), b1 = min(p.B, b0 + seg);
-    const float nan = __builtin_nanf("");
-    int flags = 0;
     int local = 0;
-    for (int b = b0; b < b1; ++b) {
-        int e = p.ell[b];
-        if (e < 0 || e > p.gamma) {
-            flags |= kStatusBadEll;
-            e = min(max(e, 0), p.gamma);
-        }
-        local += 1 + e;
-    }
+    for (int b = b0; b < b1; ++b) local += 1 + min(max(p.ell[b], 0), p.gamma);
     int total = 0;
     int base = block_exclusive_scan<1024>(local, lds, &total);
     // offsets: computed, or the caller's after a consistency check
     for (int b = b0; b < b1; ++b) {
-        const int e_raw = p.ell[b];
-        const int e = min(max(e_raw, 0), p.gamma);
-        int o = base;
-        bool ok = (e_raw == e);
-        if (p.row_offsets) {
-            o = p.row_offsets[b];
-            const int o1 = p.row_offsets[b + 1];
-            if (o < 0 || o1 - o != 1 + e_raw) {
-                ok = false;
-                flags |= kStatusBadOffsets;
-            }
-        }
-        if (ok && o + e + 1 > p.n_target_rows) {
-            ok = false;
-            flags |= kStatusRowsOutOfRange;
-        }
-        p.off[b] = ok ? o : 0;
-        p.mode[b] = ok ? kModeDone : -1;
-        p.n_accept_out[b] = -1;  // set by the pass that ends the request
-        int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
-        for (int i = 0; i <= p.gamma; ++i) tok[i] = -1;
-        if (p.diag_out)
-            for (int i = 0; i < 2 * (p.gamma + 1); ++i) p.diag_out[size_t(b) * 2 * (p.gamma + 1) + i] = nan;
-        if (p.resid_out) p.resid_out[b] = -1.f;
-        base += 1 + e;
+        int o = 0;
+        const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, base, &o);
+        p.off[b] = o;
+        p.mode[b] = f == 0 ? kModeDone : -1;
+        p.req_flags[b] = f;
+        output_defaults(b, p.gamma, 0, 1, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
+        base += 1 + min(max(p.ell[b], 0), p.gamma);
     }
     if (t == 1023) p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : total;
-    // status flags: OR across the group
-    lds[t] = flags;
-    __syncthreads();
-    for (int o = 512; o >= 1; o >>= 1) {
-        if (t < o) lds[t] |= lds[t + o];
-        __syncthreads();
-    }
+    // the status word is the OR of the requests' flags, formed by the finish
     if (t == 0) {
-        p.status[0] = lds[0];
         p.status[1] = 0;
         p.status[2] = 0;
         p.status[3] = 0;
@@ -188,7 +195,13 @@ struct PassParams {
     int seg_stride;     // partials per request in the buffers
     size_t row_stride;  // partials per row slot of a pass (B * seg_stride)
     uint32_t key0, key1, round32;
-    const int32_t *off;
+    int32_t *off;
+    // prep != 0 (first pass of a small batch): the pass also checks each
+    // request's inputs, computes its row offset and writes the output defaults
+    int prep, n_target_rows;
+    const int32_t *row_offsets;
+    int32_t *req_flags;
+    float *resid_out;
     // pass p reads what pass p - 1 left and writes into the other half of
     // each double buffer; slot q holds the pass's q-th row
     const int32_t *act_in;  // [B] 1: the request's rows of the previous pass were reduced
@@ -290,7 +303,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     // whatever the request's state.  The first pass reads buffers it ignores.
     const int hq = min(lane >> 5, D - 1), c = min(lane & 31, p.nseg_in - 1);
     const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
-    const int mode = p.mode[b];
+    const int mode_ld = p.mode[b], off_ld = p.off[b];
     const int act_raw = p.act_in[b];
     const float T = p.temperature[b];
     const int L = p.ell[b];
@@ -306,8 +319,31 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
     }
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"v"(mode), "v"(act_raw), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
+    asm volatile("" ::"v"(mode_ld), "v"(off_ld), "v"(act_raw), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
     const int act = j0 > 1 ? act_raw : 1;
+    int mode = mode_ld, offb = off_ld;
+    if (p.prep) {  // uniform: the first pass of a small batch
+        int part = 0;
+        if (!p.row_offsets)
+            for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
+        const int o_cmp = wave_isum(part);
+        const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
+        mode = f == 0 ? kModeDone : -1;
+        if (writer) {
+            if (lane == 0) {
+                p.off[b] = offb;
+                p.mode[b] = mode;
+                p.req_flags[b] = f;
+                if (b == p.B - 1) p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L, 0), p.gamma);
+            }
+            output_defaults(b, p.gamma, lane, 64, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) {  // the draw-list counters the later passes bump
+            p.status[1] = 0;
+            p.status[2] = 0;
+            p.status[3] = 0;
+        }
+    }
     if (!((lane >> 5) < D && (lane & 31) < p.nseg_in)) {
         mm = kNegInf;
         s2 = 0.f;
@@ -355,7 +391,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         if (writer && lane == 0) p.act_out[b] = 0;
         return;
     }
-    const float *trow = p.target + size_t(p.off[b] + j - 1) * p.V;
+    const float *trow = p.target + size_t(offb + j - 1) * p.V;
     const int v_lo = sg * p.seg_len, v_hi = min(p.V, v_lo + p.seg_len);
     float m = kNegInf, s = 0.f, av = kNegInf;
     int ai = 0x7fffffff;
@@ -698,7 +734,8 @@ struct FinishParams {
     const float *lse_q, *temperature;
     int B, gamma, V, nchunk, ntiles;
     uint32_t key0, key1, round32;
-    const int32_t *status, *mode, *n_accept, *slot, *off, *jpos, *prev;
+    int32_t *status;
+    const int32_t *mode, *n_accept, *slot, *off, *jpos, *prev, *req_flags;
     const float *fin_lse2, *lse2q;
     const float *dw_sum, *dw_bl;
     const int32_t *dw_bt;
@@ -734,9 +771,22 @@ __device__ void scan_out_offsets(const FinishParams &p) {
     if (t == 0) p.out_offsets[p.B] = total;
 }
 
+// The status word: the OR of every request's input flags, by one workgroup.
+__device__ void status_word(const FinishParams &p) {
+    __shared__ int flags;
+    if (threadIdx.x == 0) flags = 0;
+    __syncthreads();
+    int local = 0;
+    for (int b = threadIdx.x; b < p.B; b += blockDim.x) local |= p.req_flags[b];
+    if (local) atomicOr(&flags, local);
+    __syncthreads();
+    if (threadIdx.x == 0) p.status[0] = flags;
+}
+
 template <typename WT, int R>
 __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     if (blockIdx.x == gridDim.x - 1) {  // the extra workgroup
+        status_word(p);
         if (p.out_offsets) scan_out_offsets(p);
         return;
     }
@@ -840,9 +890,13 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
 template <typename WT, int R>
 hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyWork &w, hipStream_t s) {
     hipError_t e;
-    {
+    // a small batch has its input checks and output defaults done by the
+    // first position pass (each of its waves forms its request's row offset
+    // from ell, O(B) reads a wave); a large one by a workgroup of its own
+    const bool prep_in_pass = a.B <= kPrepInPassMaxBatch;
+    if (!prep_in_pass) {
         PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, a.n_target_rows, w.status, w.off,
-                      w.mode, a.n_accept_out, a.tokens_out, a.diag_out, a.resid_out};
+                      w.mode, w.req_flags, a.n_accept_out, a.tokens_out, a.diag_out, a.resid_out};
         int t = prof_begin("verify_prep", s);
         hipLaunchKernelGGL(verify_prep_kernel, dim3(1), dim3(1024), 0, s, pp);
         prof_end(t, s);
@@ -877,6 +931,11 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.key1 = a.key1;
         pp.round32 = a.round32;
         pp.off = w.off;
+        pp.prep = (pass == 1 && prep_in_pass) ? 1 : 0;
+        pp.n_target_rows = a.n_target_rows;
+        pp.row_offsets = a.row_offsets;
+        pp.req_flags = w.req_flags;
+        pp.resid_out = a.resid_out;
         pp.act_in = w.act + size_t(in) * a.B;
         pp.pm_in = w.seg_m + in * half;
         pp.ps_in = w.seg_s + in * half;
@@ -970,6 +1029,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         fp.key1 = a.key1;
         fp.round32 = a.round32;
         fp.status = w.status;
+        fp.req_flags = w.req_flags;
         fp.mode = w.mode;
         fp.n_accept = a.n_accept_out;
         fp.slot = w.slot;
@@ -1026,6 +1086,7 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     Carve c(ws);
     VerifyWork w{};
     w.status = c.take<int32_t>(4);
+    w.req_flags = c.take<int32_t>(B);
     w.off = c.take<int32_t>(size_t(B) + 1);
     w.act = c.take<int32_t>(size_t(2) * B);
     const size_t ns = size_t(2) * kPassRows * B * p.nseg_max;

@@ -244,8 +244,10 @@ def test_neg_inf_logits_parity():
             assert np.isfinite(rnd.U[b, k, gd["x"][b, k]])
 
 
-def test_row_offsets_given_equal_computed_and_bad_ell_flagged():
-    rnd, ell, target = _custom_round(24, 3, 500, 16, "bf16", seed=9)
+@pytest.mark.parametrize("B", [24, 600])  # input checks in the first pass / in a prep workgroup
+def test_row_offsets_given_equal_computed_and_bad_ell_flagged(B):
+    rnd, ell, target = _custom_round(B, 3, 500, 16, "bf16", seed=9)
+    _say(f"[offsets] B={B}")
     dev = to_device(rnd)
     td = torch.from_numpy(target).cuda()
     d = gpu_draft(dev, 1, 1)
@@ -259,6 +261,19 @@ def test_row_offsets_given_equal_computed_and_bad_ell_flagged():
     assert ds.dspark_verify_check(v3["workspace"]) == ds.DSPARK_ERR_DEVICE_INPUT
     assert int(v3["n"][5]) == -1
     assert np.all(np_of(v3["tokens"][5]) == -1)
+    # a packed target two rows short: the last request's rows are out of range
+    short = td[:-2].contiguous()
+    v4 = gpu_verify(dev, short, torch.from_numpy(ell).cuda(), d, 1, 1)
+    assert ds.dspark_verify_check(v4["workspace"]) == ds.DSPARK_ERR_DEVICE_INPUT
+    fits = S.pack_offsets(ell)[1:] <= target.shape[0] - 2  # requests whose rows are all there
+    assert not fits[-1]
+    n4, t4 = np_of(v4["n"]), np_of(v4["tokens"])
+    assert np.all(n4[~fits] == -1) and np.all(t4[~fits] == -1)
+    np.testing.assert_array_equal(n4[fits], np_of(v1["n"])[fits])
+    # and a clean call after the flagged ones reports no error again
+    v5 = gpu_verify(dev, td, torch.from_numpy(ell).cuda(), d, 1, 1)
+    assert ds.dspark_verify_check(v5["workspace"]) == 0
+    assert torch.equal(v5["tokens"], v1["tokens"])
 
 
 def test_bitwise_determinism():
