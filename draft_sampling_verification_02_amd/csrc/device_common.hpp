@@ -198,6 +198,11 @@ struct EFrags<uint16_t, R> {
 #pragma unroll
         for (int s = 0; s < S; ++s) e[s] = *reinterpret_cast<const uint4 *>(row + 16 * s + 8 * h);
     }
+    // the fragments as values an empty asm defines (waits for their loads)
+    __device__ __forceinline__ void pin() {
+#pragma unroll
+        for (int s = 0; s < S; ++s) asm volatile("" : "+v"(e[s].x), "+v"(e[s].y), "+v"(e[s].z), "+v"(e[s].w));
+    }
 };
 
 template <int R>
@@ -208,6 +213,10 @@ struct EFrags<float, R> {
     __device__ __forceinline__ void load(const float *row, int h) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) e[q] = *reinterpret_cast<const float4 *>(row + 8 * q + 4 * h);
+    }
+    __device__ __forceinline__ void pin() {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) asm volatile("" : "+v"(e[q].x), "+v"(e[q].y), "+v"(e[q].z), "+v"(e[q].w));
     }
 };
 

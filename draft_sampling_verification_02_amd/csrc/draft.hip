@@ -50,6 +50,10 @@ struct StepParams {
     int32_t *pi;
 };
 
+// s_waitcnt immediate that waits for all but the n most recent vector memory
+// operations of this wave (lgkm and exp counts left free)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 constexpr int kStepThreads = 512;  // 8 waves: one 32-request block each
 
 // One workgroup of 8 waves walks the tiles [t_begin, t_end) of one vocabulary
@@ -78,26 +82,45 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const bool row_ok = wave_ok && b < p.B;
     const int bc = min(b, p.B - 1);
 
-    int prev = p.xprev[size_t(bc) * p.xprev_stride];
-    prev = min(max(prev, 0), p.V - 1);
-    const float T = p.temperature[bc];
-    const bool sampled = T > 0.f;
-    const float sc = sampled ? kLog2e / T : 1.0f;  // base-2 logits; greedy keeps raw logits
-
     const WT *W2 = static_cast<const WT *>(p.W2);
-    EFrags<WT, R> ef;
-    if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
     StageDMA<WT, R, kStepThreads> dma;
     dma.init(tid);
-    SU su;
-    if (wave_ok) su.init(lane, p.U, p.u_stride, [&](int r) { return min(bb * 32 + r, p.B - 1); });
+    SU su;  // every wave (rows past the batch repeat its last request)
+    su.init(lane, p.U, p.u_stride, [&](int r) { return min(bb * 32 + r, p.B - 1); });
     uint8_t *uregion = ldsU + wave * SU::BYTES;
-
     const int t_begin = chunk * p.tiles_per_chunk;
     const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
     const int nst = (t_end - t_begin + 1) >> 1;  // stages of two tiles
     const bool tail = (t_begin + 2 * nst) * kTile > p.V;
     const int nfull = nst - (tail ? 1 : 0);
+    auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
+
+    // x_{k-1} first, then the first stage's loads, which need nothing but the
+    // tile walk, then the W1 gather: the stage streams in while the x_{k-1}
+    // round trip and the gather resolve (loads retire in order, so waiting
+    // for x_{k-1} leaves the stage in flight).  The stage is issued by every
+    // wave and clamped to the vocabulary, so that the number of loads in
+    // flight is the same on every path; a chunk that is only a tail stage
+    // reloads the buffers after a full barrier.
+    // The compiler does not count direct-to-LDS loads as younger than a
+    // register load and would drain the stage before the gather, so x_{k-1}
+    // and T are loaded and waited for in asm: with no more than this wave's
+    // own stage loads in flight (at least NI + MIN_PER_WAVE of them, issued
+    // after), both have landed.
+    int prev;
+    float T;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(prev) : "v"(p.xprev + size_t(bc) * p.xprev_stride) : "memory");
+    asm volatile("global_load_dword %0, %1, off" : "=v"(T) : "v"(p.temperature + bc) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    dma.template issue<true>(W2, v0_of(0), p.V, ldsA, wave);
+    su.template issue<true>(v0_of(0), p.V, uregion, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(prev), "+v"(T) : "n"(SU::NI + decltype(dma)::MIN_PER_WAVE));
+    prev = min(max(prev, 0), p.V - 1);
+    const bool sampled = T > 0.f;
+    const float sc = sampled ? kLog2e / T : 1.0f;  // base-2 logits; greedy keeps raw logits
+    EFrags<WT, R> ef;
+    if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
     TileRace st{kNegInf, 0.f, kNegInf, kNegInf, t_begin};
     uint4 tw = make_uint4(0u, 0u, 0u, 0u);
 
@@ -129,12 +152,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
         const uint32_t w_lo = (t0 & 2) ? tw.z : tw.x, w_hi = (t0 & 2) ? tw.w : tw.y;
         race_tile<TRACK2>(st, c0, c1, sc, sampled, t0 + h, gumbel2(h ? w_hi : w_lo));
     };
-    auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
 
-    if (nfull > 0) {
-        dma.template issue<false>(W2, v0_of(0), p.V, ldsA, wave);
-        if (wave_ok) su.template issue<false>(v0_of(0), p.V, uregion, lane);
-    }
     for (int i = 0; i < nfull; i += 2) {
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage i have landed
         __syncthreads();                // ... and every thread's; ldsB is free again
@@ -293,14 +311,72 @@ struct GemmParams {
     float *pm;  // [B, nchunk] per-chunk row maxima
 };
 
-// The draft step's walk with its epilogue cut down to a running maximum: the
-// same workgroups, W2 stages and MFMA tiles, no U_k read and no sampling.
+
+// bias_pair_lds with the A-fragment reads issued as inline asm, so that the
+// compiler, which cannot tell one stage buffer's direct loads from another's,
+// puts no wait for the stage loads in front of them; the caller has waited
+// for the stage.  The reads run D K-steps ahead and each step waits for its
+// own pair (LDS reads complete in order; any other lgkm operation in flight
+// only lengthens the wait).  The wait is tied to the pair's registers, so the
+// MFMAs that use them cannot move above it.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int R>
+__device__ __forceinline__ void gemm_pair(const EFrags<uint16_t, R> &ef, const uint8_t *buf, int lane, f32x16_t &c0,
+                                          f32x16_t &c1) {
+    using L = TileLDS<uint16_t, R>;
+    constexpr int S = EFrags<uint16_t, R>::S;
+    constexpr int D = S < 3 ? S : 3;
+    const int m = lane & 31, h = lane >> 5;
+    const uint32_t row =
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t *)buf)) + m * L::RB;
+    u32x4_t a0[D], a1[D];
+    auto rd = [&](u32x4_t &x0, u32x4_t &x1, int s) __device__ {
+        const uint32_t ad = row + L::chunk(m, 2 * s + h) * 16;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(x0) : "v"(ad));
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x1) : "v"(ad), "i"(L::BYTES));
+    };
+#pragma unroll
+    for (int s = 0; s < D; ++s) rd(a0[s], a1[s], s);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        u32x4_t x0 = a0[s % D], x1 = a1[s % D];
+        const int left = (S - s < D ? S - s : D) - 1;  // younger pairs in flight
+        if (left == 2)
+            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(x0), "+v"(x1));
+        else if (left == 1)
+            asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(x0), "+v"(x1));
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x0), "+v"(x1));
+        if (s + D < S) rd(a0[s % D], a1[s % D], s + D);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x0),
+                                                     __builtin_bit_cast(bf16x8_t, ef.e[s]), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x1),
+                                                     __builtin_bit_cast(bf16x8_t, ef.e[s]), c1, 0, 0, 0);
+    }
+}
+// f32 factors: the compiler-scheduled reads (it drains the stage loads first)
+template <int R>
+__device__ __forceinline__ void gemm_pair(const EFrags<float, R> &ef, const uint8_t *buf, int lane, f32x16_t &c0,
+                                          f32x16_t &c1) {
+    bias_pair_lds(ef, buf, lane, c0, c1);
+}
+
+// The draft step's tiling with its epilogue cut down to a running maximum: the
+// same workgroups, two-tile W2 stages and MFMA chains, no U_k read and no
+// sampling.  Without the U_k regions the LDS holds four stages, so three are
+// in flight while one is consumed: each wave waits for its own direct loads
+// of the stage (in-order vmcnt) and a bare barrier then covers every wave's,
+// without the full drain that __syncthreads' release fence would force.
 template <typename WT, int R>
 __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bias_gemm_kernel(
     GemmParams p) {
     using L = TileLDS<WT, R>;
-    __shared__ __attribute__((aligned(16))) uint8_t ldsA[2 * L::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t ldsB[2 * L::BYTES];
+    using DMA = StageDMA<WT, R, kStepThreads>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[2 * L::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds3[2 * L::BYTES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
@@ -315,7 +391,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
     if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
-    StageDMA<WT, R, kStepThreads> dma;
+    DMA dma;
     dma.init(tid);
     const int t_begin = chunk * p.tiles_per_chunk;
     const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
@@ -325,7 +401,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     float mx = kNegInf;
     auto stage = [&](const uint8_t *buf, int t0, bool masked) __device__ {
         f32x16_t c0 = {}, c1 = {};
-        bias_pair_lds(ef, buf, lane, c0, c1);
+        gemm_pair(ef, buf, lane, c0, c1);
         if (masked) {
             // value 4i+j of lane (n, h) is entry 8i + 4h + j of each tile
 #pragma unroll
@@ -351,24 +427,58 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
         mx = max3f(max3f(m0, d[14], d[15]), m1, mx);
     };
     auto v0_of = [&](int i) { return (t_begin + 2 * i) * kTile; };
-    if (nfull > 0) dma.template issue<false>(W2, v0_of(0), p.V, ldsA, wave);
-    for (int i = 0; i < nfull; i += 2) {
+    // stage i of the chunk: wait until its loads (and every older one) have
+    // landed, join the workgroup, refill the buffer stage i - 1 used with
+    // stage i + 3, consume stage i
+    // (restrict: the compiler may then tell the refill's direct loads from the
+    // buffer being read, and wait only for the older ones)
+    auto step = [&](int i, const uint8_t *__restrict__ cur, uint8_t *__restrict__ refill) __device__ {
+        const int after = min(2, nfull - 1 - i);  // younger stages in flight; uniform
+        if (after == 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA::J));
+        else if (after == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA::J));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();
+        if (i + 3 < nfull) dma.template issue<false>(W2, v0_of(i + 3), p.V, refill, wave);
+        if (wave_ok) stage(cur, t_begin + 2 * i, false);
+    };
+    if (nfull >= 3) {
+        dma.template issue<false>(W2, v0_of(0), p.V, lds0, wave);
+        dma.template issue<false>(W2, v0_of(1), p.V, lds1, wave);
+        dma.template issue<false>(W2, v0_of(2), p.V, lds2, wave);
+        // The loop's own loads write no registers and it reads the W1
+        // fragments loaded before it, so the compiler would drain every load
+        // at the loop entry, stages included.  Waiting for the fragments only
+        // (they are older than the stages) and passing them through an empty
+        // asm makes them plain register values to it.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA::J));
+        if (wave_ok) ef.pin();
+        for (int i = 0; i < nfull; i += 4) {
+            step(i, lds0, lds3);
+            if (i + 1 >= nfull) break;
+            step(i + 1, lds1, lds0);
+            if (i + 2 >= nfull) break;
+            step(i + 2, lds2, lds1);
+            if (i + 3 >= nfull) break;
+            step(i + 3, lds3, lds2);
+        }
+    } else {
+        // one or two full stages: loaded together, then consumed
+        if (nfull > 0) dma.template issue<false>(W2, v0_of(0), p.V, lds0, wave);
+        if (nfull > 1) dma.template issue<false>(W2, v0_of(1), p.V, lds1, wave);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (i + 1 < nfull) dma.template issue<false>(W2, v0_of(i + 1), p.V, ldsB, wave);
-        if (wave_ok) stage(ldsA, t_begin + 2 * i, false);
-        if (i + 1 >= nfull) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (i + 2 < nfull) dma.template issue<false>(W2, v0_of(i + 2), p.V, ldsA, wave);
-        if (wave_ok) stage(ldsB, t_begin + 2 * (i + 1), false);
+        if (wave_ok && nfull > 0) stage(lds0, t_begin, false);
+        if (wave_ok && nfull > 1) stage(lds1, t_begin + 2, false);
     }
     if (tail) {
-        __syncthreads();
-        dma.template issue<true>(W2, v0_of(nfull), p.V, ldsA, wave);
+        __syncthreads();  // every wave is done with every buffer
+        dma.template issue<true>(W2, v0_of(nfull), p.V, lds0, wave);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (wave_ok) stage(ldsA, t_begin + 2 * nfull, true);
+        if (wave_ok) stage(lds0, t_begin + 2 * nfull, true);
     }
     mx = fmaxf(mx, bfly<5>(mx));  // the two lane halves held different rows of the same tiles
     if (h == 0 && row_ok) p.pm[size_t(b) * p.nchunk + chunk] = mx;

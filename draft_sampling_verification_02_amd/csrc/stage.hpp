@@ -60,6 +60,9 @@ struct StageDMA {
     using L = TileLDS<WT, R>;
     static constexpr int SLOTS = 2 * L::SLOTS;  // 16-byte slots of a stage
     static constexpr int J = (SLOTS + NT - 1) / NT;
+    // load instructions every wave issues a stage (the last waves may issue
+    // fewer than J when a stage has fewer slots than the workgroup threads)
+    static constexpr int MIN_PER_WAVE = SLOTS > NT - 64 ? (SLOTS - (NT - 64) - 1) / NT + 1 : 0;
     uint32_t goff[J];  // byte offset of the slot's source from the stage's first row
     int row[J];        // stage row (0..63) the slot belongs to
 
@@ -103,9 +106,10 @@ struct StageRows {
     static constexpr int NI = VEC ? BYTES / 1024 : BYTES / 256;  // load instructions a stage
     const float *base;  // region row r reads base + idx * stride
     size_t stride;
-    int idx[NI];        // source row of each instruction's lane, -1 for none
+    int idx[NI];        // source row of each instruction's lane
 
-    // row(r) is the source row index of region row r (0..31), or -1 for none
+    // row(r) is the source row index of region row r (0..31); every region
+    // row has one, so that a stage is always NI load instructions a lane
     template <typename RowFn>
     __device__ __forceinline__ void init(int lane, const float *base_, size_t stride_, RowFn row) {
         base = base_;
@@ -119,14 +123,12 @@ struct StageRows {
         const int r = region_row(j, lane);
         return VEC ? 4 * ((lane & 15) ^ (r & 15)) : 4 * (((lane >> 2) ^ r) & 15) + (lane & 3);
     }
-    // rows without a source are skipped (their region rows keep stale data)
     template <bool CLAMP>
     __device__ __forceinline__ void issue(int v0, int V, uint8_t *region, int lane) const {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             int v = v0 + region_col(j, lane);
             if (CLAMP) v = min(v, V - (VEC ? 4 : 1));
-            if (idx[j] < 0) continue;
             const void *g = base + size_t(idx[j]) * stride + v;
             if constexpr (VEC)
                 __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)(region + j * 1024), 16, 0, 0);
