@@ -60,6 +60,35 @@ def _traffic_from_counters(launch_bytes):
     return float(t.group(1))
 
 
+def _logit_passes(phases, gv0, rnd, ell, B, gamma, V, r):
+    """The verify logit passes against the HBM peak: algorithmic bytes over the
+    event-timed average launch.  The first position pass reads every
+    request's first row; the later passes and the draw read what the round's
+    outcome asks for, counted here from the first round (the timed rounds
+    draw other random numbers, with the same statistics)."""
+    import numpy as np
+    n0 = np.asarray(gv0["n"])
+    sampled = np.asarray(rnd.temperature) > 0
+    n_res = int(((n0 < ell) & sampled).sum())
+    n_bon = int(((n0 == ell) & sampled).sum())
+    row = V * 4
+    out = {}
+
+    def put(name, nbytes, keys):
+        us = sum(phases[k]["avg_us"] for k in keys if k in phases)
+        if us > 0:
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[name] = {"bytes": int(nbytes), "us": round(us, 2), "gbs": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    put("verify_pass1", B * row, ["verify_pass1"])
+    later = sum(int(((n0 >= j - 1) & (ell >= j - 1)).sum()) for j in range(2, gamma + 2)) * row
+    put("verify_pass2_on", later, [k for k in phases if k.startswith("verify_pass") and k != "verify_pass1"])
+    put("verify_draw", (2 * n_res + n_bon) * row + (V * r * 2 if n_res else 0), ["verify_draw"])
+    out["draw_requests"] = {"residual": n_res, "bonus": n_bon}
+    return out
+
+
 def _round_distribution(torch, step, n, base):
     """Single-round times (HIP events on the launch stream around each round,
     rounds queued back to back): p10 / p50 / p90 in milliseconds."""
@@ -252,6 +281,8 @@ def main():
                 "mfma_frac": round(flops_per_launch / ds_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                 "kernel_source_hash": _kernel_hash()}
 
+    logit = _logit_passes(phases, gv0, rnd, ell, B, gamma, V, r)
+
     result = {
         "metric": "draft+verify positions/sec at B=256 gamma=5 V=129k; % of HBM/MFMA roofline",
         "value": round(value, 1),
@@ -273,6 +304,7 @@ def main():
                       "phases_us": {k: round(p["avg_us"], 2) for k, p in phases.items()},
                       "round_ms": round_dist,
                       "bias_gemm_alone": gemm,
+                      "logit_passes": logit,
                       "schedule": sched},
         "roofline": roofline,
     }
