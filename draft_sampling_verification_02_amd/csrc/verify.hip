@@ -278,6 +278,45 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
     return false;
 }
 
+// One batch of U float4 groups of a row into a lane's running base-2
+// logsumexp (m, s) of x * sc; group u holds entries v0 + 256 u .. + 3 and
+// counts only if valid(u).  The scale is positive, so the maximum is taken
+// on the raw values and the scale folds into one fma per entry.  ARGMAX
+// (greedy rows, sc = 1) also keeps the lowest-index maximum (av, ai).
+template <bool ARGMAX, int U, class Valid>
+__device__ __forceinline__ void row_batch(float4 (&xs)[U], int v0, Valid valid, float sc, float &m, float &s, float &av,
+                                          int &ai) {
+    float bm = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!valid(u)) xs[u] = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+        bm = fmaxf(fmaxf(bm, fmaxf(xs[u].x, xs[u].y)), fmaxf(xs[u].z, xs[u].w));
+    }
+    const float mn = fmaxf(m, bm * sc);
+    if (mn != kNegInf) {
+        const float nm = -mn;
+        float add = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            add += fast_exp2(__builtin_fmaf(xs[u].x, sc, nm)) + fast_exp2(__builtin_fmaf(xs[u].y, sc, nm)) +
+                   fast_exp2(__builtin_fmaf(xs[u].z, sc, nm)) + fast_exp2(__builtin_fmaf(xs[u].w, sc, nm));
+        s = s * fast_exp2(m - mn) + add;
+        m = mn;
+    }
+    if constexpr (ARGMAX) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float xv = f4get(xs[u], jj);
+                if (xv > av) {
+                    av = xv;
+                    ai = v0 + 256 * u + jj;
+                }
+            }
+    }
+}
+
 // Pass p, one wave per (request, row slot q, vocabulary segment), four
 // requests to a workgroup.  First the request's previous D positions are
 // decided, in order, from the segment statistics pass p - 1 wrote; a request
@@ -407,39 +446,14 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     #pragma unroll
                 for (int u = 0; u < U; ++u) xs[u] = r4[min(qb + lane + 64 * u, q_hi - 1)];
             };
+            // sampled rows keep no argmax (only greedy decisions use it); the
+            // request, and so the branch, is uniform across the wave
             auto consume = [&](float4(&xs)[U], int qb) __device__ {
-                float bm = kNegInf;
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const bool in = qb + lane + 64 * u < q_hi;
-                    xs[u].x = in ? xs[u].x * sc : kNegInf;
-                    xs[u].y = in ? xs[u].y * sc : kNegInf;
-                    xs[u].z = in ? xs[u].z * sc : kNegInf;
-                    xs[u].w = in ? xs[u].w * sc : kNegInf;
-                    bm = fmaxf(fmaxf(bm, fmaxf(xs[u].x, xs[u].y)), fmaxf(xs[u].z, xs[u].w));
-                }
-                const float mn = fmaxf(m, bm);
-                if (mn != kNegInf) {
-                    float add = 0.f;
-    #pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        add += fast_exp2(xs[u].x - mn) + fast_exp2(xs[u].y - mn) + fast_exp2(xs[u].z - mn) +
-                               fast_exp2(xs[u].w - mn);
-                    s = s * fast_exp2(m - mn) + add;
-                    m = mn;
-                }
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int v = 4 * (qb + lane + 64 * u);
-    #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float xv = f4get(xs[u], jj);
-                        if (xv > av) {
-                            av = xv;
-                            ai = v + jj;
-                        }
-                    }
-                }
+                auto valid = [&](int u) { return qb + lane + 64 * u < q_hi; };
+                if (sampled)
+                    row_batch<false>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
+                else
+                    row_batch<true>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
             };
             // The loop body is straight-line, so that every consume sees the
             // same loads in flight on every path into it; it runs while the
@@ -469,45 +483,24 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             const float4 *r4 = reinterpret_cast<const float4 *>(trow);
             const int q_hi = v_hi >> 2;
             constexpr int U = 8;
-            for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
-                float4 xs[U];
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int q = q0 + 64 * u;
-                    xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-                }
-                float bm = kNegInf;
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    xs[u].x *= sc;
-                    xs[u].y *= sc;
-                    xs[u].z *= sc;
-                    xs[u].w *= sc;
-                    bm = fmaxf(fmaxf(bm, fmaxf(xs[u].x, xs[u].y)), fmaxf(xs[u].z, xs[u].w));
-                }
-                const float mn = fmaxf(m, bm);
-                if (mn != kNegInf) {
-                    float add = 0.f;
-    #pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        add += fast_exp2(xs[u].x - mn) + fast_exp2(xs[u].y - mn) + fast_exp2(xs[u].z - mn) +
-                               fast_exp2(xs[u].w - mn);
-                    s = s * fast_exp2(m - mn) + add;
-                    m = mn;
-                }
-    #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int v = 4 * (q0 + 64 * u);
-    #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float xv = f4get(xs[u], jj);
-                        if (xv > av) {
-                            av = xv;
-                            ai = v + jj;
-                        }
+            // one loop for each kind of row (the request, and so the kind, is
+            // uniform across the wave): each keeps only its own registers
+            auto walk = [&](auto argmax) __device__ {
+                constexpr bool AM = decltype(argmax)::value;
+                for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
+                    float4 xs[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int q = q0 + 64 * u;
+                        xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
                     }
+                    row_batch<AM>(xs, 4 * q0, [](int) { return true; }, sc, m, s, av, ai);  // masked at the load
                 }
-            }
+            };
+            if (sampled)
+                walk(std::integral_constant<bool, false>{});
+            else
+                walk(std::integral_constant<bool, true>{});
         }
     } else {
         for (int v = v_lo + lane; v < v_hi; v += 64) {
