@@ -336,58 +336,76 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     const int lane = threadIdx.x & 63;
     if (b >= p.B) return;
     const bool writer = sg == 0 && q == 0;
-    // every load the decisions need, issued together and unconditionally
-    // (clamped indices; what a case does not use is masked after): lane half
-    // h holds the segment statistics of the previous pass's row slot h, read
-    // whatever the request's state.  The first pass reads buffers it ignores.
-    const int hq = min(lane >> 5, D - 1), c = min(lane & 31, p.nseg_in - 1);
-    const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
-    const int mode_ld = p.mode[b], off_ld = p.off[b];
-    const int act_raw = p.act_in[b];
-    const float T = p.temperature[b];
-    const int L = p.ell[b];
-    float mm = p.pm_in[o_in], s2 = p.ps_in[o_in], v2 = p.pv_in[o_in];
-    int i2 = p.pi_in[o_in];
+    int mode, offb, act, L;
+    float T;
+    float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
+    int i2 = 0x7fffffff;
     float tx2[D], qk[D];
     int xk[D];
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-        const int k = min(max(j0 - D + u, 1), p.gamma);  // position decided from slot u (clamped)
-        tx2[u] = p.tx_in[size_t(u) * p.B + b];
-        xk[u] = p.x[size_t(b) * p.gamma + k - 1];
-        qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"v"(mode_ld), "v"(off_ld), "v"(act_raw), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
-    const int act = j0 > 1 ? act_raw : 1;
-    int mode = mode_ld, offb = off_ld;
-    if (p.prep) {  // uniform: the first pass of a small batch
-        int part = 0;
-        if (!p.row_offsets)
-            for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
-        const int o_cmp = wave_isum(part);
-        const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
-        mode = f == 0 ? kModeDone : -1;
-        if (writer) {
-            if (lane == 0) {
-                p.off[b] = offb;
-                p.mode[b] = mode;
-                p.req_flags[b] = f;
-                if (b == p.B - 1) p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L, 0), p.gamma);
+    if constexpr (PIPE) {
+        // the first pass decides nothing: it needs the request's temperature
+        // and length and, for a small batch, does its input checks (the row
+        // offset is a wave sum over ell, read in the same round)
+        T = p.temperature[b];
+        L = p.ell[b];
+        act = 1;
+        if (p.prep) {  // uniform
+            int part = 0;
+            if (!p.row_offsets)
+                for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
+            const int o_cmp = wave_isum(part);
+            const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
+            mode = f == 0 ? kModeDone : -1;
+            if (writer) {
+                if (lane == 0) {
+                    p.off[b] = offb;
+                    p.mode[b] = mode;
+                    p.req_flags[b] = f;
+                    if (b == p.B - 1)
+                        p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L, 0), p.gamma);
+                }
+                output_defaults(b, p.gamma, lane, 64, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
             }
-            output_defaults(b, p.gamma, lane, 64, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
+            if (blockIdx.x == 0 && threadIdx.x == 0) {  // the draw-list counters the later passes bump
+                p.status[1] = 0;
+                p.status[2] = 0;
+                p.status[3] = 0;
+            }
+        } else {
+            mode = p.mode[b];
+            offb = p.off[b];
         }
-        if (blockIdx.x == 0 && threadIdx.x == 0) {  // the draw-list counters the later passes bump
-            p.status[1] = 0;
-            p.status[2] = 0;
-            p.status[3] = 0;
+    } else {
+        // every load the decisions need, issued together and unconditionally
+        // (clamped indices; what a case does not use is masked after): lane
+        // half h holds the segment statistics of the previous pass's row slot
+        // h, read whatever the request's state
+        const int hq = min(lane >> 5, D - 1), c = min(lane & 31, p.nseg_in - 1);
+        const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
+        mode = p.mode[b];
+        offb = p.off[b];
+        act = p.act_in[b];
+        T = p.temperature[b];
+        L = p.ell[b];
+        mm = p.pm_in[o_in];
+        s2 = p.ps_in[o_in];
+        v2 = p.pv_in[o_in];
+        i2 = p.pi_in[o_in];
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int k = min(max(j0 - D + u, 1), p.gamma);  // position decided from slot u (clamped)
+            tx2[u] = p.tx_in[size_t(u) * p.B + b];
+            xk[u] = p.x[size_t(b) * p.gamma + k - 1];
+            qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
         }
-    }
-    if (!((lane >> 5) < D && (lane & 31) < p.nseg_in)) {
-        mm = kNegInf;
-        s2 = 0.f;
-        v2 = kNegInf;
-        i2 = 0x7fffffff;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"v"(mode), "v"(offb), "v"(act), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
+        if (!((lane >> 5) < D && (lane & 31) < p.nseg_in)) {
+            mm = kNegInf;
+            s2 = 0.f;
+            v2 = kNegInf;
+            i2 = 0x7fffffff;
+        }
     }
     if (mode < 0 || act == 0) {
         if (writer && lane == 0) p.act_out[b] = 0;
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     }
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    if (j0 > 1) {
+    if (!PIPE && j0 > 1) {
         bfly_steps<0, 5>([&](auto st) {  // within each lane half
             constexpr int S = decltype(st)::value;
             const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
