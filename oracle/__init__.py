@@ -44,6 +44,12 @@ def _load():
                                ctypes.c_uint64, ctypes.c_uint64,
                                _i32p, _i32p, _f64p, _f64p, _f64p, _f64p]
     lib.orc_verify.restype = ctypes.c_int
+    lib.orc_confidence.argtypes = [_f32p, _f32p, _f32p, _i32p, _i32p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
+    lib.orc_confidence.restype = ctypes.c_int
+    lib.orc_acceptance.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p]
+    lib.orc_acceptance.restype = ctypes.c_int
     lib.orc_schedule.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _f64p, ctypes.c_int,
                                  _i32p, _f64p, _f64p, _i32p]
     lib.orc_schedule.restype = ctypes.c_int
@@ -147,6 +153,55 @@ def verify(target, ell, U, W1, W2, anchor, x, temperature, seed, round_id,
         raise ValueError("orc_verify: bad arguments")
     return {"n": n, "tokens": tokens, "diag": diag, "resid": resid,
             "accept_margin": am, "pick_margin": pm}
+
+
+def confidence(h, w, W1, anchor, x):
+    """Confidence head and prefix survival.  h [B, gamma, d], w [d + r],
+    W1 [V, r], anchor [B], drafts x [B, gamma].  Returns (c, a), both
+    [B, gamma] float64."""
+    lib = _load()
+    h = _f32(h)
+    w = _f32(w)
+    W1 = _f32(W1)
+    anchor = _i32(anchor)
+    x = _i32(x)
+    B, gamma, d = h.shape
+    r = W1.shape[1]
+    assert w.shape == (d + r,) and x.shape == (B, gamma)
+    c = np.zeros((B, gamma), np.float64)
+    a = np.zeros((B, gamma), np.float64)
+    st = lib.orc_confidence(_ptr(h, ctypes.c_float), _ptr(w, ctypes.c_float), _ptr(W1, ctypes.c_float),
+                            _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32), B, gamma, d, r,
+                            _ptr(c, ctypes.c_double), _ptr(a, ctypes.c_double))
+    if st != 0:
+        raise ValueError("orc_confidence: bad arguments")
+    return c, a
+
+
+def acceptance(target, ell, U, W1, W2, anchor, x, temperature, row_offsets=None):
+    """Per-position acceptance probability alpha_k = sum_v min(p_k, q_k) for
+    k <= ell_b over packed target rows [sum(1 + ell), V]; NaN past ell_b.
+    Returns alpha [B, gamma] float64."""
+    lib = _load()
+    target = _f32(target)
+    U = _f32(U)
+    W1 = _f32(W1)
+    W2 = _f32(W2)
+    ell = _i32(ell)
+    anchor = _i32(anchor)
+    x = _i32(x)
+    temperature = _f32(temperature)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    off = None if row_offsets is None else _i32(row_offsets)
+    alpha = np.zeros((B, gamma), np.float64)
+    st = lib.orc_acceptance(_ptr(target, ctypes.c_float), _ptr(off, ctypes.c_int32), _ptr(ell, ctypes.c_int32),
+                            _ptr(U, ctypes.c_float), _ptr(W1, ctypes.c_float), _ptr(W2, ctypes.c_float),
+                            _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32),
+                            _ptr(temperature, ctypes.c_float), B, gamma, V, r, _ptr(alpha, ctypes.c_double))
+    if st != 0:
+        raise ValueError("orc_acceptance: bad arguments")
+    return alpha
 
 
 def schedule(c, sps):

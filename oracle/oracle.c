@@ -48,6 +48,10 @@
  *  - ell_r drafts are verified; ell_r = 0 still emits one token drawn from p_1.
  *  - Scheduler candidates are ordered by (-a, r, j); improvement must be
  *    strict; SPS beyond the table is 0; candidates with a = 0 are dropped.
+ *  - The confidence head's weight vector is [d + r] long, its first d
+ *    entries multiplying h_k and the last r the gathered W1 row, the order
+ *    of the concatenation; there is no bias term.  alpha_k for T = 0 places
+ *    q_k's mass on the greedy draft x_k.
  *
  * parity pins: the Philox block function is pinned to published known-answer
  * vectors and to rocRAND's implementation; the sampling, verification and
@@ -420,6 +424,105 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
         if (resid_mass) resid_mass[b] = (T > 0.0 && rejected) ? S : -1.0;
         if (pick_margin) pick_margin[b] = pmargin;
         free(zq); free(zt); free(mass);
+    }
+    free(row0);
+    return status;
+}
+
+/* ------------------------------------------------------------------ */
+/* Confidence head and exact per-position acceptance                   */
+/* ------------------------------------------------------------------ */
+
+/* [MG] 4.1 (the confidence head): for each request b and position k, with
+ * x_0 = anchor and the drafted prefix x,
+ *   s_k = sum_{i<d} w[i] h[b][k][i] + sum_{i<r} w[d + i] W1[x_{k-1}][i]
+ *         (a bias-free linear layer over the concatenation [h_k, W1[x_{k-1}]]),
+ *   c_k = 1 / (1 + exp(-s_k)),
+ * and ([MG] 4.2, [CE] 04) the prefix survival a_k = c_1 * ... * c_k.
+ * h is [B, gamma, d], w is [d + r]; outputs are [B, gamma]. */
+int orc_confidence(const float *h, const float *w, const float *W1,
+                   const int32_t *anchor, const int32_t *x,
+                   int B, int gamma, int d, int r, double *c_out, double *a_out)
+{
+    if (B < 0 || gamma < 1 || d < 0 || r < 1) return ORC_ERR_ARG;
+    if (!w || !W1 || !anchor || !x || !c_out) return ORC_ERR_ARG;
+    if (d > 0 && !h) return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b) {
+        double a = 1.0;
+        for (int k = 1; k <= gamma; ++k) {
+            int prev = (k == 1) ? anchor[b] : x[(size_t)b * (size_t)gamma + (size_t)(k - 2)];
+            const float *hk = h ? h + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)d : NULL;
+            const float *e = W1 + (size_t)prev * (size_t)r;
+            double s = 0.0;
+            for (int i = 0; i < d; ++i)
+                s += (double)w[i] * (double)hk[i];
+            for (int i = 0; i < r; ++i)
+                s += (double)w[d + i] * (double)e[i];
+            double c = 1.0 / (1.0 + exp(-s));
+            a *= c;
+            size_t o = (size_t)b * (size_t)gamma + (size_t)(k - 1);
+            c_out[o] = c;
+            if (a_out) a_out[o] = a;
+        }
+    }
+    return ORC_OK;
+}
+
+/* [MG] 4.1 and [CE] 05: the probability that the draft at position k passes
+ * the rejection test, before x_k is drawn, is
+ *   alpha_k = sum_v min(p_k(v), q_k(v)) = 1 - TV(p_k, q_k),
+ * with p_k = softmax(t_k / T) and q_k = softmax((U_k + W1[x_{k-1}] W2^T) / T)
+ * on the drafted prefix (x_0 = anchor).  T = 0: both are one-hot, q_k at the
+ * greedy draft x_k and p_k at the lowest-index argmax of t_k, so alpha_k is
+ * 1 when they agree and 0 otherwise.  Computed for k = 1..ell_b (the rows
+ * the target produced, packed as in orc_verify); NaN for k > ell_b. */
+int orc_acceptance(const float *target, const int32_t *off, const int32_t *ell,
+                   const float *U, const float *W1, const float *W2,
+                   const int32_t *anchor, const int32_t *x, const float *temperature,
+                   int B, int gamma, int V, int r, double *alpha_out)
+{
+    if (B < 0 || gamma < 1 || V < 1 || r < 1) return ORC_ERR_ARG;
+    if (!target || !ell || !U || !W1 || !W2 || !anchor || !x || !temperature || !alpha_out)
+        return ORC_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (ell[b] < 0 || ell[b] > gamma) return ORC_ERR_ARG;
+    int64_t *row0 = (int64_t *)malloc((size_t)(B > 0 ? B : 1) * sizeof(int64_t));
+    if (!row0) return ORC_ERR_ARG;
+    int64_t acc = 0;
+    for (int b = 0; b < B; ++b) {
+        row0[b] = off ? (int64_t)off[b] : acc;
+        acc += 1 + ell[b];
+    }
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        double *zq = (double *)malloc((size_t)V * sizeof(double));
+        double *zt = (double *)malloc((size_t)V * sizeof(double));
+        if (!zq || !zt) { status = ORC_ERR_ARG; free(zq); free(zt); continue; }
+        double T = (double)temperature[b];
+        const int32_t *xb = x + (size_t)b * (size_t)gamma;
+        for (int k = 1; k <= gamma; ++k) {
+            double alpha = NAN;
+            if (k <= ell[b]) {
+                const float *tk = target + (size_t)(row0[b] + k - 1) * (size_t)V;
+                if (T > 0.0) {
+                    for (int v = 0; v < V; ++v) zt[v] = (double)tk[v] / T;
+                    double lse_t = orc_logsumexp(zt, V);
+                    int prev = (k == 1) ? anchor[b] : xb[k - 2];
+                    const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
+                    orc_logits(Uk, W1, W2, prev, T, V, r, zq);
+                    double lse_q = orc_logsumexp(zq, V);
+                    alpha = 0.0;
+                    for (int v = 0; v < V; ++v)
+                        alpha += fmin(exp(zt[v] - lse_t), exp(zq[v] - lse_q));
+                } else {
+                    for (int v = 0; v < V; ++v) zt[v] = (double)tk[v];
+                    alpha = (orc_argmax(zt, V, NULL) == xb[k - 1]) ? 1.0 : 0.0;
+                }
+            }
+            alpha_out[(size_t)b * (size_t)gamma + (size_t)(k - 1)] = alpha;
+        }
+        free(zq); free(zt);
     }
     free(row0);
     return status;
