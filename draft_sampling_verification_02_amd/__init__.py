@@ -67,6 +67,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_draft_sample_confidence": ([_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                            _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
+                                            _c_void_p, _c_void_p, _c_int,
+                                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                            _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_verify_workspace_size": ([_c_int] * 4, _c_size),
         "dspark_verify": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -75,6 +80,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_verify_check": ([_c_void_p, _c_void_p], _c_int),
+        "dspark_acceptance_workspace_size": ([_c_int] * 4, _c_size),
+        "dspark_acceptance": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _c_int, _c_int, _c_int, _c_int,
+                               _c_void_p, _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_schedule": ([_f64p, _c_int, _c_int, _f64p, _c_int, _i32p, _f64p, _f64p, _i32p], _c_int),
         "dspark_debug_random_words": ([_c_u64, _c_u64, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_void_p, _c_void_p], _c_int),
@@ -171,29 +182,42 @@ def _workspace(nbytes, device, workspace):
     return workspace
 
 
-def dspark_draft_sample(U, W1, W2, anchor, temperature, seed: int, round_id: int, *,
-                        margin: bool = False, out: dict | None = None, workspace=None, stream=None) -> dict:
-    """Draft half of a round.  U [B, gamma, V] float32, W1/W2 [V, r] bf16 or
-    float32, anchor [B] int32, temperature [B] float32 -- all on one HIP device.
-    Returns {"x", "lse", "qx"[, "margin"], "workspace"}; pass ``out`` (a
-    previous result) to reuse its buffers."""
+def _draft_outputs(B, gamma, dev, margin, conf, out):
     torch = _torch()
-    lib = load_library()
-    dev = U.device
-    B, gamma, V = U.shape
-    r = W1.shape[1]
-    _need(U, "U", torch.float32, (B, gamma, V), dev)
-    wdt = _weights(W1, W2, dev)
-    if W1.shape[0] != V:
-        raise ValueError("W1/W2: first dimension must be V")
-    _need(anchor, "anchor", torch.int32, (B,), dev)
-    _need(temperature, "temperature", torch.float32, (B,), dev)
     if out is None:
         out = {"x": torch.empty((B, gamma), dtype=torch.int32, device=dev),
                "lse": torch.empty((B, gamma), dtype=torch.float32, device=dev),
                "qx": torch.empty((B, gamma), dtype=torch.float32, device=dev)}
         if margin:
             out["margin"] = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        if conf:
+            out["conf"] = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+            out["survival"] = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    return out
+
+
+def _draft_inputs(U, W1, W2, anchor, temperature):
+    torch = _torch()
+    dev = U.device
+    B, gamma, V = U.shape
+    _need(U, "U", torch.float32, (B, gamma, V), dev)
+    wdt = _weights(W1, W2, dev)
+    if W1.shape[0] != V:
+        raise ValueError("W1/W2: first dimension must be V")
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    return dev, B, gamma, V, W1.shape[1], wdt
+
+
+def dspark_draft_sample(U, W1, W2, anchor, temperature, seed: int, round_id: int, *,
+                        margin: bool = False, out: dict | None = None, workspace=None, stream=None) -> dict:
+    """Draft half of a round.  U [B, gamma, V] float32, W1/W2 [V, r] bf16 or
+    float32, anchor [B] int32, temperature [B] float32 -- all on one HIP device.
+    Returns {"x", "lse", "qx"[, "margin"], "workspace"}; pass ``out`` (a
+    previous result) to reuse its buffers."""
+    lib = load_library()
+    dev, B, gamma, V, r, wdt = _draft_inputs(U, W1, W2, anchor, temperature)
+    out = _draft_outputs(B, gamma, dev, margin, False, out)
     nbytes = lib.dspark_draft_workspace_size(B, gamma, V, r)
     if nbytes == 0:
         raise DSparkError(DSPARK_ERR_ARG, "dspark_draft_workspace_size")
@@ -204,6 +228,36 @@ def dspark_draft_sample(U, W1, W2, anchor, temperature, seed: int, round_id: int
                                  _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")),
                                  _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st, "dspark_draft_sample")
+    return out
+
+
+def dspark_draft_sample_confidence(U, W1, W2, anchor, temperature, hidden, conf_w, seed: int, round_id: int, *,
+                                   margin: bool = False, out: dict | None = None, workspace=None,
+                                   stream=None) -> dict:
+    """dspark_draft_sample plus the confidence head c_k = sigmoid(conf_w .
+    [h_k, W1[x_{k-1}]]) and the survival products a_k = c_1...c_k.  hidden
+    [B, gamma, d] float32 (d may be 0), conf_w [d + r] float32.  Returns the
+    draft outputs plus {"conf", "survival"}."""
+    torch = _torch()
+    lib = load_library()
+    dev, B, gamma, V, r, wdt = _draft_inputs(U, W1, W2, anchor, temperature)
+    if hidden.dim() != 3 or tuple(hidden.shape[:2]) != (B, gamma):
+        raise ValueError("hidden: [B, gamma, d]")
+    d = hidden.shape[2]
+    _need(hidden, "hidden", torch.float32, (B, gamma, d), dev)
+    _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    out = _draft_outputs(B, gamma, dev, margin, True, out)
+    nbytes = lib.dspark_draft_workspace_size(B, gamma, V, r)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_draft_workspace_size")
+    ws = _workspace(nbytes, dev, workspace if workspace is not None else out.get("workspace"))
+    out["workspace"] = ws
+    st = lib.dspark_draft_sample_confidence(
+        _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(temperature), B, gamma, V, r, int(seed),
+        int(round_id), _ptr(hidden) if d > 0 else None, _ptr(conf_w), d,
+        _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")),
+        _ptr(out["conf"]), _ptr(out["survival"]), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_draft_sample_confidence")
     return out
 
 
@@ -252,6 +306,47 @@ def dspark_verify(target, ell, U, W1, W2, anchor, x, lse_q, qx, temperature, see
                            _ptr(out.get("diag")), _ptr(out.get("resid")),
                            _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st, "dspark_verify")
+    return out
+
+
+def dspark_acceptance_workspace_size(B: int, gamma: int, V: int, r: int) -> int:
+    return load_library().dspark_acceptance_workspace_size(B, gamma, V, r)
+
+
+def dspark_acceptance(target, ell, U, W1, W2, anchor, x, lse_q, temperature, *, row_offsets=None,
+                      out=None, workspace=None, stream=None):
+    """Per-position acceptance probability alpha_k = sum_v min(p_k, q_k) of
+    every verified position (NaN past ell).  Arguments as for dspark_verify.
+    Returns alpha [B, gamma] float32 (``out`` if given)."""
+    torch = _torch()
+    lib = load_library()
+    dev = U.device
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    _need(U, "U", torch.float32, (B, gamma, V), dev)
+    wdt = _weights(W1, W2, dev)
+    if target.dim() != 2 or target.shape[1] != V:
+        raise ValueError("target: [rows, V]")
+    _need(target, "target", torch.float32, None, dev)
+    _need(ell, "ell", torch.int32, (B,), dev)
+    if row_offsets is not None:
+        _need(row_offsets, "row_offsets", torch.int32, (B + 1,), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    _need(x, "x", torch.int32, (B, gamma), dev)
+    _need(lse_q, "lse_q", torch.float32, (B, gamma), dev)
+    _need(temperature, "temperature", torch.float32, (B,), dev)
+    if out is None:
+        out = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, gamma), dev)
+    nbytes = lib.dspark_acceptance_workspace_size(B, gamma, V, r)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_acceptance_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.dspark_acceptance(_ptr(target), target.shape[0], _ptr(ell), _ptr(row_offsets),
+                               _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q),
+                               _ptr(temperature), B, gamma, V, r, _ptr(out), _ptr(ws), ws.numel(),
+                               _stream_ptr(stream))
+    _check(st, "dspark_acceptance")
     return out
 
 

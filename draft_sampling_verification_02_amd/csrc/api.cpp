@@ -104,6 +104,13 @@ size_t draft_bytes(int B, int V) {
     return bytes;
 }
 
+size_t accept_bytes(int B, int gamma, int V) {
+    const AcceptPlan p = accept_plan(B, gamma, V);
+    size_t bytes = 0;
+    accept_carve(nullptr, B, gamma, p, &bytes);
+    return bytes;
+}
+
 size_t verify_bytes(int B, int gamma, int V) {
     const VerifyPlan p = verify_plan(B, gamma, V);
     size_t bytes = 0;
@@ -134,10 +141,15 @@ size_t dspark_draft_workspace_size(int B, int gamma, int V, int r) {
     return draft_bytes(B, V);
 }
 
-int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
-                        const float *temperature, int B, int gamma, int V, int r, uint64_t seed,
-                        uint64_t round_id, int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int draft_common(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                 const float *temperature, int B, int gamma, int V, int r, uint64_t seed, uint64_t round_id,
+                 const float *hidden, const float *conf_w, int d, int32_t *x_out, float *lse_out, float *qx_out,
+                 float *margin_out, float *conf_out, float *survival_out, void *workspace, size_t workspace_bytes,
+                 void *stream) {
     if (!U || !W1 || !W2 || !anchor || !temperature || !x_out || !lse_out || !qx_out) return DSPARK_ERR_ARG;
     if (!sizes_ok(B, gamma, V, r)) return DSPARK_ERR_ARG;
     if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
@@ -166,8 +178,38 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
     a.lse_out = lse_out;
     a.qx_out = qx_out;
     a.margin_out = margin_out;
+    a.hidden = hidden;
+    a.conf_w = conf_w;
+    a.d = d;
+    a.conf_out = conf_out;
+    a.surv_out = survival_out;
     const hipError_t e = launch_draft(a, plan, w, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                        const float *temperature, int B, int gamma, int V, int r, uint64_t seed,
+                        uint64_t round_id, int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    return draft_common(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, seed, round_id, nullptr, nullptr, 0,
+                        x_out, lse_out, qx_out, margin_out, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W2, int wdtype,
+                                   const int32_t *anchor, const float *temperature, int B, int gamma, int V, int r,
+                                   uint64_t seed, uint64_t round_id, const float *hidden, const float *conf_w, int d,
+                                   int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                                   float *conf_out, float *survival_out, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (d < 0 || d > DSPARK_MAX_HIDDEN || (d > 0 && !hidden) || !conf_w || !conf_out || !survival_out)
+        return DSPARK_ERR_ARG;
+    return draft_common(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, seed, round_id, hidden, conf_w, d,
+                        x_out, lse_out, qx_out, margin_out, conf_out, survival_out, workspace, workspace_bytes,
+                        stream);
 }
 
 size_t dspark_verify_workspace_size(int B, int gamma, int V, int r) {
@@ -220,6 +262,48 @@ int dspark_verify(const float *target, int n_target_rows, const int32_t *ell, co
     a.diag_out = diag_out;
     a.resid_out = resid_out;
     const hipError_t e = launch_verify(a, plan, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+size_t dspark_acceptance_workspace_size(int B, int gamma, int V, int r) {
+    if (!sizes_ok(B, gamma, V, r)) return 0;
+    return accept_bytes(B, gamma, V);
+}
+
+int dspark_acceptance(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                      const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                      const int32_t *x, const float *lse_q, const float *temperature, int B, int gamma, int V,
+                      int r, float *alpha_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!target || !ell || !U || !W1 || !W2 || !anchor || !x || !lse_q || !temperature || !alpha_out)
+        return DSPARK_ERR_ARG;
+    if (!sizes_ok(B, gamma, V, r) || n_target_rows < 1) return DSPARK_ERR_ARG;
+    if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
+    if (!rank_supported(wdtype, r)) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(W1) || !aligned16(W2)) return DSPARK_ERR_ARG;
+    const AcceptPlan plan = accept_plan(B, gamma, V);
+    size_t need = 0;
+    accept_carve(nullptr, B, gamma, plan, &need);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+    const AcceptWork w = accept_carve(workspace, B, gamma, plan, nullptr);
+    AcceptArgs a{};
+    a.target = target;
+    a.n_target_rows = n_target_rows;
+    a.ell = ell;
+    a.row_offsets = row_offsets;
+    a.U = U;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.wdtype = wdtype;
+    a.anchor = anchor;
+    a.x = x;
+    a.lse_q = lse_q;
+    a.temperature = temperature;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.r = r;
+    a.alpha_out = alpha_out;
+    const hipError_t e = launch_accept(a, plan, w, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
 }
 

@@ -203,12 +203,66 @@ struct ReduceParams {
     const int32_t *pi;
     int32_t *x_out;
     float *lse_out, *qx_out, *margin_out;
+    // confidence head (used by the CONF instances only)
+    const float *hidden;  // h_k of request b at hidden + b * h_stride
+    size_t h_stride;
+    const float *conf_w;  // [d + r]: the h_k part, then the W1[x_{k-1}] part
+    int d, hvec;          // hvec: h rows and conf_w allow aligned 16-byte loads
+    float *conf_out, *surv_out;
 };
+
+// w_h . h_k, this lane's share (the wave sums it): lane l takes entries
+// l, l + 64, ... (as float4 pieces when hvec); every load is issued before
+// the first product for d up to 1024 (float4) or 512 (float).
+__device__ __forceinline__ float conf_hidden_part(const ReduceParams &p, int b, int lane) {
+    const float *hk = p.hidden + size_t(b) * p.h_stride;
+    float acc = 0.f;
+    if (p.hvec) {
+        const int n4 = p.d >> 2;
+        const float4 *h4 = reinterpret_cast<const float4 *>(hk);
+        const float4 *w4 = reinterpret_cast<const float4 *>(p.conf_w);
+        for (int i0 = 0; i0 < n4; i0 += 64 * 4) {
+            float4 hv[4], wv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = min(i0 + lane + 64 * u, n4 - 1);  // clamped, masked below
+                hv[u] = h4[i];
+                wv[u] = w4[i];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float t = hv[u].x * wv[u].x;
+                t = __builtin_fmaf(hv[u].y, wv[u].y, t);
+                t = __builtin_fmaf(hv[u].z, wv[u].z, t);
+                t = __builtin_fmaf(hv[u].w, wv[u].w, t);
+                acc += (i0 + lane + 64 * u < n4) ? t : 0.f;
+            }
+        }
+    } else {
+        for (int i0 = 0; i0 < p.d; i0 += 64 * 8) {
+            float hv[8], wv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = min(i0 + lane + 64 * u, p.d - 1);
+                hv[u] = hk[i];
+                wv[u] = p.conf_w[i];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += (i0 + lane + 64 * u < p.d) ? hv[u] * wv[u] : 0.f;
+        }
+    }
+    return acc;
+}
 
 // One wave per request.  The loads that do not depend on the winning tile
 // (the W1 row, the chunk partials) go out together; the winning tile's W2
 // rows and U entries go out together once it is known.
-template <typename WT, int R>
+// CONF instances also evaluate the confidence head of position k,
+//   c_k = sigmoid(w . [h_k, W1[x_{k-1}]])  (bias-free linear layer),
+// and the prefix survival a_k = a_{k-1} c_k (a_{k-1} written by the previous
+// position's launch): the gathered W1 row is already at hand here, and the
+// h_k row streams in beside the partials.
+template <typename WT, int R, bool CONF>
 __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -237,10 +291,28 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     load_batch(0);
     __builtin_amdgcn_sched_barrier(0);  // keep the batch ahead of the dependent W1 fetch
     int prev = p.xprev[size_t(b) * p.xprev_stride];
-    prev = min(max(prev, 0), p.V - 1);
     const float T = p.temperature[b];
+    float conf_s = 0.f, a_prev = 1.f;
+    if constexpr (CONF) {
+        if (p.k > 1) a_prev = p.surv_out[size_t(b) * p.gamma + p.k - 2];
+        if (p.d > 0) conf_s = conf_hidden_part(p, b, lane);
+    }
+    prev = min(max(prev, 0), p.V - 1);
     RowHalf<WT, R> w1;
     w1.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    if constexpr (CONF) {
+        // w_e . W1[x_{k-1}], entries lane, lane + 64, ...
+        const WT *e = static_cast<const WT *>(p.W1) + size_t(prev) * R;
+#pragma unroll
+        for (int i = lane; i < R; i += 64) {
+            float ev;
+            if constexpr (sizeof(WT) == 2)
+                ev = __uint_as_float(uint32_t(e[i]) << 16);
+            else
+                ev = e[i];
+            conf_s = __builtin_fmaf(p.conf_w[p.d + i], ev, conf_s);
+        }
+    }
     float m = kNegInf, s = 0.f, best = kNegInf, second = kNegInf;
     int bt = 0x7fffffff;
     for (int c0 = 0; c0 < p.nchunk; c0 += 64 * PC) {
@@ -284,9 +356,15 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     });
     const int x = min(max(xi, tile * kTile), p.V - 1);
     const float z2x = __shfl(z2, x - tile * kTile);
+    if constexpr (CONF) bfly_steps<0, 6>([&](auto st) { conf_s += bfly<decltype(st)::value>(conf_s); });
     if (lane == 0) {
         const size_t o = size_t(b) * p.gamma + (p.k - 1);
         p.x_out[o] = x;
+        if constexpr (CONF) {
+            const float c = 1.0f / (1.0f + __expf(-conf_s));
+            p.conf_out[o] = c;
+            p.surv_out[o] = a_prev * c;
+        }
         const float gap = fminf(best - second, s1 - s2);
         if (sampled) {
             const float lse2 = m + fast_log2(s);
@@ -512,6 +590,8 @@ template <typename WT, int R>
 hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork &w, hipStream_t s) {
     const bool track2 = a.margin_out != nullptr;
     const bool vec = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
+    const bool hvec = a.d % 4 == 0 && reinterpret_cast<uintptr_t>(a.hidden) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(a.conf_w) % 16 == 0;
     for (int k = 1; k <= a.gamma; ++k) {
         StepParams sp{};
         sp.U = a.U + size_t(k - 1) * a.V;
@@ -583,7 +663,18 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         rp.qx_out = a.qx_out;
         rp.margin_out = a.margin_out;
         t = prof_begin("draft_reduce", s);
-        hipLaunchKernelGGL((draft_reduce_kernel<WT, R>), dim3((a.B + 3) / 4), dim3(256), 0, s, rp);
+        if (a.conf_out) {
+            rp.hidden = a.hidden + size_t(k - 1) * a.d;
+            rp.h_stride = size_t(a.gamma) * a.d;
+            rp.conf_w = a.conf_w;
+            rp.d = a.d;
+            rp.hvec = hvec;
+            rp.conf_out = a.conf_out;
+            rp.surv_out = a.surv_out;
+            hipLaunchKernelGGL((draft_reduce_kernel<WT, R, true>), dim3((a.B + 3) / 4), dim3(256), 0, s, rp);
+        } else {
+            hipLaunchKernelGGL((draft_reduce_kernel<WT, R, false>), dim3((a.B + 3) / 4), dim3(256), 0, s, rp);
+        }
         prof_end(t, s);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

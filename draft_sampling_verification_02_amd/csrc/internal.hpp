@@ -63,6 +63,11 @@ struct DraftArgs {
     uint32_t key0, key1, round32;
     int32_t *x_out;
     float *lse_out, *qx_out, *margin_out;
+    // confidence head; conf_out == nullptr: not evaluated
+    const float *hidden;  // [B, gamma, d]
+    const float *conf_w;  // [d + r]
+    int d;
+    float *conf_out, *surv_out;  // [B, gamma] c_k and a_k
 };
 hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork &w, hipStream_t s);
 // The bias product alone: rowmax[b] = max_v W1[idx[b]] . W2[v] (diagnostic).
@@ -121,6 +126,38 @@ struct VerifyArgs {
     float *diag_out, *resid_out;
 };
 hipError_t launch_verify(const VerifyArgs &a, const VerifyPlan &p, const VerifyWork &w, hipStream_t s);
+
+// ---- acceptance probability ------------------------------------------
+
+struct AcceptPlan {
+    int maxent;         // listed rows at most: B * gamma
+    int nseg, seg_len;  // segments of a target row in the row statistics, entries each
+    DraftPlan tile;     // vocabulary walk of the accepted-mass kernel
+};
+AcceptPlan accept_plan(int B, int gamma, int V);
+
+struct AcceptWork {
+    int32_t *count;                        // [4] sampled rows, greedy rows
+    int32_t *ent_rho, *ent_trow, *ent_prev;  // [maxent] listed rows: b * gamma + k - 1, target row, x_{k-1}
+    float *rs_m, *rs_s, *rs_v;             // [maxent, nseg] row statistics per segment
+    int32_t *rs_i;
+    float *mass;                           // [maxent, nchunk] sum of min(p, q) per chunk
+};
+AcceptWork accept_carve(void *ws, int B, int gamma, const AcceptPlan &p, size_t *bytes);
+
+struct AcceptArgs {
+    const float *target;
+    int n_target_rows;
+    const int32_t *ell, *row_offsets;
+    const float *U;
+    const void *W1, *W2;
+    int wdtype;
+    const int32_t *anchor, *x;
+    const float *lse_q, *temperature;
+    int B, gamma, V, r;
+    float *alpha_out;
+};
+hipError_t launch_accept(const AcceptArgs &a, const AcceptPlan &p, const AcceptWork &w, hipStream_t s);
 
 // ---- diagnostics -----------------------------------------------------
 

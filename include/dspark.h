@@ -6,6 +6,8 @@
  *  [MG] "DSpark：DeepSeek 线上跑的投机解码，半自回归 + 置信度调度怎么做到的"
  *       (marsggbo.github.io): 3.2 Sequential Stage -- Markov head
  *       B_k = W2(W1[x_{k-1}]) and the left-to-right sampling loop;
+ *       4.1 Confidence Head -- c_k from [h_k, W1[x_{k-1}]], acceptance
+ *       probability 1 - TV; 4.2 -- survival products;
  *       4.3 Hardware-Aware Prefix Scheduler -- a_{r,j}, B, tau, Theta, greedy
  *       extension in descending a with early stop.
  *  [CE] "DeepSeek DSpark explained" (share.concentrate1.com): section 02 --
@@ -75,6 +77,7 @@ typedef enum dspark_dtype {
 #define DSPARK_MAX_GAMMA 32
 #define DSPARK_MAX_BATCH 65536
 #define DSPARK_MAX_VOCAB 16777215
+#define DSPARK_MAX_HIDDEN 65536 /* d of the confidence head */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int dspark_version(void);
@@ -122,6 +125,34 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
                         uint64_t seed, uint64_t round_id,
                         int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* dspark_draft_sample plus the confidence head of every position ([MG] 4.1
+ * Confidence Head; [MG] 4.2 and [CE] 04 for the survival products): with
+ * x_0 = anchor and the drafts this call samples,
+ *   c_k = 1 / (1 + exp(-(w[0..d) . h_k + w[d..d+r) . W1[x_{k-1}])))
+ * -- a bias-free linear layer over the concatenation [h_k, W1[x_{k-1}]] and
+ * a sigmoid -- and a_k = c_1 * ... * c_k, the estimated probability that
+ * drafts 1..k all survive verification.  The sampling outputs are the same
+ * bits dspark_draft_sample writes for the same inputs.
+ *
+ *   hidden        device [B, gamma, d] float32: h_k of request b at row
+ *                 b * gamma + k - 1 (may be NULL when d = 0)
+ *   conf_w        device [d + r] float32: the head's weights, the h_k part
+ *                 first
+ *   d             0 .. DSPARK_MAX_HIDDEN
+ *   conf_out      device [B, gamma] float32: c_k
+ *   survival_out  device [B, gamma] float32: a_k
+ *   every other argument: as for dspark_draft_sample (same workspace size).
+ * Rows of hidden and conf_w that are 16-byte aligned with d a multiple of 4
+ * are read as float4. */
+int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W2, int wdtype,
+                                   const int32_t *anchor, const float *temperature,
+                                   int B, int gamma, int V, int r,
+                                   uint64_t seed, uint64_t round_id,
+                                   const float *hidden, const float *conf_w, int d,
+                                   int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                                   float *conf_out, float *survival_out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Verify half ([CE] 02, 05; [MG] 1, 4.1)                              */
@@ -180,6 +211,39 @@ int dspark_verify(const float *target, int n_target_rows, const int32_t *ell,
  * the device-side input checks of the last dspark_verify that used
  * `workspace` (DSPARK_ERR_HIP if the copy fails). */
 int dspark_verify_check(const void *workspace, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Per-position acceptance probability ([MG] 4.1; [CE] 05)             */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of device workspace dspark_acceptance needs; 0 for invalid sizes. */
+size_t dspark_acceptance_workspace_size(int B, int gamma, int V, int r);
+
+/* The probability that draft k of request b passes the rejection test, taken
+ * before x_k is drawn -- the confidence head's training label:
+ *   alpha_k = sum_v min(p_k(v), q_k(v)) = 1 - TV(p_k, q_k),
+ * with p_k = softmax(t_k / T_b) and q_k = softmax((U_k + W1[x_{k-1}] W2^T) / T_b)
+ * recomputed from U, W1, W2 and lse_q on the drafted prefix (x_0 = anchor).
+ * T_b = 0: alpha_k = 1 if x_k is the lowest-index argmax of t_k, else 0.
+ * Every verified position k = 1..ell[b] is evaluated, also past the first
+ * rejection (the target rows exist for the whole verified block).
+ *
+ *   target, n_target_rows, ell, row_offsets, U, W1, W2, wdtype, anchor, x,
+ *   lse_q, temperature, B, gamma, V, r: as for dspark_verify (packed target
+ *                 rows; row off_b + k - 1 holds position k)
+ *   alpha_out     device [B, gamma] float32: alpha_k for k <= ell[b], NaN for
+ *                 k > ell[b] and for every position of a request whose ell /
+ *                 row_offsets fail the checks dspark_verify makes
+ *   workspace     device, >= dspark_acceptance_workspace_size bytes
+ * Cost: every verified row is read twice (its logsumexp, then the accepted
+ * mass beside its U_k row and the W2 tiles), so this is a labelling pass, not
+ * a step of the serving round. */
+int dspark_acceptance(const float *target, int n_target_rows, const int32_t *ell,
+                      const int32_t *row_offsets,
+                      const float *U, const void *W1, const void *W2, int wdtype,
+                      const int32_t *anchor, const int32_t *x, const float *lse_q,
+                      const float *temperature, int B, int gamma, int V, int r,
+                      float *alpha_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Host scheduler ([MG] 4.3; [CE] 04)                                  */

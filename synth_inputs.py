@@ -16,6 +16,11 @@ so any request's rows can be regenerated on their own):
   anchor [B]         ~ uniform [0, V)  seed (seed, 4).
   c [B, gamma]       ~ Beta(8, 2)     seed (seed, 5)   (scheduled config).
   temperature [B]    1.0, or 0.0 (greedy) for b % greedy_every == 0.
+  Confidence head (confidence_head_inputs; d defaults to 1024):
+  h[b, k] [d]        ~ N(1, 1)        seed (seed, 6, b, k)
+  w [d + r]          first d ~ N(1.4 / d, 0.5 / d), seed (seed, 7); last r
+                     ~ N(0, 0.5 / (r w_std^2)), seed (seed, 8) -- so the head's
+                     logit is about N(1.4, 1.5) and c_k averages about 0.7.
 The target rows are packed per request: rows k = 1..ell_b + 1 of request b
 follow each other, request after request.
 """
@@ -28,7 +33,9 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "Round", "make_round", "bf16_round", "bf16_bits_to_f32",
-           "sps_table_toy", "pack_offsets"]
+           "sps_table_toy", "pack_offsets", "confidence_head_inputs", "DEFAULT_HIDDEN"]
+
+DEFAULT_HIDDEN = 1024
 
 
 @dataclasses.dataclass(frozen=True)
@@ -208,3 +215,18 @@ def make_round(cfg: Config, requests=None) -> Round:
     return Round(cfg=cfg, W1_bits=W1_bits, W2_bits=W2_bits, W1=W1, W2=W2, U=U,
                  anchor=anchor_all[reqs], temperature=temp_all[reqs], c=c, seed=cfg.seed,
                  requests=reqs)
+
+
+def confidence_head_inputs(cfg: Config, d: int = DEFAULT_HIDDEN, requests=None):
+    """(h [B, gamma, d], w [d + r]) float32 for the confidence head of ``cfg``
+    (``requests`` selects request rows, in that order)."""
+    reqs = list(range(cfg.B)) if requests is None else list(requests)
+    h = np.empty((len(reqs), cfg.gamma, d), dtype=np.float32)
+    for i, b in enumerate(reqs):
+        for k in range(1, cfg.gamma + 1):
+            h[i, k - 1] = _normal((cfg.seed, 6, b, k), d, 1.0) + np.float32(1.0)
+    w = np.empty(d + cfg.r, dtype=np.float32)
+    if d > 0:
+        w[:d] = _normal((cfg.seed, 7), d, np.sqrt(0.5 / d)) + np.float32(1.4 / d)
+    w[d:] = _normal((cfg.seed, 8), cfg.r, np.sqrt(0.5 / (cfg.r * cfg.w_std ** 2)))
+    return h, w

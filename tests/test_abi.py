@@ -127,3 +127,54 @@ def test_bias_gemm_argument_errors_need_no_gpu():
     assert call(r=24) == ds.DSPARK_ERR_UNSUPPORTED
     assert call(W1=ctypes.c_void_p(0x1004)) == ds.DSPARK_ERR_ARG
     assert call(ws_bytes=16) == ds.DSPARK_ERR_WORKSPACE
+
+
+def test_confidence_draft_argument_errors_need_no_gpu():
+    lib = ds.load_library()
+
+    def call(**kw):
+        a = dict(U=_FAKE, W1=_FAKE, W2=_FAKE, wdtype=0, anchor=_FAKE, temperature=_FAKE, B=4, gamma=5, V=1000,
+                 r=16, seed=1, round_id=0, hidden=_FAKE, w=_FAKE, d=64, x=_FAKE, lse=_FAKE, qx=_FAKE, margin=None,
+                 conf=_FAKE, surv=_FAKE, ws=_FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.dspark_draft_sample_confidence(
+            a["U"], a["W1"], a["W2"], a["wdtype"], a["anchor"], a["temperature"], a["B"], a["gamma"], a["V"],
+            a["r"], a["seed"], a["round_id"], a["hidden"], a["w"], a["d"], a["x"], a["lse"], a["qx"], a["margin"],
+            a["conf"], a["surv"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(d=-1) == ds.DSPARK_ERR_ARG
+    assert call(d=65537) == ds.DSPARK_ERR_ARG
+    assert call(hidden=None) == ds.DSPARK_ERR_ARG  # d > 0 needs h
+    assert call(w=None) == ds.DSPARK_ERR_ARG
+    assert call(conf=None) == ds.DSPARK_ERR_ARG
+    assert call(surv=None) == ds.DSPARK_ERR_ARG
+    assert call(hidden=None, d=0, U=None) == ds.DSPARK_ERR_ARG  # the draft's own checks still apply
+    assert call(hidden=None, d=0, r=24) == ds.DSPARK_ERR_UNSUPPORTED
+    assert call(ws_bytes=16) == ds.DSPARK_ERR_WORKSPACE
+
+
+def test_acceptance_argument_errors_need_no_gpu():
+    lib = ds.load_library()
+    for (B, g, V, r) in [(1, 4, 1000, 16), (256, 5, 129280, 256), (1024, 5, 129280, 256), (65536, 32, 1000, 16)]:
+        assert ds.dspark_acceptance_workspace_size(B, g, V, r) > 0
+    assert ds.dspark_acceptance_workspace_size(0, 4, 1000, 16) == 0
+
+    def call(**kw):
+        a = dict(target=_FAKE, rows=24, ell=_FAKE, off=None, U=_FAKE, W1=_FAKE, W2=_FAKE, wdtype=0, anchor=_FAKE,
+                 x=_FAKE, lse=_FAKE, temperature=_FAKE, B=4, gamma=5, V=1000, r=16, alpha=_FAKE, ws=_FAKE,
+                 ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.dspark_acceptance(a["target"], a["rows"], a["ell"], a["off"], a["U"], a["W1"], a["W2"],
+                                     a["wdtype"], a["anchor"], a["x"], a["lse"], a["temperature"], a["B"],
+                                     a["gamma"], a["V"], a["r"], a["alpha"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(target=None) == ds.DSPARK_ERR_ARG
+    assert call(alpha=None) == ds.DSPARK_ERR_ARG
+    assert call(lse=None) == ds.DSPARK_ERR_ARG
+    assert call(rows=0) == ds.DSPARK_ERR_ARG
+    assert call(gamma=0) == ds.DSPARK_ERR_ARG
+    assert call(wdtype=2) == ds.DSPARK_ERR_ARG
+    assert call(r=48) == ds.DSPARK_ERR_UNSUPPORTED
+    assert call(W1=ctypes.c_void_p(0x1002)) == ds.DSPARK_ERR_ARG
+    assert call(ws_bytes=100) == ds.DSPARK_ERR_WORKSPACE
+    assert call(ws=None) == ds.DSPARK_ERR_WORKSPACE
