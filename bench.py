@@ -15,7 +15,9 @@ the same workload (which also gates parity: eligible requests must match).
 Secondary figures: the distribution of single-round times over --rounds
 rounds, the bias product alone (the draft step's MFMA tiling without U_k or
 sampling) with W2 warm in the last-level cache and after a 512 MiB flush, the
-host scheduler's time on a 1024-request batch, and the oracle on one thread.
+host scheduler's time on a 1024-request batch, the round with the confidence
+head fused into the draft, the acceptance-probability labelling pass, and the
+oracle on one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -172,6 +174,100 @@ def _oracle_one_thread(rnd, target, ell, seed, gamma, oracle_round, rows=128):
             "sample": f"requests 0..{rows - 1} of the same round: fp64 draft + verify, {dt:.1f}s"}
 
 
+def _profiled(torch, ds, fn, reps):
+    """Per-kernel HIP-event averages (microseconds) of `reps` calls of fn."""
+    torch.cuda.synchronize()
+    ds.dspark_profile_reset()
+    ds.dspark_profile_enable(True)
+    for i in range(reps):
+        fn(i)
+    torch.cuda.synchronize()
+    ds.dspark_profile_collect()
+    ds.dspark_profile_enable(False)
+    return {k: 1e3 * ms / max(1, n) for k, (n, ms) in ds.dspark_profile_read().items()}
+
+
+def _events_ms(torch, fn, reps, base):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(base + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, reps):
+    """The round with the confidence head fused into the draft (d = 1024,
+    synthetic h and w): round time and the draft reduce's time, against the
+    plain round measured the same way."""
+    h, w = S.confidence_head_inputs(cfg)
+    hd = torch.from_numpy(h).cuda()
+    wd = torch.from_numpy(w).cuda()
+    dc = ds.dspark_draft_sample_confidence(dev["U"], dev["W1"], dev["W2"], dev["anchor"], dev["temperature"], hd, wd,
+                                           seed, 0)
+    d0 = ds.dspark_draft_sample(dev["U"], dev["W1"], dev["W2"], dev["anchor"], dev["temperature"], seed, 0)
+    v = ds.dspark_verify(td, ed, dev["U"], dev["W1"], dev["W2"], dev["anchor"], dc["x"], dc["lse"], dc["qx"],
+                         dev["temperature"], seed, 0)
+
+    def step_conf(rid):
+        ds.dspark_draft_sample_confidence(dev["U"], dev["W1"], dev["W2"], dev["anchor"], dev["temperature"], hd, wd,
+                                          seed, rid, out=dc)
+        ds.dspark_verify(td, ed, dev["U"], dev["W1"], dev["W2"], dev["anchor"], dc["x"], dc["lse"], dc["qx"],
+                         dev["temperature"], seed, rid, out=v)
+
+    def step_plain(rid):
+        ds.dspark_draft_sample(dev["U"], dev["W1"], dev["W2"], dev["anchor"], dev["temperature"], seed, rid, out=d0)
+        ds.dspark_verify(td, ed, dev["U"], dev["W1"], dev["W2"], dev["anchor"], d0["x"], d0["lse"], d0["qx"],
+                         dev["temperature"], seed, rid, out=v)
+
+    ms_plain = _events_ms(torch, step_plain, reps, 5000)
+    ms_conf = _events_ms(torch, step_conf, reps, 6000)
+    red_plain = _profiled(torch, ds, lambda i: step_plain(7000 + i), reps)["draft_reduce"]
+    red_conf = _profiled(torch, ds, lambda i: step_conf(8000 + i), reps)["draft_reduce"]
+    from roundkit import np_of
+    c = np_of(dc["conf"])
+    return {"d": h.shape[2], "round_ms": round(ms_conf, 5), "round_ms_without": round(ms_plain, 5),
+            "draft_reduce_us": round(red_conf, 2), "draft_reduce_us_without": round(red_plain, 2),
+            "mean_c": round(float(c.mean()), 4)}
+
+
+def _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, reps):
+    """The acceptance-probability labelling pass over every verified position
+    of the round: time per call and the HBM fractions of its two streaming
+    kernels (algorithmic bytes: the row statistics read every verified target
+    row; the accepted mass reads the sampled rows' target and U_k rows and W2
+    once -- its workgroups of 256 rows each walk W2 again, from the caches)."""
+    import numpy as np
+    from roundkit import np_of
+    alpha = ds.dspark_acceptance(td, ed, dev["U"], dev["W1"], dev["W2"], dev["anchor"], d["x"], d["lse"],
+                                 dev["temperature"])
+
+    def call(i):
+        ds.dspark_acceptance(td, ed, dev["U"], dev["W1"], dev["W2"], dev["anchor"], d["x"], d["lse"],
+                             dev["temperature"], out=alpha)
+
+    for i in range(5):
+        call(i)
+    ms = _events_ms(torch, call, reps, 0)
+    ph = _profiled(torch, ds, call, reps)
+    ell = np_of(ed)
+    sampled = np.asarray(rnd.temperature) > 0
+    rows = int(ell.sum())
+    srows = int(ell[sampled].sum())
+    row = V * 4
+    out = {"call_ms": round(ms, 4), "rows": rows, "sampled_rows": srows,
+           "phases_us": {k: round(v, 2) for k, v in ph.items()}}
+    for name, nbytes in (("accept_rowstats", rows * row), ("accept_mass", 2 * srows * row + V * r * 2)):
+        us = ph.get(name, 0.0)
+        if us > 0:
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[name] = {"bytes": nbytes, "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    a = np_of(alpha)
+    out["mean_alpha_sampled"] = round(float(np.nanmean(a[sampled])), 4)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +361,8 @@ def main():
     round_dist = _round_distribution(torch, step, args.rounds, 3000)
     gemm = _bias_gemm_alone(torch, ds, dev, B, V, r)
     sched = _schedule_time(ds, S)
+    conf = _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps)
+    accept = _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, 20)
 
     drafted = B * gamma
     value = drafted / (ms_step * 1e-3)
@@ -305,7 +403,9 @@ def main():
                       "round_ms": round_dist,
                       "bias_gemm_alone": gemm,
                       "logit_passes": logit,
-                      "schedule": sched},
+                      "schedule": sched,
+                      "confidence_head": conf,
+                      "acceptance": accept},
         "roofline": roofline,
     }
 

@@ -429,9 +429,7 @@ hipError_t launch_accept_typed(const AcceptArgs &a, const AcceptPlan &pl, const 
     {
         AccPrepParams pp{a.ell, a.row_offsets, a.anchor, a.x, a.temperature, a.B, a.gamma, a.V, a.n_target_rows,
                          w.count, w.ent_rho, w.ent_trow, w.ent_prev, a.alpha_out};
-        int t = prof_begin("accept_prep", s);
-        hipLaunchKernelGGL(accept_prep_kernel, dim3(1), dim3(1024), 0, s, pp);
-        prof_end(t, s);
+        launch_kernel("accept_prep", accept_prep_kernel, dim3(1), dim3(1024), s, pp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const bool vec_t = reinterpret_cast<uintptr_t>(a.target) % 16 == 0 && a.V % 4 == 0;
@@ -440,12 +438,10 @@ hipError_t launch_accept_typed(const AcceptArgs &a, const AcceptPlan &pl, const 
         AccRowParams rp{a.target, a.temperature, a.gamma, a.V, pl.nseg, pl.seg_len,
                         w.count, w.ent_rho, w.ent_trow, w.rs_m, w.rs_s, w.rs_v, w.rs_i};
         const dim3 grid(unsigned(size_t(pl.maxent) * pl.nseg));
-        int t = prof_begin("accept_rowstats", s);
         if (vec_t)
-            hipLaunchKernelGGL(accept_rowstats_kernel<true>, grid, dim3(kRowThreads), 0, s, rp);
+            launch_kernel("accept_rowstats", accept_rowstats_kernel<true>, grid, dim3(kRowThreads), s, rp);
         else
-            hipLaunchKernelGGL(accept_rowstats_kernel<false>, grid, dim3(kRowThreads), 0, s, rp);
-        prof_end(t, s);
+            launch_kernel("accept_rowstats", accept_rowstats_kernel<false>, grid, dim3(kRowThreads), s, rp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -470,19 +466,15 @@ hipError_t launch_accept_typed(const AcceptArgs &a, const AcceptPlan &pl, const 
         mp.rs_m = w.rs_m;
         mp.rs_s = w.rs_s;
         mp.mass = w.mass;
-        int t = prof_begin("accept_mass", s);
         if (vec_u && vec_t)
-            hipLaunchKernelGGL((accept_mass_kernel<WT, R, true>), dim3(pl.tile.blocks), dim3(kAccThreads), 0, s, mp);
+            launch_kernel("accept_mass", (accept_mass_kernel<WT, R, true>), dim3(pl.tile.blocks), dim3(kAccThreads), s, mp);
         else
-            hipLaunchKernelGGL((accept_mass_kernel<WT, R, false>), dim3(pl.tile.blocks), dim3(kAccThreads), 0, s, mp);
-        prof_end(t, s);
+            launch_kernel("accept_mass", (accept_mass_kernel<WT, R, false>), dim3(pl.tile.blocks), dim3(kAccThreads), s, mp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
         AccFinishParams fp{w.count, w.ent_rho, a.x, pl.tile.nchunk, pl.nseg, w.mass, w.rs_v, w.rs_i, a.alpha_out};
-        int t = prof_begin("accept_finish", s);
-        hipLaunchKernelGGL(accept_finish_kernel, dim3((pl.maxent + 255) / 256), dim3(256), 0, s, fp);
-        prof_end(t, s);
+        launch_kernel("accept_finish", accept_finish_kernel, dim3((pl.maxent + 255) / 256), dim3(256), s, fp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -60,22 +60,14 @@ Profiler &prof() {
 
 }  // namespace
 
-int prof_begin(const char *name, hipStream_t s) {
+ProfEvents prof_events(const char *name) {
     Profiler &p = prof();
     std::lock_guard<std::mutex> g(p.mu);
-    if (!p.enabled) return -1;
+    if (!p.enabled) return {};
     Pending pd{p.entry_for(name), p.take_event(), p.take_event()};
-    if (!pd.start || !pd.stop) return -1;
-    (void)hipEventRecord(pd.start, s);
+    if (!pd.start || !pd.stop) return {};
     p.pending.push_back(pd);
-    return int(p.pending.size() - 1);
-}
-
-void prof_end(int token, hipStream_t s) {
-    if (token < 0) return;
-    Profiler &p = prof();
-    std::lock_guard<std::mutex> g(p.mu);
-    if (token < int(p.pending.size())) (void)hipEventRecord(p.pending[size_t(token)].stop, s);
+    return {pd.start, pd.stop};
 }
 
 }  // namespace dspark

@@ -577,9 +577,7 @@ template <typename WT, int R>
 hipError_t launch_gemm_typed(const void *W1, const void *W2, const int32_t *idx, int B, int V, const DraftPlan &pl,
                              const DraftWork &w, float *rowmax, hipStream_t s) {
     GemmParams gp{W1, W2, idx, B, V, pl.nbb, pl.nbg, pl.ntiles, pl.tiles_per_chunk, pl.nchunk, w.pm};
-    int t = prof_begin("bias_gemm", s);
-    hipLaunchKernelGGL((bias_gemm_kernel<WT, R>), dim3(pl.blocks), dim3(kStepThreads), 0, s, gp);
-    prof_end(t, s);
+    launch_kernel("bias_gemm", (bias_gemm_kernel<WT, R>), dim3(pl.blocks), dim3(kStepThreads), s, gp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bias_rowmax_kernel, dim3((B + 3) / 4), dim3(256), 0, s, w.pm, B, pl.nchunk, rowmax);
@@ -619,20 +617,18 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         sp.pb = w.pb;
         sp.p2 = w.p2;
         sp.pi = w.pi;
-        int t = prof_begin("draft_step", s);
         const dim3 grid(pl.blocks), block(kStepThreads);
         if (track2) {
             if (vec)
-                hipLaunchKernelGGL((draft_step_kernel<WT, R, true, true>), grid, block, 0, s, sp);
+                launch_kernel("draft_step", (draft_step_kernel<WT, R, true, true>), grid, block, s, sp);
             else
-                hipLaunchKernelGGL((draft_step_kernel<WT, R, true, false>), grid, block, 0, s, sp);
+                launch_kernel("draft_step", (draft_step_kernel<WT, R, true, false>), grid, block, s, sp);
         } else {
             if (vec)
-                hipLaunchKernelGGL((draft_step_kernel<WT, R, false, true>), grid, block, 0, s, sp);
+                launch_kernel("draft_step", (draft_step_kernel<WT, R, false, true>), grid, block, s, sp);
             else
-                hipLaunchKernelGGL((draft_step_kernel<WT, R, false, false>), grid, block, 0, s, sp);
+                launch_kernel("draft_step", (draft_step_kernel<WT, R, false, false>), grid, block, s, sp);
         }
-        prof_end(t, s);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
 
@@ -662,7 +658,6 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         rp.lse_out = a.lse_out;
         rp.qx_out = a.qx_out;
         rp.margin_out = a.margin_out;
-        t = prof_begin("draft_reduce", s);
         if (a.conf_out) {
             rp.hidden = a.hidden + size_t(k - 1) * a.d;
             rp.h_stride = size_t(a.gamma) * a.d;
@@ -671,11 +666,10 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
             rp.hvec = hvec;
             rp.conf_out = a.conf_out;
             rp.surv_out = a.surv_out;
-            hipLaunchKernelGGL((draft_reduce_kernel<WT, R, true>), dim3((a.B + 3) / 4), dim3(256), 0, s, rp);
+            launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, true>), dim3((a.B + 3) / 4), dim3(256), s, rp);
         } else {
-            hipLaunchKernelGGL((draft_reduce_kernel<WT, R, false>), dim3((a.B + 3) / 4), dim3(256), 0, s, rp);
+            launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, false>), dim3((a.B + 3) / 4), dim3(256), s, rp);
         }
-        prof_end(t, s);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

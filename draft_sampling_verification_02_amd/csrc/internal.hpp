@@ -2,6 +2,7 @@
 // the kernel translation units (draft.hip, verify.hip, debug.hip).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -9,10 +10,21 @@
 
 namespace dspark {
 
-// Per-launch profiling hooks (api.cpp).  prof_begin returns a token that
-// prof_end closes on the same stream; both are no-ops while profiling is off.
-int prof_begin(const char *name, hipStream_t s);
-void prof_end(int token, hipStream_t s);
+// Per-launch profiling (api.cpp): while profiling is on, prof_events hands out
+// a start / stop event pair filed under `name`, which the launch below passes
+// to hipExtLaunchKernel so that the events carry the kernel's own start and
+// end; while it is off both are null.
+struct ProfEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents prof_events(const char *name);
+
+// Launches kernel<<<grid, block, 0, s>>>(args...) (timed when profiling is on).
+template <typename F, typename... Args>
+inline void launch_kernel(const char *name, F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+    const ProfEvents ev = prof_events(name);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+}
 
 // Bump allocator over the caller's workspace: every region 256-byte aligned.
 struct Carve {

@@ -908,9 +908,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     if (!prep_in_pass) {
         PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, a.n_target_rows, w.status, w.off,
                       w.mode, w.req_flags, a.n_accept_out, a.tokens_out, a.diag_out, a.resid_out};
-        int t = prof_begin("verify_prep", s);
-        hipLaunchKernelGGL(verify_prep_kernel, dim3(1), dim3(1024), 0, s, pp);
-        prof_end(t, s);
+        launch_kernel("verify_prep", verify_prep_kernel, dim3(1), dim3(1024), s, pp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
@@ -974,13 +972,11 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.diag_out = a.diag_out;
         static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
                                             "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
-        int t = prof_begin(names[std::min(pass, 8) - 1], s);
         const dim3 grid(size_t((a.B + 3) / 4) * nseg * kPassRows);
         if (pass == 1)
-            hipLaunchKernelGGL(verify_pass_kernel<true>, grid, dim3(256), 0, s, pp);
+            launch_kernel(names[std::min(pass, 8) - 1], verify_pass_kernel<true>, grid, dim3(256), s, pp);
         else
-            hipLaunchKernelGGL(verify_pass_kernel<false>, grid, dim3(256), 0, s, pp);
-        prof_end(t, s);
+            launch_kernel(names[std::min(pass, 8) - 1], verify_pass_kernel<false>, grid, dim3(256), s, pp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -1013,12 +1009,10 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.dw_sum = w.dw_sum;
         dp.dw_bl = w.dw_bl;
         dp.dw_bt = w.dw_bt;
-        int t = prof_begin("verify_draw", s);
         if (vec_u && vec_t)
-            hipLaunchKernelGGL((verify_draw_kernel<WT, R, true>), dim3(pl.draw_blocks), dim3(kDrawThreads), 0, s, dp);
+            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, true>), dim3(pl.draw_blocks), dim3(kDrawThreads), s, dp);
         else
-            hipLaunchKernelGGL((verify_draw_kernel<WT, R, false>), dim3(pl.draw_blocks), dim3(kDrawThreads), 0, s, dp);
-        prof_end(t, s);
+            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, false>), dim3(pl.draw_blocks), dim3(kDrawThreads), s, dp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -1055,9 +1049,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         fp.tokens_out = a.tokens_out;
         fp.out_offsets = a.out_offsets;
         fp.resid_out = a.resid_out;
-        int t = prof_begin("verify_finish", s);
-        hipLaunchKernelGGL((verify_finish_kernel<WT, R>), dim3((a.B + 3) / 4 + 1), dim3(256), 0, s, fp);
-        prof_end(t, s);
+        launch_kernel("verify_finish", (verify_finish_kernel<WT, R>), dim3((a.B + 3) / 4 + 1), dim3(256), s, fp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

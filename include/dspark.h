@@ -291,11 +291,12 @@ int dspark_debug_gumbel(const uint32_t *words, int n, float *out, void *stream);
 int dspark_debug_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,
                            float *rowmax_out, void *workspace, size_t workspace_bytes, void *stream);
 
-/* Per-kernel timing with HIP events on the launch stream.  While enabled,
- * every kernel the library enqueues is bracketed by an event pair; calling
- * dspark_profile_collect waits for the recorded events and adds their
- * durations to per-kernel totals.  Not for concurrent use from several
- * threads. */
+/* Per-kernel timing with HIP events.  While enabled, every kernel the
+ * library enqueues is launched with a start / stop event pair that the
+ * dispatch itself stamps (hipExtLaunchKernel), so a duration is the kernel's
+ * own execution time, without the launch gap; dspark_profile_collect waits
+ * for the events and adds their durations to per-kernel totals.  Not for
+ * concurrent use from several threads. */
 int dspark_profile_enable(int enable);
 int dspark_profile_collect(void);
 /* Number of kernel names with totals, and the totals of entry i. */

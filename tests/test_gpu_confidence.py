@@ -156,7 +156,8 @@ def _compare_alpha(alpha_g, gx, ox, alpha_o, temperature, ell, tag):
     (300, 3, 1024, 16, "bf16", 7),    # more listed rows than one workgroup holds
 ])
 def test_acceptance_parity(B, gamma, V, r, wdtype, greedy):
-    cfg, rnd, ell = _case(B, gamma, V, r, wdtype, seed=B * 17 + V, greedy_every=greedy)
+    cfg, rnd, ell = _case(B, gamma, V, r, wdtype, seed=B * 17 + V, greedy_every=greedy,
+                          ell=np.full(B, gamma) if B == 1 else None)
     target = rnd.target_packed(ell)
     _say(f"[alpha] B={B} gamma={gamma} V={V} r={r} {wdtype} greedy_every={greedy} ell={ell.tolist()[:8]}")
     dev = to_device(rnd)
