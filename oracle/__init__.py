@@ -39,7 +39,7 @@ def _load():
                               ctypes.c_uint64, ctypes.c_uint64,
                               _i32p, _f64p, _f64p, _f64p]
     lib.orc_draft.restype = ctypes.c_int
-    lib.orc_verify.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p, _i32p,
+    lib.orc_verify.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p, _i32p,
                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_uint64, ctypes.c_uint64,
                                _i32p, _i32p, _f64p, _f64p, _f64p, _f64p]
@@ -47,9 +47,16 @@ def _load():
     lib.orc_confidence.argtypes = [_f32p, _f32p, _f32p, _i32p, _i32p,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
     lib.orc_confidence.restype = ctypes.c_int
-    lib.orc_acceptance.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p,
+    lib.orc_acceptance.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p]
     lib.orc_acceptance.restype = ctypes.c_int
+    lib.orc_bf16_round.argtypes = [ctypes.c_double]
+    lib.orc_bf16_round.restype = ctypes.c_double
+    lib.orc_draft_rnn.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _i32p, _f32p, _i32p,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_uint64, ctypes.c_uint64,
+                                  _i32p, _f64p, _f64p, _f64p, _f64p, _f64p]
+    lib.orc_draft_rnn.restype = ctypes.c_int
     lib.orc_schedule.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _f64p, ctypes.c_int,
                                  _i32p, _f64p, _f64p, _i32p]
     lib.orc_schedule.restype = ctypes.c_int
@@ -117,11 +124,54 @@ def draft(U, W1, W2, anchor, temperature, seed, round_id, req_ids=None):
     return {"x": x, "lse": lse, "qx": qx, "margin": margin}
 
 
+def bf16_round(x):
+    """x rounded to the nearest bfloat16 value, ties to even (from double)."""
+    return _load().orc_bf16_round(float(x))
+
+
+def draft_rnn(U, W1, W2, Wgco, h, anchor, temperature, seed, round_id, req_ids=None):
+    """Draft sampling with the RNN head.  U [B, gamma, V], W1/W2 [V, r],
+    Wgco [3r, 2r + d], h [B, gamma, d] (float32 values).  Returns the dict of
+    draft() plus the final state [B, r] and the head rows e [B, gamma, r]
+    (bfloat16 values) the W2 product used, both float64."""
+    lib = _load()
+    U = _f32(U)
+    W1 = _f32(W1)
+    W2 = _f32(W2)
+    Wgco = _f32(Wgco)
+    h = _f32(h)
+    anchor = _i32(anchor)
+    temperature = _f32(temperature)
+    B, gamma, V = U.shape
+    r = W1.shape[1]
+    d = h.shape[2]
+    assert Wgco.shape == (3 * r, 2 * r + d) and h.shape[:2] == (B, gamma)
+    rid = None if req_ids is None else _i32(req_ids)
+    x = np.zeros((B, gamma), np.int32)
+    lse = np.zeros((B, gamma), np.float64)
+    qx = np.zeros((B, gamma), np.float64)
+    margin = np.zeros((B, gamma), np.float64)
+    state = np.zeros((B, r), np.float64)
+    e = np.zeros((B, gamma, r), np.float64)
+    st = lib.orc_draft_rnn(_ptr(U, ctypes.c_float), _ptr(W1, ctypes.c_float), _ptr(W2, ctypes.c_float),
+                           _ptr(Wgco, ctypes.c_float), _ptr(h, ctypes.c_float) if d > 0 else None,
+                           _ptr(anchor, ctypes.c_int32), _ptr(temperature, ctypes.c_float),
+                           _ptr(rid, ctypes.c_int32), B, gamma, V, r, d, seed, round_id,
+                           _ptr(x, ctypes.c_int32), _ptr(lse, ctypes.c_double),
+                           _ptr(qx, ctypes.c_double), _ptr(margin, ctypes.c_double),
+                           _ptr(state, ctypes.c_double), _ptr(e, ctypes.c_double))
+    if st != 0:
+        raise ValueError("orc_draft_rnn: bad arguments")
+    return {"x": x, "lse": lse, "qx": qx, "margin": margin, "state": state, "e": e}
+
+
 def verify(target, ell, U, W1, W2, anchor, x, temperature, seed, round_id,
-           req_ids=None, row_offsets=None):
+           req_ids=None, row_offsets=None, head_rows=None):
     """Exact rejection-sampling verification against packed target rows
-    [sum(1 + ell), V].  Returns n [B], tokens [B, gamma+1], diag
-    [B, gamma+1, 2], resid [B], accept_margin [B, gamma], pick_margin [B]."""
+    [sum(1 + ell), V].  head_rows [B, gamma, r]: the rows the head fed the W2
+    product (the RNN head's e_k); None: the Markov head's W1[x_{k-1}].
+    Returns n [B], tokens [B, gamma+1], diag [B, gamma+1, 2], resid [B],
+    accept_margin [B, gamma], pick_margin [B]."""
     lib = _load()
     target = _f32(target)
     U = _f32(U)
@@ -135,6 +185,7 @@ def verify(target, ell, U, W1, W2, anchor, x, temperature, seed, round_id,
     r = W1.shape[1]
     rid = None if req_ids is None else _i32(req_ids)
     off = None if row_offsets is None else _i32(row_offsets)
+    E = None if head_rows is None else _f32(head_rows)
     n = np.zeros(B, np.int32)
     tokens = np.zeros((B, gamma + 1), np.int32)
     diag = np.zeros((B, gamma + 1, 2), np.float64)
@@ -143,7 +194,7 @@ def verify(target, ell, U, W1, W2, anchor, x, temperature, seed, round_id,
     pm = np.zeros(B, np.float64)
     st = lib.orc_verify(_ptr(target, ctypes.c_float), _ptr(off, ctypes.c_int32), _ptr(ell, ctypes.c_int32),
                         _ptr(U, ctypes.c_float), _ptr(W1, ctypes.c_float), _ptr(W2, ctypes.c_float),
-                        _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32),
+                        _ptr(E, ctypes.c_float), _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32),
                         _ptr(temperature, ctypes.c_float), _ptr(rid, ctypes.c_int32),
                         B, gamma, V, r, seed, round_id,
                         _ptr(n, ctypes.c_int32), _ptr(tokens, ctypes.c_int32),
@@ -178,7 +229,7 @@ def confidence(h, w, W1, anchor, x):
     return c, a
 
 
-def acceptance(target, ell, U, W1, W2, anchor, x, temperature, row_offsets=None):
+def acceptance(target, ell, U, W1, W2, anchor, x, temperature, row_offsets=None, head_rows=None):
     """Per-position acceptance probability alpha_k = sum_v min(p_k, q_k) for
     k <= ell_b over packed target rows [sum(1 + ell), V]; NaN past ell_b.
     Returns alpha [B, gamma] float64."""
@@ -194,10 +245,11 @@ def acceptance(target, ell, U, W1, W2, anchor, x, temperature, row_offsets=None)
     B, gamma, V = U.shape
     r = W1.shape[1]
     off = None if row_offsets is None else _i32(row_offsets)
+    E = None if head_rows is None else _f32(head_rows)
     alpha = np.zeros((B, gamma), np.float64)
     st = lib.orc_acceptance(_ptr(target, ctypes.c_float), _ptr(off, ctypes.c_int32), _ptr(ell, ctypes.c_int32),
                             _ptr(U, ctypes.c_float), _ptr(W1, ctypes.c_float), _ptr(W2, ctypes.c_float),
-                            _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32),
+                            _ptr(E, ctypes.c_float), _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32),
                             _ptr(temperature, ctypes.c_float), B, gamma, V, r, _ptr(alpha, ctypes.c_double))
     if st != 0:
         raise ValueError("orc_acceptance: bad arguments")

@@ -130,12 +130,12 @@ static double orc_gumbel(uint32_t w)
 /* Shared pieces of the draft and verify halves                        */
 /* ------------------------------------------------------------------ */
 
-/* z(v) = (U_k(v) + B_k(v)) / T with B_k(v) = sum_i W1[prev][i] * W2[v][i]
- * ([MG] 3.2 Markov head; [CE] 03).  T = 0 leaves the raw logit. */
-static void orc_logits(const float *Uk, const float *W1, const float *W2, int prev,
+/* z(v) = (U_k(v) + B_k(v)) / T with B_k(v) = sum_i e[i] * W2[v][i], e the
+ * head's row for position k: W1[x_{k-1}] for the Markov head ([MG] 3.2;
+ * [CE] 03), the RNN head's e_k otherwise.  T = 0 leaves the raw logit. */
+static void orc_logits(const float *Uk, const float *e, const float *W2,
                        double T, int V, int r, double *z)
 {
-    const float *e = W1 + (size_t)prev * (size_t)r;
     for (int v = 0; v < V; ++v) {
         const float *w = W2 + (size_t)v * (size_t)r;
         double bias = 0.0;
@@ -144,6 +144,17 @@ static void orc_logits(const float *Uk, const float *W1, const float *W2, int pr
         double logit = (double)Uk[v] + bias;
         z[v] = (T > 0.0) ? logit / T : logit;
     }
+}
+
+/* The head's row for request b at position k: E[b][k-1] when the caller
+ * passes the rows the head produced ([B, gamma, r], the RNN head), else the
+ * Markov head's W1[x_{k-1}] with x_0 = anchor. */
+static const float *orc_head_row(const float *W1, const float *E, const int32_t *anchor, const int32_t *x,
+                                 int b, int k, int gamma, int r)
+{
+    if (E) return E + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)r;
+    int prev = (k == 1) ? anchor[b] : x[(size_t)b * (size_t)gamma + (size_t)(k - 2)];
+    return W1 + (size_t)prev * (size_t)r;
 }
 
 /* log sum_v exp(z(v)); -inf when no entry is finite. */
@@ -259,7 +270,7 @@ int orc_draft(const float *U, const float *W1, const float *W2,
         int prev = anchor[b];
         for (int k = 1; k <= gamma; ++k) {
             const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
-            orc_logits(Uk, W1, W2, prev, T, V, r, z);
+            orc_logits(Uk, W1 + (size_t)prev * (size_t)r, W2, T, V, r, z);
             int x;
             double lse, qx, margin;
             if (T > 0.0) {
@@ -284,6 +295,115 @@ int orc_draft(const float *U, const float *W1, const float *W2,
 }
 
 /* ------------------------------------------------------------------ */
+/* Draft half with the RNN head                                        */
+/* ------------------------------------------------------------------ */
+
+/* x rounded to the nearest bfloat16 value (8 significant bits), ties to
+ * even, straight from double precision. */
+double orc_bf16_round(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    const double tiny = ldexp(1.0, -126); /* below it bfloat16 steps by 2^-133 */
+    if (fabs(x) < tiny) return ldexp(nearbyint(ldexp(x, 133)), -133);
+    int e;
+    double m = frexp(x, &e); /* |m| in [0.5, 1) */
+    double r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+    if (fabs(r) > 3.3895313892515355e38) r = copysign(INFINITY, r); /* past the largest bf16 */
+    return r;
+}
+
+/* [MG] 3.2 RNN Head: a recurrent state s_k (s_0 = 0) carried across the
+ * block positions.  For each request b and k = 1..gamma, with x_0 = anchor:
+ *   z    = [s_{k-1}, W1[x_{k-1}], h_k]                     (2r + d entries)
+ *   y    = Wgco z,  Wgco [3r, 2r + d] (nn.Linear weight layout),
+ *          split as (gate, candidate, output), r entries each
+ *   g    = sigmoid(y_gate),  s_k = g * s_{k-1} + (1 - g) * tanh(y_cand)
+ *   e_k  = tanh(y_out),      B_k(v) = sum_i e_k[i] W2[v][i]
+ *   z_k  = (U_k + B_k) / T,  x_k drawn exactly as orc_draft draws it.
+ * Precision reading: the head's two products take bfloat16 operands, as
+ * its weights are, so s_{k-1} and h_k enter the gate product rounded to
+ * bfloat16 and e_k enters the W2 product rounded to bfloat16 (nearest, ties
+ * to even); everything else is double.  Outputs as orc_draft's, plus the
+ * final state s_gamma [B, r] and the rows e_k [B, gamma, r] the W2 product
+ * used (both nullable; e_k is what verification needs to rebuild q_k). */
+int orc_draft_rnn(const float *U, const float *W1, const float *W2, const float *Wgco, const float *h,
+                  const int32_t *anchor, const float *temperature, const int32_t *req_ids,
+                  int B, int gamma, int V, int r, int d, uint64_t seed, uint64_t round_id,
+                  int32_t *x_out, double *lse_out, double *qx_out, double *margin_out, double *state_out,
+                  double *e_out)
+{
+    if (B < 0 || gamma < 1 || V < 1 || r < 1 || d < 0) return ORC_ERR_ARG;
+    if (!U || !W1 || !W2 || !Wgco || !anchor || !temperature || !x_out) return ORC_ERR_ARG;
+    if (d > 0 && !h) return ORC_ERR_ARG;
+    const int K = 2 * r + d;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        double *z = (double *)malloc((size_t)V * sizeof(double));
+        double *st = (double *)calloc((size_t)r, sizeof(double));
+        double *in = (double *)malloc((size_t)K * sizeof(double));
+        double *ek = (double *)malloc((size_t)r * sizeof(double));
+        if (!z || !st || !in || !ek) { status = ORC_ERR_ARG; free(z); free(st); free(in); free(ek); continue; }
+        int req = req_ids ? req_ids[b] : b;
+        double T = (double)temperature[b];
+        int prev = anchor[b];
+        for (int k = 1; k <= gamma; ++k) {
+            const float *hk = d > 0 ? h + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)d : NULL;
+            for (int i = 0; i < r; ++i) in[i] = orc_bf16_round(st[i]);
+            for (int i = 0; i < r; ++i) in[r + i] = (double)W1[(size_t)prev * (size_t)r + i];
+            for (int i = 0; i < d; ++i) in[2 * r + i] = orc_bf16_round((double)hk[i]);
+            for (int i = 0; i < r; ++i) {
+                double yg = 0.0, yc = 0.0, yo = 0.0;
+                const float *wg = Wgco + (size_t)i * (size_t)K;
+                const float *wc = Wgco + (size_t)(r + i) * (size_t)K;
+                const float *wo = Wgco + (size_t)(2 * r + i) * (size_t)K;
+                for (int j = 0; j < K; ++j) {
+                    yg += (double)wg[j] * in[j];
+                    yc += (double)wc[j] * in[j];
+                    yo += (double)wo[j] * in[j];
+                }
+                double g = 1.0 / (1.0 + exp(-yg));
+                st[i] = g * st[i] + (1.0 - g) * tanh(yc);
+                ek[i] = orc_bf16_round(tanh(yo));
+            }
+            if (e_out)
+                for (int i = 0; i < r; ++i)
+                    e_out[((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)r + i] = ek[i];
+            const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
+            for (int v = 0; v < V; ++v) {
+                const float *w = W2 + (size_t)v * (size_t)r;
+                double bias = 0.0;
+                for (int i = 0; i < r; ++i)
+                    bias += ek[i] * (double)w[i];
+                double logit = (double)Uk[v] + bias;
+                z[v] = (T > 0.0) ? logit / T : logit;
+            }
+            int x;
+            double lse, qx, margin;
+            if (T > 0.0) {
+                lse = orc_logsumexp(z, V);
+                x = orc_two_level_draw(z, V, seed, round_id, 3, 0, k, req, &margin);
+                qx = exp(z[x] - lse);
+            } else {
+                x = orc_argmax(z, V, &margin);
+                lse = z[x];
+                qx = 1.0;
+            }
+            size_t o = (size_t)b * (size_t)gamma + (size_t)(k - 1);
+            x_out[o] = x;
+            if (lse_out) lse_out[o] = lse;
+            if (qx_out) qx_out[o] = qx;
+            if (margin_out) margin_out[o] = margin;
+            prev = x;
+        }
+        if (state_out)
+            for (int i = 0; i < r; ++i) state_out[(size_t)b * (size_t)r + i] = st[i];
+        free(z); free(st); free(in); free(ek);
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------ */
 /* Verify half: exact rejection sampling with per-request lengths      */
 /* ------------------------------------------------------------------ */
 
@@ -293,7 +413,8 @@ int orc_draft(const float *U, const float *W1, const float *W2,
  *
  * For each request ([CE] 02 and 05; [MG] 1 and 4.1):
  *   p_k = softmax(t_k / T) (T = 0: one-hot at the lowest-index argmax),
- *   q_k = softmax(z_k) recomputed from U_k, W1[x_{k-1}], W2 as in the draft;
+ *   q_k = softmax(z_k) recomputed from U_k, the head's row (W1[x_{k-1}], or
+ *         E[b][k-1] when E is given) and W2 as in the draft;
  *   k = 1..ell: u from stream 1, accept iff u * q_k(x_k) < p_k(x_k)
  *               (T = 0: accept iff x_k = argmax t_k);
  *   first rejection j: y ~ max(p_j - q_j, 0) by the two-level Gumbel-max
@@ -308,7 +429,7 @@ int orc_draft(const float *U, const float *W1, const float *W2,
  * smaller top-two score gap of the two-level draw of y (T > 0) or the
  * top-two gap of t_j (T = 0). */
 int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
-               const float *U, const float *W1, const float *W2,
+               const float *U, const float *W1, const float *W2, const float *E,
                const int32_t *anchor, const int32_t *x, const float *temperature,
                const int32_t *req_ids, int B, int gamma, int V, int r,
                uint64_t seed, uint64_t round_id,
@@ -361,9 +482,8 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
                 for (int v = 0; v < V; ++v) zt[v] = (double)tk[v] / T;
                 double lse_t = orc_logsumexp(zt, V);
                 pk = exp(zt[xk] - lse_t);
-                int prev = (k == 1) ? anchor[b] : xb[k - 2];
                 const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
-                orc_logits(Uk, W1, W2, prev, T, V, r, zq);
+                orc_logits(Uk, orc_head_row(W1, E, anchor, x, b, k, gamma, r), W2, T, V, r, zq);
                 double lse_q = orc_logsumexp(zq, V);
                 double qk = exp(zq[xk] - lse_q);
                 double u = orc_u01(orc_random_word(seed, round_id, 1, k, req, 0));
@@ -396,9 +516,8 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
             double lse_t = orc_logsumexp(zt, V);
             for (int v = 0; v < V; ++v) mass[v] = zt[v] - lse_t;
             if (rejected) {
-                int prev = (j == 1) ? anchor[b] : xb[j - 2];
                 const float *Uj = U + ((size_t)b * (size_t)gamma + (size_t)(j - 1)) * (size_t)V;
-                orc_logits(Uj, W1, W2, prev, T, V, r, zq);
+                orc_logits(Uj, orc_head_row(W1, E, anchor, x, b, j, gamma, r), W2, T, V, r, zq);
                 double lse_q = orc_logsumexp(zq, V);
                 double tot = 0.0;
                 for (int v = 0; v < V; ++v) {
@@ -477,7 +596,7 @@ int orc_confidence(const float *h, const float *w, const float *W1,
  * 1 when they agree and 0 otherwise.  Computed for k = 1..ell_b (the rows
  * the target produced, packed as in orc_verify); NaN for k > ell_b. */
 int orc_acceptance(const float *target, const int32_t *off, const int32_t *ell,
-                   const float *U, const float *W1, const float *W2,
+                   const float *U, const float *W1, const float *W2, const float *E,
                    const int32_t *anchor, const int32_t *x, const float *temperature,
                    int B, int gamma, int V, int r, double *alpha_out)
 {
@@ -508,9 +627,8 @@ int orc_acceptance(const float *target, const int32_t *off, const int32_t *ell,
                 if (T > 0.0) {
                     for (int v = 0; v < V; ++v) zt[v] = (double)tk[v] / T;
                     double lse_t = orc_logsumexp(zt, V);
-                    int prev = (k == 1) ? anchor[b] : xb[k - 2];
                     const float *Uk = U + ((size_t)b * (size_t)gamma + (size_t)(k - 1)) * (size_t)V;
-                    orc_logits(Uk, W1, W2, prev, T, V, r, zq);
+                    orc_logits(Uk, orc_head_row(W1, E, anchor, x, b, k, gamma, r), W2, T, V, r, zq);
                     double lse_q = orc_logsumexp(zq, V);
                     alpha = 0.0;
                     for (int v = 0; v < V; ++v)
