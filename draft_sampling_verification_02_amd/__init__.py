@@ -72,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             _c_void_p, _c_void_p, _c_int,
                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                             _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_draft_rnn_workspace_size": ([_c_int] * 5, _c_size),
+        "dspark_draft_sample_rnn": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_verify_workspace_size": ([_c_int] * 4, _c_size),
         "dspark_verify": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -80,6 +85,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_verify_check": ([_c_void_p, _c_void_p], _c_int),
+        "dspark_verify_rnn": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
+                               _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                               _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_acceptance_rnn": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_int, _c_int, _c_int, _c_int,
+                                   _c_void_p, _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_acceptance_workspace_size": ([_c_int] * 4, _c_size),
         "dspark_acceptance": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
                                _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -261,12 +277,68 @@ def dspark_draft_sample_confidence(U, W1, W2, anchor, temperature, hidden, conf_
     return out
 
 
+def dspark_draft_rnn_workspace_size(B: int, gamma: int, V: int, r: int, d: int) -> int:
+    return load_library().dspark_draft_rnn_workspace_size(B, gamma, V, r, d)
+
+
+def dspark_draft_sample_rnn(U, W1, W2, Wgco, anchor, temperature, hidden, seed: int, round_id: int, *,
+                            margin: bool = False, state: bool = False, out: dict | None = None, workspace=None,
+                            stream=None) -> dict:
+    """Draft half with the RNN head.  W1/W2 [V, r] and Wgco [3r, 2r + d]
+    bfloat16, hidden [B, gamma, d] float32 (d a multiple of 32, may be 0).
+    Returns the draft outputs plus {"e"} (the head's rows [B, gamma, r]
+    bfloat16, for dspark_verify_rnn) [and {"state"} = s_gamma [B, r]]."""
+    torch = _torch()
+    lib = load_library()
+    dev, B, gamma, V, r, wdt = _draft_inputs(U, W1, W2, anchor, temperature)
+    if hidden.dim() != 3 or tuple(hidden.shape[:2]) != (B, gamma):
+        raise ValueError("hidden: [B, gamma, d]")
+    d = hidden.shape[2]
+    _need(hidden, "hidden", torch.float32, (B, gamma, d), dev)
+    _need(Wgco, "Wgco", W1.dtype, (3 * r, 2 * r + d), dev)
+    out = _draft_outputs(B, gamma, dev, margin, False, out)
+    if "e" not in out:
+        out["e"] = torch.empty((B, gamma, r), dtype=torch.bfloat16, device=dev)
+    if state and "state" not in out:
+        out["state"] = torch.empty((B, r), dtype=torch.float32, device=dev)
+    nbytes = lib.dspark_draft_rnn_workspace_size(B, gamma, V, r, d)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_draft_rnn_workspace_size")
+    ws = _workspace(nbytes, dev, workspace if workspace is not None else out.get("workspace"))
+    out["workspace"] = ws
+    st = lib.dspark_draft_sample_rnn(
+        _ptr(U), _ptr(W1), _ptr(W2), _ptr(Wgco), wdt, _ptr(anchor), _ptr(temperature),
+        _ptr(hidden) if d > 0 else None, d, B, gamma, V, r, int(seed), int(round_id),
+        _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")), _ptr(out["e"]),
+        _ptr(out.get("state")), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_draft_sample_rnn")
+    return out
+
+
 def dspark_verify(target, ell, U, W1, W2, anchor, x, lse_q, qx, temperature, seed: int, round_id: int, *,
                   row_offsets=None, diag: bool = False, resid: bool = False, out_offsets: bool = True,
                   out: dict | None = None, workspace=None, stream=None) -> dict:
     """Verify half of a round.  target [rows, V] float32 packed per request
     (rows off_b .. off_b + ell_b), ell [B] int32, and the draft's inputs and
     outputs.  Returns {"n", "tokens"[, "offsets", "diag", "resid"], "workspace"}."""
+    return _verify(target, ell, U, W1, W2, anchor, x, lse_q, qx, temperature, seed, round_id, None,
+                   row_offsets, diag, resid, out_offsets, out, workspace, stream)
+
+
+def dspark_verify_rnn(target, ell, U, head_rows, W2, anchor, x, lse_q, qx, temperature, seed: int, round_id: int, *,
+                      row_offsets=None, diag: bool = False, resid: bool = False, out_offsets: bool = True,
+                      out: dict | None = None, workspace=None, stream=None) -> dict:
+    """dspark_verify for RNN-head drafts: q_k from head_rows [B, gamma, r]
+    (the "e" output of dspark_draft_sample_rnn) instead of W1[x_{k-1}]."""
+    torch = _torch()
+    B, gamma, _ = U.shape
+    _need(head_rows, "head_rows", W2.dtype, (B, gamma, W2.shape[1]), U.device)
+    return _verify(target, ell, U, W2, W2, anchor, x, lse_q, qx, temperature, seed, round_id, head_rows,
+                   row_offsets, diag, resid, out_offsets, out, workspace, stream)
+
+
+def _verify(target, ell, U, W1, W2, anchor, x, lse_q, qx, temperature, seed, round_id, rows,
+            row_offsets, diag, resid, out_offsets, out, workspace, stream):
     torch = _torch()
     lib = load_library()
     dev = U.device
@@ -299,13 +371,14 @@ def dspark_verify(target, ell, U, W1, W2, anchor, x, lse_q, qx, temperature, see
         raise DSparkError(DSPARK_ERR_ARG, "dspark_verify_workspace_size")
     ws = _workspace(nbytes, dev, workspace if workspace is not None else out.get("workspace"))
     out["workspace"] = ws
-    st = lib.dspark_verify(_ptr(target), target.shape[0], _ptr(ell), _ptr(row_offsets),
-                           _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q), _ptr(qx),
-                           _ptr(temperature), B, gamma, V, r, int(seed), int(round_id),
-                           _ptr(out["n"]), _ptr(out["tokens"]), _ptr(out.get("offsets")),
-                           _ptr(out.get("diag")), _ptr(out.get("resid")),
-                           _ptr(ws), ws.numel(), _stream_ptr(stream))
-    _check(st, "dspark_verify")
+    fn = lib.dspark_verify if rows is None else lib.dspark_verify_rnn
+    st = fn(_ptr(target), target.shape[0], _ptr(ell), _ptr(row_offsets),
+            _ptr(U), _ptr(W1 if rows is None else rows), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q),
+            _ptr(qx), _ptr(temperature), B, gamma, V, r, int(seed), int(round_id),
+            _ptr(out["n"]), _ptr(out["tokens"]), _ptr(out.get("offsets")),
+            _ptr(out.get("diag")), _ptr(out.get("resid")),
+            _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_verify" if rows is None else "dspark_verify_rnn")
     return out
 
 
@@ -318,6 +391,20 @@ def dspark_acceptance(target, ell, U, W1, W2, anchor, x, lse_q, temperature, *, 
     """Per-position acceptance probability alpha_k = sum_v min(p_k, q_k) of
     every verified position (NaN past ell).  Arguments as for dspark_verify.
     Returns alpha [B, gamma] float32 (``out`` if given)."""
+    return _acceptance(target, ell, U, W1, W2, anchor, x, lse_q, temperature, None, row_offsets, out, workspace,
+                       stream)
+
+
+def dspark_acceptance_rnn(target, ell, U, head_rows, W2, anchor, x, lse_q, temperature, *, row_offsets=None,
+                          out=None, workspace=None, stream=None):
+    """dspark_acceptance for RNN-head drafts (q_k from head_rows)."""
+    B, gamma, _ = U.shape
+    _need(head_rows, "head_rows", W2.dtype, (B, gamma, W2.shape[1]), U.device)
+    return _acceptance(target, ell, U, W2, W2, anchor, x, lse_q, temperature, head_rows, row_offsets, out,
+                       workspace, stream)
+
+
+def _acceptance(target, ell, U, W1, W2, anchor, x, lse_q, temperature, rows, row_offsets, out, workspace, stream):
     torch = _torch()
     lib = load_library()
     dev = U.device
@@ -342,11 +429,11 @@ def dspark_acceptance(target, ell, U, W1, W2, anchor, x, lse_q, temperature, *, 
     if nbytes == 0:
         raise DSparkError(DSPARK_ERR_ARG, "dspark_acceptance_workspace_size")
     ws = _workspace(nbytes, dev, workspace)
-    st = lib.dspark_acceptance(_ptr(target), target.shape[0], _ptr(ell), _ptr(row_offsets),
-                               _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q),
-                               _ptr(temperature), B, gamma, V, r, _ptr(out), _ptr(ws), ws.numel(),
-                               _stream_ptr(stream))
-    _check(st, "dspark_acceptance")
+    fn = lib.dspark_acceptance if rows is None else lib.dspark_acceptance_rnn
+    st = fn(_ptr(target), target.shape[0], _ptr(ell), _ptr(row_offsets),
+            _ptr(U), _ptr(W1 if rows is None else rows), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q),
+            _ptr(temperature), B, gamma, V, r, _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "dspark_acceptance" if rows is None else "dspark_acceptance_rnn")
     return out
 
 

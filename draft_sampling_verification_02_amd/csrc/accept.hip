@@ -66,8 +66,9 @@ struct AccPrepParams {
     int32_t *count;     // [2] sampled rows, greedy rows
     int32_t *ent_rho;   // [B * gamma] row b * gamma + k - 1 of the listed entry
     int32_t *ent_trow;  // packed target row
-    int32_t *ent_prev;  // x_{k-1}
+    int32_t *ent_prev;  // the head's row: x_{k-1}, or b * gamma + k - 1 (erow_mode)
     float *alpha_out;
+    int erow_mode;
 };
 
 // A request is listed when 0 <= ell_b <= gamma and its rows lie in the target
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(1024) void accept_prep_kernel(AccPrepParams p) {
             p.ent_rho[slot] = rho;
             p.ent_trow[slot] = off + k - 1;
             const int prev = k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2];
-            p.ent_prev[slot] = min(max(prev, 0), p.V - 1);
+            p.ent_prev[slot] = p.erow_mode ? rho : min(max(prev, 0), p.V - 1);
         }
         o += 1 + e;
     }
@@ -428,7 +429,7 @@ hipError_t launch_accept_typed(const AcceptArgs &a, const AcceptPlan &pl, const 
     hipError_t e;
     {
         AccPrepParams pp{a.ell, a.row_offsets, a.anchor, a.x, a.temperature, a.B, a.gamma, a.V, a.n_target_rows,
-                         w.count, w.ent_rho, w.ent_trow, w.ent_prev, a.alpha_out};
+                         w.count, w.ent_rho, w.ent_trow, w.ent_prev, a.alpha_out, a.erow_mode};
         launch_kernel("accept_prep", accept_prep_kernel, dim3(1), dim3(1024), s, pp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

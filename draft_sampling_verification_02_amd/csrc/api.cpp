@@ -204,17 +204,71 @@ int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W
                         stream);
 }
 
+size_t dspark_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d) {
+    if (!sizes_ok(B, gamma, V, r) || d < 0 || d > DSPARK_MAX_HIDDEN) return 0;
+    const DraftPlan p = draft_plan(B, V);
+    size_t bytes = 0;
+    draft_carve(nullptr, B, p, &bytes, r);
+    return bytes;
+}
+
+int dspark_draft_sample_rnn(const float *U, const void *W1, const void *W2, const void *Wgco, int wdtype,
+                            const int32_t *anchor, const float *temperature, const float *hidden, int d, int B,
+                            int gamma, int V, int r, uint64_t seed, uint64_t round_id, int32_t *x_out, float *lse_out,
+                            float *qx_out, float *margin_out, void *e_out, float *state_out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    if (!U || !W1 || !W2 || !Wgco || !anchor || !temperature || !x_out || !lse_out || !qx_out || !e_out)
+        return DSPARK_ERR_ARG;
+    if (!sizes_ok(B, gamma, V, r)) return DSPARK_ERR_ARG;
+    if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
+    if (wdtype != DSPARK_BF16 || !rank_supported(wdtype, r)) return DSPARK_ERR_UNSUPPORTED;
+    if (d < 0 || d > DSPARK_MAX_HIDDEN || (d > 0 && !hidden)) return DSPARK_ERR_ARG;
+    if (d % 32 != 0) return DSPARK_ERR_UNSUPPORTED;
+    if (!aligned16(W1) || !aligned16(W2) || !aligned16(Wgco) || !aligned16(e_out) || (d > 0 && !aligned16(hidden)))
+        return DSPARK_ERR_ARG;
+    const DraftPlan plan = draft_plan(B, V);
+    size_t need = 0;
+    draft_carve(nullptr, B, plan, &need, r);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+    const DraftWork w = draft_carve(workspace, B, plan, nullptr, r);
+    DraftArgs a{};
+    a.U = U;
+    a.W1 = W1;
+    a.W2 = W2;
+    a.wdtype = wdtype;
+    a.anchor = anchor;
+    a.temperature = temperature;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.r = r;
+    a.key0 = uint32_t(seed);
+    a.key1 = uint32_t(seed >> 32);
+    a.round32 = uint32_t(round_id);
+    a.x_out = x_out;
+    a.lse_out = lse_out;
+    a.qx_out = qx_out;
+    a.margin_out = margin_out;
+    a.Wgco = Wgco;
+    a.rnn_h = hidden;
+    a.rnn_d = d;
+    a.e_out = static_cast<uint16_t *>(e_out);
+    a.state_out = state_out;
+    const hipError_t e = launch_draft(a, plan, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
 size_t dspark_verify_workspace_size(int B, int gamma, int V, int r) {
     if (!sizes_ok(B, gamma, V, r)) return 0;
     return verify_bytes(B, gamma, V);
 }
 
-int dspark_verify(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
-                  const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
-                  const int32_t *x, const float *lse_q, const float *qx, const float *temperature, int B,
-                  int gamma, int V, int r, uint64_t seed, uint64_t round_id, int32_t *n_accept_out,
-                  int32_t *tokens_out, int32_t *out_offsets, float *diag_out, float *resid_out,
-                  void *workspace, size_t workspace_bytes, void *stream) {
+static int verify_common(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                         const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                         const int32_t *x, const float *lse_q, const float *qx, const float *temperature, int B,
+                         int gamma, int V, int r, uint64_t seed, uint64_t round_id, int32_t *n_accept_out,
+                         int32_t *tokens_out, int32_t *out_offsets, float *diag_out, float *resid_out,
+                         void *workspace, size_t workspace_bytes, void *stream, int erow_mode) {
     if (!target || !ell || !U || !W1 || !W2 || !anchor || !x || !lse_q || !qx || !temperature ||
         !n_accept_out || !tokens_out)
         return DSPARK_ERR_ARG;
@@ -253,8 +307,31 @@ int dspark_verify(const float *target, int n_target_rows, const int32_t *ell, co
     a.out_offsets = out_offsets;
     a.diag_out = diag_out;
     a.resid_out = resid_out;
+    a.erow_mode = erow_mode;
     const hipError_t e = launch_verify(a, plan, w, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+int dspark_verify(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                  const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                  const int32_t *x, const float *lse_q, const float *qx, const float *temperature, int B,
+                  int gamma, int V, int r, uint64_t seed, uint64_t round_id, int32_t *n_accept_out,
+                  int32_t *tokens_out, int32_t *out_offsets, float *diag_out, float *resid_out,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_common(target, n_target_rows, ell, row_offsets, U, W1, W2, wdtype, anchor, x, lse_q, qx,
+                         temperature, B, gamma, V, r, seed, round_id, n_accept_out, tokens_out, out_offsets, diag_out,
+                         resid_out, workspace, workspace_bytes, stream, 0);
+}
+
+int dspark_verify_rnn(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                      const float *U, const void *head_rows, const void *W2, int wdtype, const int32_t *anchor,
+                      const int32_t *x, const float *lse_q, const float *qx, const float *temperature, int B,
+                      int gamma, int V, int r, uint64_t seed, uint64_t round_id, int32_t *n_accept_out,
+                      int32_t *tokens_out, int32_t *out_offsets, float *diag_out, float *resid_out,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_common(target, n_target_rows, ell, row_offsets, U, head_rows, W2, wdtype, anchor, x, lse_q, qx,
+                         temperature, B, gamma, V, r, seed, round_id, n_accept_out, tokens_out, out_offsets, diag_out,
+                         resid_out, workspace, workspace_bytes, stream, 1);
 }
 
 size_t dspark_acceptance_workspace_size(int B, int gamma, int V, int r) {
@@ -262,10 +339,11 @@ size_t dspark_acceptance_workspace_size(int B, int gamma, int V, int r) {
     return accept_bytes(B, gamma, V);
 }
 
-int dspark_acceptance(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
-                      const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
-                      const int32_t *x, const float *lse_q, const float *temperature, int B, int gamma, int V,
-                      int r, float *alpha_out, void *workspace, size_t workspace_bytes, void *stream) {
+static int acceptance_common(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                             const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                             const int32_t *x, const float *lse_q, const float *temperature, int B, int gamma,
+                             int V, int r, float *alpha_out, void *workspace, size_t workspace_bytes, void *stream,
+                             int erow_mode) {
     if (!target || !ell || !U || !W1 || !W2 || !anchor || !x || !lse_q || !temperature || !alpha_out)
         return DSPARK_ERR_ARG;
     if (!sizes_ok(B, gamma, V, r) || n_target_rows < 1) return DSPARK_ERR_ARG;
@@ -295,8 +373,25 @@ int dspark_acceptance(const float *target, int n_target_rows, const int32_t *ell
     a.V = V;
     a.r = r;
     a.alpha_out = alpha_out;
+    a.erow_mode = erow_mode;
     const hipError_t e = launch_accept(a, plan, w, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+int dspark_acceptance(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                      const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                      const int32_t *x, const float *lse_q, const float *temperature, int B, int gamma, int V,
+                      int r, float *alpha_out, void *workspace, size_t workspace_bytes, void *stream) {
+    return acceptance_common(target, n_target_rows, ell, row_offsets, U, W1, W2, wdtype, anchor, x, lse_q,
+                             temperature, B, gamma, V, r, alpha_out, workspace, workspace_bytes, stream, 0);
+}
+
+int dspark_acceptance_rnn(const float *target, int n_target_rows, const int32_t *ell, const int32_t *row_offsets,
+                          const float *U, const void *head_rows, const void *W2, int wdtype, const int32_t *anchor,
+                          const int32_t *x, const float *lse_q, const float *temperature, int B, int gamma, int V,
+                          int r, float *alpha_out, void *workspace, size_t workspace_bytes, void *stream) {
+    return acceptance_common(target, n_target_rows, ell, row_offsets, U, head_rows, W2, wdtype, anchor, x, lse_q,
+                             temperature, B, gamma, V, r, alpha_out, workspace, workspace_bytes, stream, 1);
 }
 
 int dspark_verify_check(const void *workspace, void *stream) {

@@ -43,6 +43,7 @@ struct StepParams {
     int xprev_stride;
     const float *temperature;
     int B, V, k;
+    int erows;  // rows of W1 (the E rows are W1 + xprev * R, clamped below erows)
     uint32_t key0, key1, round32;
     int nbb, nw, nbg, ntiles, tiles_per_chunk, nchunk;
     int vec;  // U rows allow aligned 16-byte loads
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     su.template issue<true>(v0_of(0), p.V, uregion, lane);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%2)" : "+v"(prev), "+v"(T) : "n"(SU::NI + decltype(dma)::MIN_PER_WAVE));
-    prev = min(max(prev, 0), p.V - 1);
+    prev = min(max(prev, 0), p.erows - 1);
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;  // base-2 logits; greedy keeps raw logits
     EFrags<WT, R> ef;
@@ -198,6 +199,7 @@ struct ReduceParams {
     int xprev_stride;
     const float *temperature;
     int B, V, k, gamma, nchunk, ntiles;
+    int erows;  // as for StepParams
     uint32_t key0, key1, round32;
     const float *pm, *ps, *pb, *p2;
     const int32_t *pi;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
         if (p.k > 1) a_prev = p.surv_out[size_t(b) * p.gamma + p.k - 2];
         if (p.d > 0) conf_s = conf_hidden_part(p, b, lane);
     }
-    prev = min(max(prev, 0), p.V - 1);
+    prev = min(max(prev, 0), p.erows - 1);
     RowHalf<WT, R> w1;
     w1.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
     if constexpr (CONF) {
@@ -590,14 +592,42 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
     const bool vec = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
     const bool hvec = a.d % 4 == 0 && reinterpret_cast<uintptr_t>(a.hidden) % 16 == 0 &&
                       reinterpret_cast<uintptr_t>(a.conf_w) % 16 == 0;
+    bool rnn = false;
+    if constexpr (sizeof(WT) == 2) rnn = a.Wgco != nullptr;
     for (int k = 1; k <= a.gamma; ++k) {
+        const int32_t *xprev = (k == 1) ? a.anchor : a.x_out + (k - 2);
+        const int xprev_stride = (k == 1) ? 1 : a.gamma;
+        if (rnn) {
+            // the RNN head's e_k replaces W1[x_{k-1}]: the step reads row
+            // b * gamma + k - 1 of e_out as row rnn_idx[b] of e_out + (k - 1) r
+            RnnGateArgs g{};
+            g.s_in = (k == 1) ? nullptr : w.rnn_s[(k - 1) & 1];
+            g.s_out = (k == a.gamma && a.state_out) ? a.state_out : w.rnn_s[k & 1];
+            g.xprev = xprev;
+            g.xprev_stride = xprev_stride;
+            g.h = a.rnn_h + size_t(k - 1) * a.rnn_d;
+            g.h_stride = size_t(a.gamma) * a.rnn_d;
+            g.W1 = static_cast<const uint16_t *>(a.W1);
+            g.Wgco = static_cast<const uint16_t *>(a.Wgco);
+            g.e_out = a.e_out + size_t(k - 1) * a.r;
+            g.e_stride = size_t(a.gamma) * a.r;
+            g.idx_out = (k == 1) ? w.rnn_idx : nullptr;
+            g.gamma = a.gamma;
+            g.B = a.B;
+            g.V = a.V;
+            g.r = a.r;
+            g.d = a.rnn_d;
+            const hipError_t e = launch_rnn_gate(g, s);
+            if (e != hipSuccess) return e;
+        }
         StepParams sp{};
         sp.U = a.U + size_t(k - 1) * a.V;
         sp.u_stride = size_t(a.gamma) * a.V;
-        sp.W1 = a.W1;
+        sp.W1 = rnn ? static_cast<const void *>(a.e_out + size_t(k - 1) * a.r) : a.W1;
         sp.W2 = a.W2;
-        sp.xprev = (k == 1) ? a.anchor : a.x_out + (k - 2);
-        sp.xprev_stride = (k == 1) ? 1 : a.gamma;
+        sp.xprev = rnn ? w.rnn_idx : xprev;
+        sp.xprev_stride = rnn ? 1 : xprev_stride;
+        sp.erows = rnn ? a.B * a.gamma : a.V;
         sp.temperature = a.temperature;
         sp.B = a.B;
         sp.V = a.V;
@@ -635,10 +665,11 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         ReduceParams rp{};
         rp.U = sp.U;
         rp.u_stride = sp.u_stride;
-        rp.W1 = a.W1;
+        rp.W1 = sp.W1;
         rp.W2 = a.W2;
         rp.xprev = sp.xprev;
         rp.xprev_stride = sp.xprev_stride;
+        rp.erows = sp.erows;
         rp.temperature = a.temperature;
         rp.B = a.B;
         rp.V = a.V;
@@ -699,7 +730,7 @@ DraftPlan draft_plan(int B, int V) {
     return tile_walk_plan(B, V, kStepThreads / 64, 256, 2);
 }
 
-DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes) {
+DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rnn_r) {
     Carve c(ws);
     const size_t n = size_t(B) * p.nchunk;
     DraftWork w{};
@@ -708,6 +739,11 @@ DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes) {
     w.pb = c.take<float>(n);
     w.p2 = c.take<float>(n);
     w.pi = c.take<int32_t>(n);
+    if (rnn_r > 0) {
+        w.rnn_s[0] = c.take<float>(size_t(B) * rnn_r);
+        w.rnn_s[1] = c.take<float>(size_t(B) * rnn_r);
+        w.rnn_idx = c.take<int32_t>(B);
+    }
     if (bytes) *bytes = c.off + 256;
     return w;
 }

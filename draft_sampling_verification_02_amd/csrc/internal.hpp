@@ -62,8 +62,11 @@ DraftPlan tile_walk_plan(int B, int V, int nw_max, long long target_blocks, int 
 struct DraftWork {
     float *pm, *ps, *pb, *p2;  // [B, nchunk] partial max, sum, best score, second score
     int32_t *pi;               // [B, nchunk] partial best index
+    float *rnn_s[2];           // RNN head: [B, r] states of alternate positions
+    int32_t *rnn_idx;          // RNN head: [B] the draft step's row of e_out for request b (b * gamma)
 };
-DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes);
+// rnn_r > 0 also carves the RNN head's buffers for rank rnn_r.
+DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rnn_r = 0);
 
 struct DraftArgs {
     const float *U;
@@ -80,7 +83,30 @@ struct DraftArgs {
     const float *conf_w;  // [d + r]
     int d;
     float *conf_out, *surv_out;  // [B, gamma] c_k and a_k
+    // RNN head (bf16 weights only); Wgco == nullptr: the Markov head
+    const void *Wgco;      // [3r, 2r + rnn_d]
+    const float *rnn_h;    // [B, gamma, rnn_d]
+    int rnn_d;
+    uint16_t *e_out;       // [B, gamma, r] the rows e_k fed to the W2 product
+    float *state_out;      // [B, r] s_gamma, or nullptr
 };
+
+// One position of the RNN head: s_out, e_out from s_in (nullptr: s_0 = 0),
+// x_{k-1}, h_k, W1 and Wgco.
+struct RnnGateArgs {
+    const float *s_in;
+    float *s_out;
+    const int32_t *xprev;
+    int xprev_stride;
+    const float *h;
+    size_t h_stride;
+    const uint16_t *W1, *Wgco;
+    uint16_t *e_out;
+    size_t e_stride;
+    int32_t *idx_out;
+    int gamma, B, V, r, d;
+};
+hipError_t launch_rnn_gate(const RnnGateArgs &a, hipStream_t s);
 hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork &w, hipStream_t s);
 // The bias product alone: rowmax[b] = max_v W1[idx[b]] . W2[v] (diagnostic).
 hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,
@@ -136,6 +162,7 @@ struct VerifyArgs {
     uint32_t key0, key1, round32;
     int32_t *n_accept_out, *tokens_out, *out_offsets;
     float *diag_out, *resid_out;
+    int erow_mode;  // 0: q_k from W1[x_{k-1}]; 1: W1 holds the head's rows [B, gamma, r]
 };
 hipError_t launch_verify(const VerifyArgs &a, const VerifyPlan &p, const VerifyWork &w, hipStream_t s);
 
@@ -168,6 +195,7 @@ struct AcceptArgs {
     const float *lse_q, *temperature;
     int B, gamma, V, r;
     float *alpha_out;
+    int erow_mode;  // as for VerifyArgs
 };
 hipError_t launch_accept(const AcceptArgs &a, const AcceptPlan &p, const AcceptWork &w, hipStream_t s);
 

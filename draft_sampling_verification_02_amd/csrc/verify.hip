@@ -212,6 +212,7 @@ struct PassParams {
     int32_t *pi_out;
     int32_t *status, *mode, *jpos, *slot, *draw_list, *prev;
     float *fin_lse2, *lse2q;
+    int erow_mode;  // 1: the residual's head row is row b * gamma + k - 1 of W1 (the head's rows)
     const int32_t *anchor;
     const float *lse_q;
     int32_t *n_accept_out, *tokens_out;
@@ -272,7 +273,8 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
         p.slot[b] = e;
         p.mode[b] = kModeResidual;
         // what the residual draw needs to rebuild q_k
-        p.prev[b] = min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
+        p.prev[b] = p.erow_mode ? b * p.gamma + k - 1
+                                : min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
         p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + k - 1] * kLog2e;
     }
     return false;
@@ -964,6 +966,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.draw_list = w.draw_list;
         pp.fin_lse2 = w.fin_lse2;
         pp.prev = w.prev;
+        pp.erow_mode = a.erow_mode;
         pp.lse2q = w.lse2q;
         pp.anchor = a.anchor;
         pp.lse_q = a.lse_q;

@@ -5,7 +5,8 @@
  * Sources (page title -- section):
  *  [MG] "DSpark：DeepSeek 线上跑的投机解码，半自回归 + 置信度调度怎么做到的"
  *       (marsggbo.github.io): 3.2 Sequential Stage -- Markov head
- *       B_k = W2(W1[x_{k-1}]) and the left-to-right sampling loop;
+ *       B_k = W2(W1[x_{k-1}]), the RNN head, and the left-to-right sampling
+ *       loop;
  *       4.1 Confidence Head -- c_k from [h_k, W1[x_{k-1}]], acceptance
  *       probability 1 - TV; 4.2 -- survival products;
  *       4.3 Hardware-Aware Prefix Scheduler -- a_{r,j}, B, tau, Theta, greedy
@@ -154,6 +155,42 @@ int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W
                                    float *conf_out, float *survival_out,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace dspark_draft_sample_rnn needs; 0 for invalid
+ * sizes. */
+size_t dspark_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d);
+
+/* Draft sampling with the RNN head ([MG] 3.2, RNN Head) in place of the
+ * Markov head: a recurrent state s_k over the block, s_0 = 0.  For every
+ * request b and k = 1..gamma, with x_0 = anchor[b]:
+ *   z   = [s_{k-1}, W1[x_{k-1}], h_k]                       (2r + d entries)
+ *   g   = sigmoid(Wgco[0:r] z),  c = tanh(Wgco[r:2r] z),  o = Wgco[2r:3r] z
+ *   s_k = g * s_{k-1} + (1 - g) * c,   e_k = tanh(o)
+ *   z_k = (U[b, k-1, :] + e_k . W2^T) / T_b, and x_k drawn from it exactly as
+ *   dspark_draft_sample draws (same streams, same outputs).
+ * The head's products take bfloat16 operands: s_{k-1} and h_k are rounded to
+ * bfloat16 (nearest, ties to even) where they enter the gate product, and e_k
+ * is rounded to bfloat16 before the W2 product; s_k is kept in float32.
+ *
+ *   Wgco        device [3r, 2r + d] bfloat16 (nn.Linear weight layout: row j
+ *               holds the weights of gate output j; rows 0..r-1 gate,
+ *               r..2r-1 candidate, 2r..3r-1 output; columns in z's order)
+ *   hidden      device [B, gamma, d] float32: h_k of request b at row
+ *               b * gamma + k - 1 (may be NULL when d = 0); 16-byte aligned
+ *   d           0 .. DSPARK_MAX_HIDDEN, a multiple of 32
+ *   e_out       device [B, gamma, r] bfloat16, 16-byte aligned: the rows e_k
+ *               the W2 product used -- what dspark_verify_rnn and
+ *               dspark_acceptance_rnn need to rebuild q_k
+ *   state_out   device [B, r] float32 or NULL: s_gamma
+ *   workspace   device, >= dspark_draft_rnn_workspace_size bytes
+ *   every other argument: as for dspark_draft_sample; wdtype must be
+ *   DSPARK_BF16 (DSPARK_F32 returns DSPARK_ERR_UNSUPPORTED). */
+int dspark_draft_sample_rnn(const float *U, const void *W1, const void *W2, const void *Wgco, int wdtype,
+                            const int32_t *anchor, const float *temperature, const float *hidden, int d,
+                            int B, int gamma, int V, int r, uint64_t seed, uint64_t round_id,
+                            int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                            void *e_out, float *state_out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Verify half ([CE] 02, 05; [MG] 1, 4.1)                              */
 /* ------------------------------------------------------------------ */
@@ -212,6 +249,20 @@ int dspark_verify(const float *target, int n_target_rows, const int32_t *ell,
  * `workspace` (DSPARK_ERR_HIP if the copy fails). */
 int dspark_verify_check(const void *workspace, void *stream);
 
+/* dspark_verify for drafts of the RNN head: q_k is rebuilt from the head's
+ * rows e_k (head_rows, the e_out of dspark_draft_sample_rnn, [B, gamma, r]
+ * of `wdtype`, 16-byte aligned) instead of W1[x_{k-1}].  Arguments, outputs,
+ * workspace and device checks as for dspark_verify. */
+int dspark_verify_rnn(const float *target, int n_target_rows, const int32_t *ell,
+                      const int32_t *row_offsets,
+                      const float *U, const void *head_rows, const void *W2, int wdtype,
+                      const int32_t *anchor, const int32_t *x, const float *lse_q, const float *qx,
+                      const float *temperature, int B, int gamma, int V, int r,
+                      uint64_t seed, uint64_t round_id,
+                      int32_t *n_accept_out, int32_t *tokens_out, int32_t *out_offsets,
+                      float *diag_out, float *resid_out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Per-position acceptance probability ([MG] 4.1; [CE] 05)             */
 /* ------------------------------------------------------------------ */
@@ -244,6 +295,15 @@ int dspark_acceptance(const float *target, int n_target_rows, const int32_t *ell
                       const int32_t *anchor, const int32_t *x, const float *lse_q,
                       const float *temperature, int B, int gamma, int V, int r,
                       float *alpha_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* dspark_acceptance for drafts of the RNN head: q_k from head_rows as in
+ * dspark_verify_rnn. */
+int dspark_acceptance_rnn(const float *target, int n_target_rows, const int32_t *ell,
+                          const int32_t *row_offsets,
+                          const float *U, const void *head_rows, const void *W2, int wdtype,
+                          const int32_t *anchor, const int32_t *x, const float *lse_q,
+                          const float *temperature, int B, int gamma, int V, int r,
+                          float *alpha_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Host scheduler ([MG] 4.3; [CE] 04)                                  */

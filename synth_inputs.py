@@ -16,6 +16,9 @@ so any request's rows can be regenerated on their own):
   anchor [B]         ~ uniform [0, V)  seed (seed, 4).
   c [B, gamma]       ~ Beta(8, 2)     seed (seed, 5)   (scheduled config).
   temperature [B]    1.0, or 0.0 (greedy) for b % greedy_every == 0.
+  RNN head (rnn_head_weights): Wgco [3r, 2r + d] ~ N(0, (2r + d)^-1/2),
+                     seed (seed, 9), rounded to bfloat16; it reads the same
+                     h as the confidence head.
   Confidence head (confidence_head_inputs; d defaults to 1024):
   h[b, k] [d]        ~ N(1, 1)        seed (seed, 6, b, k)
   w [d + r]          first d ~ N(1.4 / d, 0.5 / d), seed (seed, 7); last r
@@ -33,7 +36,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = ["Config", "CONFIGS", "Round", "make_round", "bf16_round", "bf16_bits_to_f32",
-           "sps_table_toy", "pack_offsets", "confidence_head_inputs", "DEFAULT_HIDDEN"]
+           "sps_table_toy", "pack_offsets", "confidence_head_inputs", "rnn_head_weights",
+           "DEFAULT_HIDDEN"]
 
 DEFAULT_HIDDEN = 1024
 
@@ -230,3 +234,12 @@ def confidence_head_inputs(cfg: Config, d: int = DEFAULT_HIDDEN, requests=None):
         w[:d] = _normal((cfg.seed, 7), d, np.sqrt(0.5 / d)) + np.float32(1.4 / d)
     w[d:] = _normal((cfg.seed, 8), cfg.r, np.sqrt(0.5 / (cfg.r * cfg.w_std ** 2)))
     return h, w
+
+
+def rnn_head_weights(cfg: Config, d: int = DEFAULT_HIDDEN):
+    """(Wgco bfloat16 bits [3r, 2r + d] uint16, their float32 values) for the
+    RNN head of ``cfg``."""
+    K = 2 * cfg.r + d
+    w = _normal((cfg.seed, 9), 3 * cfg.r * K, 1.0 / np.sqrt(K)).reshape(3 * cfg.r, K)
+    bits = bf16_round(w)
+    return bits, bf16_bits_to_f32(bits)

@@ -178,3 +178,47 @@ def test_acceptance_argument_errors_need_no_gpu():
     assert call(W1=ctypes.c_void_p(0x1002)) == ds.DSPARK_ERR_ARG
     assert call(ws_bytes=100) == ds.DSPARK_ERR_WORKSPACE
     assert call(ws=None) == ds.DSPARK_ERR_WORKSPACE
+
+
+def test_rnn_argument_errors_need_no_gpu():
+    lib = ds.load_library()
+    assert ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, 1024) > ds.dspark_draft_workspace_size(256, 5, 129280, 256)
+    assert ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, -1) == 0
+
+    def call(**kw):
+        a = dict(U=_FAKE, W1=_FAKE, W2=_FAKE, Wgco=_FAKE, wdtype=0, anchor=_FAKE, temperature=_FAKE, hidden=_FAKE,
+                 d=64, B=4, gamma=5, V=1000, r=16, seed=1, round_id=0, x=_FAKE, lse=_FAKE, qx=_FAKE, margin=None,
+                 e=_FAKE, state=None, ws=_FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.dspark_draft_sample_rnn(
+            a["U"], a["W1"], a["W2"], a["Wgco"], a["wdtype"], a["anchor"], a["temperature"], a["hidden"], a["d"],
+            a["B"], a["gamma"], a["V"], a["r"], a["seed"], a["round_id"], a["x"], a["lse"], a["qx"], a["margin"],
+            a["e"], a["state"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(Wgco=None) == ds.DSPARK_ERR_ARG
+    assert call(e=None) == ds.DSPARK_ERR_ARG
+    assert call(hidden=None) == ds.DSPARK_ERR_ARG
+    assert call(d=-32) == ds.DSPARK_ERR_ARG
+    assert call(d=48) == ds.DSPARK_ERR_UNSUPPORTED  # not a multiple of 32
+    assert call(wdtype=1) == ds.DSPARK_ERR_UNSUPPORTED  # bfloat16 weights only
+    assert call(r=24) == ds.DSPARK_ERR_UNSUPPORTED
+    assert call(hidden=ctypes.c_void_p(0x1004)) == ds.DSPARK_ERR_ARG
+    assert call(e=ctypes.c_void_p(0x1002)) == ds.DSPARK_ERR_ARG
+    assert call(ws_bytes=64) == ds.DSPARK_ERR_WORKSPACE
+
+    def vcall(**kw):
+        a = dict(target=_FAKE, rows=24, ell=_FAKE, off=None, U=_FAKE, E=_FAKE, W2=_FAKE, wdtype=0, anchor=_FAKE,
+                 x=_FAKE, lse=_FAKE, qx=_FAKE, temperature=_FAKE, B=4, gamma=5, V=1000, r=16, seed=1, round_id=0,
+                 n=_FAKE, tokens=_FAKE, offsets=None, diag=None, resid=None, ws=_FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.dspark_verify_rnn(a["target"], a["rows"], a["ell"], a["off"], a["U"], a["E"], a["W2"],
+                                     a["wdtype"], a["anchor"], a["x"], a["lse"], a["qx"], a["temperature"], a["B"],
+                                     a["gamma"], a["V"], a["r"], a["seed"], a["round_id"], a["n"], a["tokens"],
+                                     a["offsets"], a["diag"], a["resid"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert vcall(E=None) == ds.DSPARK_ERR_ARG
+    assert vcall(E=ctypes.c_void_p(0x1008)) == ds.DSPARK_ERR_ARG
+    assert vcall(ws_bytes=8) == ds.DSPARK_ERR_WORKSPACE
+    st = lib.dspark_acceptance_rnn(_FAKE, 24, _FAKE, None, _FAKE, None, _FAKE, 0, _FAKE, _FAKE, _FAKE, _FAKE,
+                                   4, 5, 1000, 16, _FAKE, _FAKE, 1 << 30, None)
+    assert st == ds.DSPARK_ERR_ARG
