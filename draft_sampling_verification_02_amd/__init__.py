@@ -69,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_draft_sample_confidence": ([_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
                                             _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
-                                            _c_void_p, _c_void_p, _c_int,
+                                            _c_void_p, _c_void_p, _c_int, _c_void_p,
                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                             _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_draft_rnn_workspace_size": ([_c_int] * 5, _c_size),
@@ -77,6 +77,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_sts_workspace_size": ([_c_int] * 4, _c_size),
+        "dspark_sts_fit": ([_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p, _c_int, _c_int,
+                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_verify_workspace_size": ([_c_int] * 4, _c_size),
         "dspark_verify": ([_c_void_p, _c_int, _c_void_p, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_int,
@@ -248,12 +251,13 @@ def dspark_draft_sample(U, W1, W2, anchor, temperature, seed: int, round_id: int
 
 
 def dspark_draft_sample_confidence(U, W1, W2, anchor, temperature, hidden, conf_w, seed: int, round_id: int, *,
-                                   margin: bool = False, out: dict | None = None, workspace=None,
+                                   conf_tau=None, margin: bool = False, out: dict | None = None, workspace=None,
                                    stream=None) -> dict:
     """dspark_draft_sample plus the confidence head c_k = sigmoid(conf_w .
-    [h_k, W1[x_{k-1}]]) and the survival products a_k = c_1...c_k.  hidden
-    [B, gamma, d] float32 (d may be 0), conf_w [d + r] float32.  Returns the
-    draft outputs plus {"conf", "survival"}."""
+    [h_k, W1[x_{k-1}]] / tau_k) and the survival products a_k = c_1...c_k.
+    hidden [B, gamma, d] float32 (d may be 0), conf_w [d + r] float32,
+    conf_tau [gamma] float32 or None (tau = 1; dspark_sts_fit's output).
+    Returns the draft outputs plus {"conf", "survival"}."""
     torch = _torch()
     lib = load_library()
     dev, B, gamma, V, r, wdt = _draft_inputs(U, W1, W2, anchor, temperature)
@@ -262,6 +266,8 @@ def dspark_draft_sample_confidence(U, W1, W2, anchor, temperature, hidden, conf_
     d = hidden.shape[2]
     _need(hidden, "hidden", torch.float32, (B, gamma, d), dev)
     _need(conf_w, "conf_w", torch.float32, (d + r,), dev)
+    if conf_tau is not None:
+        _need(conf_tau, "conf_tau", torch.float32, (gamma,), dev)
     out = _draft_outputs(B, gamma, dev, margin, True, out)
     nbytes = lib.dspark_draft_workspace_size(B, gamma, V, r)
     if nbytes == 0:
@@ -270,7 +276,7 @@ def dspark_draft_sample_confidence(U, W1, W2, anchor, temperature, hidden, conf_
     out["workspace"] = ws
     st = lib.dspark_draft_sample_confidence(
         _ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(temperature), B, gamma, V, r, int(seed),
-        int(round_id), _ptr(hidden) if d > 0 else None, _ptr(conf_w), d,
+        int(round_id), _ptr(hidden) if d > 0 else None, _ptr(conf_w), d, _ptr(conf_tau),
         _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")),
         _ptr(out["conf"]), _ptr(out["survival"]), _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st, "dspark_draft_sample_confidence")
@@ -434,6 +440,41 @@ def _acceptance(target, ell, U, W1, W2, anchor, x, lse_q, temperature, rows, row
             _ptr(U), _ptr(W1 if rows is None else rows), _ptr(W2), wdt, _ptr(anchor), _ptr(x), _ptr(lse_q),
             _ptr(temperature), B, gamma, V, r, _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st, "dspark_acceptance" if rows is None else "dspark_acceptance_rnn")
+    return out
+
+
+def dspark_sts_workspace_size(N: int, gamma: int, G: int, n_bins: int) -> int:
+    return load_library().dspark_sts_workspace_size(N, gamma, G, n_bins)
+
+
+def dspark_sts_fit(conf, n_accept, grid, *, ell=None, n_bins: int = 15, ece_grid: bool = False, workspace=None,
+                   stream=None) -> dict:
+    """Sequential temperature scaling of the confidence head from N observed
+    rounds: conf [N, gamma] float32 (raw head, tau = 1), n_accept [N] int32,
+    grid [G] float32 temperatures, ell [N] int32 or None (gamma).  Returns
+    {"tau" [gamma], "ece" [gamma][, "ece_grid" [gamma, G]]} (device)."""
+    torch = _torch()
+    lib = load_library()
+    dev = conf.device
+    N, gamma = conf.shape
+    _need(conf, "conf", torch.float32, (N, gamma), dev)
+    _need(n_accept, "n_accept", torch.int32, (N,), dev)
+    if ell is not None:
+        _need(ell, "ell", torch.int32, (N,), dev)
+    G = grid.shape[0]
+    _need(grid, "grid", torch.float32, (G,), dev)
+    out = {"tau": torch.empty(gamma, dtype=torch.float32, device=dev),
+           "ece": torch.empty(gamma, dtype=torch.float32, device=dev)}
+    if ece_grid:
+        out["ece_grid"] = torch.empty((gamma, G), dtype=torch.float32, device=dev)
+    nbytes = lib.dspark_sts_workspace_size(N, gamma, G, n_bins)
+    if nbytes == 0:
+        raise DSparkError(DSPARK_ERR_ARG, "dspark_sts_workspace_size")
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib.dspark_sts_fit(_ptr(conf), _ptr(n_accept), _ptr(ell), N, gamma, _ptr(grid), G, n_bins,
+                            _ptr(out["tau"]), _ptr(out["ece"]), _ptr(out.get("ece_grid")), _ptr(ws), ws.numel(),
+                            _stream_ptr(stream))
+    _check(st, "dspark_sts_fit")
     return out
 
 

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdspark.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "schedule.cpp", "draft.hip", "verify.hip", "accept.hip", "rnn.hip", "debug.hip"]
+SOURCES = ["api.cpp", "schedule.cpp", "draft.hip", "verify.hip", "accept.hip", "rnn.hip", "sts.hip", "debug.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
     "-Wno-unused-parameter", "-Wno-cuda-compat",

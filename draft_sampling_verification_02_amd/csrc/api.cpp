@@ -139,9 +139,9 @@ namespace {
 
 int draft_common(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
                  const float *temperature, int B, int gamma, int V, int r, uint64_t seed, uint64_t round_id,
-                 const float *hidden, const float *conf_w, int d, int32_t *x_out, float *lse_out, float *qx_out,
-                 float *margin_out, float *conf_out, float *survival_out, void *workspace, size_t workspace_bytes,
-                 void *stream) {
+                 const float *hidden, const float *conf_w, int d, const float *conf_tau, int32_t *x_out,
+                 float *lse_out, float *qx_out, float *margin_out, float *conf_out, float *survival_out,
+                 void *workspace, size_t workspace_bytes, void *stream) {
     if (!U || !W1 || !W2 || !anchor || !temperature || !x_out || !lse_out || !qx_out) return DSPARK_ERR_ARG;
     if (!sizes_ok(B, gamma, V, r)) return DSPARK_ERR_ARG;
     if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
@@ -173,6 +173,7 @@ int draft_common(const float *U, const void *W1, const void *W2, int wdtype, con
     a.hidden = hidden;
     a.conf_w = conf_w;
     a.d = d;
+    a.conf_tau = conf_tau;
     a.conf_out = conf_out;
     a.surv_out = survival_out;
     const hipError_t e = launch_draft(a, plan, w, static_cast<hipStream_t>(stream));
@@ -188,20 +189,22 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
                         uint64_t round_id, int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
                         void *workspace, size_t workspace_bytes, void *stream) {
     return draft_common(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, seed, round_id, nullptr, nullptr, 0,
-                        x_out, lse_out, qx_out, margin_out, nullptr, nullptr, workspace, workspace_bytes, stream);
+                        nullptr, x_out, lse_out, qx_out, margin_out, nullptr, nullptr, workspace, workspace_bytes,
+                        stream);
 }
 
 int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W2, int wdtype,
                                    const int32_t *anchor, const float *temperature, int B, int gamma, int V, int r,
                                    uint64_t seed, uint64_t round_id, const float *hidden, const float *conf_w, int d,
-                                   int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                                   const float *conf_tau, int32_t *x_out, float *lse_out, float *qx_out,
+                                   float *margin_out,
                                    float *conf_out, float *survival_out, void *workspace, size_t workspace_bytes,
                                    void *stream) {
     if (d < 0 || d > DSPARK_MAX_HIDDEN || (d > 0 && !hidden) || !conf_w || !conf_out || !survival_out)
         return DSPARK_ERR_ARG;
     return draft_common(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, seed, round_id, hidden, conf_w, d,
-                        x_out, lse_out, qx_out, margin_out, conf_out, survival_out, workspace, workspace_bytes,
-                        stream);
+                        conf_tau, x_out, lse_out, qx_out, margin_out, conf_out, survival_out, workspace,
+                        workspace_bytes, stream);
 }
 
 size_t dspark_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d) {
@@ -255,6 +258,42 @@ int dspark_draft_sample_rnn(const float *U, const void *W1, const void *W2, cons
     a.e_out = static_cast<uint16_t *>(e_out);
     a.state_out = state_out;
     const hipError_t e = launch_draft(a, plan, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
+}
+
+size_t dspark_sts_workspace_size(int N, int gamma, int G, int n_bins) {
+    if (N < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || G < 1 || n_bins < 1 || G > DSPARK_MAX_STS_GRID ||
+        G * n_bins > DSPARK_MAX_STS_CELLS)
+        return 0;
+    size_t bytes = 0;
+    sts_carve(nullptr, N, gamma, G, n_bins, &bytes);
+    return bytes;
+}
+
+int dspark_sts_fit(const float *c, const int32_t *n_accept, const int32_t *ell, int N, int gamma, const float *grid,
+                   int G, int n_bins, float *tau_out, float *ece_out, float *ece_grid_out, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    if (!c || !n_accept || !grid || !tau_out || !ece_out) return DSPARK_ERR_ARG;
+    if (N < 1 || N > DSPARK_MAX_STS_SAMPLES || gamma < 1 || gamma > DSPARK_MAX_GAMMA || G < 1 || n_bins < 1 ||
+        G > DSPARK_MAX_STS_GRID || G * n_bins > DSPARK_MAX_STS_CELLS)
+        return DSPARK_ERR_ARG;
+    size_t need = 0;
+    sts_carve(nullptr, N, gamma, G, n_bins, &need);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
+    const StsWork w = sts_carve(workspace, N, gamma, G, n_bins, nullptr);
+    StsArgs a{};
+    a.c = c;
+    a.n = n_accept;
+    a.ell = ell;
+    a.N = N;
+    a.gamma = gamma;
+    a.grid = grid;
+    a.G = G;
+    a.M = n_bins;
+    a.tau_out = tau_out;
+    a.ece_out = ece_out;
+    a.ece_grid = ece_grid_out;
+    const hipError_t e = launch_sts(a, sts_plan(N, gamma, G, n_bins), w, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP;
 }
 

@@ -210,6 +210,7 @@ struct ReduceParams {
     size_t h_stride;
     const float *conf_w;  // [d + r]: the h_k part, then the W1[x_{k-1}] part
     int d, hvec;          // hvec: h rows and conf_w allow aligned 16-byte loads
+    const float *conf_tau;  // [gamma] temperatures of the head's logit, or nullptr (1)
     float *conf_out, *surv_out;
 };
 
@@ -294,9 +295,10 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     __builtin_amdgcn_sched_barrier(0);  // keep the batch ahead of the dependent W1 fetch
     int prev = p.xprev[size_t(b) * p.xprev_stride];
     const float T = p.temperature[b];
-    float conf_s = 0.f, a_prev = 1.f;
+    float conf_s = 0.f, a_prev = 1.f, conf_t = 1.f;
     if constexpr (CONF) {
         if (p.k > 1) a_prev = p.surv_out[size_t(b) * p.gamma + p.k - 2];
+        if (p.conf_tau) conf_t = p.conf_tau[p.k - 1];
         if (p.d > 0) conf_s = conf_hidden_part(p, b, lane);
     }
     prev = min(max(prev, 0), p.erows - 1);
@@ -363,7 +365,7 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
         const size_t o = size_t(b) * p.gamma + (p.k - 1);
         p.x_out[o] = x;
         if constexpr (CONF) {
-            const float c = 1.0f / (1.0f + __expf(-conf_s));
+            const float c = 1.0f / (1.0f + __expf(-conf_s / conf_t));
             p.conf_out[o] = c;
             p.surv_out[o] = a_prev * c;
         }
@@ -695,6 +697,7 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
             rp.conf_w = a.conf_w;
             rp.d = a.d;
             rp.hvec = hvec;
+            rp.conf_tau = a.conf_tau;
             rp.conf_out = a.conf_out;
             rp.surv_out = a.surv_out;
             launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, true>), dim3((a.B + 3) / 4), dim3(256), s, rp);

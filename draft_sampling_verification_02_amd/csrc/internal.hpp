@@ -82,6 +82,7 @@ struct DraftArgs {
     const float *hidden;  // [B, gamma, d]
     const float *conf_w;  // [d + r]
     int d;
+    const float *conf_tau;       // [gamma] temperatures of the head's logits, or nullptr (1)
     float *conf_out, *surv_out;  // [B, gamma] c_k and a_k
     // RNN head (bf16 weights only); Wgco == nullptr: the Markov head
     const void *Wgco;      // [3r, 2r + rnn_d]
@@ -198,6 +199,32 @@ struct AcceptArgs {
     int erow_mode;  // as for VerifyArgs
 };
 hipError_t launch_accept(const AcceptArgs &a, const AcceptPlan &p, const AcceptWork &w, hipStream_t s);
+
+// ---- sequential temperature scaling ------------------------------------
+
+struct StsPlan {
+    int blocks;   // histogram workgroups: one per 256 samples
+    size_t lds;   // dynamic LDS of a histogram workgroup
+};
+StsPlan sts_plan(int N, int gamma, int G, int M);
+
+struct StsWork {
+    float *a;                   // [N] calibrated prefix survival of each sample
+    unsigned long long *acc_p;  // [gamma, G, M] sum of a' in 2^-32 fixed point
+    uint32_t *acc_y;            // [gamma, G, M] outcome counts
+    uint32_t *acc_n;            // [gamma] samples that verified each position
+};
+StsWork sts_carve(void *ws, int N, int gamma, int G, int M, size_t *bytes);
+
+struct StsArgs {
+    const float *c;
+    const int32_t *n, *ell;
+    int N, gamma;
+    const float *grid;
+    int G, M;
+    float *tau_out, *ece_out, *ece_grid;
+};
+hipError_t launch_sts(const StsArgs &a, const StsPlan &p, const StsWork &w, hipStream_t s);
 
 // ---- diagnostics -----------------------------------------------------
 

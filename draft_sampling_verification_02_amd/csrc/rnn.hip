@@ -59,17 +59,21 @@ __device__ __forceinline__ uint4 pack8(const float4 &a, const float4 &b) {
 }
 
 // entries kk .. kk + 7 of z for request b (kk a multiple of 8, so the eight
-// lie in one of the three parts)
+// lie in one of the three parts).  Both loads are issued whatever the part
+// (the float32 one from a valid stand-in address when the part is W1's, or
+// s_0 = 0), and the part is selected after: loads inside branches would make
+// the compiler wait for them at every join.
 template <int R>
 __device__ __forceinline__ uint4 z8(const GateParams &p, int b, int prev, int kk) {
-    if (kk < R) {
-        if (!p.s_in) return make_uint4(0u, 0u, 0u, 0u);
-        const float4 *q = reinterpret_cast<const float4 *>(p.s_in + size_t(b) * R + kk);
-        return pack8(q[0], q[1]);
-    }
-    if (kk < 2 * R) return *reinterpret_cast<const uint4 *>(p.W1 + size_t(prev) * R + (kk - R));
-    const float4 *q = reinterpret_cast<const float4 *>(p.h + size_t(b) * p.h_stride + (kk - 2 * R));
-    return pack8(q[0], q[1]);
+    const uint16_t *w1row = p.W1 + size_t(prev) * R;
+    const bool in_s = kk < R, in_w1 = !in_s && kk < 2 * R;
+    const float *stand_in = reinterpret_cast<const float *>(w1row);  // 2R >= 32 bytes
+    const float *fsrc = in_s ? (p.s_in ? p.s_in + size_t(b) * R + kk : stand_in)
+                             : (in_w1 ? stand_in : p.h + size_t(b) * p.h_stride + (kk - 2 * R));
+    const uint4 w = *reinterpret_cast<const uint4 *>(w1row + min(max(kk - R, 0), R - 8));
+    const float4 f0 = reinterpret_cast<const float4 *>(fsrc)[0], f1 = reinterpret_cast<const float4 *>(fsrc)[1];
+    const uint4 z = in_w1 ? w : pack8(f0, f1);
+    return (in_s && !p.s_in) ? make_uint4(0u, 0u, 0u, 0u) : z;
 }
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, const f32x4_t &c) {

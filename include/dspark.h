@@ -79,6 +79,9 @@ typedef enum dspark_dtype {
 #define DSPARK_MAX_BATCH 65536
 #define DSPARK_MAX_VOCAB 16777215
 #define DSPARK_MAX_HIDDEN 65536 /* d of the confidence head */
+#define DSPARK_MAX_STS_SAMPLES (1 << 28) /* samples of one calibration fit */
+#define DSPARK_MAX_STS_CELLS 4096        /* grid values x bins of one fit */
+#define DSPARK_MAX_STS_GRID 1024         /* grid values of one fit */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int dspark_version(void);
@@ -130,7 +133,7 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
 /* dspark_draft_sample plus the confidence head of every position ([MG] 4.1
  * Confidence Head; [MG] 4.2 and [CE] 04 for the survival products): with
  * x_0 = anchor and the drafts this call samples,
- *   c_k = 1 / (1 + exp(-(w[0..d) . h_k + w[d..d+r) . W1[x_{k-1}])))
+ *   c_k = 1 / (1 + exp(-(w[0..d) . h_k + w[d..d+r) . W1[x_{k-1}]) / tau_k))
  * -- a bias-free linear layer over the concatenation [h_k, W1[x_{k-1}]] and
  * a sigmoid -- and a_k = c_1 * ... * c_k, the estimated probability that
  * drafts 1..k all survive verification.  The sampling outputs are the same
@@ -141,6 +144,8 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
  *   conf_w        device [d + r] float32: the head's weights, the h_k part
  *                 first
  *   d             0 .. DSPARK_MAX_HIDDEN
+ *   conf_tau      device [gamma] float32 or NULL: the head's per-position
+ *                 temperatures tau_k (those dspark_sts_fit chooses; NULL = 1)
  *   conf_out      device [B, gamma] float32: c_k
  *   survival_out  device [B, gamma] float32: a_k
  *   every other argument: as for dspark_draft_sample (same workspace size).
@@ -150,7 +155,7 @@ int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W
                                    const int32_t *anchor, const float *temperature,
                                    int B, int gamma, int V, int r,
                                    uint64_t seed, uint64_t round_id,
-                                   const float *hidden, const float *conf_w, int d,
+                                   const float *hidden, const float *conf_w, int d, const float *conf_tau,
                                    int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
                                    float *conf_out, float *survival_out,
                                    void *workspace, size_t workspace_bytes, void *stream);
@@ -190,6 +195,41 @@ int dspark_draft_sample_rnn(const float *U, const void *W1, const void *W2, cons
                             int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
                             void *e_out, float *state_out,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Sequential temperature scaling of the confidences ([MG] 4.2)        */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of device workspace dspark_sts_fit needs; 0 for invalid sizes. */
+size_t dspark_sts_workspace_size(int N, int gamma, int G, int n_bins);
+
+/* Calibrates the confidence head from N observed rounds, left to right: for
+ * k = 1..gamma, with the temperatures of positions < k fixed, tau_k is the
+ * first grid value that minimises
+ *   ECE_k(tau) = sum over n_bins equal-width bins of |sum y - sum a'| / N_k,
+ *   a'_k = c'_1 ... c'_k,  c'_i = 1 / (1 + exp(-logit(c_i) / tau_i)),
+ *   y_k = 1 if sample n accepted drafts 1..k (n_accept >= k), else 0,
+ * over the N_k samples that verified position k (ell >= k); a' falls in bin
+ * min(floor(a' n_bins), n_bins - 1).  Temperature scaling keeps the drafts'
+ * order (tau > 0).  A position that no sample verified keeps tau_k = 1 and
+ * gets ECE NaN; grid values <= 0 are never chosen.  The sums over samples
+ * are exact integer sums (a' in 2^-32 fixed point), so results do not depend
+ * on the order the GPU adds them in.
+ *
+ *   c            device [N, gamma] float32: the head's confidences (raw, tau = 1)
+ *   n_accept     device [N] int32: accepted drafts of the sample's round
+ *   ell          device [N] int32 or NULL (= gamma): verified positions
+ *   grid         device [G] float32: candidate temperatures
+ *   N            1 .. DSPARK_MAX_STS_SAMPLES
+ *   G, n_bins    >= 1, G <= DSPARK_MAX_STS_GRID, G * n_bins <= DSPARK_MAX_STS_CELLS
+ *   tau_out      device [gamma] float32 (feed it to the head's conf_tau)
+ *   ece_out      device [gamma] float32: the ECE at the chosen tau_k
+ *   ece_grid_out device [gamma, G] float32 or NULL: every grid value's ECE
+ *                (+inf for grid values <= 0)
+ *   workspace    device, >= dspark_sts_workspace_size bytes */
+int dspark_sts_fit(const float *c, const int32_t *n_accept, const int32_t *ell, int N, int gamma,
+                   const float *grid, int G, int n_bins, float *tau_out, float *ece_out,
+                   float *ece_grid_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Verify half ([CE] 02, 05; [MG] 1, 4.1)                              */

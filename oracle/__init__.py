@@ -44,7 +44,7 @@ def _load():
                                ctypes.c_uint64, ctypes.c_uint64,
                                _i32p, _i32p, _f64p, _f64p, _f64p, _f64p]
     lib.orc_verify.restype = ctypes.c_int
-    lib.orc_confidence.argtypes = [_f32p, _f32p, _f32p, _i32p, _i32p,
+    lib.orc_confidence.argtypes = [_f32p, _f32p, _f32p, _i32p, _i32p, _f32p,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
     lib.orc_confidence.restype = ctypes.c_int
     lib.orc_acceptance.argtypes = [_f32p, _i32p, _i32p, _f32p, _f32p, _f32p, _f32p, _i32p, _i32p, _f32p,
@@ -57,6 +57,9 @@ def _load():
                                   ctypes.c_uint64, ctypes.c_uint64,
                                   _i32p, _f64p, _f64p, _f64p, _f64p, _f64p]
     lib.orc_draft_rnn.restype = ctypes.c_int
+    lib.orc_sts_fit.argtypes = [_f32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, _f32p, ctypes.c_int,
+                                ctypes.c_int, _f64p, _f64p, _f64p]
+    lib.orc_sts_fit.restype = ctypes.c_int
     lib.orc_schedule.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _f64p, ctypes.c_int,
                                  _i32p, _f64p, _f64p, _i32p]
     lib.orc_schedule.restype = ctypes.c_int
@@ -206,10 +209,10 @@ def verify(target, ell, U, W1, W2, anchor, x, temperature, seed, round_id,
             "accept_margin": am, "pick_margin": pm}
 
 
-def confidence(h, w, W1, anchor, x):
+def confidence(h, w, W1, anchor, x, tau=None):
     """Confidence head and prefix survival.  h [B, gamma, d], w [d + r],
     W1 [V, r], anchor [B], drafts x [B, gamma].  Returns (c, a), both
-    [B, gamma] float64."""
+    [B, gamma] float64.  tau [gamma]: temperatures of the head's logits."""
     lib = _load()
     h = _f32(h)
     w = _f32(w)
@@ -219,10 +222,12 @@ def confidence(h, w, W1, anchor, x):
     B, gamma, d = h.shape
     r = W1.shape[1]
     assert w.shape == (d + r,) and x.shape == (B, gamma)
+    t = None if tau is None else _f32(tau)
     c = np.zeros((B, gamma), np.float64)
     a = np.zeros((B, gamma), np.float64)
     st = lib.orc_confidence(_ptr(h, ctypes.c_float), _ptr(w, ctypes.c_float), _ptr(W1, ctypes.c_float),
-                            _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32), B, gamma, d, r,
+                            _ptr(anchor, ctypes.c_int32), _ptr(x, ctypes.c_int32), _ptr(t, ctypes.c_float),
+                            B, gamma, d, r,
                             _ptr(c, ctypes.c_double), _ptr(a, ctypes.c_double))
     if st != 0:
         raise ValueError("orc_confidence: bad arguments")
@@ -254,6 +259,27 @@ def acceptance(target, ell, U, W1, W2, anchor, x, temperature, row_offsets=None,
     if st != 0:
         raise ValueError("orc_acceptance: bad arguments")
     return alpha
+
+
+def sts_fit(c, n, grid, n_bins=15, ell=None):
+    """Sequential temperature scaling.  c [N, gamma] confidences, n [N]
+    accepted counts, grid [G] temperatures, ell [N] verified lengths (None:
+    gamma).  Returns (tau [gamma], ece [gamma], ece_grid [gamma, G])."""
+    lib = _load()
+    c = _f32(c)
+    n = _i32(n)
+    grid = _f32(grid)
+    N, gamma = c.shape
+    L = None if ell is None else _i32(ell)
+    tau = np.zeros(gamma, np.float64)
+    ece = np.zeros(gamma, np.float64)
+    eg = np.zeros((gamma, len(grid)), np.float64)
+    st = lib.orc_sts_fit(_ptr(c, ctypes.c_float), _ptr(n, ctypes.c_int32), _ptr(L, ctypes.c_int32), N, gamma,
+                         _ptr(grid, ctypes.c_float), len(grid), n_bins, _ptr(tau, ctypes.c_double),
+                         _ptr(ece, ctypes.c_double), _ptr(eg, ctypes.c_double))
+    if st != 0:
+        raise ValueError("orc_sts_fit: bad arguments")
+    return tau, ece, eg
 
 
 def schedule(c, sps):

@@ -557,10 +557,12 @@ int orc_verify(const float *target, const int32_t *off, const int32_t *ell,
  *   s_k = sum_{i<d} w[i] h[b][k][i] + sum_{i<r} w[d + i] W1[x_{k-1}][i]
  *         (a bias-free linear layer over the concatenation [h_k, W1[x_{k-1}]]),
  *   c_k = 1 / (1 + exp(-s_k)),
- * and ([MG] 4.2, [CE] 04) the prefix survival a_k = c_1 * ... * c_k.
+ * and ([MG] 4.2, [CE] 04) the prefix survival a_k = c_1 * ... * c_k.  With
+ * tau (nullable, [gamma]) the head is the temperature-scaled one of [MG] 4.2:
+ * c_k = 1 / (1 + exp(-s_k / tau_k)).
  * h is [B, gamma, d], w is [d + r]; outputs are [B, gamma]. */
 int orc_confidence(const float *h, const float *w, const float *W1,
-                   const int32_t *anchor, const int32_t *x,
+                   const int32_t *anchor, const int32_t *x, const float *tau,
                    int B, int gamma, int d, int r, double *c_out, double *a_out)
 {
     if (B < 0 || gamma < 1 || d < 0 || r < 1) return ORC_ERR_ARG;
@@ -577,6 +579,7 @@ int orc_confidence(const float *h, const float *w, const float *W1,
                 s += (double)w[i] * (double)hk[i];
             for (int i = 0; i < r; ++i)
                 s += (double)w[d + i] * (double)e[i];
+            if (tau) s /= (double)tau[k - 1]; /* [MG] 4.2: the calibrated head */
             double c = 1.0 / (1.0 + exp(-s));
             a *= c;
             size_t o = (size_t)b * (size_t)gamma + (size_t)(k - 1);
@@ -644,6 +647,86 @@ int orc_acceptance(const float *target, const int32_t *off, const int32_t *ell,
     }
     free(row0);
     return status;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sequential temperature scaling of the confidences                   */
+/* ------------------------------------------------------------------ */
+
+/* [MG] 4.2: calibrate the head's confidences position by position, left to
+ * right, each with a one-dimensional grid search for the temperature that
+ * minimises the expected calibration error of the prefix survival product,
+ * the earlier positions' temperatures held fixed.  Readings:
+ *  - temperature scaling acts on the logit: c' = sigmoid(logit(c) / tau), an
+ *    order-preserving map for tau > 0;
+ *  - the calibrated quantity at position k is a'_k = c'_1 ... c'_k and its
+ *    outcome is y_k = [n >= k] (drafts 1..k all accepted), over the samples
+ *    that verified position k (ell >= k);
+ *  - ECE = sum over M equal-width bins of |sum_bin y - sum_bin a'| / N_k
+ *    (the usual weighted gap between accuracy and confidence), a' in bin
+ *    min(floor(a' M), M - 1);
+ *  - the smallest-index grid value wins ties; grid values <= 0 never win;
+ *    a position no sample verified keeps tau = 1 and ECE = NaN.
+ * c [N, gamma], n [N], ell [N] (nullable: every sample verified gamma
+ * positions).  Outputs tau [gamma], ece [gamma], ece_grid [gamma, G]
+ * (nullable; +inf for grid values <= 0). */
+int orc_sts_fit(const float *c, const int32_t *n, const int32_t *ell, int N, int gamma,
+                const float *grid, int G, int M, double *tau_out, double *ece_out, double *ece_grid)
+{
+    if (N < 0 || gamma < 1 || G < 1 || M < 1 || !c || !n || !grid || !tau_out || !ece_out) return ORC_ERR_ARG;
+    double *a = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    double *sp = (double *)malloc((size_t)M * sizeof(double));
+    double *sy = (double *)malloc((size_t)M * sizeof(double));
+    if (!a || !sp || !sy) { free(a); free(sp); free(sy); return ORC_ERR_ARG; }
+    for (int i = 0; i < N; ++i) a[i] = 1.0;
+    for (int k = 1; k <= gamma; ++k) {
+        int Nk = 0;
+        for (int i = 0; i < N; ++i) {
+            int L = ell ? ell[i] : gamma;
+            if (L >= k && L <= gamma) ++Nk;
+        }
+        double best = INFINITY, tau = 1.0;
+        for (int g = 0; g < G; ++g) {
+            double t = (double)grid[g];
+            double e = INFINITY;
+            if (t > 0.0 && Nk > 0) {
+                for (int m = 0; m < M; ++m) sp[m] = sy[m] = 0.0;
+                for (int i = 0; i < N; ++i) {
+                    int L = ell ? ell[i] : gamma;
+                    if (L < k || L > gamma) continue;
+                    double ci = (double)c[(size_t)i * (size_t)gamma + (size_t)(k - 1)];
+                    double lg = log(ci) - log1p(-ci);
+                    double p = a[i] / (1.0 + exp(-lg / t));
+                    int m = (int)floor(p * M);
+                    if (m > M - 1) m = M - 1;
+                    if (m < 0) m = 0;
+                    sp[m] += p;
+                    sy[m] += (n[i] >= k) ? 1.0 : 0.0;
+                }
+                e = 0.0;
+                for (int m = 0; m < M; ++m) e += fabs(sy[m] - sp[m]);
+                e /= (double)Nk;
+            }
+            if (ece_grid) ece_grid[(size_t)(k - 1) * (size_t)G + g] = e;
+            if (e < best) {
+                best = e;
+                tau = t;
+            }
+        }
+        if (Nk == 0 || best == INFINITY) {
+            tau = 1.0;
+            best = NAN;
+        }
+        tau_out[k - 1] = tau;
+        ece_out[k - 1] = best;
+        for (int i = 0; i < N; ++i) {
+            double ci = (double)c[(size_t)i * (size_t)gamma + (size_t)(k - 1)];
+            double lg = log(ci) - log1p(-ci);
+            a[i] = a[i] / (1.0 + exp(-lg / tau));
+        }
+    }
+    free(a); free(sp); free(sy);
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------ */

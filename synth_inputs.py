@@ -19,6 +19,10 @@ so any request's rows can be regenerated on their own):
   RNN head (rnn_head_weights): Wgco [3r, 2r + d] ~ N(0, (2r + d)^-1/2),
                      seed (seed, 9), rounded to bfloat16; it reads the same
                      h as the confidence head.
+  Calibration samples (sts_samples): true conditional logits s ~ N(0.8, 1.5)
+                     seed (seed, 10); position k survives iff k - 1 did and
+                     u < sigmoid(s_k), u ~ U(0, 1) seed (seed, 11); the head
+                     reports sigmoid(scale_k s_k) (scale > 1: overconfident).
   Confidence head (confidence_head_inputs; d defaults to 1024):
   h[b, k] [d]        ~ N(1, 1)        seed (seed, 6, b, k)
   w [d + r]          first d ~ N(1.4 / d, 0.5 / d), seed (seed, 7); last r
@@ -37,7 +41,7 @@ import numpy as np
 
 __all__ = ["Config", "CONFIGS", "Round", "make_round", "bf16_round", "bf16_bits_to_f32",
            "sps_table_toy", "pack_offsets", "confidence_head_inputs", "rnn_head_weights",
-           "DEFAULT_HIDDEN"]
+           "sts_samples", "DEFAULT_HIDDEN"]
 
 DEFAULT_HIDDEN = 1024
 
@@ -243,3 +247,15 @@ def rnn_head_weights(cfg: Config, d: int = DEFAULT_HIDDEN):
     w = _normal((cfg.seed, 9), 3 * cfg.r * K, 1.0 / np.sqrt(K)).reshape(3 * cfg.r, K)
     bits = bf16_round(w)
     return bits, bf16_bits_to_f32(bits)
+
+
+def sts_samples(N: int, scales, seed: int):
+    """(c [N, gamma] float32, n [N] int32): N synthetic rounds whose reported
+    confidences are miscalibrated by known logit scales (recipe above)."""
+    gamma = len(scales)
+    s = np.random.default_rng((seed, 10)).normal(0.8, 1.5, (N, gamma))
+    u = np.random.default_rng((seed, 11)).uniform(size=(N, gamma))
+    accept = u < 1.0 / (1.0 + np.exp(-s))
+    n = np.argmin(np.concatenate([accept, np.zeros((N, 1), bool)], axis=1), axis=1).astype(np.int32)
+    c = (1.0 / (1.0 + np.exp(-np.asarray(scales, np.float64) * s))).astype(np.float32)
+    return c, n

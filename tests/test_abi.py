@@ -134,12 +134,14 @@ def test_confidence_draft_argument_errors_need_no_gpu():
 
     def call(**kw):
         a = dict(U=_FAKE, W1=_FAKE, W2=_FAKE, wdtype=0, anchor=_FAKE, temperature=_FAKE, B=4, gamma=5, V=1000,
-                 r=16, seed=1, round_id=0, hidden=_FAKE, w=_FAKE, d=64, x=_FAKE, lse=_FAKE, qx=_FAKE, margin=None,
+                 r=16, seed=1, round_id=0, hidden=_FAKE, w=_FAKE, d=64, tau=None, x=_FAKE, lse=_FAKE, qx=_FAKE,
+                 margin=None,
                  conf=_FAKE, surv=_FAKE, ws=_FAKE, ws_bytes=1 << 30, stream=None)
         a.update(kw)
         return lib.dspark_draft_sample_confidence(
             a["U"], a["W1"], a["W2"], a["wdtype"], a["anchor"], a["temperature"], a["B"], a["gamma"], a["V"],
-            a["r"], a["seed"], a["round_id"], a["hidden"], a["w"], a["d"], a["x"], a["lse"], a["qx"], a["margin"],
+            a["r"], a["seed"], a["round_id"], a["hidden"], a["w"], a["d"], a["tau"], a["x"], a["lse"], a["qx"],
+            a["margin"],
             a["conf"], a["surv"], a["ws"], a["ws_bytes"], a["stream"])
 
     assert call(d=-1) == ds.DSPARK_ERR_ARG
@@ -222,3 +224,25 @@ def test_rnn_argument_errors_need_no_gpu():
     st = lib.dspark_acceptance_rnn(_FAKE, 24, _FAKE, None, _FAKE, None, _FAKE, 0, _FAKE, _FAKE, _FAKE, _FAKE,
                                    4, 5, 1000, 16, _FAKE, _FAKE, 1 << 30, None)
     assert st == ds.DSPARK_ERR_ARG
+
+
+def test_sts_argument_errors_need_no_gpu():
+    lib = ds.load_library()
+    assert ds.dspark_sts_workspace_size(100000, 5, 201, 15) > 0
+    assert ds.dspark_sts_workspace_size(100000, 5, 1024, 16) == 0  # more than 4096 cells
+    assert ds.dspark_sts_workspace_size(0, 5, 10, 15) == 0
+
+    def call(**kw):
+        a = dict(c=_FAKE, n=_FAKE, ell=None, N=1000, gamma=5, grid=_FAKE, G=50, M=15, tau=_FAKE, ece=_FAKE,
+                 eg=None, ws=_FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.dspark_sts_fit(a["c"], a["n"], a["ell"], a["N"], a["gamma"], a["grid"], a["G"], a["M"], a["tau"],
+                                  a["ece"], a["eg"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert call(c=None) == ds.DSPARK_ERR_ARG
+    assert call(tau=None) == ds.DSPARK_ERR_ARG
+    assert call(grid=None) == ds.DSPARK_ERR_ARG
+    assert call(N=0) == ds.DSPARK_ERR_ARG
+    assert call(gamma=33) == ds.DSPARK_ERR_ARG
+    assert call(G=300, M=15) == ds.DSPARK_ERR_ARG
+    assert call(ws_bytes=64) == ds.DSPARK_ERR_WORKSPACE
