@@ -60,6 +60,10 @@ def _load():
     lib.orc_sts_fit.argtypes = [_f32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, _f32p, ctypes.c_int,
                                 ctypes.c_int, _f64p, _f64p, _f64p]
     lib.orc_sts_fit.restype = ctypes.c_int
+    lib.orc_history_capacity.argtypes = [_i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.orc_history_capacity.restype = ctypes.c_int64
+    lib.orc_schedule_capacity.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, ctypes.c_int64, _i32p, _f64p, _i32p]
+    lib.orc_schedule_capacity.restype = ctypes.c_int
     lib.orc_schedule.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _f64p, ctypes.c_int,
                                  _i32p, _f64p, _f64p, _i32p]
     lib.orc_schedule.restype = ctypes.c_int
@@ -299,3 +303,26 @@ def schedule(c, sps):
     if st != 0:
         raise ValueError("orc_schedule: bad arguments")
     return ell, theta.value, tau.value, Bo.value
+
+
+def history_capacity(B_hist, R_hist, R, gamma):
+    """Capacity of the current step from the previous steps' (B, R)."""
+    B_hist = _i32(B_hist)
+    R_hist = _i32(R_hist)
+    return int(_load().orc_history_capacity(_ptr(B_hist, ctypes.c_int32), _ptr(R_hist, ctypes.c_int32),
+                                            len(B_hist), R, gamma))
+
+
+def schedule_capacity(c, capacity):
+    """Lengths for a fixed capacity: (ell [R] int32, tau, B)."""
+    lib = _load()
+    c = np.ascontiguousarray(c, dtype=np.float64)
+    R, gamma = c.shape
+    ell = np.zeros(R, np.int32)
+    tau = ctypes.c_double()
+    Bo = ctypes.c_int32()
+    st = lib.orc_schedule_capacity(_ptr(c, ctypes.c_double), R, gamma, int(capacity), _ptr(ell, ctypes.c_int32),
+                                   ctypes.byref(tau), ctypes.byref(Bo))
+    if st != 0:
+        raise ValueError("orc_schedule_capacity: bad arguments")
+    return ell, tau.value, Bo.value

@@ -818,3 +818,71 @@ int orc_schedule(const double *c, int R, int gamma, const double *sps, int sps_l
     free(len);
     return ORC_OK;
 }
+
+/* [CE] 04 (the paragraph on the strict implementation): the synchronous
+ * scheduler above stops early on the current step's own Theta; the
+ * production scheme fixes the step's capacity from the previous two steps'
+ * predictions and only sorts the current candidates, which suits an
+ * asynchronous pipeline and a cost curve that is not smooth.  Readings:
+ *  - capacity_t = round(R_t * mean over the previous two steps of B / R),
+ *    B the synchronous scheduler's choice for that step (its predictions),
+ *    steps with R = 0 skipped, rounding half up, clamped to [R_t,
+ *    R_t (1 + gamma)]; with no history, R_t (1 + gamma) (verify everything);
+ *  - the current candidates, in the synchronous order (-a, r, j), each extend
+ *    their request when they are its next position, until B = capacity; no
+ *    early stop; candidates with a = 0 are dropped.
+ * orc_history_capacity returns the capacity; orc_schedule_capacity the
+ * lengths, tau and B for a given capacity. */
+int64_t orc_history_capacity(const int32_t *B_hist, const int32_t *R_hist, int n_hist, int R, int gamma)
+{
+    double sum = 0.0;
+    int used = 0;
+    for (int i = 0; i < n_hist && i < 2; ++i) {
+        if (R_hist[i] <= 0) continue;
+        sum += (double)B_hist[i] / (double)R_hist[i];
+        ++used;
+    }
+    int64_t hi = (int64_t)R * (int64_t)(1 + gamma);
+    if (used == 0) return hi;
+    int64_t cap = (int64_t)floor((double)R * (sum / used) + 0.5);
+    if (cap < R) cap = R;
+    if (cap > hi) cap = hi;
+    return cap;
+}
+
+int orc_schedule_capacity(const double *c, int R, int gamma, int64_t capacity,
+                          int32_t *ell_out, double *tau_out, int32_t *B_out)
+{
+    if (R < 0 || gamma < 1 || (R > 0 && (!c || !ell_out))) return ORC_ERR_ARG;
+    size_t ncand_max = (size_t)R * (size_t)gamma;
+    orc_cand *cand = (orc_cand *)malloc((ncand_max ? ncand_max : 1) * sizeof(orc_cand));
+    int32_t *len = (int32_t *)calloc((size_t)(R ? R : 1), sizeof(int32_t));
+    if (!cand || !len) { free(cand); free(len); return ORC_ERR_ARG; }
+    size_t n = 0;
+    for (int r = 0; r < R; ++r) {
+        double a = 1.0;
+        for (int j = 0; j < gamma; ++j) {
+            a *= c[(size_t)r * (size_t)gamma + j];
+            if (a > 0.0) {
+                cand[n].a = a; cand[n].r = r; cand[n].j = j;
+                ++n;
+            }
+        }
+    }
+    qsort(cand, n, sizeof(orc_cand), orc_cand_cmp);
+    int64_t B = R;
+    double tau = (double)R;
+    for (size_t i = 0; i < n && B < capacity; ++i) {
+        const orc_cand *cd = &cand[i];
+        if (cd->j != len[cd->r]) continue;
+        len[cd->r] += 1;
+        B += 1;
+        tau += cd->a;
+    }
+    for (int r = 0; r < R; ++r) ell_out[r] = len[r];
+    if (tau_out) *tau_out = tau;
+    if (B_out) *B_out = (int32_t)B;
+    free(cand);
+    free(len);
+    return ORC_OK;
+}
