@@ -16,8 +16,10 @@ Secondary figures: the distribution of single-round times over --rounds
 rounds, the bias product alone (the draft step's MFMA tiling without U_k or
 sampling) with W2 warm in the last-level cache and after a 512 MiB flush, the
 host scheduler's time on a 1024-request batch, the round with the confidence
-head fused into the draft, the acceptance-probability labelling pass, and the
-oracle on one thread.
+head fused into the draft, the acceptance-probability labelling pass, the
+round with the RNN head in place of the Markov head, the calibration fit of
+the head (sequential temperature scaling) on 200,000 synthetic samples, and
+the oracle on one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -140,7 +142,8 @@ def _bias_gemm_alone(torch, ds, dev, B, V, r, reps=30):
 def _schedule_time(ds, S, reps=400):
     """Host scheduler on the scheduled-batch workload (1024 requests, gamma 5,
     confidences ~ Beta(8, 2), SPS(B) tabulated for every batch size): median
-    and p90 microseconds per call, including the ctypes call."""
+    and p90 microseconds per call, including the ctypes call; the same for
+    the production-style scheduler at a capacity from its history rule."""
     import numpy as np
     cfg = S.CONFIGS["sched"]
     c = np.random.default_rng((cfg.seed, 5)).beta(8.0, 2.0, size=(cfg.B, cfg.gamma))
@@ -152,8 +155,19 @@ def _schedule_time(ds, S, reps=400):
         ds.dspark_schedule(c, sps)
         t.append((time.perf_counter_ns() - t0) / 1e3)
     t = np.array(t)
+    # the production-style scheduler at a capacity of half the drafts (its
+    # history rule from two previous steps with B/R = 3.5 and 2.5)
+    cap = ds.dspark_history_capacity([cfg.B * 7 // 2, cfg.B * 5 // 2], [cfg.B, cfg.B], cfg.B, cfg.gamma)
+    tc = []
+    for _ in range(reps):
+        t0 = time.perf_counter_ns()
+        ds.dspark_schedule_capacity(c, cap)
+        tc.append((time.perf_counter_ns() - t0) / 1e3)
+    tc = np.array(tc)
     return {"requests": cfg.B, "gamma": cfg.gamma, "sps_len": len(sps), "p50_us": round(float(np.median(t)), 2),
-            "p90_us": round(float(np.percentile(t, 90)), 2)}
+            "p90_us": round(float(np.percentile(t, 90)), 2),
+            "capacity": {"capacity": cap, "p50_us": round(float(np.median(tc)), 2),
+                         "p90_us": round(float(np.percentile(tc, 90)), 2)}}
 
 
 def _oracle_one_thread(rnd, target, ell, seed, gamma, oracle_round, rows=128):
@@ -230,6 +244,57 @@ def _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, reps):
     return {"d": h.shape[2], "round_ms": round(ms_conf, 5), "round_ms_without": round(ms_plain, 5),
             "draft_reduce_us": round(red_conf, 2), "draft_reduce_us_without": round(red_plain, 2),
             "mean_c": round(float(c.mean()), 4)}
+
+
+def _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, reps):
+    """The round with the RNN head in place of the Markov head (d = 1024,
+    synthetic h and Wgco): round time, and the gate kernel's time with its
+    MFMA rate (2 B (2r + d) 3r flops a launch)."""
+    import numpy as np
+    from roundkit import np_of
+    h, _ = S.confidence_head_inputs(cfg)
+    bits, _ = S.rnn_head_weights(cfg)
+    hd = torch.from_numpy(h).cuda()
+    wg = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    g = ds.dspark_draft_sample_rnn(dev["U"], dev["W1"], dev["W2"], wg, dev["anchor"], dev["temperature"], hd, seed, 0)
+    v = ds.dspark_verify_rnn(td, ed, dev["U"], g["e"], dev["W2"], dev["anchor"], g["x"], g["lse"], g["qx"],
+                             dev["temperature"], seed, 0)
+
+    def step(rid):
+        ds.dspark_draft_sample_rnn(dev["U"], dev["W1"], dev["W2"], wg, dev["anchor"], dev["temperature"], hd, seed,
+                                   rid, out=g)
+        ds.dspark_verify_rnn(td, ed, dev["U"], g["e"], dev["W2"], dev["anchor"], g["x"], g["lse"], g["qx"],
+                             dev["temperature"], seed, rid, out=v)
+
+    for i in range(20):
+        step(9000 + i)
+    ms = _events_ms(torch, step, reps, 9100)
+    ph = _profiled(torch, ds, lambda i: step(9300 + i), reps)
+    B, r, d = cfg.B, cfg.r, h.shape[2]
+    flops = 2.0 * B * (2 * r + d) * 3 * r
+    us = ph.get("rnn_gate", 0.0)
+    return {"d": d, "round_ms": round(ms, 5), "rnn_gate_us": round(us, 2),
+            "rnn_gate_tflops": round(flops / (us * 1e-6) / 1e12, 1) if us > 0 else None,
+            "draft_step_us": round(ph.get("draft_step", 0.0), 2), "draft_reduce_us": round(ph.get("draft_reduce", 0.0), 2),
+            "emitted_per_round": int(np_of(v["n"]).sum()) + B}
+
+
+def _sts_fit(torch, ds, S, reps=10):
+    """Sequential temperature scaling of the head from 200,000 synthetic
+    calibration samples (gamma 5, 76 grid temperatures 0.25..4, 15 bins):
+    time per fit call."""
+    import numpy as np
+    c, n = S.sts_samples(200_000, [2.0, 0.5, 1.0, 1.5, 0.75], seed=1)
+    grid = torch.from_numpy(np.round(np.arange(0.25, 4.0001, 0.05), 2).astype(np.float32)).cuda()
+    cd, nd = torch.from_numpy(c).cuda(), torch.from_numpy(n).cuda()
+    out = ds.dspark_sts_fit(cd, nd, grid)
+    ws = torch.empty(ds.dspark_sts_workspace_size(len(c), c.shape[1], grid.numel(), 15), dtype=torch.uint8,
+                     device="cuda")
+    ms = _events_ms(torch, lambda i: ds.dspark_sts_fit(cd, nd, grid, workspace=ws), reps, 0)
+    ph = _profiled(torch, ds, lambda i: ds.dspark_sts_fit(cd, nd, grid, workspace=ws), reps)
+    return {"samples": len(c), "gamma": c.shape[1], "grid": grid.numel(), "bins": 15, "call_ms": round(ms, 4),
+            "sts_hist_us": round(ph.get("sts_hist", 0.0), 2), "sts_pick_us": round(ph.get("sts_pick", 0.0), 2),
+            "tau": [round(float(t), 2) for t in out["tau"].cpu()]}
 
 
 def _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, reps):
@@ -363,6 +428,8 @@ def main():
     sched = _schedule_time(ds, S)
     conf = _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps)
     accept = _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, 20)
+    rnn = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps)
+    sts = _sts_fit(torch, ds, S)
 
     drafted = B * gamma
     value = drafted / (ms_step * 1e-3)
@@ -405,7 +472,9 @@ def main():
                       "logit_passes": logit,
                       "schedule": sched,
                       "confidence_head": conf,
-                      "acceptance": accept},
+                      "acceptance": accept,
+                      "rnn_head": rnn,
+                      "sts_fit": sts},
         "roofline": roofline,
     }
 

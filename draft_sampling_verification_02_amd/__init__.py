@@ -106,6 +106,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                _c_int, _c_int, _c_int, _c_int,
                                _c_void_p, _c_void_p, _c_size, _c_void_p], _c_int),
         "dspark_schedule": ([_f64p, _c_int, _c_int, _f64p, _c_int, _i32p, _f64p, _f64p, _i32p], _c_int),
+        "dspark_history_capacity": ([_i32p, _i32p, _c_int, _c_int, _c_int, ctypes.POINTER(ctypes.c_int64)], _c_int),
+        "dspark_schedule_capacity": ([_f64p, _c_int, _c_int, ctypes.c_int64, _i32p, _f64p, _i32p], _c_int),
         "dspark_debug_random_words": ([_c_u64, _c_u64, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_void_p, _c_void_p], _c_int),
         "dspark_debug_gumbel": ([_c_void_p, _c_int, _c_void_p, _c_void_p], _c_int),
@@ -500,6 +502,35 @@ def dspark_schedule(c, sps):
                              ell.ctypes.data_as(_i32p), ctypes.byref(theta), ctypes.byref(tau), ctypes.byref(Bo))
     _check(st, "dspark_schedule")
     return ell, theta.value, tau.value, Bo.value
+
+
+def dspark_history_capacity(B_hist, R_hist, R: int, gamma: int) -> int:
+    """Capacity of the current step from the previous steps' (B, R)."""
+    lib = load_library()
+    Bh = np.ascontiguousarray(B_hist, dtype=np.int32)
+    Rh = np.ascontiguousarray(R_hist, dtype=np.int32)
+    cap = ctypes.c_int64()
+    st = lib.dspark_history_capacity(Bh.ctypes.data_as(_i32p), Rh.ctypes.data_as(_i32p), len(Bh), R, gamma,
+                                     ctypes.byref(cap))
+    _check(st, "dspark_history_capacity")
+    return cap.value
+
+
+def dspark_schedule_capacity(c, capacity: int):
+    """Fixed-capacity scheduling.  c [R, gamma] float64 in [0, 1].  Returns
+    (ell [R] int32, tau, B)."""
+    lib = load_library()
+    c = np.ascontiguousarray(c, dtype=np.float64)
+    if c.ndim != 2:
+        raise ValueError("c: [R, gamma]")
+    R, gamma = c.shape
+    ell = np.zeros(R, np.int32)
+    tau = ctypes.c_double()
+    Bo = ctypes.c_int32()
+    st = lib.dspark_schedule_capacity(c.ctypes.data_as(_f64p), R, gamma, int(capacity), ell.ctypes.data_as(_i32p),
+                                      ctypes.byref(tau), ctypes.byref(Bo))
+    _check(st, "dspark_schedule_capacity")
+    return ell, tau.value, Bo.value
 
 
 def dspark_debug_random_words(seed, round_id, stream_id, k, req, v0, n, device="cuda", stream=None):

@@ -91,3 +91,67 @@ extern "C" int dspark_schedule(const double *c, int R, int gamma, const double *
     if (B_out) *B_out = int32_t(B);
     return DSPARK_OK;
 }
+
+// Production-style scheduling ("DeepSeek DSpark explained", section 04, the
+// strict implementation): the step's capacity comes from the previous two
+// steps' predictions, and the current candidates only fill it, in the same
+// descending-a order as above, with no early stop on the current step.
+extern "C" int dspark_history_capacity(const int32_t *B_hist, const int32_t *R_hist, int n_hist, int R, int gamma,
+                                       int64_t *capacity_out) {
+    if (R < 0 || R > DSPARK_MAX_BATCH || gamma < 1 || gamma > DSPARK_MAX_GAMMA || n_hist < 0 || !capacity_out)
+        return DSPARK_ERR_ARG;
+    if (n_hist > 0 && (!B_hist || !R_hist)) return DSPARK_ERR_ARG;
+    double sum = 0.0;
+    int used = 0;
+    for (int i = 0; i < n_hist && i < 2; ++i) {
+        if (R_hist[i] <= 0) continue;
+        sum += double(B_hist[i]) / double(R_hist[i]);
+        ++used;
+    }
+    const int64_t hi = int64_t(R) * (1 + gamma);
+    int64_t cap = hi;
+    if (used > 0) {
+        cap = int64_t(std::floor(double(R) * (sum / used) + 0.5));
+        cap = cap < R ? R : (cap > hi ? hi : cap);
+    }
+    *capacity_out = cap;
+    return DSPARK_OK;
+}
+
+extern "C" int dspark_schedule_capacity(const double *c, int R, int gamma, int64_t capacity, int32_t *ell_out,
+                                        double *tau_out, int32_t *B_out) {
+    if (R < 0 || R > DSPARK_MAX_BATCH || gamma < 1 || gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_ARG;
+    if (R > 0 && (!c || !ell_out)) return DSPARK_ERR_ARG;
+    const size_t n = size_t(R) * size_t(gamma);
+    for (size_t i = 0; i < n; ++i)
+        if (!(c[i] >= 0.0 && c[i] <= 1.0)) return DSPARK_ERR_ARG;
+    std::vector<double> a(n);
+    for (int r = 0; r < R; ++r) {
+        double p = 1.0;
+        for (int j = 0; j < gamma; ++j) {
+            p *= c[size_t(r) * gamma + j];
+            a[size_t(r) * gamma + j] = p;
+        }
+    }
+    std::vector<int32_t> len(size_t(R), 0);
+    std::priority_queue<Head, std::vector<Head>, HeadLess> heap;
+    for (int r = 0; r < R; ++r)
+        if (a[size_t(r) * gamma] > 0.0) heap.push(Head{a[size_t(r) * gamma], r});
+    long long B = R;
+    double tau = double(R);
+    while (!heap.empty() && B < capacity) {
+        const Head h = heap.top();
+        heap.pop();
+        B += 1;
+        tau += h.a;
+        const int j = ++len[size_t(h.r)];
+        if (j < gamma) {
+            const double an = a[size_t(h.r) * gamma + j];
+            if (an > 0.0) heap.push(Head{an, h.r});
+        }
+    }
+    for (int r = 0; r < R; ++r) ell_out[r] = len[size_t(r)];
+    if (tau_out) *tau_out = tau;
+    if (B_out) *B_out = int32_t(B);
+    return DSPARK_OK;
+}

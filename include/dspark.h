@@ -363,6 +363,27 @@ int dspark_acceptance_rnn(const float *target, int n_target_rows, const int32_t 
 int dspark_schedule(const double *c, int R, int gamma, const double *sps, int sps_len,
                     int32_t *ell_out, double *theta_out, double *tau_out, int32_t *B_out);
 
+/* Production-style scheduling ([CE] 04, the strict implementation: in an
+ * asynchronous pipeline the step's capacity comes from the previous two
+ * steps' predictions and the current candidates are only sorted into it).
+ *
+ * dspark_history_capacity: the capacity of the current step, R requests,
+ *   round(R * mean_i B_hist[i] / R_hist[i]) over the first min(n_hist, 2)
+ *   entries with R_hist[i] > 0 (the synchronous scheduler's B and R of the
+ *   previous steps), rounding half up, clamped to [R, R (1 + gamma)];
+ *   R (1 + gamma) (verify everything) when no entry is usable.  Host.
+ * dspark_schedule_capacity: with c, R, gamma as for dspark_schedule, extends
+ *   the requests in the same candidate order (-a, r, j) under the same
+ *   prefix rule until B = capacity (or the candidates with a > 0 run out),
+ *   without the early stop; ell_out [R], tau_out and B_out as for
+ *   dspark_schedule.  With the capacity the synchronous scheduler chose it
+ *   returns that scheduler's lengths; for any capacity its tau is the largest
+ *   a prefix-valid choice of that B reaches.  Host, synchronous. */
+int dspark_history_capacity(const int32_t *B_hist, const int32_t *R_hist, int n_hist, int R, int gamma,
+                            int64_t *capacity_out);
+int dspark_schedule_capacity(const double *c, int R, int gamma, int64_t capacity,
+                             int32_t *ell_out, double *tau_out, int32_t *B_out);
+
 /* ------------------------------------------------------------------ */
 /* Diagnostics                                                         */
 /* ------------------------------------------------------------------ */

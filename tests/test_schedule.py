@@ -63,3 +63,38 @@ def test_large_batch_matches_oracle():
         n = 4096 * 9 + 1
         sps = 1000.0 / (50 + lin * np.arange(n))
         _same(c, sps)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_capacity_scheduler_matches_oracle(seed):
+    """The library's heap merge with a fixed capacity against the oracle's
+    sort: identical lengths, tau and B for every capacity."""
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.integers(0, 50))
+    gamma = int(rng.integers(1, 9))
+    c = rng.beta(6.0, 2.0, size=(R, gamma))
+    c[rng.uniform(size=c.shape) < 0.05] = 0.0
+    c[:, 0][rng.uniform(size=R) < 0.1] = 1.0
+    for cap in sorted({0, R, R + 1, R + R * gamma // 3, R * (1 + gamma), R * (1 + gamma) + 5,
+                       int(rng.integers(0, R * (1 + gamma) + 1))}):
+        got = ds.dspark_schedule_capacity(c, cap)
+        want = oracle.schedule_capacity(c, cap)
+        assert got[0].tolist() == want[0].tolist() and got[1] == want[1] and got[2] == want[2]
+
+
+def test_history_capacity_matches_oracle():
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        gamma = int(rng.integers(1, 9))
+        R = int(rng.integers(0, 300))
+        Rh = rng.integers(0, 300, 2).astype(np.int32)
+        Bh = (Rh * rng.uniform(1.0, 1.0 + gamma, 2)).astype(np.int32)
+        n = int(rng.integers(0, 3))
+        assert ds.dspark_history_capacity(Bh[:n], Rh[:n], R, gamma) == oracle.history_capacity(Bh[:n], Rh[:n], R, gamma)
+
+
+def test_capacity_scheduler_rejects_bad_confidences():
+    with pytest.raises(ds.DSparkError):
+        ds.dspark_schedule_capacity(np.array([[0.5, 1.5]]), 3)
+    with pytest.raises(ds.DSparkError):
+        ds.dspark_schedule_capacity(np.array([[np.nan]]), 3)
