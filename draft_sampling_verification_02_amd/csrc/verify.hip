@@ -14,15 +14,19 @@
 // (stream 2).
 //
 // Kernels, in launch order:
-//   verify_prep      1 workgroup: packed row offsets (scan of 1 + ell, or the
-//                    caller's, checked), output defaults, pass state.
-//   verify_pass      once per position j = 1..gamma+1, over the requests
-//                    still testing at j: the row's vocabulary is split into
-//                    segments, one workgroup streams each for logsumexp(t / T)
-//                    in base 2 and the lowest-index argmax, and the last
-//                    segment to finish merges them and runs the accept test
-//                    u*q < p at j (or takes the bonus row).  A request stops
-//                    at its first rejection, so rows past it are never read.
+//   verify_prep      1 workgroup, for batches above 512 requests (smaller
+//                    ones have the first pass do it): packed row offsets
+//                    (scan of 1 + ell, or the caller's, checked), output
+//                    defaults, pass state.
+//   verify_pass      gamma + 2 launches; launch p runs over the requests
+//                    still testing: one wave per (request, vocabulary
+//                    segment) first decides position p - 1 from the segment
+//                    statistics launch p - 1 left (the accept test u*q < p,
+//                    or the bonus row), then, if the request goes on,
+//                    streams its segment of row p for logsumexp(t / T) in
+//                    base 2 and the lowest-index argmax.  The last launch
+//                    only decides.  A request stops at its first rejection,
+//                    so rows past it are never read.
 //   verify_draw      level 1: waves of 32 listed requests walk vocabulary
 //                    chunks; residual rows recompute q_j with the draft's
 //                    LDS-staged MFMA bias tile and sum max(p_j - q_j, 0) per
