@@ -246,14 +246,16 @@ def _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, reps):
             "mean_c": round(float(c.mean()), 4)}
 
 
-def _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, reps):
-    """The round with the RNN head in place of the Markov head (d = 1024,
-    synthetic h and Wgco): round time, and the gate kernel's time with its
-    MFMA rate (2 B (2r + d) 3r flops a launch)."""
+def _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, reps, d):
+    """The round with the RNN head in place of the Markov head (hidden width
+    d, synthetic h and Wgco): round time; the h-part product's time and MFMA
+    rate (2 B gamma d 3r flops, once a round) and the per-position gate
+    kernel's (2 B 2r 3r flops a launch; 2 B (2r + d) 3r when the h part is
+    not precomputed)."""
     import numpy as np
     from roundkit import np_of
-    h, _ = S.confidence_head_inputs(cfg)
-    bits, _ = S.rnn_head_weights(cfg)
+    h, _ = S.confidence_head_inputs(cfg, d)
+    bits, _ = S.rnn_head_weights(cfg, d)
     hd = torch.from_numpy(h).cuda()
     wg = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
     g = ds.dspark_draft_sample_rnn(dev["U"], dev["W1"], dev["W2"], wg, dev["anchor"], dev["temperature"], hd, seed, 0)
@@ -271,9 +273,13 @@ def _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, reps):
     ms = _events_ms(torch, step, reps, 9100)
     ph = _profiled(torch, ds, lambda i: step(9300 + i), reps)
     B, r, d = cfg.B, cfg.r, h.shape[2]
-    flops = 2.0 * B * (2 * r + d) * 3 * r
+    pus = ph.get("rnn_hproj", 0.0)
+    flops = 2.0 * B * (2 * r + (0 if pus > 0 else d)) * 3 * r
+    pflops = 2.0 * B * cfg.gamma * d * 3 * r
     us = ph.get("rnn_gate", 0.0)
-    return {"d": d, "round_ms": round(ms, 5), "rnn_gate_us": round(us, 2),
+    return {"d": d, "round_ms": round(ms, 5), "rnn_hproj_us": round(pus, 2),
+            "rnn_hproj_tflops": round(pflops / (pus * 1e-6) / 1e12, 1) if pus > 0 else None,
+            "rnn_gate_us": round(us, 2),
             "rnn_gate_tflops": round(flops / (us * 1e-6) / 1e12, 1) if us > 0 else None,
             "draft_step_us": round(ph.get("draft_step", 0.0), 2), "draft_reduce_us": round(ph.get("draft_reduce", 0.0), 2),
             "emitted_per_round": int(np_of(v["n"]).sum()) + B}
@@ -428,7 +434,8 @@ def main():
     sched = _schedule_time(ds, S)
     conf = _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps)
     accept = _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, 20)
-    rnn = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps)
+    rnn = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps, S.DEFAULT_HIDDEN)
+    rnn_wide = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, args.steps, 4 * S.DEFAULT_HIDDEN)
     sts = _sts_fit(torch, ds, S)
 
     drafted = B * gamma
@@ -473,7 +480,7 @@ def main():
                       "schedule": sched,
                       "confidence_head": conf,
                       "acceptance": accept,
-                      "rnn_head": rnn,
+                      "rnn_head": rnn, "rnn_head_wide": rnn_wide,
                       "sts_fit": sts},
         "roofline": roofline,
     }

@@ -211,7 +211,7 @@ size_t dspark_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d) {
     if (!sizes_ok(B, gamma, V, r) || d < 0 || d > DSPARK_MAX_HIDDEN) return 0;
     const DraftPlan p = draft_plan(B, V);
     size_t bytes = 0;
-    draft_carve(nullptr, B, p, &bytes, r);
+    draft_carve(nullptr, B, p, &bytes, r, gamma, d);
     return bytes;
 }
 
@@ -231,9 +231,9 @@ int dspark_draft_sample_rnn(const float *U, const void *W1, const void *W2, cons
         return DSPARK_ERR_ARG;
     const DraftPlan plan = draft_plan(B, V);
     size_t need = 0;
-    draft_carve(nullptr, B, plan, &need, r);
+    draft_carve(nullptr, B, plan, &need, r, gamma, d);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return DSPARK_ERR_WORKSPACE;
-    const DraftWork w = draft_carve(workspace, B, plan, nullptr, r);
+    const DraftWork w = draft_carve(workspace, B, plan, nullptr, r, gamma, d);
     DraftArgs a{};
     a.U = U;
     a.W1 = W1;

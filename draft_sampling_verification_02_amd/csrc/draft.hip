@@ -596,6 +596,18 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
                       reinterpret_cast<uintptr_t>(a.conf_w) % 16 == 0;
     bool rnn = false;
     if constexpr (sizeof(WT) == 2) rnn = a.Wgco != nullptr;
+    RnnProjPlan pp{};
+    if (rnn) {
+        // the h part of every position's gate product, before position 1
+        pp = rnn_proj_plan(a.B, a.gamma, a.r, a.rnn_d);
+        if (pp.S > 0 && w.rnn_yh) {
+            const hipError_t e = launch_rnn_hproj(a.rnn_h, static_cast<const uint16_t *>(a.Wgco), w.rnn_yh, a.B,
+                                                  a.gamma, a.r, a.rnn_d, pp, s);
+            if (e != hipSuccess) return e;
+        } else {
+            pp.S = 0;
+        }
+    }
     for (int k = 1; k <= a.gamma; ++k) {
         const int32_t *xprev = (k == 1) ? a.anchor : a.x_out + (k - 2);
         const int xprev_stride = (k == 1) ? 1 : a.gamma;
@@ -619,6 +631,12 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
             g.V = a.V;
             g.r = a.r;
             g.d = a.rnn_d;
+            if (pp.S > 0) {
+                g.yh = w.rnn_yh;
+                g.yh_split = size_t(a.B) * a.gamma * 3 * a.r;
+                g.yS = pp.S;
+                g.kpos = k - 1;
+            }
             const hipError_t e = launch_rnn_gate(g, s);
             if (e != hipSuccess) return e;
         }
@@ -733,7 +751,7 @@ DraftPlan draft_plan(int B, int V) {
     return tile_walk_plan(B, V, kStepThreads / 64, 256, 2);
 }
 
-DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rnn_r) {
+DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rnn_r, int rnn_gamma, int rnn_d) {
     Carve c(ws);
     const size_t n = size_t(B) * p.nchunk;
     DraftWork w{};
@@ -746,6 +764,8 @@ DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rn
         w.rnn_s[0] = c.take<float>(size_t(B) * rnn_r);
         w.rnn_s[1] = c.take<float>(size_t(B) * rnn_r);
         w.rnn_idx = c.take<int32_t>(B);
+        const RnnProjPlan pp = rnn_proj_plan(B, rnn_gamma, rnn_r, rnn_d);
+        if (pp.S > 0) w.rnn_yh = c.take<float>(pp.floats);
     }
     if (bytes) *bytes = c.off + 256;
     return w;

@@ -64,9 +64,12 @@ struct DraftWork {
     int32_t *pi;               // [B, nchunk] partial best index
     float *rnn_s[2];           // RNN head: [B, r] states of alternate positions
     int32_t *rnn_idx;          // RNN head: [B] the draft step's row of e_out for request b (b * gamma)
+    float *rnn_yh;             // RNN head: precomputed h part of the gate product (RnnProjPlan)
 };
-// rnn_r > 0 also carves the RNN head's buffers for rank rnn_r.
-DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rnn_r = 0);
+// rnn_r > 0 also carves the RNN head's buffers for rank rnn_r, block gamma
+// and width rnn_d.
+DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rnn_r = 0, int rnn_gamma = 0,
+                      int rnn_d = 0);
 
 struct DraftArgs {
     const float *U;
@@ -106,8 +109,21 @@ struct RnnGateArgs {
     size_t e_stride;
     int32_t *idx_out;
     int gamma, B, V, r, d;
+    const float *yh;  // precomputed h part [yS, B * gamma, 3r], or nullptr
+    size_t yh_split;
+    int yS, kpos;     // its splits; k - 1
 };
 hipError_t launch_rnn_gate(const RnnGateArgs &a, hipStream_t s);
+
+// The h part of the RNN head's gate product for every position at once;
+// S == 0: not used (d == 0, or the partials would exceed 512 MiB).
+struct RnnProjPlan {
+    int S, kchunk, blocks;
+    size_t floats;  // S * B * gamma * 3r
+};
+RnnProjPlan rnn_proj_plan(int B, int gamma, int r, int d);
+hipError_t launch_rnn_hproj(const float *h, const uint16_t *Wgco, float *y, int B, int gamma, int r, int d,
+                            const RnnProjPlan &p, hipStream_t s);
 hipError_t launch_draft(const DraftArgs &a, const DraftPlan &p, const DraftWork &w, hipStream_t s);
 // The bias product alone: rowmax[b] = max_v W1[idx[b]] . W2[v] (diagnostic).
 hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const int32_t *idx, int B, int V, int r,

@@ -13,11 +13,20 @@
 // bfloat16 (nearest, ties to even) where they enter the gate product, e_k
 // where it enters the W2 product; the state itself stays float32.
 //
+// rnn_hproj (once a block, before position 1): h_k is known for every
+// position before the block starts, so the h part of the gate product,
+// Y_h = bf16(h) Wgco[:, 2r:]^T, is one [B gamma, d] x [d, 3r] product over
+// all positions: 128 x 128 output tiles staged through LDS (h converted to
+// bf16 on the way), four waves of 2 x 2 bf16 32x32x16 MFMA tiles, the K
+// range split so that up to 256 workgroups run in one wave; each split
+// writes its own partial tile, which the gate kernel sums in split order.
+//
 // rnn_gate: one workgroup of 8 waves per (16 requests, 16 state entries).
-// Each wave takes one eighth of the 2r + d inputs and runs three 16x16x32
-// bf16 MFMA chains (gate, candidate and output rows of the same 16 entries),
-// with z read straight from its three sources and Wgco rows from the caches;
-// the eight partial tiles meet in LDS and 256 threads apply the update.
+// Each wave takes one eighth of the s and W1 inputs (all 2r + d inputs when
+// no Y_h is given) and runs three 16x16x32 bf16 MFMA chains (gate,
+// candidate and output rows of the same 16 entries), with z read straight
+// from its sources and Wgco rows from the caches; the eight partial tiles
+// meet in LDS and 256 threads add Y_h and apply the update.
 // 256 workgroups at B = 256, r = 256.
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -32,6 +41,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGateThreads = 512;
 constexpr int kGateSteps = 4;  // K steps of 32 whose loads go out together
+constexpr int kMaxSplits = 8;  // K splits of the precomputed h part
 
 struct GateParams {
     const float *s_in;  // [B, R] s_{k-1}; nullptr at k = 1 (s_0 = 0)
@@ -45,6 +55,10 @@ struct GateParams {
     size_t e_stride;
     int32_t *idx_out;  // k = 1 only: idx_out[b] = b * gamma, the draft step's row of e_out
     int gamma, B, V, d;
+    // precomputed h part: partial S of request b's row at yh + S * yh_split + (b * gamma + k - 1) * 3R
+    const float *yh;   // nullptr: the gate product covers h itself
+    size_t yh_split;
+    int yS, kpos;      // splits, k - 1
 };
 
 // float32 -> bfloat16 bits, nearest with ties to even (finite inputs)
@@ -90,7 +104,8 @@ __global__ __launch_bounds__(kGateThreads) void rnn_gate_kernel(GateParams p) {
     constexpr int NW = kGateThreads / 64;
     const int ct = blockIdx.x % NCB, bt = blockIdx.x / NCB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int K = 2 * R + p.d, nks = K >> 5;
+    const int K = 2 * R + p.d;                // Wgco row length
+    const int nks = (p.yh ? 2 * R : K) >> 5;  // K steps this kernel runs
     const int m = lane & 15, grp = lane >> 4;
     const int b = min(bt * 16 + m, p.B - 1);  // rows past the batch repeat its last request
     const int prev = min(max(p.xprev[size_t(b) * p.xprev_stride], 0), p.V - 1);
@@ -99,6 +114,31 @@ __global__ __launch_bounds__(kGateThreads) void rnn_gate_kernel(GateParams p) {
     const uint16_t *wc = wg + size_t(R) * K;
     const uint16_t *wo = wc + size_t(R) * K;
     const int s0 = (nks * wave) / NW, s1 = (nks * (wave + 1)) / NW;
+    // the update's own inputs (threads 0..255, one (request, entry) each):
+    // loaded before the product so that their latency overlaps it
+    const int ul = tid & 63, uv = (tid >> 6) & 3;
+    const int urow = bt * 16 + 4 * (ul >> 4) + uv, ucol = c0 + (ul & 15);
+    const bool upd = tid < 256 && urow < p.B;
+    const int ur = min(urow, p.B - 1);
+    float yg = 0.f, yc = 0.f, yo = 0.f;
+    if (p.yh) {
+        const float *y = p.yh + (size_t(ur) * p.gamma + p.kpos) * (3 * R) + ucol;
+        float t[kMaxSplits][3];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) {
+            const float *ys = y + size_t(min(sp, p.yS - 1)) * p.yh_split;
+            t[sp][0] = ys[0];
+            t[sp][1] = ys[R];
+            t[sp][2] = ys[2 * R];
+        }
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) {
+            yg += sp < p.yS ? t[sp][0] : 0.f;
+            yc += sp < p.yS ? t[sp][1] : 0.f;
+            yo += sp < p.yS ? t[sp][2] : 0.f;
+        }
+    }
+    const float sprev = p.s_in ? p.s_in[size_t(ur) * R + ucol] : 0.f;
     f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, ac = ag, ao = ag;
     for (int st = s0; st < s1; st += kGateSteps) {
         uint4 za[kGateSteps], xg[kGateSteps], xc[kGateSteps], xo[kGateSteps];
@@ -127,28 +167,169 @@ __global__ __launch_bounds__(kGateThreads) void rnn_gate_kernel(GateParams p) {
         part[wave][2][lane][v] = ao[v];
     }
     __syncthreads();
-    if (tid < 256) {
-        const int l = tid & 63, v = tid >> 6;
-        float yg = 0.f, yc = 0.f, yo = 0.f;
+    if (upd) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            yg += part[w][0][l][v];
-            yc += part[w][1][l][v];
-            yo += part[w][2][l][v];
+            yg += part[w][0][ul][uv];
+            yc += part[w][1][ul][uv];
+            yo += part[w][2][ul][uv];
         }
-        const int row = bt * 16 + 4 * (l >> 4) + v;
-        const int col = c0 + (l & 15);
-        if (row < p.B) {
-            const float sp = p.s_in ? p.s_in[size_t(row) * R + col] : 0.f;
-            const float g = 1.0f / (1.0f + expf(-yg));
-            p.s_out[size_t(row) * R + col] = g * sp + (1.0f - g) * tanhf(yc);
-            p.e_out[size_t(row) * p.e_stride + col] = uint16_t(bf16_bits(tanhf(yo)));
-        }
+        const float g = 1.0f / (1.0f + expf(-yg));
+        p.s_out[size_t(urow) * R + ucol] = g * sprev + (1.0f - g) * tanhf(yc);
+        p.e_out[size_t(urow) * p.e_stride + ucol] = uint16_t(bf16_bits(tanhf(yo)));
     }
     if (p.idx_out && ct == 0 && tid < 16 && bt * 16 + tid < p.B) p.idx_out[bt * 16 + tid] = (bt * 16 + tid) * p.gamma;
 }
 
+constexpr int kProjTile = 128;  // output tile edge
+constexpr int kProjBK = 64;     // K entries a stage
+constexpr int kProjPad = 72;    // LDS row length in bf16 (64 used): 144-byte rows
+
+struct HprojParams {
+    const float *h;        // [M, d]
+    const uint16_t *Wgco;  // [N, 2R + d]; the h part of row j starts at column 2R
+    float *y;              // [S, M, N]
+    int M, N, d, K, R, kchunk;
+};
+
+// C[m][j] = sum_i bf16(h[m][i]) Wgco[j][2R + i] over this workgroup's K
+// split, for a 128 x 128 tile.  Wave w computes rows 64 (w / 2) .. + 63 and
+// columns 64 (w % 2) .. + 63 as 2 x 2 MFMA tiles; each 64-wide K stage is
+// staged in LDS (double-buffered) by the whole workgroup while the next one
+// is loaded into registers.  K splits are multiples of 32, so a split's
+// last stage may hold only 32 entries: its upper half is then loaded from
+// the lower half's addresses and not used.
+__global__ __launch_bounds__(256) void rnn_hproj_kernel(HprojParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kProjTile][kProjPad];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kProjTile][kProjPad];
+    const int nb = (p.N + kProjTile - 1) / kProjTile, mb = (p.M + kProjTile - 1) / kProjTile;
+    const int bn = blockIdx.x % nb, bm = (blockIdx.x / nb) % mb, sk = blockIdx.x / (nb * mb);
+    const int m0 = bm * kProjTile, n0 = bn * kProjTile;
+    const int k_lo = sk * p.kchunk, k_hi = min(p.d, k_lo + p.kchunk);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, hh = lane >> 5;
+    const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);
+    // staging slots: A 8 float4 a thread (row idx / 16, columns 4 (idx % 16)),
+    // B 4 uint4 (row idx / 8, columns 8 (idx % 8)); rows past the matrix
+    // repeat its last row (their outputs are not written)
+    float4 ra[8];
+    uint4 rb[4];
+    auto load = [&](int k0) __device__ {
+        const int hmask = k0 + kProjBK <= k_hi ? kProjBK - 1 : kProjBK / 2 - 1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = tid + 256 * u, row = min(m0 + idx / 16, p.M - 1);
+            ra[u] = *reinterpret_cast<const float4 *>(p.h + size_t(row) * p.d + k0 + ((4 * (idx % 16)) & hmask));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u, row = min(n0 + idx / 8, p.N - 1);
+            rb[u] = *reinterpret_cast<const uint4 *>(p.Wgco + size_t(row) * p.K + 2 * p.R + k0 +
+                                                     ((8 * (idx % 8)) & hmask));
+        }
+    };
+    auto store = [&](int buf) __device__ {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = tid + 256 * u;
+            const uint2 v = make_uint2(bf16_bits(ra[u].x) | (bf16_bits(ra[u].y) << 16),
+                                       bf16_bits(ra[u].z) | (bf16_bits(ra[u].w) << 16));
+            *reinterpret_cast<uint2 *>(&As[buf][idx / 16][4 * (idx % 16)]) = v;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + 256 * u;
+            *reinterpret_cast<uint4 *>(&Bs[buf][idx / 8][8 * (idx % 8)]) = rb[u];
+        }
+    };
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    int buf = 0;
+    if (k_lo < k_hi) {
+        load(k_lo);
+        store(0);
+    }
+    __syncthreads();
+    for (int k0 = k_lo; k0 < k_hi; k0 += kProjBK) {
+        const bool more = k0 + kProjBK < k_hi;
+        const int nsub = min(kProjBK, k_hi - k0) / 16;  // 16-wide MFMA steps in this stage: 2 or 4
+        if (more) load(k0 + kProjBK);
+#pragma unroll
+        for (int ks = 0; ks < kProjBK / 16; ++ks) {
+            if (ks < nsub) {
+                uint4 fa[2], fb[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    fa[t] = *reinterpret_cast<const uint4 *>(&As[buf][wr + 32 * t + n][16 * ks + 8 * hh]);
+                    fb[t] = *reinterpret_cast<const uint4 *>(&Bs[buf][wc + 32 * t + n][16 * ks + 8 * hh]);
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
+                                                                            __builtin_bit_cast(bf16x8_t, fb[j]),
+                                                                            acc[i][j], 0, 0, 0);
+            }
+        }
+        // buf ^ 1 was last read in the previous stage, before the barrier
+        // that closed it: one barrier a stage suffices
+        if (more) store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    // value 4q + e of lane (n, hh) is row 8q + 4hh + e of the A tile, column n of the B tile
+    float *y = p.y + size_t(sk) * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wc + 32 * j + n;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = m0 + wr + 32 * i + 8 * q + 4 * hh + e;
+                    if (row < p.M && col < p.N) y[size_t(row) * p.N + col] = acc[i][j][4 * q + e];
+                }
+        }
+}
+
 }  // namespace
+
+RnnProjPlan rnn_proj_plan(int B, int gamma, int r, int d) {
+    RnnProjPlan pl{};
+    const long long M = 1LL * B * gamma, N = 3LL * r;
+    // worth it once the h part dominates the per-position product: measured
+    // at B = 256, r = 256, gamma = 5, a block takes 5 us longer with it at
+    // d = 1024 and 19 us / 56 us less at d = 2048 / 4096
+    if (d <= 4 * r || gamma < 2) return pl;
+    const long long tiles = ((M + kProjTile - 1) / kProjTile) * ((N + kProjTile - 1) / kProjTile);
+    const int ksteps = d / 32;
+    // as many K splits as fit one workgroup a CU (256 CUs), at most
+    // kMaxSplits (the gate kernel sums them)
+    int S = int(std::max(1LL, std::min<long long>(std::min(ksteps, kMaxSplits), 256 / tiles)));
+    const int kchunk = 32 * ((ksteps + S - 1) / S);
+    S = (d + kchunk - 1) / kchunk;
+    if (size_t(S) * M * N * 4 > (size_t(512) << 20)) return pl;  // too large: the gate kernel covers h itself
+    pl.S = S;
+    pl.kchunk = kchunk;
+    pl.blocks = int(tiles * S);
+    pl.floats = size_t(S) * M * N;
+    return pl;
+}
+
+hipError_t launch_rnn_hproj(const float *h, const uint16_t *Wgco, float *y, int B, int gamma, int r, int d,
+                            const RnnProjPlan &pl, hipStream_t s) {
+    HprojParams p{h, Wgco, y, B * gamma, 3 * r, d, 2 * r + d, r, pl.kchunk};
+    launch_kernel("rnn_hproj", rnn_hproj_kernel, dim3(pl.blocks), dim3(256), s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_rnn_gate(const RnnGateArgs &a, hipStream_t s) {
     GateParams p{};
@@ -163,6 +344,10 @@ hipError_t launch_rnn_gate(const RnnGateArgs &a, hipStream_t s) {
     p.e_out = a.e_out;
     p.e_stride = a.e_stride;
     p.idx_out = a.idx_out;
+    p.yh = a.yh;
+    p.yh_split = a.yh_split;
+    p.yS = a.yS;
+    p.kpos = a.kpos;
     p.gamma = a.gamma;
     p.B = a.B;
     p.V = a.V;

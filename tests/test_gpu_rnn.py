@@ -129,6 +129,12 @@ def _compare_rnn_draft(gd, od, bound, temperature, tag):
     (40, 5, 2053, 256, 1024), # the headline head shape
     (70, 6, 4099, 64, 96),
     (300, 2, 700, 128, 32),   # many request tiles
+    # d > 4r (and gamma >= 2): the h part is precomputed for the whole block
+    (40, 5, 2053, 256, 2048), # 8 K splits of 256
+    (17, 3, 1003, 16, 96),    # 3 splits, each a single 32-wide stage
+    (70, 4, 4099, 64, 288),   # 5 splits, the last one 32 wide
+    (1, 2, 1000, 16, 96),     # one request: a 2-row product
+    (9, 1, 1000, 16, 96),     # gamma 1: not precomputed
 ])
 def test_rnn_draft_parity(B, gamma, V, r, d):
     cfg, rnd, h, bits, Wg = _rnn_case(B, gamma, V, r, d, seed=B * 7 + r + d, greedy_every=4)
@@ -149,16 +155,18 @@ def test_rnn_draft_parity(B, gamma, V, r, d):
     assert full.any() and s_err < 2e-3  # the neighbouring-rounding effect above, carried through the block
 
 
-def test_rnn_round_large_batch_config():
-    """Batch 256, gamma 5, V 129,280, r 256, d 1024: RNN draft and its verify
-    against the oracle on a sample of requests."""
+@pytest.mark.parametrize("d", [1024, 4096])
+def test_rnn_round_large_batch_config(d):
+    """Batch 256, gamma 5, V 129,280, r 256, d 1024 (the per-position product
+    covers h) and 4096 (h part precomputed): RNN draft and its verify against
+    the oracle on a sample of requests."""
     cfg = S.CONFIGS["large"]
     rnd = S.make_round(cfg)
-    h, _ = S.confidence_head_inputs(cfg)
-    bits, Wg = S.rnn_head_weights(cfg)
+    h, _ = S.confidence_head_inputs(cfg, d)
+    bits, Wg = S.rnn_head_weights(cfg, d)
     ell = np.full(cfg.B, cfg.gamma, np.int32)
     target = rnd.target_packed(ell)
-    _say(f"[rnn-large] B={cfg.B} V={cfg.V}")
+    _say(f"[rnn-large] B={cfg.B} V={cfg.V} d={d}")
     dev = _dev_rnn(rnd, h, bits)
     g = _gpu_draft_rnn(dev, cfg.seed, 0)
     td = torch.from_numpy(target).cuda()
