@@ -134,7 +134,7 @@ hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const in
 struct VerifyPlan {
     int nseg_first, seg_len_first;  // segments of a target row in the first position pass, entries each
     int nseg, seg_len;              // the same for the later passes (entries a multiple of 4)
-    int nseg_max;                   // partials kept per request
+    int nseg_max;                   // partials kept per request (at most 64 / rows a pass)
     int nbb;          // ceil(B / 32)
     DraftPlan tile;   // vocabulary walk of the resample / bonus draw
     int draw_nbg;     // workgroups per chunk of the draw (room for both lists)

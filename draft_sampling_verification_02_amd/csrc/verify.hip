@@ -188,6 +188,12 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
 // gamma + 2; at the headline size the extra bytes cost more than the passes
 // they save, so one row a pass it is.
 constexpr int kPassRows = 1;
+// segments of a row in the first position pass and in the later ones
+// (measured at the headline size: 8 first-pass segments take 1 us less than
+// 4; 16 or 64 later segments take 1-2 us a pass more than 32)
+constexpr int kSegFirst = 8, kSegLater = 32;
+static_assert(kSegFirst <= 64 / kPassRows && kSegLater <= 64 / kPassRows,
+              "the next pass merges a row's segment statistics in 64 / kPassRows lanes");
 
 struct PassParams {
     const float *target;
@@ -335,6 +341,8 @@ template <bool PIPE>
 __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     constexpr int D = kPassRows;
     static_assert(D <= 2, "two row slots fit the two lane halves");
+    constexpr int LPS = 64 / D;  // lanes holding one row slot's segment statistics
+    constexpr int LOG_LPS = D == 1 ? 6 : 5;
     const int sg = blockIdx.x % p.nseg;
     const int q = (blockIdx.x / p.nseg) % D;
     const int b = (blockIdx.x / (p.nseg * D)) * 4 + (threadIdx.x >> 6);
@@ -384,9 +392,9 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     } else {
         // every load the decisions need, issued together and unconditionally
         // (clamped indices; what a case does not use is masked after): lane
-        // half h holds the segment statistics of the previous pass's row slot
-        // h, read whatever the request's state
-        const int hq = min(lane >> 5, D - 1), c = min(lane & 31, p.nseg_in - 1);
+        // group h (of LPS lanes) holds the segment statistics of the previous
+        // pass's row slot h, read whatever the request's state
+        const int hq = min(lane / LPS, D - 1), c = min(lane % LPS, p.nseg_in - 1);
         const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
         mode = p.mode[b];
         offb = p.off[b];
@@ -406,7 +414,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::"v"(mode), "v"(offb), "v"(act), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
-        if (!((lane >> 5) < D && (lane & 31) < p.nseg_in)) {
+        if (!((lane / LPS) < D && (lane % LPS) < p.nseg_in)) {
             mm = kNegInf;
             s2 = 0.f;
             v2 = kNegInf;
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
     if (!PIPE && j0 > 1) {
-        bfly_steps<0, 5>([&](auto st) {  // within each lane half
+        bfly_steps<0, LOG_LPS>([&](auto st) {  // within each lane group
             constexpr int S = decltype(st)::value;
             const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
             const int i_o = bfly<S>(i2);
@@ -431,9 +439,9 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         int amax[D];
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            const float mu = __shfl(mm, 32 * u), su = __shfl(s2, 32 * u);
+            const float mu = __shfl(mm, LPS * u), su = __shfl(s2, LPS * u);
             lse2[u] = (mu == kNegInf) ? kNegInf : mu + fast_log2(su);
-            amax[u] = min(max(__shfl(i2, 32 * u), 0), p.V - 1);
+            amax[u] = min(max(__shfl(i2, LPS * u), 0), p.V - 1);
         }
         int go_on = 0;
         if (lane == 0) {
@@ -904,6 +912,13 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     }
 }
 
+// Segments a row of position pass `pass` is split into (the decide-only last
+// pass: one); at most 64 / kPassRows, the lanes the next pass merges them in.
+int pass_segments(const VerifyPlan &pl, int pass, int npass) {
+    if (pass == 1) return pl.nseg_first;
+    return pass == npass ? 1 : pl.nseg;
+}
+
 template <typename WT, int R>
 hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyWork &w, hipStream_t s) {
     hipError_t e;
@@ -925,7 +940,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
         const size_t half = rs * kPassRows;
         // the last pass only decides: one wave a request
-        const int nseg = (pass == 1) ? pl.nseg_first : (pass == npass ? 1 : pl.nseg);
+        const int nseg = pass_segments(pl, pass, npass);
         PassParams pp{};
         pp.target = a.target;
         pp.x = a.x;
@@ -938,8 +953,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.j0 = (pass - 1) * kPassRows + 1;
         pp.vec = vec_t;
         pp.nseg = nseg;
-        pp.seg_len = (pass == 1) ? pl.seg_len_first : pl.seg_len;
-        pp.nseg_in = (pass == 2) ? pl.nseg_first : pl.nseg;
+        pp.seg_len = pass == 1 ? pl.seg_len_first : pl.seg_len;
+        pp.nseg_in = pass_segments(pl, pass - 1, npass);
         pp.seg_stride = pl.nseg_max;
         pp.row_stride = rs;
         pp.key0 = a.key0;
@@ -1070,14 +1085,14 @@ VerifyPlan verify_plan(int B, int gamma, int V) {
     // Position passes split a row into segments of whole float4 groups: the
     // first pass, which reads every request's row, in a few long ones (long
     // streams per workgroup), the later ones, which read fewer and fewer rows,
-    // in up to 32 short ones (more waves per row).
+    // in up to kSegLater short ones (more waves per row).
     const int n4 = (V + 3) / 4;
     auto split = [&](int k, int &nseg, int &len) {
         len = 4 * ((n4 + k - 1) / k);
         nseg = (V + len - 1) / len;
     };
-    split(4, p.nseg_first, p.seg_len_first);
-    split(32, p.nseg, p.seg_len);
+    split(kSegFirst, p.nseg_first, p.seg_len_first);
+    split(kSegLater, p.nseg, p.seg_len);
     p.nseg_max = std::max(p.nseg_first, p.nseg);
     p.nbb = (B + 31) / 32;
     // 8-wave workgroups holding two one-tile stages of W2 rows and wave
