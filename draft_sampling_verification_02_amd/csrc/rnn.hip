@@ -182,8 +182,10 @@ __global__ __launch_bounds__(kGateThreads) void rnn_gate_kernel(GateParams p) {
 }
 
 constexpr int kProjTile = 128;  // output tile edge
-constexpr int kProjBK = 64;     // K entries a stage
-constexpr int kProjPad = 72;    // LDS row length in bf16 (64 used): 144-byte rows
+constexpr int kProjBK = 64;     // K entries a stage (a multiple of 32)
+constexpr int kProjPad = kProjBK + 8;  // LDS row length in bf16: rows 16 bytes apart from a bank multiple
+constexpr int kProjA = kProjTile * kProjBK / 4 / 256;  // float4 loads of h a thread a stage
+constexpr int kProjB = kProjTile * kProjBK / 8 / 256;  // uint4 loads of Wgco a thread a stage
 
 struct HprojParams {
     const float *h;        // [M, d]
@@ -197,8 +199,8 @@ struct HprojParams {
 // columns 64 (w % 2) .. + 63 as 2 x 2 MFMA tiles; each 64-wide K stage is
 // staged in LDS (double-buffered) by the whole workgroup while the next one
 // is loaded into registers.  K splits are multiples of 32, so a split's
-// last stage may hold only 32 entries: its upper half is then loaded from
-// the lower half's addresses and not used.
+// last stage may hold fewer entries (a multiple of 32): its loads past them
+// repeat the last group and are not used.
 __global__ __launch_bounds__(256) void rnn_hproj_kernel(HprojParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kProjTile][kProjPad];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kProjTile][kProjPad];
@@ -209,37 +211,39 @@ __global__ __launch_bounds__(256) void rnn_hproj_kernel(HprojParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, hh = lane >> 5;
     const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);
-    // staging slots: A 8 float4 a thread (row idx / 16, columns 4 (idx % 16)),
-    // B 4 uint4 (row idx / 8, columns 8 (idx % 8)); rows past the matrix
-    // repeat its last row (their outputs are not written)
-    float4 ra[8];
-    uint4 rb[4];
+    // staging slots: A kProjA float4 a thread (row idx / (BK / 4), columns
+    // 4 (idx % (BK / 4))), B kProjB uint4 (row idx / (BK / 8), columns
+    // 8 (idx % (BK / 8))); rows past the matrix repeat its last row (their
+    // outputs are not written)
+    constexpr int AC = kProjBK / 4, BC = kProjBK / 8;
+    float4 ra[kProjA];
+    uint4 rb[kProjB];
     auto load = [&](int k0) __device__ {
-        const int hmask = k0 + kProjBK <= k_hi ? kProjBK - 1 : kProjBK / 2 - 1;
+        const int rem = min(kProjBK, k_hi - k0);  // entries of this stage
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = tid + 256 * u, row = min(m0 + idx / 16, p.M - 1);
-            ra[u] = *reinterpret_cast<const float4 *>(p.h + size_t(row) * p.d + k0 + ((4 * (idx % 16)) & hmask));
+        for (int u = 0; u < kProjA; ++u) {
+            const int idx = tid + 256 * u, row = min(m0 + idx / AC, p.M - 1);
+            ra[u] = *reinterpret_cast<const float4 *>(p.h + size_t(row) * p.d + k0 + min(4 * (idx % AC), rem - 4));
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = tid + 256 * u, row = min(n0 + idx / 8, p.N - 1);
+        for (int u = 0; u < kProjB; ++u) {
+            const int idx = tid + 256 * u, row = min(n0 + idx / BC, p.N - 1);
             rb[u] = *reinterpret_cast<const uint4 *>(p.Wgco + size_t(row) * p.K + 2 * p.R + k0 +
-                                                     ((8 * (idx % 8)) & hmask));
+                                                     min(8 * (idx % BC), rem - 8));
         }
     };
     auto store = [&](int buf) __device__ {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kProjA; ++u) {
             const int idx = tid + 256 * u;
             const uint2 v = make_uint2(bf16_bits(ra[u].x) | (bf16_bits(ra[u].y) << 16),
                                        bf16_bits(ra[u].z) | (bf16_bits(ra[u].w) << 16));
-            *reinterpret_cast<uint2 *>(&As[buf][idx / 16][4 * (idx % 16)]) = v;
+            *reinterpret_cast<uint2 *>(&As[buf][idx / AC][4 * (idx % AC)]) = v;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kProjB; ++u) {
             const int idx = tid + 256 * u;
-            *reinterpret_cast<uint4 *>(&Bs[buf][idx / 8][8 * (idx % 8)]) = rb[u];
+            *reinterpret_cast<uint4 *>(&Bs[buf][idx / BC][8 * (idx % BC)]) = rb[u];
         }
     };
     f32x16_t acc[2][2];
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256) void rnn_hproj_kernel(HprojParams p) {
     __syncthreads();
     for (int k0 = k_lo; k0 < k_hi; k0 += kProjBK) {
         const bool more = k0 + kProjBK < k_hi;
-        const int nsub = min(kProjBK, k_hi - k0) / 16;  // 16-wide MFMA steps in this stage: 2 or 4
+        const int nsub = min(kProjBK, k_hi - k0) / 16;  // 16-wide MFMA steps in this stage (even)
         if (more) load(k0 + kProjBK);
 #pragma unroll
         for (int ks = 0; ks < kProjBK / 16; ++ks) {
