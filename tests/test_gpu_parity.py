@@ -7,6 +7,7 @@ decisions all clear their margins (draft and resample Gumbel top-two gaps
 gap > 1e-3); probabilities agree within 1e-4.  The rest are counted and
 reported.
 """
+import dataclasses
 import math
 import os
 
@@ -242,6 +243,60 @@ def test_neg_inf_logits_parity():
     for b in range(40):
         for k in range(4):
             assert np.isfinite(rnd.U[b, k, gd["x"][b, k]])
+
+
+def test_nonfinite_inputs_stay_in_bounds_and_leave_other_requests_alone():
+    """NaN and +inf inputs have no defined result, but a call with them must
+    finish, write only where it may, and keep requests independent: base
+    logits, target rows and a temperature poisoned for a few requests leave
+    every other request's draft, verify and acceptance outputs bit for bit
+    as in the clean call, and the poisoned requests still get tokens in
+    range, counts within their lengths and -1 padding after them."""
+    B, gamma, V = 40, 4, 3001
+    rnd, ell, target = _custom_round(B, gamma, V, 64, "bf16", seed=12, greedy_every=6)
+    off = S.pack_offsets(ell)
+
+    def run(r, t):
+        dev = to_device(r)
+        td, ed = torch.from_numpy(t).cuda(), torch.from_numpy(ell).cuda()
+        d = gpu_draft(dev, 5, 3)
+        v = gpu_verify(dev, td, ed, d, 5, 3)
+        a = ds.dspark_acceptance(td, ed, dev["U"], dev["W1"], dev["W2"], dev["anchor"], d["x"], d["lse"],
+                                 dev["temperature"])
+        torch.cuda.synchronize()
+        assert ds.dspark_verify_check(v["workspace"]) == 0
+        out = {k: np_of(x) for k, x in list(d.items()) + list(v.items()) if k != "workspace"}
+        out["alpha"] = np_of(a)
+        return out
+
+    clean = run(rnd, target)
+    bad_u = rnd.U.copy()
+    bad_u[3] = np.nan                 # every base logit of a request
+    bad_u[7, 1, ::5] = np.nan         # a fifth of one position's
+    bad_u[11, 0, 17] = np.inf         # one +inf logit
+    bad_u[13, 2] = -np.inf            # a position with no finite logit
+    bad_t = target.copy()
+    bad_t[off[23]:off[24]] = np.nan   # every target row of a request
+    bad_t[off[29] + min(ell[29], 1), 40] = np.inf
+    temp = rnd.temperature.copy()
+    temp[19] = np.nan
+    poisoned = dataclasses.replace(rnd, U=bad_u, temperature=temp)
+    got = run(poisoned, bad_t)
+    hit = np.zeros(B, bool)
+    hit[[3, 7, 11, 13, 19, 23, 29]] = True
+    _say(f"[nonfinite] poisoned requests {np.flatnonzero(hit).tolist()}")
+    for k in clean:
+        if k == "offsets":  # a scan over every request: checked against the counts below
+            continue
+        a, b = clean[k][~hit], got[k][~hit]
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{k} changed for an untouched request"
+    np.testing.assert_array_equal(got["offsets"], np.concatenate([[0], np.cumsum(got["n"] + 1)]))
+    assert np.all((got["x"] >= 0) & (got["x"] < V))
+    n, tok = got["n"], got["tokens"]
+    assert np.all((n >= 0) & (n <= ell))
+    for b in range(B):
+        assert np.all((tok[b, :n[b] + 1] >= 0) & (tok[b, :n[b] + 1] < V)), b
+        assert np.all(tok[b, n[b] + 1:] == -1), b
 
 
 @pytest.mark.parametrize("B", [24, 600])  # input checks in the first pass / in a prep workgroup
