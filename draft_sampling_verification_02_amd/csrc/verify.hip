@@ -18,15 +18,17 @@
 //                    ones have the first pass do it): packed row offsets
 //                    (scan of 1 + ell, or the caller's, checked), output
 //                    defaults, pass state.
-//   verify_pass      gamma + 2 launches; launch p runs over the requests
-//                    still testing: one wave per (request, vocabulary
-//                    segment) first decides position p - 1 from the segment
-//                    statistics launch p - 1 left (the accept test u*q < p,
-//                    or the bonus row), then, if the request goes on,
-//                    streams its segment of row p for logsumexp(t / T) in
-//                    base 2 and the lowest-index argmax.  The last launch
-//                    only decides.  A request stops at its first rejection,
-//                    so rows past it are never read.
+//   verify_pass      one launch a position for the first few positions, one
+//                    a pair of positions after them, and a last one that
+//                    only decides; each runs over the requests still
+//                    testing: one wave per (request, row, vocabulary
+//                    segment) first decides the positions the previous
+//                    launch reduced, from the segment statistics it left
+//                    (the accept test u*q < p, or the bonus row), then, if
+//                    the request goes on, streams its segment of the row for
+//                    logsumexp(t / T) in base 2 and the lowest-index argmax.
+//                    A request stops at its first rejection, so rows past it
+//                    are never read (but the second row of a pair).
 //   verify_draw      level 1: waves of 32 listed requests walk vocabulary
 //                    chunks; residual rows recompute q_j with the draft's
 //                    LDS-staged MFMA bias tile and sum max(p_j - q_j, 0) per
@@ -37,6 +39,7 @@
 //                    races them; writes the emitted token and S.  One more
 //                    workgroup scans the emitted counts into out_offsets.
 #include "device_common.hpp"
+#include "dspark.h"
 #include "internal.hpp"
 #include "stage.hpp"
 
@@ -181,13 +184,16 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
 
 // ------------------------------------------------------------------ position pass
 
-// Rows a position pass reduces: pass p reduces positions (p-1)*D+1 .. p*D of
-// the requests still testing and decides the D positions pass p - 1 reduced.
-// With D = 2 a request that rejects at the first of a pair has the second row
-// read for nothing, in exchange for (gamma + 1) / 2 + 1 passes instead of
-// gamma + 2; at the headline size the extra bytes cost more than the passes
-// they save, so one row a pass it is.
-constexpr int kPassRows = 1;
+// Rows a position pass reduces: one or two consecutive positions of the
+// requests still testing; the pass first decides the positions the previous
+// pass reduced.  A request that rejects at the first of a pair has the second
+// row read for nothing, against one launch less.  Few requests are still
+// testing late in the block, so there the launch costs more than the row:
+// the first kSinglePasses positions get a pass each, the rest go in pairs
+// (an odd one left first on its own), then one pass decides the last rows.
+constexpr int kPassRows = 2;  // row slots a pass can hold
+constexpr int kSinglePasses = 3;
+static_assert(kSinglePasses >= 1, "the first pass reduces one row");
 // segments of a row in the first position pass and in the later ones
 // (measured at the headline size: 8 first-pass segments take 1 us less than
 // 4; 16 or 64 later segments take 1-2 us a pass more than 32)
@@ -329,23 +335,23 @@ __device__ __forceinline__ void row_batch(float4 (&xs)[U], int v0, Valid valid, 
     }
 }
 
-// Pass p, one wave per (request, row slot q, vocabulary segment), four
-// requests to a workgroup.  First the request's previous D positions are
+// Pass p, one wave per (request, row slot q < DOUT, vocabulary segment),
+// four requests to a workgroup.  First the request's DIN previous positions are
 // decided, in order, from the segment statistics pass p - 1 wrote; a request
 // that goes on streams segment sg of its row j0 + q: every lane keeps its own
 // running max / sum of exp2 and argmax over batches of eight float4 loads
 // (PIPE: two batches, one in flight while the other is reduced, for the long
 // segments of the first pass), and the wave merges them.  The waves never
 // wait for one another.
-template <bool PIPE>
+template <bool PIPE, int DIN, int DOUT>
 __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
-    constexpr int D = kPassRows;
-    static_assert(D <= 2, "two row slots fit the two lane halves");
-    constexpr int LPS = 64 / D;  // lanes holding one row slot's segment statistics
-    constexpr int LOG_LPS = D == 1 ? 6 : 5;
+    static_assert(DIN >= 1 && DIN <= kPassRows && DOUT >= 1 && DOUT <= kPassRows,
+                  "row slots: the previous pass's (DIN) and this pass's (DOUT)");
+    constexpr int LPS = 64 / DIN;  // lanes holding one previous row slot's segment statistics
+    constexpr int LOG_LPS = DIN == 1 ? 6 : 5;
     const int sg = blockIdx.x % p.nseg;
-    const int q = (blockIdx.x / p.nseg) % D;
-    const int b = (blockIdx.x / (p.nseg * D)) * 4 + (threadIdx.x >> 6);
+    const int q = (blockIdx.x / p.nseg) % DOUT;
+    const int b = (blockIdx.x / (p.nseg * DOUT)) * 4 + (threadIdx.x >> 6);
     const int j0 = p.j0, j = j0 + q;
     const int lane = threadIdx.x & 63;
     if (b >= p.B) return;
@@ -354,8 +360,8 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     float T;
     float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
     int i2 = 0x7fffffff;
-    float tx2[D], qk[D];
-    int xk[D];
+    float tx2[DIN], qk[DIN];
+    int xk[DIN];
     if constexpr (PIPE) {
         // the first pass decides nothing: it needs the request's temperature
         // and length and, for a small batch, does its input checks (the row
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         // (clamped indices; what a case does not use is masked after): lane
         // group h (of LPS lanes) holds the segment statistics of the previous
         // pass's row slot h, read whatever the request's state
-        const int hq = min(lane / LPS, D - 1), c = min(lane % LPS, p.nseg_in - 1);
+        const int hq = min(lane / LPS, DIN - 1), c = min(lane % LPS, p.nseg_in - 1);
         const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
         mode = p.mode[b];
         offb = p.off[b];
@@ -406,15 +412,15 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         v2 = p.pv_in[o_in];
         i2 = p.pi_in[o_in];
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int k = min(max(j0 - D + u, 1), p.gamma);  // position decided from slot u (clamped)
+        for (int u = 0; u < DIN; ++u) {
+            const int k = min(max(j0 - DIN + u, 1), p.gamma);  // position decided from slot u (clamped)
             tx2[u] = p.tx_in[size_t(u) * p.B + b];
             xk[u] = p.x[size_t(b) * p.gamma + k - 1];
             qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
         }
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::"v"(mode), "v"(offb), "v"(act), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
-        if (!((lane / LPS) < D && (lane % LPS) < p.nseg_in)) {
+        if (!((lane / LPS) < DIN && (lane % LPS) < p.nseg_in)) {
             mm = kNegInf;
             s2 = 0.f;
             v2 = kNegInf;
@@ -435,10 +441,10 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             lse_merge(mm, s2, m_o, s_o);
             argmax_merge(v2, i2, v_o, i_o);
         });
-        float lse2[D];
-        int amax[D];
+        float lse2[DIN];
+        int amax[DIN];
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
+        for (int u = 0; u < DIN; ++u) {
             const float mu = __shfl(mm, LPS * u), su = __shfl(s2, LPS * u);
             lse2[u] = (mu == kNegInf) ? kNegInf : mu + fast_log2(su);
             amax[u] = min(max(__shfl(i2, LPS * u), 0), p.V - 1);
@@ -447,8 +453,8 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         if (lane == 0) {
             go_on = 1;
 #pragma unroll
-            for (int u = 0; u < D; ++u) {
-                const int k = j0 - D + u;
+            for (int u = 0; u < DIN; ++u) {
+                const int k = j0 - DIN + u;
                 if (!go_on || k > L + 1) break;
                 go_on = pass_decide(p, b, L, k, sampled, lse2[u], amax[u], tx2[u], xk[u], qk[u], writer);
             }
@@ -912,11 +918,20 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     }
 }
 
-// Segments a row of position pass `pass` is split into (the decide-only last
-// pass: one); at most 64 / kPassRows, the lanes the next pass merges them in.
-int pass_segments(const VerifyPlan &pl, int pass, int npass) {
-    if (pass == 1) return pl.nseg_first;
-    return pass == npass ? 1 : pl.nseg;
+// The position passes of a block of gamma: first row and row count of each
+// (kSinglePasses single rows, then pairs, an odd row left over first), then
+// the decide-only pass (rows 0 at j0 = gamma + 2).
+struct PassRows {
+    int j0, rows;
+};
+int pass_schedule(int gamma, PassRows *out) {
+    int n = 0, j = 1;
+    const int last = gamma + 1;
+    for (; j <= last && j <= kSinglePasses; ++j) out[n++] = {j, 1};
+    if ((last - j + 1) % 2 == 1 && j <= last) out[n++] = {j++, 1};
+    for (; j <= last; j += 2) out[n++] = {j, 2};
+    out[n++] = {last + 1, 0};
+    return n;
 }
 
 template <typename WT, int R>
@@ -934,13 +949,17 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
-    const int npass = (a.gamma + 1 + kPassRows - 1) / kPassRows + 1;
+    PassRows sched[DSPARK_MAX_GAMMA + 2];  // gamma is checked at the boundary
+    const int npass = pass_schedule(a.gamma, sched);
     for (int pass = 1; pass <= npass; ++pass) {
         const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
         const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
         const size_t half = rs * kPassRows;
+        const PassRows cur = sched[pass - 1];
+        const int din = pass > 1 ? sched[pass - 2].rows : 1;  // rows this pass decides
+        const int dout = cur.rows > 0 ? cur.rows : 1;         // row slots of its grid
         // the last pass only decides: one wave a request
-        const int nseg = pass_segments(pl, pass, npass);
+        const int nseg = pass == 1 ? pl.nseg_first : (cur.rows == 0 ? 1 : pl.nseg);
         PassParams pp{};
         pp.target = a.target;
         pp.x = a.x;
@@ -950,11 +969,11 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.B = a.B;
         pp.gamma = a.gamma;
         pp.V = a.V;
-        pp.j0 = (pass - 1) * kPassRows + 1;
+        pp.j0 = cur.j0;
         pp.vec = vec_t;
         pp.nseg = nseg;
         pp.seg_len = pass == 1 ? pl.seg_len_first : pl.seg_len;
-        pp.nseg_in = pass_segments(pl, pass - 1, npass);
+        pp.nseg_in = pass == 2 ? pl.nseg_first : pl.nseg;
         pp.seg_stride = pl.nseg_max;
         pp.row_stride = rs;
         pp.key0 = a.key0;
@@ -994,11 +1013,18 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         pp.diag_out = a.diag_out;
         static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
                                             "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
-        const dim3 grid(size_t((a.B + 3) / 4) * nseg * kPassRows);
+        const dim3 grid(size_t((a.B + 3) / 4) * nseg * dout);
+        const char *name = names[std::min(pass, 8) - 1];
         if (pass == 1)
-            launch_kernel(names[std::min(pass, 8) - 1], verify_pass_kernel<true>, grid, dim3(256), s, pp);
+            launch_kernel(name, (verify_pass_kernel<true, 1, 1>), grid, dim3(256), s, pp);
+        else if (din == 1 && dout == 1)
+            launch_kernel(name, (verify_pass_kernel<false, 1, 1>), grid, dim3(256), s, pp);
+        else if (din == 1)
+            launch_kernel(name, (verify_pass_kernel<false, 1, 2>), grid, dim3(256), s, pp);
+        else if (dout == 1)
+            launch_kernel(name, (verify_pass_kernel<false, 2, 1>), grid, dim3(256), s, pp);
         else
-            launch_kernel(names[std::min(pass, 8) - 1], verify_pass_kernel<false>, grid, dim3(256), s, pp);
+            launch_kernel(name, (verify_pass_kernel<false, 2, 2>), grid, dim3(256), s, pp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
