@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kRowThreads) void accept_rowstats_kernel(AccRowPara
             for (int u = 0; u < 4; ++u) {
                 const int v = min(v0 + W * kRowThreads * u, v_hi - W);
                 if constexpr (VEC) {
-                    const float4 q = *reinterpret_cast<const float4 *>(row + v);
+                    const float4 q = load_stream(reinterpret_cast<const float4 *>(row + v));
                     x[u][0] = q.x;
                     x[u][1] = q.y;
                     x[u][2] = q.z;

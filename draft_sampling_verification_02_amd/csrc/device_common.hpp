@@ -412,6 +412,15 @@ __device__ __forceinline__ uint32_t u4get(const uint4 &a, int j) {
     return j == 0 ? a.x : (j == 1 ? a.y : (j == 2 ? a.z : a.w));
 }
 
+// A float4 of a logit row that is read once (target rows in the position
+// passes and the acceptance statistics): a non-temporal load, which leaves
+// the caches to the W2 rows and gathered W1 rows that are reused.
+__device__ __forceinline__ float4 load_stream(const float4 *q) {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4 *>(q));
+    return make_float4(x.x, x.y, x.z, x.w);
+}
+
 // Workgroup index remapped so that consecutive logical groups share one XCD:
 // the hardware deals workgroups round-robin over the 8 XCDs of the chip.
 __device__ __forceinline__ int xcd_remap(int b, int n) {

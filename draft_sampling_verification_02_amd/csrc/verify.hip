@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             // loads past the segment re-read its last group and are masked when used
             auto load = [&](float4(&xs)[U], int qb) __device__ {
     #pragma unroll
-                for (int u = 0; u < U; ++u) xs[u] = r4[min(qb + lane + 64 * u, q_hi - 1)];
+                for (int u = 0; u < U; ++u) xs[u] = load_stream(r4 + min(qb + lane + 64 * u, q_hi - 1));
             };
             // sampled rows keep no argmax (only greedy decisions use it); the
             // request, and so the branch, is uniform across the wave
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int q = q0 + 64 * u;
-                        xs[u] = q < q_hi ? r4[q] : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+                        xs[u] = q < q_hi ? load_stream(r4 + q) : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
                     }
                     row_batch<AM>(xs, 4 * q0, [](int) { return true; }, sc, m, s, av, ai);  // masked at the load
                 }
