@@ -87,6 +87,9 @@ def _logit_passes(phases, gv0, rnd, ell, B, gamma, V, r):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     put("verify_pass1", B * row, ["verify_pass1"])
+    # rows the method needs after the first: row j of every request that
+    # accepted positions 1 .. j - 1 (the second row of a paired pass, read
+    # for a request that then rejects the first, is not counted)
     later = sum(int(((n0 >= j - 1) & (ell >= j - 1)).sum()) for j in range(2, gamma + 2)) * row
     put("verify_pass2_on", later, [k for k in phases if k.startswith("verify_pass") and k != "verify_pass1"])
     put("verify_draw", (2 * n_res + n_bon) * row + (V * r * 2 if n_res else 0), ["verify_draw"])
