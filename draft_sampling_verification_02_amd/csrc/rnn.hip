@@ -310,9 +310,9 @@ RnnProjPlan rnn_proj_plan(int B, int gamma, int r, int d) {
     RnnProjPlan pl{};
     const long long M = 1LL * B * gamma, N = 3LL * r;
     // worth it once the h part dominates the per-position product: measured
-    // at B = 256, r = 256, gamma = 5, a block takes 5 us longer with it at
-    // d = 1024 and 19 us / 56 us less at d = 2048 / 4096
-    if (d <= 4 * r || gamma < 2) return pl;
+    // at B = 256, r = 256, gamma = 5, a block's draft takes 5.5 us less with
+    // it at d = 1024, and as much or less at d = 2048 and 4096
+    if (d < 4 * r || gamma < 2) return pl;
     const long long tiles = ((M + kProjTile - 1) / kProjTile) * ((N + kProjTile - 1) / kProjTile);
     const int ksteps = d / 32;
     // as many K splits as fit one workgroup a CU (256 CUs), at most

@@ -161,11 +161,11 @@ int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace dspark_draft_sample_rnn needs; 0 for invalid
- * sizes.  Besides the draft step's partials and the two states it holds the
- * h part of every position's gate product, Wgco[:, 2r:] h_k, computed for the
- * whole block before position 1 (float32 split-K partials, at most 512 MiB;
- * beyond that the per-position product covers h itself and the space is not
- * taken). */
+ * sizes.  Besides the draft step's partials and the two states it holds,
+ * when d >= 4r and gamma >= 2, the h part of every position's gate product,
+ * Wgco[:, 2r:] h_k, computed for the whole block before position 1 (float32
+ * split-K partials, at most 512 MiB; otherwise the per-position product
+ * covers h itself and the space is not taken). */
 size_t dspark_draft_rnn_workspace_size(int B, int gamma, int V, int r, int d);
 
 /* Draft sampling with the RNN head ([MG] 3.2, RNN Head) in place of the

@@ -126,10 +126,11 @@ def _compare_rnn_draft(gd, od, bound, temperature, tag):
     (1, 4, 1000, 16, 32),
     (5, 3, 17, 16, 0),        # no hidden part; a K step straddles s / W1
     (33, 4, 1003, 32, 64),    # ragged batch and vocabulary
-    (40, 5, 2053, 256, 1024), # the headline head shape
+    (40, 5, 2053, 256, 512),  # the headline rank, the per-position product covering h
     (70, 6, 4099, 64, 96),
     (300, 2, 700, 128, 32),   # many request tiles
-    # d > 4r (and gamma >= 2): the h part is precomputed for the whole block
+    # d >= 4r (and gamma >= 2): the h part is precomputed for the whole block
+    (40, 5, 2053, 256, 1024), # the headline head shape
     (40, 5, 2053, 256, 2048), # 8 K splits of 256
     (17, 3, 1003, 16, 96),    # 3 splits, each a single 32-wide stage
     (70, 4, 4099, 64, 288),   # 5 splits, the last one 32 wide
@@ -155,11 +156,11 @@ def test_rnn_draft_parity(B, gamma, V, r, d):
     assert full.any() and s_err < 2e-3  # the neighbouring-rounding effect above, carried through the block
 
 
-@pytest.mark.parametrize("d", [1024, 4096])
+@pytest.mark.parametrize("d", [512, 1024, 4096])
 def test_rnn_round_large_batch_config(d):
-    """Batch 256, gamma 5, V 129,280, r 256, d 1024 (the per-position product
-    covers h) and 4096 (h part precomputed): RNN draft and its verify against
-    the oracle on a sample of requests."""
+    """Batch 256, gamma 5, V 129,280, r 256, d 512 (the per-position product
+    covers h), 1024 and 4096 (h part precomputed): RNN draft and its verify
+    against the oracle on a sample of requests."""
     cfg = S.CONFIGS["large"]
     rnd = S.make_round(cfg)
     h, _ = S.confidence_head_inputs(cfg, d)
