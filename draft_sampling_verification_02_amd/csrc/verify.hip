@@ -19,8 +19,8 @@
 //                    (scan of 1 + ell, or the caller's, checked), output
 //                    defaults, pass state.
 //   verify_pass      one launch a position for the first few positions, one
-//                    a pair of positions after them, and a last one that
-//                    only decides; each runs over the requests still
+//                    a pair of positions after them (from the first one on
+//                    for a small batch), and a last one that only decides; each runs over the requests still
 //                    testing: one wave per (request, row, vocabulary
 //                    segment) first decides the positions the previous
 //                    launch reduced, from the segment statistics it left
@@ -191,9 +191,12 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
 // testing late in the block, so there the launch costs more than the row:
 // the first kSinglePasses positions get a pass each, the rest go in pairs
 // (an odd one left first on its own), then one pass decides the last rows.
+// A batch whose rows at one position take at most kPairAllBytes pairs from
+// the first position on: a launch costs about 7 us, about 45 MB of reads,
+// against at most B V 4 bytes read for nothing a pair.
 constexpr int kPassRows = 2;  // row slots a pass can hold
 constexpr int kSinglePasses = 3;
-static_assert(kSinglePasses >= 1, "the first pass reduces one row");
+constexpr size_t kPairAllBytes = size_t(64) << 20;
 // segments of a row in the first position pass and in the later ones
 // (measured at the headline size: 8 first-pass segments take 1 us less than
 // 4; 16 or 64 later segments take 1-2 us a pass more than 32)
@@ -919,15 +922,15 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
 }
 
 // The position passes of a block of gamma: first row and row count of each
-// (kSinglePasses single rows, then pairs, an odd row left over first), then
+// (`single` single rows, then pairs, an odd row left over first), then
 // the decide-only pass (rows 0 at j0 = gamma + 2).
 struct PassRows {
     int j0, rows;
 };
-int pass_schedule(int gamma, PassRows *out) {
+int pass_schedule(int gamma, int single, PassRows *out) {
     int n = 0, j = 1;
     const int last = gamma + 1;
-    for (; j <= last && j <= kSinglePasses; ++j) out[n++] = {j, 1};
+    for (; j <= last && j <= single; ++j) out[n++] = {j, 1};
     if ((last - j + 1) % 2 == 1 && j <= last) out[n++] = {j++, 1};
     for (; j <= last; j += 2) out[n++] = {j, 2};
     out[n++] = {last + 1, 0};
@@ -950,7 +953,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
     PassRows sched[DSPARK_MAX_GAMMA + 2];  // gamma is checked at the boundary
-    const int npass = pass_schedule(a.gamma, sched);
+    const int single = size_t(a.B) * a.V * sizeof(float) <= kPairAllBytes ? 0 : kSinglePasses;
+    const int npass = pass_schedule(a.gamma, single, sched);
     for (int pass = 1; pass <= npass; ++pass) {
         const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
         const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
@@ -1015,8 +1019,10 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
                                             "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
         const dim3 grid(size_t((a.B + 3) / 4) * nseg * dout);
         const char *name = names[std::min(pass, 8) - 1];
-        if (pass == 1)
+        if (pass == 1 && dout == 1)
             launch_kernel(name, (verify_pass_kernel<true, 1, 1>), grid, dim3(256), s, pp);
+        else if (pass == 1)
+            launch_kernel(name, (verify_pass_kernel<true, 1, 2>), grid, dim3(256), s, pp);
         else if (din == 1 && dout == 1)
             launch_kernel(name, (verify_pass_kernel<false, 1, 1>), grid, dim3(256), s, pp);
         else if (din == 1)
