@@ -137,6 +137,7 @@ struct VerifyPlan {
     int nseg_max;                   // partials kept per request (at most 64 / rows a pass)
     int nbb;          // ceil(B / 32)
     DraftPlan tile;   // vocabulary walk of the resample / bonus draw
+    int draw_nw;      // waves per workgroup of the draw
     int draw_nbg;     // workgroups per chunk of the draw (room for both lists)
     int draw_blocks;  // workgroups of the draw kernel
 };

@@ -596,6 +596,11 @@ struct DrawParams {
 };
 
 constexpr int kDrawThreads = 512;  // 8 waves: one block of 32 listed requests each
+// A batch of at most two 32-request blocks draws with 2-wave workgroups
+// instead: their stages take 64 KB of LDS, so two workgroups share a CU and
+// the walk spreads over about 512 of them, where an 8-wave workgroup would
+// hold one busy wave and the LDS of seven idle ones.
+constexpr int kDrawSmallWaves = 2;
 
 // Level 1 of the resample / bonus draws.  A workgroup of 8 waves walks the
 // tiles of one vocabulary chunk, one tile per stage, each wave holding 32
@@ -607,12 +612,11 @@ constexpr int kDrawThreads = 512;  // 8 waves: one block of 32 listed requests e
 // waves take the tile logsumexp of p.  Either way the tile score takes its
 // noise from stream 4.  The two halves of a wave hold the two halves of the
 // tile and combine their sums with one lane-half exchange.
-template <typename WT, int R, bool VEC>
-__global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_draw_kernel(
+template <typename WT, int R, bool VEC, int NWV>
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_draw_kernel(
     DrawParams p) {
     using L = TileLDS<WT, R>;
     using TR = TileRows<VEC>;
-    constexpr int NWV = kDrawThreads / 64;
     __shared__ __attribute__((aligned(16))) uint8_t ldsW0[L::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsW1[L::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsU0[NWV * TR::BYTES];
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(kDrawThreads) __attribute__((amdgpu_waves_per_eu(2,
             lse2q = p.lse2q[req];
         }
     }
-    TileDMA<WT, R, kDrawThreads> dma;
+    TileDMA<WT, R, NWV * 64> dma;
     if (need_w2) dma.init(tid);
     TR su, stg;
     if (wave_ok) stg.init(lane, p.target, size_t(p.V), [&](int r) { return __shfl(trow_i, r); });
@@ -1063,10 +1067,16 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.dw_sum = w.dw_sum;
         dp.dw_bl = w.dw_bl;
         dp.dw_bt = w.dw_bt;
-        if (vec_u && vec_t)
-            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, true>), dim3(pl.draw_blocks), dim3(kDrawThreads), s, dp);
+        const dim3 grid(pl.draw_blocks), block(64 * pl.draw_nw);
+        const bool vec = vec_u && vec_t, small = pl.draw_nw == kDrawSmallWaves;
+        if (vec && small)
+            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, true, kDrawSmallWaves>), grid, block, s, dp);
+        else if (small)
+            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, false, kDrawSmallWaves>), grid, block, s, dp);
+        else if (vec)
+            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, true, kDrawThreads / 64>), grid, block, s, dp);
         else
-            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, false>), dim3(pl.draw_blocks), dim3(kDrawThreads), s, dp);
+            launch_kernel("verify_draw", (verify_draw_kernel<WT, R, false, kDrawThreads / 64>), grid, block, s, dp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -1129,10 +1139,12 @@ VerifyPlan verify_plan(int B, int gamma, int V) {
     p.nbb = (B + 31) / 32;
     // 8-wave workgroups holding two one-tile stages of W2 rows and wave
     // regions (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them
-    // for the requests
-    p.tile = tile_walk_plan(B, V, kDrawThreads / 64, 256, 1);
+    // for the requests; a batch of at most two request blocks: 2-wave ones,
+    // two a CU, about 512
+    p.draw_nw = p.nbb <= kDrawSmallWaves ? kDrawSmallWaves : kDrawThreads / 64;
+    p.tile = tile_walk_plan(B, V, p.draw_nw, p.draw_nw == kDrawSmallWaves ? 512 : 256, 1);
     // the draw list holds every drawing request in B entries
-    p.draw_nbg = (p.nbb + kDrawThreads / 64 - 1) / (kDrawThreads / 64);
+    p.draw_nbg = (p.nbb + p.draw_nw - 1) / p.draw_nw;
     p.draw_blocks = p.tile.nchunk * p.draw_nbg;
     return p;
 }
