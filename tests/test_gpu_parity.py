@@ -299,6 +299,55 @@ def test_nonfinite_inputs_stay_in_bounds_and_leave_other_requests_alone():
         assert np.all(tok[b, n[b] + 1:] == -1), b
 
 
+def test_round_replays_from_a_graph_as_it_runs_eagerly():
+    """A round (draft + verify) makes no allocation, memset or host
+    synchronisation, so a caller can capture it in a graph: replays, with
+    eager rounds of other inputs between them, give the eager outputs bit
+    for bit.  Two input sets, each captured once, replayed three times."""
+    rnd, ell, target = _custom_round(40, 4, 3001, 64, "bf16", seed=21, greedy_every=5)
+    dev = to_device(rnd)
+    U2 = (dev["U"] + 0.25).contiguous()
+    tds = [torch.from_numpy(target).cuda(), torch.from_numpy(target).cuda() * 0.5]
+    ed = torch.from_numpy(ell).cuda()
+    d = gpu_draft(dev, 7, 1)
+    v = gpu_verify(dev, tds[0], ed, d, 7, 1)
+
+    def step(i):
+        U = dev["U"] if i == 0 else U2
+        ds.dspark_draft_sample(U, dev["W1"], dev["W2"], dev["anchor"], dev["temperature"], 7, 1 + i, out=d)
+        ds.dspark_verify(tds[i], ed, U, dev["W1"], dev["W2"], dev["anchor"], d["x"], d["lse"], d["qx"],
+                         dev["temperature"], 7, 1 + i, out=v)
+
+    keys = ("x", "lse", "qx")
+    ref = []
+    for i in range(2):
+        step(i)
+        torch.cuda.synchronize()
+        ref.append({k: d[k].clone() for k in keys} | {k: v[k].clone() for k in ("n", "tokens", "offsets")})
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+        step(1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for rep in range(3):
+        for i in range(2):
+            graphs[i].replay()
+            torch.cuda.synchronize()
+            got = {k: d[k] for k in keys} | {k: v[k] for k in ("n", "tokens", "offsets")}
+            for k, t in got.items():
+                assert torch.equal(t.view(torch.int32), ref[i][k].view(torch.int32)), (rep, i, k)
+            step(1 - i)  # an eager round of the other inputs between replays
+            torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("B", [24, 600])  # input checks in the first pass / in a prep workgroup
 def test_row_offsets_given_equal_computed_and_bad_ell_flagged(B):
     rnd, ell, target = _custom_round(B, 3, 500, 16, "bf16", seed=9)
