@@ -186,6 +186,16 @@ def test_rnn_argument_errors_need_no_gpu():
     lib = ds.load_library()
     assert ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, 1024) > ds.dspark_draft_workspace_size(256, 5, 129280, 256)
     assert ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, -1) == 0
+    # the h part of the gate product is precomputed for d >= 4r and gamma >= 2:
+    # float32 partials of B gamma 3r entries (one or more K splits) join the
+    # workspace there, and only there
+    base = ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, 0)
+    below = ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, 4 * 256 - 32)
+    at = ds.dspark_draft_rnn_workspace_size(256, 5, 129280, 256, 4 * 256)
+    assert below == base
+    assert at - base >= 256 * 5 * 3 * 256 * 4
+    assert ds.dspark_draft_rnn_workspace_size(256, 1, 129280, 256, 4096) == \
+        ds.dspark_draft_rnn_workspace_size(256, 1, 129280, 256, 0)  # gamma 1: not precomputed
 
     def call(**kw):
         a = dict(U=_FAKE, W1=_FAKE, W2=_FAKE, Wgco=_FAKE, wdtype=0, anchor=_FAKE, temperature=_FAKE, hidden=_FAKE,
