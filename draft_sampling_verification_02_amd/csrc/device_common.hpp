@@ -198,6 +198,15 @@ struct EFrags<uint16_t, R> {
 #pragma unroll
         for (int s = 0; s < S; ++s) e[s] = *reinterpret_cast<const uint4 *>(row + 16 * s + 8 * h);
     }
+    // from a packed block (PackedE): one 1 KiB contiguous load a fragment
+    __device__ __forceinline__ void load_packed(const uint4 *blk, int lane) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) e[s] = blk[s * 64 + lane];
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int s = 0; s < S; ++s) e[s] = make_uint4(0u, 0u, 0u, 0u);
+    }
     // the fragments as values an empty asm defines (waits for their loads)
     __device__ __forceinline__ void pin() {
 #pragma unroll
@@ -213,6 +222,14 @@ struct EFrags<float, R> {
     __device__ __forceinline__ void load(const float *row, int h) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) e[q] = *reinterpret_cast<const float4 *>(row + 8 * q + 4 * h);
+    }
+    __device__ __forceinline__ void load_packed(const uint4 *blk, int lane) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) e[q] = reinterpret_cast<const float4 *>(blk)[q * 64 + lane];
+    }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) e[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __device__ __forceinline__ void pin() {
 #pragma unroll
@@ -274,6 +291,19 @@ __device__ __forceinline__ f32x16_t bias_tile_lds(const EFrags<float, R> &ef, co
     return acc;
 }
 
+// Packed E rows: the B-operand fragments of a block of 32 requests laid out
+// in the order the MFMA tile reads them, so that a wave loads each fragment
+// with one contiguous 1 KiB instruction.  A row of RB bytes is 2 NF chunks of
+// 16 bytes (NF = RB / 32); chunk c of request n's row sits at 16-byte slot
+// (f * 64 + n + 32 hh) of its block, f = c / 2, hh = c % 2 (lane (n, hh)
+// feeds chunk 2 f + hh at K-step f, as EFrags::load does from the row).
+template <typename WT, int R>
+struct PackedE {
+    static constexpr int NF = R * int(sizeof(WT)) / 32;  // fragments (K-steps) a row
+    static constexpr int BLOCK = NF * 64;                 // 16-byte slots a block of 32 requests
+    __device__ static __forceinline__ int slot(int n, int c) { return (c >> 1) * 64 + n + 32 * (c & 1); }
+};
+
 // One lane half's share of a W1 row (entries [h * R/2, (h + 1) * R/2)) held
 // in registers, and its dot product with the same share of a W2 row.
 template <typename WT, int R>
@@ -285,6 +315,12 @@ struct RowHalf {
         const uint4 *q = reinterpret_cast<const uint4 *>(row + h * HALF);
 #pragma unroll
         for (int i = 0; i < N; ++i) w[i] = q[i];
+    }
+    // this half of the row into row n of a PackedE block: piece i is chunk
+    // h N + i of the row
+    __device__ __forceinline__ void store_packed(uint4 *blk, int n, int h) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) blk[PackedE<WT, R>::slot(n, h * N + i)] = w[i];
     }
     // the full dot product W1row . W2row, summed over the two lane halves:
     // four independent accumulator chains, bf16 pairs through v_dot2 (each
@@ -310,6 +346,77 @@ struct RowHalf {
         }
         const float t = (d[0] + d[1]) + (d[2] + d[3]);
         return t + bfly<5>(t);
+    }
+};
+
+// The 32 dot products e . row(m), m = 0..31, of a tile of rows of R entries
+// (W2 rows of a vocabulary tile), read in whole lines: load instruction j of
+// the wave covers 1 KiB of the tile, lane l the 16-byte chunk c = l % CPR of
+// row RPI j + l / CPR.  Each lane dots its chunks with chunk c of e (one
+// 16-byte piece a lane), then a transposing butterfly over the CPR lanes of a
+// row group sums every row: at the step on lane bit b (highest first) each
+// lane keeps the half of its remaining rows that bit b selects and adds its
+// partner's sums for them (the partner flips bit b and agrees on every bit
+// already taken, so the mirror permutes serve too).  Lane l ends up with the
+// full sum of row RPI (c >> 1) + l / CPR; lanes l and l ^ 1 hold the same row.
+template <typename WT, int R>
+struct TileDot {
+    static constexpr int RB = R * int(sizeof(WT));
+    static constexpr int CPR = RB / 16;               // 16-byte chunks a row
+    static constexpr int NI = CPR / 2 > 0 ? CPR / 2 : 1;  // load instructions a tile
+    static constexpr int RPI = 64 / CPR;              // rows an instruction covers
+    static_assert(CPR >= 2 && CPR <= 32 && (CPR & (CPR - 1)) == 0, "tile row size");
+    uint4 w[NI];
+    __device__ static __forceinline__ int row_of(int lane) { return RPI * ((lane % CPR) >> 1) + lane / CPR; }
+    __device__ static __forceinline__ int lane_of(int m) { return (m % RPI) * CPR + 2 * (m / RPI); }
+    // rows v0 .. v0 + 31 of M (row stride R), rows past vmax repeat row vmax
+    __device__ __forceinline__ void load(const WT *M, int v0, int vmax, int lane) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int v = min(v0 + RPI * j + lane / CPR, vmax);
+            w[j] = reinterpret_cast<const uint4 *>(M + size_t(v) * R)[lane % CPR];
+        }
+    }
+    __device__ static __forceinline__ float chunk_dot(const uint4 &a, const uint4 &e) {
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, ev[4] = {e.x, e.y, e.z, e.w};
+        float d0 = 0.f, d1 = 0.f;
+        if constexpr (sizeof(WT) == 2) {
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[0]), __builtin_bit_cast(bf16x2_t, ev[0]),
+                                                 d0, false);
+            d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[1]), __builtin_bit_cast(bf16x2_t, ev[1]),
+                                                 d1, false);
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[2]), __builtin_bit_cast(bf16x2_t, ev[2]),
+                                                 d0, false);
+            d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[3]), __builtin_bit_cast(bf16x2_t, ev[3]),
+                                                 d1, false);
+        } else {
+            d0 = __uint_as_float(av[0]) * __uint_as_float(ev[0]);
+            d1 = __uint_as_float(av[1]) * __uint_as_float(ev[1]);
+            d0 = __builtin_fmaf(__uint_as_float(av[2]), __uint_as_float(ev[2]), d0);
+            d1 = __builtin_fmaf(__uint_as_float(av[3]), __uint_as_float(ev[3]), d1);
+        }
+        return d0 + d1;
+    }
+    // e: chunk lane % CPR of the vector; every lane of the wave must be active
+    __device__ __forceinline__ float dot(const uint4 &e) const {
+        float p[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) p[j] = chunk_dot(w[j], e);
+        const int lane = threadIdx.x & 63;
+        bfly_steps<0, 6>([&](auto st) {
+            constexpr int B = 5 - decltype(st)::value;  // lane bit, highest first
+            if constexpr ((1 << B) < CPR && B >= 1) {
+                constexpr int HALF = 1 << (B - 1);  // rows a lane keeps: 2^B before the step
+                const bool up = (lane >> B) & 1;
+#pragma unroll
+                for (int t = 0; t < HALF; ++t) {
+                    const float keep = up ? p[HALF + t] : p[t];
+                    const float send = up ? p[t] : p[HALF + t];
+                    p[t] = keep + bfly<B>(send);
+                }
+            }
+        });
+        return p[0] + bfly<0>(p[0]);
     }
 };
 

@@ -12,17 +12,21 @@
 // from q_k that needs per-entry noise for a single tile only.
 //
 // Per position k the work is one pass over the [B, V] plane:
-//   draft_step    a workgroup of up to 4 waves (32 requests each) walks the
-//                 vocabulary tiles of one chunk; the W2 tile is staged in LDS
-//                 by direct loads (double buffered, shared by the waves) and
-//                 the U_k tile is prefetched into registers one tile ahead.
-//                 The bias tile comes from MFMA (bf16 32x32x16, or f32
-//                 32x32x2); + U_k and 1/T give the tile's base-2 logsumexp,
-//                 which feeds both the running softmax sum and the tile race.
+//   draft_step    a workgroup of up to 8 waves (32 requests each) walks the
+//                 vocabulary tiles of one chunk, two tiles a stage: the
+//                 stage's W2 rows (shared by the waves) and each wave's U_k
+//                 entries are staged in LDS by direct loads, double buffered.
+//                 The U_k entries seed the MFMA accumulators (bf16 32x32x16,
+//                 or f32 32x32x2), which add the bias tile; 1/T gives the
+//                 tile's base-2 logsumexp, which feeds both the running
+//                 softmax sum and the tile race.
 //   draft_reduce  one wave per request: merges the chunk partials (row
 //                 logsumexp, best tile), recomputes the winning tile's 32
 //                 logits on the vector ALUs and races their entry noise:
-//                 x_k, lse_k, q_k(x_k) and the draw's margin.
+//                 x_k, lse_k, q_k(x_k) and the draw's margin.  For the next
+//                 position it also writes W1[x_k] as a packed fragment block
+//                 (it fetches the W1 rows of the whole winning tile with the
+//                 tile's W2 rows, so the chosen row needs no further trip).
 // The bias plane is never stored; HBM traffic per step is U_k, W2 and the
 // gathered W1 rows.
 #include "device_common.hpp"
@@ -30,6 +34,7 @@
 #include "stage.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dspark {
 
@@ -49,6 +54,7 @@ struct StepParams {
     int vec;  // U rows allow aligned 16-byte loads
     float *pm, *ps, *pb, *p2;
     int32_t *pi;
+    const uint4 *ep;  // PACKED instances: the E rows of every request as PackedE blocks
 };
 
 // s_waitcnt immediate that waits for all but the n most recent vector memory
@@ -65,7 +71,11 @@ constexpr int kStepThreads = 512;  // 8 waves: one 32-request block each
 // accumulators, and after the two MFMA chains a lane-half swap hands the
 // first tile of the pair to lanes 0..31 and the second to lanes 32..63.  A
 // last stage that runs past the vocabulary is done on its own, after the loop.
-template <typename WT, int R, bool TRACK2, bool VEC>
+// PACKED: the E rows come as PackedE blocks, written by the previous
+// position's reduce, so that the fragments go out first, as whole 1 KiB loads
+// with no dependency; otherwise every wave gathers its 32 rows of W1 (or of
+// the head's rows) from x_{k-1}.
+template <typename WT, int R, bool TRACK2, bool VEC, bool PACKED>
 __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void draft_step_kernel(StepParams p) {
     using L = TileLDS<WT, R>;
     using SU = StageRows<VEC>;
@@ -108,20 +118,31 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     // and T are loaded and waited for in asm: with no more than this wave's
     // own stage loads in flight (at least NI + MIN_PER_WAVE of them, issued
     // after), both have landed.
-    int prev;
     float T;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(prev) : "v"(p.xprev + size_t(bc) * p.xprev_stride) : "memory");
-    asm volatile("global_load_dword %0, %1, off" : "=v"(T) : "v"(p.temperature + bc) : "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    dma.template issue<true>(W2, v0_of(0), p.V, ldsA, wave);
-    su.template issue<true>(v0_of(0), p.V, uregion, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(prev), "+v"(T) : "n"(SU::NI + decltype(dma)::MIN_PER_WAVE));
-    prev = min(max(prev, 0), p.erows - 1);
+    EFrags<WT, R> ef;
+    if constexpr (PACKED) {
+        // the fragments and T first, then the first stage: nothing here waits
+        // for anything before the first stage has landed (the padded rows of
+        // the last block hold stale fragments; their columns are never written)
+        T = p.temperature[bc];
+        if (wave_ok) ef.load_packed(p.ep + size_t(bb) * PackedE<WT, R>::BLOCK, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        dma.template issue<true>(W2, v0_of(0), p.V, ldsA, wave);
+        su.template issue<true>(v0_of(0), p.V, uregion, lane);
+    } else {
+        int prev;
+        asm volatile("global_load_dword %0, %1, off" : "=v"(prev) : "v"(p.xprev + size_t(bc) * p.xprev_stride) : "memory");
+        asm volatile("global_load_dword %0, %1, off" : "=v"(T) : "v"(p.temperature + bc) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        dma.template issue<true>(W2, v0_of(0), p.V, ldsA, wave);
+        su.template issue<true>(v0_of(0), p.V, uregion, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(prev), "+v"(T) : "n"(SU::NI + decltype(dma)::MIN_PER_WAVE));
+        prev = min(max(prev, 0), p.erows - 1);
+        if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    }
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;  // base-2 logits; greedy keeps raw logits
-    EFrags<WT, R> ef;
-    if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
     TileRace st{kNegInf, 0.f, kNegInf, kNegInf, t_begin};
     uint4 tw = make_uint4(0u, 0u, 0u, 0u);
 
@@ -212,6 +233,7 @@ struct ReduceParams {
     int d, hvec;          // hvec: h rows and conf_w allow aligned 16-byte loads
     const float *conf_tau;  // [gamma] temperatures of the head's logit, or nullptr (1)
     float *conf_out, *surv_out;
+    uint4 *ep_out;  // PackedE blocks of W1[x_k] for the next position's step, or nullptr
 };
 
 // w_h . h_k, this lane's share (the wave sums it): lane l takes entries
@@ -265,13 +287,16 @@ __device__ __forceinline__ float conf_hidden_part(const ReduceParams &p, int b, 
 // and the prefix survival a_k = a_{k-1} c_k (a_{k-1} written by the previous
 // position's launch): the gathered W1 row is already at hand here, and the
 // h_k row streams in beside the partials.
+// One wave a workgroup, so that the requests' tile fetches (their W2 and W1
+// rows, 32 KiB a request) spread over every CU.
+constexpr int kReduceWaves = 1;
+
 template <typename WT, int R, bool CONF>
-__global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
+__global__ __launch_bounds__(64 * kReduceWaves) void draft_reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int b = blockIdx.x * kReduceWaves + (threadIdx.x >> 6);
     if (b >= p.B) return;
     const bool track2 = p.margin_out != nullptr;
-    const int i = lane & 31, h = lane >> 5;
     // level 1: row logsumexp and the winning tile, four chunks a lane per
     // batch.  The loads go out first and unconditionally (an index past the
     // chunks re-reads chunk 0 and is masked after), so that the first batch
@@ -302,8 +327,9 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
         if (p.d > 0) conf_s = conf_hidden_part(p, b, lane);
     }
     prev = min(max(prev, 0), p.erows - 1);
-    RowHalf<WT, R> w1;
-    w1.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    using TD = TileDot<WT, R>;
+    // the chunk of W1[x_{k-1}] this lane dots with the winning tile's rows
+    const uint4 ech = reinterpret_cast<const uint4 *>(static_cast<const WT *>(p.W1) + size_t(prev) * R)[lane % TD::CPR];
     if constexpr (CONF) {
         // w_e . W1[x_{k-1}], entries lane, lane + 64, ...
         const WT *e = static_cast<const WT *>(p.W1) + size_t(prev) * R;
@@ -340,16 +366,22 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
     // level 2: the winning tile's logits on the vector ALUs, then the entry race
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    const int v = tile * kTile + i;
+    // this lane's entry of the tile (lanes l and l ^ 1 share one)
+    const int v = tile * kTile + TD::row_of(lane);
     const bool valid = v < p.V;
     const int vc = min(v, p.V - 1);
+    // the tile's W2 rows and, for the next position's packed block, the W1
+    // rows of every candidate, all in whole lines
+    TD w2t, w1t;
+    w2t.load(static_cast<const WT *>(p.W2), tile * kTile, p.V - 1, lane);
+    if (p.ep_out) w1t.load(static_cast<const WT *>(p.W1), tile * kTile, p.V - 1, lane);
     const float u_v = p.U[size_t(b) * p.u_stride + vc];
-    const float d = w1.dot(static_cast<const WT *>(p.W2) + size_t(vc) * R, h);
+    const float d = w2t.dot(ech);
     const float logit = valid ? u_v + d : kNegInf;
     const float z2 = logit * sc;
     float score = logit;
     if (sampled) score = z2 + gumbel2(noise_word(kStreamDraft, p.k, uint32_t(vc), uint32_t(b), p.round32, p.key0, p.key1));
-    if (h != 0) score = kNegInf;  // the upper half duplicates the lower half
+    if (lane & 1) score = kNegInf;  // the odd lanes duplicate the even ones
     float s1 = score, s2 = kNegInf;
     int xi = v;
     bfly_steps<0, 6>([&](auto st) {
@@ -359,7 +391,18 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
         best_merge(s1, xi, s2, b2, i2, c2);
     });
     const int x = min(max(xi, tile * kTile), p.V - 1);
-    const float z2x = __shfl(z2, x - tile * kTile);
+    const int wn = x - tile * kTile;  // the winner's row in the tile
+    const float z2x = __shfl(z2, TD::lane_of(wn));
+    if (p.ep_out) {
+        // W1[x]'s chunks sit in load slot wn / RPI of the lanes of row group wn % RPI
+        const int js = wn / TD::RPI;  // uniform
+        uint4 row = w1t.w[0];
+#pragma unroll
+        for (int j = 1; j < TD::NI; ++j)
+            if (j == js) row = w1t.w[j];
+        if (lane / TD::CPR == wn % TD::RPI)
+            p.ep_out[size_t(b >> 5) * PackedE<WT, R>::BLOCK + PackedE<WT, R>::slot(b & 31, lane % TD::CPR)] = row;
+    }
     if constexpr (CONF) bfly_steps<0, 6>([&](auto st) { conf_s += bfly<decltype(st)::value>(conf_s); });
     if (lane == 0) {
         const size_t o = size_t(b) * p.gamma + (p.k - 1);
@@ -386,12 +429,24 @@ __global__ __launch_bounds__(256) void draft_reduce_kernel(ReduceParams p) {
 // ---- the bias product alone (a diagnostic of the matrix-unit tiling)
 
 struct GemmParams {
-    const void *W1, *W2;
-    const int32_t *idx;
+    const uint4 *ep;  // PackedE blocks of the rows W1[idx[b]]
+    const void *W2;
     int B, V;
     int nbb, nbg, ntiles, tiles_per_chunk, nchunk;
     float *pm;  // [B, nchunk] per-chunk row maxima
 };
+
+// The gather W1[idx[b]] into PackedE blocks: one thread per 16-byte chunk.
+template <typename WT, int R>
+__global__ __launch_bounds__(256) void bias_pack_kernel(const WT *W1, const int32_t *idx, int B, int V, uint4 *ep) {
+    constexpr int C = 2 * PackedE<WT, R>::NF;  // chunks a row
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= B * C) return;
+    const int b = t / C, c = t % C;
+    const int row = min(max(idx[b], 0), V - 1);
+    ep[size_t(b >> 5) * PackedE<WT, R>::BLOCK + PackedE<WT, R>::slot(b & 31, c)] =
+        reinterpret_cast<const uint4 *>(W1 + size_t(row) * R)[c];
+}
 
 
 // bias_pair_lds with the A-fragment reads issued as inline asm, so that the
@@ -468,11 +523,9 @@ __global__ __launch_bounds__(kStepThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int n = lane & 31, h = lane >> 5;
     const int b = bb * 32 + n;
     const bool row_ok = wave_ok && b < p.B;
-    const int bc = min(b, p.B - 1);
-    const int prev = min(max(p.idx[bc], 0), p.V - 1);
     const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
-    if (wave_ok) ef.load(static_cast<const WT *>(p.W1) + size_t(prev) * R, h);
+    if (wave_ok) ef.load_packed(p.ep + size_t(bb) * PackedE<WT, R>::BLOCK, lane);
     DMA dma;
     dma.init(tid);
     const int t_begin = chunk * p.tiles_per_chunk;
@@ -580,9 +633,16 @@ __global__ __launch_bounds__(256) void bias_rowmax_kernel(const float *pm, int B
 template <typename WT, int R>
 hipError_t launch_gemm_typed(const void *W1, const void *W2, const int32_t *idx, int B, int V, const DraftPlan &pl,
                              const DraftWork &w, float *rowmax, hipStream_t s) {
-    GemmParams gp{W1, W2, idx, B, V, pl.nbb, pl.nbg, pl.ntiles, pl.tiles_per_chunk, pl.nchunk, w.pm};
-    launch_kernel("bias_gemm", (bias_gemm_kernel<WT, R>), dim3(pl.blocks), dim3(kStepThreads), s, gp);
+    // the rows packed first (the draft step's later positions get them from
+    // the reduce), so that the product's time is the product alone
+    constexpr int C = 2 * PackedE<WT, R>::NF;
+    launch_kernel("bias_pack", (bias_pack_kernel<WT, R>), dim3((B * C + 255) / 256), dim3(256), s,
+                  static_cast<const WT *>(W1), idx, B, V, w.ep);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemmParams gp{w.ep, W2, B, V, pl.nbb, pl.nbg, pl.ntiles, pl.tiles_per_chunk, pl.nchunk, w.pm};
+    launch_kernel("bias_gemm", (bias_gemm_kernel<WT, R>), dim3(pl.blocks), dim3(kStepThreads), s, gp);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bias_rowmax_kernel, dim3((B + 3) / 4), dim3(256), 0, s, w.pm, B, pl.nchunk, rowmax);
     return hipGetLastError();
@@ -667,17 +727,27 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         sp.pb = w.pb;
         sp.p2 = w.p2;
         sp.pi = w.pi;
+        // the Markov head's later positions take the rows the previous reduce packed
+        const bool packed = !rnn && k > 1;
+        sp.ep = w.ep;
         const dim3 grid(pl.blocks), block(kStepThreads);
+        auto step = [&](auto t2, auto vc, auto pk) {
+            launch_kernel("draft_step",
+                          (draft_step_kernel<WT, R, decltype(t2)::value, decltype(vc)::value, decltype(pk)::value>),
+                          grid, block, s, sp);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
         if (track2) {
             if (vec)
-                launch_kernel("draft_step", (draft_step_kernel<WT, R, true, true>), grid, block, s, sp);
+                packed ? step(T_{}, T_{}, T_{}) : step(T_{}, T_{}, F_{});
             else
-                launch_kernel("draft_step", (draft_step_kernel<WT, R, true, false>), grid, block, s, sp);
+                packed ? step(T_{}, F_{}, T_{}) : step(T_{}, F_{}, F_{});
         } else {
             if (vec)
-                launch_kernel("draft_step", (draft_step_kernel<WT, R, false, true>), grid, block, s, sp);
+                packed ? step(F_{}, T_{}, T_{}) : step(F_{}, T_{}, F_{});
             else
-                launch_kernel("draft_step", (draft_step_kernel<WT, R, false, false>), grid, block, s, sp);
+                packed ? step(F_{}, F_{}, T_{}) : step(F_{}, F_{}, F_{});
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -709,6 +779,7 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
         rp.lse_out = a.lse_out;
         rp.qx_out = a.qx_out;
         rp.margin_out = a.margin_out;
+        rp.ep_out = (!rnn && k < a.gamma) ? w.ep : nullptr;
         if (a.conf_out) {
             rp.hidden = a.hidden + size_t(k - 1) * a.d;
             rp.h_stride = size_t(a.gamma) * a.d;
@@ -718,9 +789,11 @@ hipError_t launch_typed(const DraftArgs &a, const DraftPlan &pl, const DraftWork
             rp.conf_tau = a.conf_tau;
             rp.conf_out = a.conf_out;
             rp.surv_out = a.surv_out;
-            launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, true>), dim3((a.B + 3) / 4), dim3(256), s, rp);
+            launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, true>), dim3((a.B + kReduceWaves - 1) / kReduceWaves),
+                          dim3(64 * kReduceWaves), s, rp);
         } else {
-            launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, false>), dim3((a.B + 3) / 4), dim3(256), s, rp);
+            launch_kernel("draft_reduce", (draft_reduce_kernel<WT, R, false>), dim3((a.B + kReduceWaves - 1) / kReduceWaves),
+                          dim3(64 * kReduceWaves), s, rp);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -760,6 +833,8 @@ DraftWork draft_carve(void *ws, int B, const DraftPlan &p, size_t *bytes, int rn
     w.pb = c.take<float>(n);
     w.p2 = c.take<float>(n);
     w.pi = c.take<int32_t>(n);
+    // packed E rows of every request block, at the largest row size (512 bytes)
+    w.ep = c.take<uint4>(size_t(p.nbb) * 32 * 32);
     if (rnn_r > 0) {
         w.rnn_s[0] = c.take<float>(size_t(B) * rnn_r);
         w.rnn_s[1] = c.take<float>(size_t(B) * rnn_r);

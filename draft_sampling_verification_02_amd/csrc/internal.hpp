@@ -65,6 +65,7 @@ struct DraftWork {
     float *rnn_s[2];           // RNN head: [B, r] states of alternate positions
     int32_t *rnn_idx;          // RNN head: [B] the draft step's row of e_out for request b (b * gamma)
     float *rnn_yh;             // RNN head: precomputed h part of the gate product (RnnProjPlan)
+    uint4 *ep;                 // [nbb, 32 rows of at most 512 bytes] packed E rows for the next position's step
 };
 // rnn_r > 0 also carves the RNN head's buffers for rank rnn_r, block gamma
 // and width rnn_d.
