@@ -57,11 +57,11 @@ constexpr int kStatusRowsOutOfRange = 4;
 constexpr int kModeDone = 0;
 constexpr int kModeResidual = 1;
 constexpr int kModeBonus = 2;
-constexpr int kPrepInPassMaxBatch = 512;
+constexpr int kPrepInWalkMaxBatch = 512;
 
-__device__ __forceinline__ float wave_max(float v) {
-    bfly_steps<0, 6>([&](auto st) { v = fmaxf(v, bfly<decltype(st)::value>(v)); });
-    return v;
+// v of the first active lane, as a scalar
+__device__ __forceinline__ float uniform_f(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -114,7 +114,7 @@ __device__ int block_exclusive_scan(int v, int *lds, int *total) {
 struct PrepParams {
     const int32_t *ell, *row_offsets;
     int B, gamma, n_target_rows;
-    int32_t *status, *off, *mode, *req_flags;
+    int32_t *off, *mode, *req_flags;
     int32_t *n_accept_out, *tokens_out;
     float *diag_out, *resid_out;
 };
@@ -175,61 +175,47 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
     }
     if (t == 1023) p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : total;
     // the status word is the OR of the requests' flags, formed by the finish
-    if (t == 0) {
-        p.status[1] = 0;
-        p.status[2] = 0;
-        p.status[3] = 0;
-    }
 }
 
-// ------------------------------------------------------------------ position pass
+// ------------------------------------------------------------------ position walk
 
-// Rows a position pass reduces: one or two consecutive positions of the
-// requests still testing; the pass first decides the positions the previous
-// pass reduced.  A request that rejects at the first of a pair has the second
-// row read for nothing, against one launch less.  Few requests are still
-// testing late in the block, so there the launch costs more than the row:
-// the first kSinglePasses positions get a pass each, the rest go in pairs
-// (an odd one left first on its own), then one pass decides the last rows.
-// A batch whose rows at one position take at most kPairAllBytes pairs from
-// the first position on: a launch costs about 7 us, about 45 MB of reads,
-// against at most B V 4 bytes read for nothing a pair.
-constexpr int kPassRows = 2;  // row slots a pass can hold
-constexpr int kSinglePasses = 3;
-constexpr size_t kPairAllBytes = size_t(64) << 20;
-// segments of a row in the first position pass and in the later ones
-// (measured at the headline size: 8 first-pass segments take 1 us less than
-// 4; 16 or 64 later segments take 1-2 us a pass more than 32)
-constexpr int kSegFirst = 8, kSegLater = 32;
-static_assert(kSegFirst <= 64 / kPassRows && kSegLater <= 64 / kPassRows,
-              "the next pass merges a row's segment statistics in 64 / kPassRows lanes");
+// One workgroup walks one request's target rows in position order: it streams
+// row j for the base-2 logsumexp of t / T (and the lowest-index argmax of a
+// greedy row), decides position j from it (the accept test for j <= ell, the
+// bonus row for j = ell + 1) and goes on to row j + 1 only after an accepted
+// draft, so no row past the first rejection is read.  The decision needs the
+// whole row, and the whole row is this workgroup's: its waves meet once a row
+// in LDS, and every wave merges the same statistics and takes the same
+// decision, so no other workgroup and no fence is involved.  A batch fills
+// the chip with one row a CU at first; the few requests still testing late in
+// the block each stream a row at a CU's own load and exp2 rate.
+// One wave a SIMD: with two a SIMD the arbiter favours the older wave, and
+// a row's merge waited for the last wave (measured 2.4-3.3 us a row late in
+// the block, 6 us on the first row).  Each lane keeps two batches of 16 float4
+// groups.
+constexpr int kWalkThreads = 256;
+constexpr int kWalkGroups = 16;
+// third word of a raw buffer descriptor (dword data, no swizzle) on gfx9-family chips
+constexpr int kBufferWord3 = 0x00020000;
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(4))) const float kconst_float;  // scalar-loadable (read-only) float
+constexpr int kWalkWaves = kWalkThreads / 64;
+static_assert(kWalkWaves <= 16, "the per-row merge runs over 16 lanes");
 
-struct PassParams {
+struct WalkParams {
     const float *target;
     const int32_t *x, *ell;
     const float *qx, *temperature;
-    int B, gamma, V, j0, vec;  // j0: first position this pass reduces
-    int nseg, seg_len;  // this pass's segments of a row
-    int nseg_in;        // the previous pass's
-    int seg_stride;     // partials per request in the buffers
-    size_t row_stride;  // partials per row slot of a pass (B * seg_stride)
+    int B, gamma, V, vec;
     uint32_t key0, key1, round32;
     int32_t *off;
-    // prep != 0 (first pass of a small batch): the pass also checks each
-    // request's inputs, computes its row offset and writes the output defaults
+    // prep != 0: the walk also checks each request's inputs, forms its row
+    // offset (a sum over ell) and writes the output defaults
     int prep, n_target_rows;
     const int32_t *row_offsets;
     int32_t *req_flags;
     float *resid_out;
-    // pass p reads what pass p - 1 left and writes into the other half of
-    // each double buffer; slot q holds the pass's q-th row
-    const int32_t *act_in;  // [B] 1: the request's rows of the previous pass were reduced
-    const float *pm_in, *ps_in, *pv_in, *tx_in;
-    const int32_t *pi_in;
-    int32_t *act_out;
-    float *pm_out, *ps_out, *pv_out, *tx_out;
-    int32_t *pi_out;
-    int32_t *status, *mode, *jpos, *slot, *draw_list, *prev;
+    int32_t *mode, *jpos, *prev;
     float *fin_lse2, *lse2q;
     int erow_mode;  // 1: the residual's head row is row b * gamma + k - 1 of W1 (the head's rows)
     const int32_t *anchor;
@@ -238,73 +224,12 @@ struct PassParams {
     float *diag_out;
 };
 
-// Position k = j - 1 of request b, from its merged row statistics: the accept
-// test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
-// request takes the same decision; only `writer` stores it.  Returns whether
-// the request goes on to position j.
-// xk, qk: x_k and q_k(x_k) (any value when k > ell).
-__device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampled, float lse2, int amax, float tx2,
-                            int xk, float qk, bool writer) {
-    int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
-    bool bonus = false;
-    if (k <= L) {
-        bool acc;
-        float pk, ratio;
-        if (sampled) {
-            pk = fast_exp2(tx2 - lse2);
-            const float u = uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
-            acc = u * qk < pk;
-            ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
-        } else {
-            acc = (xk == amax);
-            pk = acc ? 1.f : 0.f;
-            ratio = pk;
-        }
-        if (writer && p.diag_out) {
-            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = pk;
-            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = ratio;
-        }
-        if (acc) {
-            if (writer) tok[k - 1] = xk;
-            return true;
-        }
-        if (writer) p.n_accept_out[b] = k - 1;
-    } else {
-        if (writer) p.n_accept_out[b] = L;
-        bonus = true;
-    }
-    if (!writer) return false;
-    p.jpos[b] = k;
-    if (!sampled) {
-        tok[k - 1] = amax;
-        p.mode[b] = kModeDone;
-        return false;
-    }
-    p.fin_lse2[b] = lse2;
-    if (bonus) {
-        const int e = p.B - 1 - atomicAdd(&p.status[3], 1);
-        p.draw_list[e] = b;
-        p.slot[b] = e;
-        p.mode[b] = kModeBonus;
-    } else {
-        const int e = atomicAdd(&p.status[2], 1);
-        p.draw_list[e] = b;
-        p.slot[b] = e;
-        p.mode[b] = kModeResidual;
-        // what the residual draw needs to rebuild q_k
-        p.prev[b] = p.erow_mode ? b * p.gamma + k - 1
-                                : min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
-        p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + k - 1] * kLog2e;
-    }
-    return false;
-}
-
-// One batch of U float4 groups of a row into a lane's running base-2
-// logsumexp (m, s) of x * sc; group u holds entries v0 + 256 u .. + 3 and
+// One batch of U float4 groups of a row into a thread's running base-2
+// logsumexp (m, s) of x * sc; group u holds entries v0 + STRIDE u .. + 3 and
 // counts only if valid(u).  The scale is positive, so the maximum is taken
 // on the raw values and the scale folds into one fma per entry.  ARGMAX
 // (greedy rows, sc = 1) also keeps the lowest-index maximum (av, ai).
-template <bool ARGMAX, int U, class Valid>
+template <bool ARGMAX, int U, int STRIDE, class Valid>
 __device__ __forceinline__ void row_batch(float4 (&xs)[U], int v0, Valid valid, float sc, float &m, float &s, float &av,
                                           int &ai) {
     float bm = kNegInf;
@@ -332,249 +257,347 @@ __device__ __forceinline__ void row_batch(float4 (&xs)[U], int v0, Valid valid, 
                 const float xv = f4get(xs[u], jj);
                 if (xv > av) {
                     av = xv;
-                    ai = v0 + 256 * u + jj;
+                    ai = v0 + STRIDE * u + jj;
                 }
             }
     }
 }
 
-// Pass p, one wave per (request, row slot q < DOUT, vocabulary segment),
-// four requests to a workgroup.  First the request's DIN previous positions are
-// decided, in order, from the segment statistics pass p - 1 wrote; a request
-// that goes on streams segment sg of its row j0 + q: every lane keeps its own
-// running max / sum of exp2 and argmax over batches of eight float4 loads
-// (PIPE: two batches, one in flight while the other is reduced, for the long
-// segments of the first pass), and the wave merges them.  The waves never
-// wait for one another.
-template <bool PIPE, int DIN, int DOUT>
-__global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
-    static_assert(DIN >= 1 && DIN <= kPassRows && DOUT >= 1 && DOUT <= kPassRows,
-                  "row slots: the previous pass's (DIN) and this pass's (DOUT)");
-    constexpr int LPS = 64 / DIN;  // lanes holding one previous row slot's segment statistics
-    constexpr int LOG_LPS = DIN == 1 ? 6 : 5;
-    const int sg = blockIdx.x % p.nseg;
-    const int q = (blockIdx.x / p.nseg) % DOUT;
-    const int b = (blockIdx.x / (p.nseg * DOUT)) * 4 + (threadIdx.x >> 6);
-    const int j0 = p.j0, j = j0 + q;
-    const int lane = threadIdx.x & 63;
-    if (b >= p.B) return;
-    const bool writer = sg == 0 && q == 0;
-    int mode, offb, act, L;
-    float T;
-    float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
-    int i2 = 0x7fffffff;
-    float tx2[DIN], qk[DIN];
-    int xk[DIN];
-    if constexpr (PIPE) {
-        // the first pass decides nothing: it needs the request's temperature
-        // and length and, for a small batch, does its input checks (the row
-        // offset is a wave sum over ell, read in the same round)
-        T = p.temperature[b];
-        L = p.ell[b];
-        act = 1;
-        if (p.prep) {  // uniform
+// One batch of U float4 groups into a thread's running base-2 logsumexp
+// (m, s) of x * sc, the walk's form of row_batch: FULL batches lie inside the
+// row (no masking); the maximum is taken with v_max3 on the raw values (the
+// scale is positive), two entries an instruction.  ARGMAX (greedy rows,
+// sc = 1) also keeps the lowest-index maximum; group u holds entries
+// v0 + STRIDE u .. + 3.
+template <bool ARGMAX, bool FULL, int U, int STRIDE>
+__device__ __forceinline__ void walk_batch(float4 (&xs)[U], int v0, int nvalid_groups, float sc, float &m, float &s,
+                                           float &av, int &ai) {
+    static_assert(U % 2 == 0, "groups in pairs");
+    if constexpr (!FULL) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u >= nvalid_groups) xs[u] = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+    }
+    if constexpr (ARGMAX) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float xv = f4get(xs[u], jj);
+                if (xv > av) {
+                    av = xv;
+                    ai = v0 + STRIDE * u + jj;
+                }
+            }
+    }
+    float b0 = max3f(xs[0].x, xs[0].y, xs[0].z), b1 = max3f(xs[0].w, xs[1].x, xs[1].y);
+#pragma unroll
+    for (int u = 1; u < U; u += 2) {
+        b0 = max3f(b0, xs[u].z, xs[u].w);
+        if (u + 1 < U) {
+            b1 = max3f(b1, xs[u + 1].x, xs[u + 1].y);
+            b0 = max3f(b0, xs[u + 1].z, xs[u + 1].w);
+        }
+    }
+    const float mn = fmaxf(m, fmaxf(b0, b1) * sc);
+    const float mg = (mn == kNegInf) ? 0.f : mn;  // an all -inf batch adds 2^-inf = 0
+    const float nm = -mg;
+    // every exponential first (independent), then a balanced sum
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        xs[u].x = fast_exp2(__builtin_fmaf(xs[u].x, sc, nm));
+        xs[u].y = fast_exp2(__builtin_fmaf(xs[u].y, sc, nm));
+        xs[u].z = fast_exp2(__builtin_fmaf(xs[u].z, sc, nm));
+        xs[u].w = fast_exp2(__builtin_fmaf(xs[u].w, sc, nm));
+    }
+    float t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = (xs[u].x + xs[u].y) + (xs[u].z + xs[u].w);
+#pragma unroll
+    for (int w = 1; w < U; w *= 2)
+#pragma unroll
+        for (int u = 0; u + w < U; u += 2 * w) t[u] += t[u + w];
+    s = __builtin_fmaf(s, fast_exp2(m - mg), t[0]);
+    m = mn;
+}
+
+// The statistics of one row of V entries at trow (any alignment), reduced over
+// the thread's share: entries t, t + NT, ...
+template <bool ARGMAX>
+__device__ __forceinline__ void walk_row_scalar(const float *trow, int V, float sc, float &m, float &s, float &av,
+                                                int &ai) {
+    for (int v = threadIdx.x; v < V; v += kWalkThreads) {
+        const float xv = trow[v] * sc;
+        const float mn = fmaxf(m, xv);
+        if (mn != kNegInf) {
+            s = s * fast_exp2(m - mn) + fast_exp2(xv - mn);
+            m = mn;
+        }
+        if (ARGMAX && xv > av) {
+            av = xv;
+            ai = v;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_walk_kernel(
+    WalkParams p) {
+    __shared__ float s_m[2][kWalkWaves], s_s[2][kWalkWaves], s_v[2][kWalkWaves];
+    __shared__ int s_i[2][kWalkWaves];
+    __shared__ int s_x[DSPARK_MAX_GAMMA];
+    __shared__ float s_q[DSPARK_MAX_GAMMA], s_thr[DSPARK_MAX_GAMMA];
+    __shared__ float s_dp[DSPARK_MAX_GAMMA], s_dr[DSPARK_MAX_GAMMA];  // p_k(x_k), min(1, p/q) of tested positions
+    __shared__ int s_off, s_mode;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float T = p.temperature[b];
+    const int L_raw = p.ell[b];
+    const bool sampled = T > 0.f;
+    if (wave == 0) {
+        // the request's state: its row offset and input checks (in the walk
+        // for a small batch), its drafts, q(x) and accept thresholds u q
+        int offb, md;
+        if (p.prep) {
             int part = 0;
             if (!p.row_offsets)
                 for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
             const int o_cmp = wave_isum(part);
             const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
-            mode = f == 0 ? kModeDone : -1;
-            if (writer) {
-                if (lane == 0) {
-                    p.off[b] = offb;
-                    p.mode[b] = mode;
-                    p.req_flags[b] = f;
-                    if (b == p.B - 1)
-                        p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L, 0), p.gamma);
-                }
-                output_defaults(b, p.gamma, lane, 64, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
+            md = f == 0 ? kModeDone : -1;
+            if (lane == 0) {
+                p.off[b] = offb;
+                p.req_flags[b] = f;
+                if (b == p.B - 1)
+                    p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L_raw, 0), p.gamma);
             }
-            if (blockIdx.x == 0 && threadIdx.x == 0) {  // the draw-list counters the later passes bump
-                p.status[1] = 0;
-                p.status[2] = 0;
-                p.status[3] = 0;
-            }
+            output_defaults(b, p.gamma, lane, 64, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
         } else {
-            mode = p.mode[b];
             offb = p.off[b];
+            md = p.mode[b];
         }
-    } else {
-        // every load the decisions need, issued together and unconditionally
-        // (clamped indices; what a case does not use is masked after): lane
-        // group h (of LPS lanes) holds the segment statistics of the previous
-        // pass's row slot h, read whatever the request's state
-        const int hq = min(lane / LPS, DIN - 1), c = min(lane % LPS, p.nseg_in - 1);
-        const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
-        mode = p.mode[b];
-        offb = p.off[b];
-        act = p.act_in[b];
-        T = p.temperature[b];
-        L = p.ell[b];
-        mm = p.pm_in[o_in];
-        s2 = p.ps_in[o_in];
-        v2 = p.pv_in[o_in];
-        i2 = p.pi_in[o_in];
-#pragma unroll
-        for (int u = 0; u < DIN; ++u) {
-            const int k = min(max(j0 - DIN + u, 1), p.gamma);  // position decided from slot u (clamped)
-            tx2[u] = p.tx_in[size_t(u) * p.B + b];
-            xk[u] = p.x[size_t(b) * p.gamma + k - 1];
-            qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
+        if (lane < p.gamma) {
+            const size_t o = size_t(b) * p.gamma + lane;
+            const float q = p.qx[o];
+            s_x[lane] = p.x[o];
+            s_q[lane] = q;
+            // u q < p is the accept test; u q is formed here once
+            s_thr[lane] = sampled ? uniform01(scalar_word(kStreamAccept, lane + 1, uint32_t(b), p.round32, p.key0,
+                                                          p.key1)) * q
+                                  : 0.f;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::"v"(mode), "v"(offb), "v"(act), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
-        if (!((lane / LPS) < DIN && (lane % LPS) < p.nseg_in)) {
-            mm = kNegInf;
-            s2 = 0.f;
-            v2 = kNegInf;
-            i2 = 0x7fffffff;
-        }
-    }
-    if (mode < 0 || act == 0) {
-        if (writer && lane == 0) p.act_out[b] = 0;
-        return;
-    }
-    const bool sampled = T > 0.f;
-    const float sc = sampled ? kLog2e / T : 1.0f;
-    if (!PIPE && j0 > 1) {
-        bfly_steps<0, LOG_LPS>([&](auto st) {  // within each lane group
-            constexpr int S = decltype(st)::value;
-            const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
-            const int i_o = bfly<S>(i2);
-            lse_merge(mm, s2, m_o, s_o);
-            argmax_merge(v2, i2, v_o, i_o);
-        });
-        float lse2[DIN];
-        int amax[DIN];
-#pragma unroll
-        for (int u = 0; u < DIN; ++u) {
-            const float mu = __shfl(mm, LPS * u), su = __shfl(s2, LPS * u);
-            lse2[u] = (mu == kNegInf) ? kNegInf : mu + fast_log2(su);
-            amax[u] = min(max(__shfl(i2, LPS * u), 0), p.V - 1);
-        }
-        int go_on = 0;
         if (lane == 0) {
-            go_on = 1;
-#pragma unroll
-            for (int u = 0; u < DIN; ++u) {
-                const int k = j0 - DIN + u;
-                if (!go_on || k > L + 1) break;
-                go_on = pass_decide(p, b, L, k, sampled, lse2[u], amax[u], tx2[u], xk[u], qk[u], writer);
-            }
-        }
-        if (!__shfl(go_on, 0)) {
-            if (writer && lane == 0) p.act_out[b] = 0;
-            return;
+            s_off = offb;
+            s_mode = md;
         }
     }
-    if (j > L + 1) {  // no row at this slot (slot 0 always has one once the request goes on)
-        if (writer && lane == 0) p.act_out[b] = 0;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_mode) < 0) {  // failed its input checks: outputs keep their defaults
+        if (tid == 0) p.mode[b] = -1;
         return;
     }
-    const float *trow = p.target + size_t(offb + j - 1) * p.V;
-    const int v_lo = sg * p.seg_len, v_hi = min(p.V, v_lo + p.seg_len);
+    const int offb = __builtin_amdgcn_readfirstlane(s_off);
+    const int L = L_raw;  // in [0, gamma] once the checks passed
+    const float sc = sampled ? kLog2e / T : 1.0f;
+    auto row_of = [&](int j) { return p.target + size_t(offb + j - 1) * p.V; };
+    // the thread's state for the current row: running base-2 logsumexp and
+    // argmax (greedy)
     float m = kNegInf, s = 0.f, av = kNegInf;
     int ai = 0x7fffffff;
-    if (p.vec) {
-        if constexpr (PIPE) {
-            // two batches of U float4 a lane, one in flight while the other is
-            // reduced
-            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
-            const int q_hi = v_hi >> 2;
-            constexpr int U = 8;
-            // loads past the segment re-read its last group and are masked when used
-            auto load = [&](float4(&xs)[U], int qb) __device__ {
-    #pragma unroll
-                for (int u = 0; u < U; ++u) xs[u] = load_stream(r4 + min(qb + lane + 64 * u, q_hi - 1));
-            };
-            // sampled rows keep no argmax (only greedy decisions use it); the
-            // request, and so the branch, is uniform across the wave
-            auto consume = [&](float4(&xs)[U], int qb) __device__ {
-                auto valid = [&](int u) { return qb + lane + 64 * u < q_hi; };
-                if (sampled)
-                    row_batch<false>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
-                else
-                    row_batch<true>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
-            };
-            // The loop body is straight-line, so that every consume sees the
-            // same loads in flight on every path into it; it runs while the
-            // batch after the pair exists, and the last one or two batches
-            // follow it.  The batch bounds are uniform across the wave.
-            constexpr int NB = 64 * U;  // float4 groups a batch
-            const int qs = v_lo >> 2;
-            float4 xa[U], xb[U];
-            load(xa, qs);
-            int qb = qs;
-            for (; qb + 2 * NB < q_hi; qb += 2 * NB) {
-                load(xb, qb + NB);
-                consume(xa, qb);
-                load(xa, qb + 2 * NB);
-                consume(xb, qb + NB);
-            }
-            if (qb + NB < q_hi) {
-                load(xb, qb + NB);
-                consume(xa, qb);
-                consume(xb, qb + NB);
+    // t(x_j) / T of the row being read, for its accept test: a scalar load
+    // (through the constant address space; the rows are read-only here),
+    // issued when the row starts and counted apart from the row's vector loads
+    float txs = kNegInf;
+    auto locate_x = [&](int j) {
+        if (sampled && j <= L) {
+            const int q = min(max(__builtin_amdgcn_readfirstlane(s_x[j - 1]), 0), p.V - 1);
+            txs = reinterpret_cast<const kconst_float *>(reinterpret_cast<uintptr_t>(row_of(j)))[q] * sc;
+        }
+    };
+    // the walk's outcome, the same in every thread; no global store is made
+    // before the walk ends (the outputs go out after it)
+    int r_n = 0, r_j = 0, r_mode = kModeDone, r_tok = -1;
+    float r_lse2 = 0.f;
+    // Row j is complete in the threads' states: merge it over the workgroup
+    // and decide position j.  Returns whether the walk goes on to row j + 1.
+    auto finish_row = [&](int j) -> bool {
+        const int par = j & 1;
+        bfly_steps<0, 6>([&](auto st) {
+            constexpr int S = decltype(st)::value;
+            const float m_o = bfly<S>(m), s_o = bfly<S>(s), v_o = bfly<S>(av);
+            const int i_o = bfly<S>(ai);
+            lse_merge(m, s, m_o, s_o);
+            argmax_merge(av, ai, v_o, i_o);
+        });
+        if (lane == 0) {
+            s_m[par][wave] = m;
+            s_s[par][wave] = s;
+            s_v[par][wave] = av;
+            s_i[par][wave] = ai;
+        }
+        __syncthreads();
+        // every wave merges the same statistics in the same order and takes
+        // the same decision (buffers alternate by row, so the next row's
+        // writes never meet this row's reads)
+        float mm = kNegInf, ss = 0.f, vv = kNegInf;
+        int ii = 0x7fffffff;
+        if (lane < kWalkWaves) {
+            mm = s_m[par][lane];
+            ss = s_s[par][lane];
+            vv = s_v[par][lane];
+            ii = s_i[par][lane];
+        }
+        bfly_steps<0, 4>([&](auto st) {
+            constexpr int S = decltype(st)::value;
+            const float m_o = bfly<S>(mm), s_o = bfly<S>(ss), v_o = bfly<S>(vv);
+            const int i_o = bfly<S>(ii);
+            lse_merge(mm, ss, m_o, s_o);
+            argmax_merge(vv, ii, v_o, i_o);
+        });
+        // lane 0's merge as scalars: the decision and the walk's loop are
+        // then uniform to the compiler as well (scalar branches, exact load
+        // counts across the loop)
+        mm = uniform_f(mm);
+        ss = uniform_f(ss);
+        ii = __builtin_amdgcn_readfirstlane(ii);
+        m = kNegInf;  // the thread's state for the next row
+        s = 0.f;
+        av = kNegInf;
+        ai = 0x7fffffff;
+        const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(ss);
+        const int amax = min(max(ii, 0), p.V - 1);
+        if (j <= L) {
+            bool acc;
+            float pk, ratio;
+            if (sampled) {
+                const float qk = uniform_f(s_q[j - 1]);
+                pk = fast_exp2(txs - lse2);
+                acc = uniform_f(s_thr[j - 1]) < pk;
+                ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
             } else {
-                consume(xa, qb);
+                acc = (__builtin_amdgcn_readfirstlane(s_x[j - 1]) == amax);
+                pk = acc ? 1.f : 0.f;
+                ratio = pk;
             }
+            if (tid == 0) {
+                s_dp[j - 1] = pk;
+                s_dr[j - 1] = ratio;
+            }
+            if (acc) return true;
+            r_n = j - 1;  // first rejection at j: the residual draw (sampled) or the target's argmax (greedy)
+            r_mode = sampled ? kModeResidual : kModeDone;
         } else {
-            // one batch of U float4 a lane at a time: fewer registers, twice
-            // the waves a SIMD for the short segments of the later passes
-            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
-            const int q_hi = v_hi >> 2;
-            constexpr int U = 8;
-            // one loop for each kind of row (the request, and so the kind, is
-            // uniform across the wave): each keeps only its own registers
-            auto walk = [&](auto argmax) __device__ {
-                constexpr bool AM = decltype(argmax)::value;
-                for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
-                    float4 xs[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int q = q0 + 64 * u;
-                        xs[u] = q < q_hi ? load_stream(r4 + q) : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-                    }
-                    row_batch<AM>(xs, 4 * q0, [](int) { return true; }, sc, m, s, av, ai);  // masked at the load
-                }
-            };
+            r_n = L;  // every draft accepted: the bonus token from row ell + 1
+            r_mode = sampled ? kModeBonus : kModeDone;
+        }
+        r_j = j;
+        r_lse2 = lse2;
+        r_tok = amax;
+        return false;
+    };
+    locate_x(1);
+    if (!p.vec) {
+        for (int j = 1; j <= L + 1; ++j) {
             if (sampled)
-                walk(std::integral_constant<bool, false>{});
+                walk_row_scalar<false>(row_of(j), p.V, sc, m, s, av, ai);
             else
-                walk(std::integral_constant<bool, true>{});
+                walk_row_scalar<true>(row_of(j), p.V, sc, m, s, av, ai);
+            if (!finish_row(j)) break;
+            locate_x(j + 1);
         }
     } else {
-        for (int v = v_lo + lane; v < v_hi; v += 64) {
-            const float xv = trow[v] * sc;
-            const float mn = fmaxf(m, xv);
-            if (mn != kNegInf) {
-                s = s * fast_exp2(m - mn) + fast_exp2(xv - mn);
-                m = mn;
+        // One pipeline over the batches of consecutive rows: thread t takes
+        // float4 groups t, t + NT, ... of each batch of NT U groups (a fixed
+        // share, so the sums are formed in the same order on every run).  Two
+        // batches are in flight, so the first batch of row j + 1 goes out
+        // before position j is decided (and is dropped when the walk stops
+        // there): the loads do not drain at a row boundary.  A batch past the
+        // last row the walk may read gets an empty buffer descriptor: it is
+        // issued like the others (the counts of loads in flight are the same on
+        // every path) but touches no memory.  The row and batch of each buffer
+        // are tracked as scalar counters.
+        constexpr int U = kWalkGroups, NB = kWalkThreads * U;
+        const int n4 = p.V >> 2;
+        const int nbr = (n4 + NB - 1) / NB;  // batches a row
+        const int last_qb = (nbr - 1) * NB;  // first group of a row's last batch
+        // Buffer loads: the row is a scalar descriptor whose range check
+        // returns 0 past its end (masked when reduced), and a group's offset
+        // is the thread's fixed part plus a scalar one, so a batch needs no
+        // address registers of its own.
+        const int voff = tid * 16;
+        auto load = [&](float4(&xs)[U], int j, int qb) __device__ {
+            const bool any = j <= L + 1;  // uniform
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(row_of(any ? j : 1)), 0, any ? n4 * 16 : 0, kBufferWord3);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const v4f_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (qb + kWalkThreads * u) * 16,
+                                                                      kStreamPolicy);
+                xs[u] = make_float4(x[0], x[1], x[2], x[3]);
             }
-            if (xv > av) {
-                av = xv;
-                ai = v;
+        };
+        auto consume = [&](float4(&xs)[U], int qb) __device__ {
+            if (qb + NB <= n4) {  // uniform: a full batch
+                if (sampled)
+                    walk_batch<false, true, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), U, sc, m, s, av, ai);
+                else
+                    walk_batch<true, true, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), U, sc, m, s, av, ai);
+            } else {
+                const int nv = (n4 - qb - tid + kWalkThreads - 1) / kWalkThreads;  // this thread's groups in the row
+                if (sampled)
+                    walk_batch<false, false, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), nv, sc, m, s, av, ai);
+                else
+                    walk_batch<true, false, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), nv, sc, m, s, av, ai);
+            }
+        };
+        // (row, first group) of the batch in each buffer
+        int ja = 1, qa = 0, jb, qb;
+        auto advance = [&](int j, int q, int &jn, int &qn) {
+            if (q == last_qb) {
+                jn = j + 1;
+                qn = 0;
+            } else {
+                jn = j;
+                qn = q + NB;
+            }
+        };
+        float4 xa[U], xb[U];
+        load(xa, ja, qa);
+        for (;;) {
+            advance(ja, qa, jb, qb);
+            load(xb, jb, qb);
+            consume(xa, qa);
+            if (qa == last_qb) {
+                if (!finish_row(ja)) break;
+                locate_x(ja + 1);
+            }
+            advance(jb, qb, ja, qa);
+            load(xa, ja, qa);
+            consume(xb, qb);
+            if (qb == last_qb) {
+                if (!finish_row(jb)) break;
+                locate_x(jb + 1);
             }
         }
     }
-    bfly_steps<0, 6>([&](auto st) {
-        constexpr int S = decltype(st)::value;
-        const float m_o = bfly<S>(m), s_o = bfly<S>(s), v_o = bfly<S>(av);
-        const int i_o = bfly<S>(ai);
-        lse_merge(m, s, m_o, s_o);
-        argmax_merge(av, ai, v_o, i_o);
-    });
-    if (lane == 0) {
-        const size_t o = q * p.row_stride + size_t(b) * p.seg_stride + sg;
-        p.pm_out[o] = m;
-        p.ps_out[o] = s;
-        p.pv_out[o] = av;
-        p.pi_out[o] = ai;
-        if (writer) p.act_out[b] = 1;
-        // t(x_j) for the accept test at j, from the segment that holds x_j
-        if (sampled && j <= L) {
-            const int xj = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
-            if (xj >= v_lo && xj < v_hi) p.tx_out[size_t(q) * p.B + b] = trow[xj] * sc;
+    if (tid == 0) {
+        // the outcome: accepted drafts, the first rejection's or the bonus
+        // row's data for the draw, diagnostics of every tested position
+        int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
+        for (int k = 1; k <= r_n; ++k) tok[k - 1] = s_x[k - 1];
+        if (!sampled) tok[r_j - 1] = r_tok;
+        if (p.diag_out)
+            for (int k = 1; k <= min(r_j, L); ++k) {
+                p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = s_dp[k - 1];
+                p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = s_dr[k - 1];
+            }
+        p.n_accept_out[b] = r_n;
+        p.jpos[b] = r_j;
+        p.mode[b] = r_mode;
+        if (sampled) p.fin_lse2[b] = r_lse2;
+        if (r_mode == kModeResidual) {
+            p.prev[b] = p.erow_mode ? b * p.gamma + r_j - 1
+                                    : min(max(r_j == 1 ? p.anchor[b] : s_x[r_j - 2], 0), p.V - 1);
+            p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + r_j - 1] * kLog2e;
         }
     }
 }
@@ -589,11 +612,62 @@ struct DrawParams {
     int B, gamma, V;
     int nbg, ntiles, tiles_per_chunk, nchunk;
     uint32_t key0, key1, round32;
-    const int32_t *status, *draw_list, *jpos, *off, *prev;
+    const int32_t *mode, *jpos, *off, *prev;
     const float *fin_lse2, *lse2q;
+    int32_t *slot;
     float *dw_sum, *dw_bl;
     int32_t *dw_bt;
 };
+
+// The draw list, in request order: residual draws at entries [0, nres), bonus
+// draws at [B - nbon, B).  Every workgroup forms it from the requests' modes
+// (wave ballots over blocks of 64 requests, block counts in LDS) and keeps the
+// NE entries from e0 on in lreq (-1 for none); scratch holds 2 ceil(B / 64) +
+// NE ints.  Ends with a workgroup barrier.
+template <int NW>
+__device__ void build_draw_list(const int32_t *mode, int B, int e0, int NE, int *scratch, int &nres, int &nbon,
+                                int *&lreq) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nch = (B + 63) / 64;
+    int *cr = scratch, *cb = scratch + nch;
+    lreq = scratch + 2 * nch;
+    for (int i = tid; i < NE; i += NW * 64) lreq[i] = -1;
+    for (int c = wave; c < nch; c += NW) {
+        const int bq = c * 64 + lane;
+        const int md = bq < B ? mode[bq] : kModeDone;
+        const uint64_t br = __ballot(md == kModeResidual), bb = __ballot(md == kModeBonus);
+        if (lane == 0) {
+            cr[c] = __popcll(br);
+            cb[c] = __popcll(bb);
+        }
+    }
+    __syncthreads();
+    int tr = 0, tb = 0;
+    for (int i = lane; i < nch; i += 64) {
+        tr += cr[i];
+        tb += cb[i];
+    }
+    nres = wave_isum(tr);
+    nbon = wave_isum(tb);
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    for (int c = wave; c < nch; c += NW) {
+        int pr = 0, pb = 0;  // draws of each kind in the blocks before block c
+        for (int i = lane; i < c; i += 64) {
+            pr += cr[i];
+            pb += cb[i];
+        }
+        pr = wave_isum(pr);
+        pb = wave_isum(pb);
+        const int bq = c * 64 + lane;
+        const int md = bq < B ? mode[bq] : kModeDone;
+        const uint64_t br = __ballot(md == kModeResidual), bb = __ballot(md == kModeBonus);
+        int e = -1;
+        if (md == kModeResidual) e = pr + __popcll(br & below);
+        if (md == kModeBonus) e = B - nbon + pb + __popcll(bb & below);
+        if (e >= e0 && e < e0 + NE) lreq[e - e0] = bq;
+    }
+    __syncthreads();
+}
 
 constexpr int kDrawThreads = 512;  // 8 waves: one block of 32 listed requests each
 // A batch of at most two 32-request blocks draws with 2-wave workgroups
@@ -623,16 +697,32 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(16))) uint8_t ldsU1[NWV * TR::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsT0[NWV * TR::BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t ldsT1[NWV * TR::BYTES];
-    // entries [0, nres) of the draw list are residual draws, [B - nbon, B)
-    // bonus draws; the two never overlap, so at most one wave holds both kinds
-    const int nres = p.status[2], nbon = p.status[3];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
     const int chunk = lg / p.nbg, bg = lg % p.nbg;
     const int e0 = bg * NWV * 32;  // first list entry of the workgroup
-    const int bon0 = p.B - nbon;   // first bonus entry
-    if (e0 >= nres && (nbon == 0 || e0 + NWV * 32 <= bon0 || e0 >= p.B)) return;  // the whole workgroup is idle
+    const int t_begin = chunk * p.tiles_per_chunk;
+    const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
+    const bool tail = t_end * kTile > p.V;  // the chunk's last tile runs past the vocabulary
+    const int nfull = (t_end - t_begin) - (tail ? 1 : 0);
+    const WT *W2 = static_cast<const WT *>(p.W2);
+    TileDMA<WT, R, NWV * 64> dma;
+    dma.init(tid);
+    // the first W2 tile needs no list: it goes out first (and is only wasted
+    // by a workgroup that holds no residual draw)
+    if (nfull > 0) dma.template issue<false>(W2, t_begin * kTile, p.V, ldsW0, wave);
+    // entries [0, nres) of the draw list are residual draws, [B - nbon, B)
+    // bonus draws; the two never overlap, so at most one wave holds both kinds.
+    // The list is built in the second target buffer, which the first stage
+    // leaves free.
+    int nres, nbon, *lreq;
+    build_draw_list<NWV>(p.mode, p.B, e0, NWV * 32, reinterpret_cast<int *>(ldsT1), nres, nbon, lreq);
+    const int bon0 = p.B - nbon;  // first bonus entry
+    if (e0 >= nres && (nbon == 0 || e0 + NWV * 32 <= bon0 || e0 >= p.B)) {
+        __builtin_amdgcn_s_waitcnt(0);  // the whole workgroup is idle: its direct loads land before it leaves
+        return;
+    }
     const bool need_w2 = e0 < nres;  // uniform across the workgroup
     const int w0 = e0 + wave * 32;   // first entry of the wave
     const bool wave_resid = w0 < nres;                          // uniform across the wave
@@ -642,14 +732,14 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int e = w0 + n;
     const bool resid = e < nres;
     const bool ok = resid || (e >= bon0 && e < p.B);
-    const int req = ok ? p.draw_list[e] : 0;
+    const int req = ok ? max(lreq[wave * 32 + n], 0) : 0;
     const int slot = e;
+    if (chunk == 0 && h == 0 && ok) p.slot[req] = slot;  // for the level-2 draw
     const int j = wave_ok ? p.jpos[req] : 1;
     const float sc = wave_ok ? kLog2e / p.temperature[req] : 1.0f;
     const float lse2t = wave_ok ? p.fin_lse2[req] : 0.f;
     const int trow_i = ok ? p.off[req] + j - 1 : -1;  // packed target row
 
-    const WT *W2 = static_cast<const WT *>(p.W2);
     EFrags<WT, R> ef;
     int urow_i = -1;  // row of U
     float lse2q = 0.f;
@@ -660,25 +750,19 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
             lse2q = p.lse2q[req];
         }
     }
-    TileDMA<WT, R, NWV * 64> dma;
-    if (need_w2) dma.init(tid);
     TR su, stg;
     if (wave_ok) stg.init(lane, p.target, size_t(p.V), [&](int r) { return __shfl(trow_i, r); });
     if (wave_resid) su.init(lane, p.U, size_t(p.V), [&](int r) { return __shfl(urow_i, r); });
     const int roff = wave * TR::BYTES;  // this wave's region in each region buffer
 
-    const int t_begin = chunk * p.tiles_per_chunk;
-    const int t_end = min(p.ntiles, t_begin + p.tiles_per_chunk);
-    const bool tail = t_end * kTile > p.V;  // the chunk's last tile runs past the vocabulary
-    const int nfull = (t_end - t_begin) - (tail ? 1 : 0);
     float S = 0.f;  // residual mass (both halves hold the same sum)
     float best = kNegInf;
     int bt = t_begin;
     uint4 tw = make_uint4(0u, 0u, 0u, 0u);
 
-    auto issue = [&](int t, uint8_t *w, uint8_t *ur, uint8_t *tr, auto clamp) __device__ {
+    auto issue = [&](int t, uint8_t *w, uint8_t *ur, uint8_t *tr, auto clamp, bool with_w2 = true) __device__ {
         constexpr bool C = decltype(clamp)::value;
-        if (need_w2) dma.template issue<C>(W2, t * kTile, p.V, w, wave);
+        if (need_w2 && with_w2) dma.template issue<C>(W2, t * kTile, p.V, w, wave);
         if (wave_ok) stg.template issue<C>(t * kTile, p.V, tr + roff, lane);
         if (wave_resid) su.template issue<C>(t * kTile, p.V, ur + roff, lane);
     };
@@ -735,7 +819,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     using NoClamp = std::integral_constant<bool, false>;
     using Clamp = std::integral_constant<bool, true>;
-    if (nfull > 0) issue(t_begin, ldsW0, ldsU0, ldsT0, NoClamp{});
+    if (nfull > 0) issue(t_begin, ldsW0, ldsU0, ldsT0, NoClamp{}, false);  // its W2 tile is out already
     for (int i = 0; i < nfull; i += 2) {
         const int t = t_begin + i;
         __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of stage i have landed
@@ -925,116 +1009,53 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     }
 }
 
-// The position passes of a block of gamma: first row and row count of each
-// (`single` single rows, then pairs, an odd row left over first), then
-// the decide-only pass (rows 0 at j0 = gamma + 2).
-struct PassRows {
-    int j0, rows;
-};
-int pass_schedule(int gamma, int single, PassRows *out) {
-    int n = 0, j = 1;
-    const int last = gamma + 1;
-    for (; j <= last && j <= single; ++j) out[n++] = {j, 1};
-    if ((last - j + 1) % 2 == 1 && j <= last) out[n++] = {j++, 1};
-    for (; j <= last; j += 2) out[n++] = {j, 2};
-    out[n++] = {last + 1, 0};
-    return n;
-}
-
 template <typename WT, int R>
 hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyWork &w, hipStream_t s) {
     hipError_t e;
     // a small batch has its input checks and output defaults done by the
-    // first position pass (each of its waves forms its request's row offset
-    // from ell, O(B) reads a wave); a large one by a workgroup of its own
-    const bool prep_in_pass = a.B <= kPrepInPassMaxBatch;
-    if (!prep_in_pass) {
-        PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, a.n_target_rows, w.status, w.off,
+    // walk (each workgroup forms its request's row offset from ell, O(B)
+    // reads); a large one by a workgroup of its own
+    const bool prep_in_walk = a.B <= kPrepInWalkMaxBatch;
+    if (!prep_in_walk) {
+        PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, a.n_target_rows, w.off,
                       w.mode, w.req_flags, a.n_accept_out, a.tokens_out, a.diag_out, a.resid_out};
         launch_kernel("verify_prep", verify_prep_kernel, dim3(1), dim3(1024), s, pp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
-    PassRows sched[DSPARK_MAX_GAMMA + 2];  // gamma is checked at the boundary
-    const int single = size_t(a.B) * a.V * sizeof(float) <= kPairAllBytes ? 0 : kSinglePasses;
-    const int npass = pass_schedule(a.gamma, single, sched);
-    for (int pass = 1; pass <= npass; ++pass) {
-        const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
-        const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
-        const size_t half = rs * kPassRows;
-        const PassRows cur = sched[pass - 1];
-        const int din = pass > 1 ? sched[pass - 2].rows : 1;  // rows this pass decides
-        const int dout = cur.rows > 0 ? cur.rows : 1;         // row slots of its grid
-        // the last pass only decides: one wave a request
-        const int nseg = pass == 1 ? pl.nseg_first : (cur.rows == 0 ? 1 : pl.nseg);
-        PassParams pp{};
-        pp.target = a.target;
-        pp.x = a.x;
-        pp.ell = a.ell;
-        pp.qx = a.qx;
-        pp.temperature = a.temperature;
-        pp.B = a.B;
-        pp.gamma = a.gamma;
-        pp.V = a.V;
-        pp.j0 = cur.j0;
-        pp.vec = vec_t;
-        pp.nseg = nseg;
-        pp.seg_len = pass == 1 ? pl.seg_len_first : pl.seg_len;
-        pp.nseg_in = pass == 2 ? pl.nseg_first : pl.nseg;
-        pp.seg_stride = pl.nseg_max;
-        pp.row_stride = rs;
-        pp.key0 = a.key0;
-        pp.key1 = a.key1;
-        pp.round32 = a.round32;
-        pp.off = w.off;
-        pp.prep = (pass == 1 && prep_in_pass) ? 1 : 0;
-        pp.n_target_rows = a.n_target_rows;
-        pp.row_offsets = a.row_offsets;
-        pp.req_flags = w.req_flags;
-        pp.resid_out = a.resid_out;
-        pp.act_in = w.act + size_t(in) * a.B;
-        pp.pm_in = w.seg_m + in * half;
-        pp.ps_in = w.seg_s + in * half;
-        pp.pv_in = w.seg_v + in * half;
-        pp.pi_in = w.seg_i + in * half;
-        pp.tx_in = w.seg_tx + size_t(in) * kPassRows * a.B;
-        pp.act_out = w.act + size_t(out) * a.B;
-        pp.pm_out = w.seg_m + out * half;
-        pp.ps_out = w.seg_s + out * half;
-        pp.pv_out = w.seg_v + out * half;
-        pp.pi_out = w.seg_i + out * half;
-        pp.tx_out = w.seg_tx + size_t(out) * kPassRows * a.B;
-        pp.status = w.status;
-        pp.mode = w.mode;
-        pp.jpos = w.jpos;
-        pp.slot = w.slot;
-        pp.draw_list = w.draw_list;
-        pp.fin_lse2 = w.fin_lse2;
-        pp.prev = w.prev;
-        pp.erow_mode = a.erow_mode;
-        pp.lse2q = w.lse2q;
-        pp.anchor = a.anchor;
-        pp.lse_q = a.lse_q;
-        pp.n_accept_out = a.n_accept_out;
-        pp.tokens_out = a.tokens_out;
-        pp.diag_out = a.diag_out;
-        static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
-                                            "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
-        const dim3 grid(size_t((a.B + 3) / 4) * nseg * dout);
-        const char *name = names[std::min(pass, 8) - 1];
-        if (pass == 1 && dout == 1)
-            launch_kernel(name, (verify_pass_kernel<true, 1, 1>), grid, dim3(256), s, pp);
-        else if (pass == 1)
-            launch_kernel(name, (verify_pass_kernel<true, 1, 2>), grid, dim3(256), s, pp);
-        else if (din == 1 && dout == 1)
-            launch_kernel(name, (verify_pass_kernel<false, 1, 1>), grid, dim3(256), s, pp);
-        else if (din == 1)
-            launch_kernel(name, (verify_pass_kernel<false, 1, 2>), grid, dim3(256), s, pp);
-        else if (dout == 1)
-            launch_kernel(name, (verify_pass_kernel<false, 2, 1>), grid, dim3(256), s, pp);
-        else
-            launch_kernel(name, (verify_pass_kernel<false, 2, 2>), grid, dim3(256), s, pp);
+    {
+        WalkParams wp{};
+        wp.target = a.target;
+        wp.x = a.x;
+        wp.ell = a.ell;
+        wp.qx = a.qx;
+        wp.temperature = a.temperature;
+        wp.B = a.B;
+        wp.gamma = a.gamma;
+        wp.V = a.V;
+        wp.vec = vec_t;
+        wp.key0 = a.key0;
+        wp.key1 = a.key1;
+        wp.round32 = a.round32;
+        wp.off = w.off;
+        wp.prep = prep_in_walk ? 1 : 0;
+        wp.n_target_rows = a.n_target_rows;
+        wp.row_offsets = a.row_offsets;
+        wp.req_flags = w.req_flags;
+        wp.resid_out = a.resid_out;
+        wp.mode = w.mode;
+        wp.jpos = w.jpos;
+        wp.prev = w.prev;
+        wp.fin_lse2 = w.fin_lse2;
+        wp.lse2q = w.lse2q;
+        wp.erow_mode = a.erow_mode;
+        wp.anchor = a.anchor;
+        wp.lse_q = a.lse_q;
+        wp.n_accept_out = a.n_accept_out;
+        wp.tokens_out = a.tokens_out;
+        wp.diag_out = a.diag_out;
+        launch_kernel("verify_walk", verify_walk_kernel, dim3(a.B), dim3(kWalkThreads), s, wp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -1057,8 +1078,8 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.key0 = a.key0;
         dp.key1 = a.key1;
         dp.round32 = a.round32;
-        dp.status = w.status;
-        dp.draw_list = w.draw_list;
+        dp.mode = w.mode;
+        dp.slot = w.slot;
         dp.jpos = w.jpos;
         dp.off = w.off;
         dp.fin_lse2 = w.fin_lse2;
@@ -1124,18 +1145,6 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
 VerifyPlan verify_plan(int B, int gamma, int V) {
     (void)gamma;
     VerifyPlan p{};
-    // Position passes split a row into segments of whole float4 groups: the
-    // first pass, which reads every request's row, in a few long ones (long
-    // streams per workgroup), the later ones, which read fewer and fewer rows,
-    // in up to kSegLater short ones (more waves per row).
-    const int n4 = (V + 3) / 4;
-    auto split = [&](int k, int &nseg, int &len) {
-        len = 4 * ((n4 + k - 1) / k);
-        nseg = (V + len - 1) / len;
-    };
-    split(kSegFirst, p.nseg_first, p.seg_len_first);
-    split(kSegLater, p.nseg, p.seg_len);
-    p.nseg_max = std::max(p.nseg_first, p.nseg);
     p.nbb = (B + 31) / 32;
     // 8-wave workgroups holding two one-tile stages of W2 rows and wave
     // regions (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them
@@ -1154,23 +1163,15 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     (void)V;
     Carve c(ws);
     VerifyWork w{};
-    w.status = c.take<int32_t>(4);
+    w.status = c.take<int32_t>(4);  // first: dspark_verify_check reads word 0
     w.req_flags = c.take<int32_t>(B);
     w.off = c.take<int32_t>(size_t(B) + 1);
-    w.act = c.take<int32_t>(size_t(2) * B);
-    const size_t ns = size_t(2) * kPassRows * B * p.nseg_max;
-    w.seg_m = c.take<float>(ns);
-    w.seg_s = c.take<float>(ns);
-    w.seg_v = c.take<float>(ns);
-    w.seg_i = c.take<int32_t>(ns);
-    w.seg_tx = c.take<float>(size_t(2) * kPassRows * B);
     w.fin_lse2 = c.take<float>(B);
     w.prev = c.take<int32_t>(B);
     w.lse2q = c.take<float>(B);
     w.mode = c.take<int32_t>(B);
     w.jpos = c.take<int32_t>(B);
     w.slot = c.take<int32_t>(B);
-    w.draw_list = c.take<int32_t>(B);
     const size_t nd = size_t(B) * p.tile.nchunk;
     w.dw_sum = c.take<float>(nd);
     w.dw_bl = c.take<float>(nd);
