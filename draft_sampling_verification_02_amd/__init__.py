@@ -30,6 +30,8 @@ DSPARK_ERR_UNSUPPORTED = -2
 DSPARK_ERR_WORKSPACE = -3
 DSPARK_ERR_HIP = -4
 DSPARK_ERR_DEVICE_INPUT = -5
+DSPARK_ERR_SCRATCH = -6
+DSPARK_NOALLOC_SCRATCH_BYTES = 8 << 20  # the allocation-free draft's fixed scratch (include/dspark.h)
 DSPARK_BF16 = 0
 DSPARK_F32 = 1
 
@@ -67,6 +69,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
                                  _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _c_size, _c_void_p], _c_int),
+        "dspark_draft_sample_noalloc": ([_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                         _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p], _c_int),
         "dspark_draft_sample_confidence": ([_c_void_p, _c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
                                             _c_int, _c_int, _c_int, _c_int, _c_u64, _c_u64,
                                             _c_void_p, _c_void_p, _c_int, _c_void_p,
@@ -249,6 +254,23 @@ def dspark_draft_sample(U, W1, W2, anchor, temperature, seed: int, round_id: int
                                  _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")),
                                  _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st, "dspark_draft_sample")
+    return out
+
+
+def dspark_draft_sample_noalloc(U, W1, W2, anchor, temperature, seed: int, round_id: int, *,
+                                margin: bool = False, out: dict | None = None, stream=None) -> dict:
+    """dspark_draft_sample without a workspace: the library's fixed per-device
+    scratch serves instead, and the C call allocates nothing.  Pass ``out`` (a
+    previous result) so that this wrapper allocates no outputs either.
+    Returns {"x", "lse", "qx"[, "margin"]}."""
+    lib = load_library()
+    dev, B, gamma, V, r, wdt = _draft_inputs(U, W1, W2, anchor, temperature)
+    out = _draft_outputs(B, gamma, dev, margin, False, out)
+    st = lib.dspark_draft_sample_noalloc(_ptr(U), _ptr(W1), _ptr(W2), wdt, _ptr(anchor), _ptr(temperature),
+                                         B, gamma, V, r, int(seed), int(round_id),
+                                         _ptr(out["x"]), _ptr(out["lse"]), _ptr(out["qx"]), _ptr(out.get("margin")),
+                                         _stream_ptr(stream))
+    _check(st, "dspark_draft_sample_noalloc")
     return out
 
 

@@ -2,6 +2,7 @@
 // validation, workspace layout, kernel sequencing and per-kernel profiling.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -124,6 +125,7 @@ const char *dspark_status_string(int status) {
         case DSPARK_ERR_WORKSPACE: return "workspace missing or too small";
         case DSPARK_ERR_HIP: return "HIP runtime error";
         case DSPARK_ERR_DEVICE_INPUT: return "device-side input check failed";
+        case DSPARK_ERR_SCRATCH: return "sizes exceed the allocation-free entry point's fixed scratch";
         default: return "unknown status";
     }
 }
@@ -137,16 +139,25 @@ size_t dspark_draft_workspace_size(int B, int gamma, int V, int r) {
 
 namespace {
 
-int draft_common(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
-                 const float *temperature, int B, int gamma, int V, int r, uint64_t seed, uint64_t round_id,
-                 const float *hidden, const float *conf_w, int d, const float *conf_tau, int32_t *x_out,
-                 float *lse_out, float *qx_out, float *margin_out, float *conf_out, float *survival_out,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+// The host-side argument checks of the draft entry points.
+int draft_args(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+               const float *temperature, int B, int gamma, int V, int r, const int32_t *x_out, const float *lse_out,
+               const float *qx_out) {
     if (!U || !W1 || !W2 || !anchor || !temperature || !x_out || !lse_out || !qx_out) return DSPARK_ERR_ARG;
     if (!sizes_ok(B, gamma, V, r)) return DSPARK_ERR_ARG;
     if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32) return DSPARK_ERR_ARG;
     if (!rank_supported(wdtype, r)) return DSPARK_ERR_UNSUPPORTED;
     if (!aligned16(W1) || !aligned16(W2)) return DSPARK_ERR_ARG;
+    return DSPARK_OK;
+}
+
+int draft_common(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                 const float *temperature, int B, int gamma, int V, int r, uint64_t seed, uint64_t round_id,
+                 const float *hidden, const float *conf_w, int d, const float *conf_tau, int32_t *x_out,
+                 float *lse_out, float *qx_out, float *margin_out, float *conf_out, float *survival_out,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    const int st = draft_args(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, x_out, lse_out, qx_out);
+    if (st != DSPARK_OK) return st;
     const DraftPlan plan = draft_plan(B, V);
     size_t need = 0;
     draft_carve(nullptr, B, plan, &need);
@@ -191,6 +202,58 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
     return draft_common(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, seed, round_id, nullptr, nullptr, 0,
                         nullptr, x_out, lse_out, qx_out, margin_out, nullptr, nullptr, workspace, workspace_bytes,
                         stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The allocation-free entry point's scratch: a fixed array in the library's
+// device code, so each device the library runs on holds its own copy from
+// module load until the process ends.  Host code never uses the array's name
+// as an address (it is a host-side stand-in); the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept
+// here.  The fast path is one atomic load; the first call on a device
+// resolves the address under a lock.
+static __device__ __align__(256) uint8_t scratch[DSPARK_NOALLOC_SCRATCH_BYTES];
+constexpr int kScratchDevices = 256;
+std::atomic<void *> scratch_addr[kScratchDevices];
+std::mutex scratch_mu;
+
+int scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return DSPARK_ERR_HIP;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DSPARK_ERR_HIP;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_draft_sample_noalloc(const float *U, const void *W1, const void *W2, int wdtype, const int32_t *anchor,
+                                const float *temperature, int B, int gamma, int V, int r, uint64_t seed,
+                                uint64_t round_id, int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
+                                void *stream) {
+    const int st = draft_args(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, x_out, lse_out, qx_out);
+    if (st != DSPARK_OK) return st;
+    if (draft_bytes(B, V) > DSPARK_NOALLOC_SCRATCH_BYTES) return DSPARK_ERR_SCRATCH;
+    void *ws = nullptr;
+    const int sc = scratch_for_current_device(&ws);
+    if (sc != DSPARK_OK) return sc;
+    // the draft's scratch needs no clearing: every partial is written before it is read
+    return draft_common(U, W1, W2, wdtype, anchor, temperature, B, gamma, V, r, seed, round_id, nullptr, nullptr, 0,
+                        nullptr, x_out, lse_out, qx_out, margin_out, nullptr, nullptr, ws,
+                        DSPARK_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int dspark_draft_sample_confidence(const float *U, const void *W1, const void *W2, int wdtype,

@@ -26,6 +26,8 @@
  *    matching *_workspace_size query.  Workspace contents need no
  *    initialisation and are not meaningful between calls, except that
  *    dspark_verify_check reads the status the last dspark_verify left there.
+ *    The one exception is dspark_draft_sample_noalloc, which takes no
+ *    workspace and uses a fixed array the library holds on each device.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Device entry
  *    points only enqueue work on it and return; results are ready when the
  *    stream is.  Two calls that share a workspace must be ordered on one
@@ -65,7 +67,8 @@ typedef enum dspark_status {
     DSPARK_ERR_UNSUPPORTED = -2,  /* valid arguments this build has no kernel for */
     DSPARK_ERR_WORKSPACE = -3,    /* workspace missing or smaller than queried */
     DSPARK_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
-    DSPARK_ERR_DEVICE_INPUT = -5  /* device-resident input failed its check */
+    DSPARK_ERR_DEVICE_INPUT = -5, /* device-resident input failed its check */
+    DSPARK_ERR_SCRATCH = -6       /* sizes need more than the allocation-free entry point's fixed scratch */
 } dspark_status;
 
 /* Element type of the Markov factors W1 and W2. */
@@ -129,6 +132,37 @@ int dspark_draft_sample(const float *U, const void *W1, const void *W2, int wdty
                         uint64_t seed, uint64_t round_id,
                         int32_t *x_out, float *lse_out, float *qx_out, float *margin_out,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of the fixed device array dspark_draft_sample_noalloc draws its
+ * scratch from (one array on each device the library runs on, held until the
+ * process ends). */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* dspark_draft_sample for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: its scratch is a fixed array of
+ * DSPARK_NOALLOC_SCRATCH_BYTES in the library, one per device, whose address
+ * is resolved once per device on the first call made with that device
+ * current.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine; with per-kernel profiling off, no host
+ * allocation either).  Outputs are the bits dspark_draft_sample writes for the
+ * same inputs.
+ *
+ *   every argument: as for dspark_draft_sample, without the workspace; the
+ *   device current at the call must be the one that holds the buffers and
+ *   owns `stream`.
+ * Returns DSPARK_ERR_SCRATCH when dspark_draft_workspace_size(B, gamma, V, r)
+ * exceeds DSPARK_NOALLOC_SCRATCH_BYTES (B above 13,696 at V = 129,280,
+ * r = 256), DSPARK_ERR_HIP when the array's address cannot be resolved, and
+ * otherwise the errors of dspark_draft_sample.
+ * Every call on one device shares that device's array and leaves it in an
+ * arbitrary state; nothing in it needs clearing before a call.  Calls that
+ * overlap on one device (on different streams, or from threads that do not
+ * order their streams) race on the array and give undefined outputs. */
+int dspark_draft_sample_noalloc(const float *U, const void *W1, const void *W2, int wdtype,
+                                const int32_t *anchor, const float *temperature, int B, int gamma, int V,
+                                int r, uint64_t seed, uint64_t round_id, int32_t *x_out, float *lse_out,
+                                float *qx_out, float *margin_out, void *stream);
 
 /* dspark_draft_sample plus the confidence head of every position ([MG] 4.1
  * Confidence Head; [MG] 4.2 and [CE] 04 for the survival products): with

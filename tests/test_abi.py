@@ -72,6 +72,32 @@ def test_draft_argument_errors_need_no_gpu():
     assert _draft_call(lib, ws_bytes=16) == ds.DSPARK_ERR_WORKSPACE
 
 
+def test_noalloc_draft_argument_errors_need_no_gpu():
+    # the same checks as dspark_draft_sample, then the fixed-scratch limit,
+    # all before the device is touched
+    lib = ds.load_library()
+
+    def call(**kw):
+        a = dict(U=_FAKE, W1=_FAKE, W2=_FAKE, wdtype=0, anchor=_FAKE, temperature=_FAKE, B=4, gamma=5, V=1000, r=16,
+                 x=_FAKE, lse=_FAKE, qx=_FAKE)
+        a.update(kw)
+        return lib.dspark_draft_sample_noalloc(a["U"], a["W1"], a["W2"], a["wdtype"], a["anchor"], a["temperature"],
+                                               a["B"], a["gamma"], a["V"], a["r"], 1, 0, a["x"], a["lse"], a["qx"],
+                                               None, None)
+
+    assert call(U=None) == ds.DSPARK_ERR_ARG
+    assert call(qx=None) == ds.DSPARK_ERR_ARG
+    assert call(B=0) == ds.DSPARK_ERR_ARG
+    assert call(r=24) == ds.DSPARK_ERR_UNSUPPORTED
+    assert call(W1=ctypes.c_void_p(0x1008)) == ds.DSPARK_ERR_ARG
+    # the limit is the workspace the same call would need with a workspace
+    need = lambda B: ds.dspark_draft_workspace_size(B, 5, 129280, 256)
+    assert need(13696) <= ds.DSPARK_NOALLOC_SCRATCH_BYTES < need(13697)
+    assert call(B=13697, V=129280, r=256) == ds.DSPARK_ERR_SCRATCH
+    assert call(B=65536, V=16777215, r=256) == ds.DSPARK_ERR_SCRATCH
+    assert "scratch" in ds.dspark_status_string(ds.DSPARK_ERR_SCRATCH)
+
+
 def _verify_call(lib, **kw):
     a = dict(target=_FAKE, rows=24, ell=_FAKE, off=None, U=_FAKE, W1=_FAKE, W2=_FAKE, wdtype=0, anchor=_FAKE,
              x=_FAKE, lse=_FAKE, qx=_FAKE, temperature=_FAKE, B=4, gamma=5, V=1000, r=16, seed=1, round_id=0,
