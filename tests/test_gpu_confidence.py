@@ -95,7 +95,7 @@ def test_confidence_head_parity(B, gamma, V, r, wdtype, d):
 
 def test_confidence_head_large_batch_config():
     """Batch 256, gamma 5, V 129,280, r 256, bf16, d 1024, in the bench's
-    launch configuration; the oracle checks a sample of requests."""
+    launch configuration; the oracle checks every request."""
     cfg = S.CONFIGS["large"]
     rnd = S.make_round(cfg)
     h, w = S.confidence_head_inputs(cfg)
@@ -103,7 +103,7 @@ def test_confidence_head_large_batch_config():
     dev = to_device(rnd)
     gc = _gpu_conf(dev, h, w, cfg.seed, 0)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 7, 10, 55, 128, 200, 255])
+    rows = np.arange(cfg.B)
     U, anchor, temp = rnd.U[rows], rnd.anchor[rows], rnd.temperature[rows]
     od = oracle.draft(U, rnd.W1, rnd.W2, anchor, temp, cfg.seed, 0, req_ids=rows.astype(np.int32))
     c, a = oracle.confidence(h[rows], w, rnd.W1, anchor, od["x"])
@@ -223,7 +223,7 @@ def test_acceptance_offsets_and_bad_requests():
 
 def test_acceptance_large_batch_config():
     """Batch 256, gamma 5, V 129,280, r 256, every position verified: alpha
-    against the oracle on a sample of requests, and at every sampled
+    against the oracle on every request, and at every sampled
     rejection of the GPU's own verify alpha_j = 1 - S (the residual mass the
     draw kernels sum, an independent reduction)."""
     cfg = S.CONFIGS["large"]
@@ -255,7 +255,7 @@ def test_acceptance_large_batch_config():
         assert np.all(alpha[b, :n[b]] == 1.0)
         if n[b] < cfg.gamma:
             assert alpha[b, n[b]] == 0.0
-    rows = np.array([0, 3, 10, 77, 129, 254])  # rows 0 and 10 are greedy
+    rows = np.arange(cfg.B)  # every tenth request is greedy
     sub = packed_subset(target, ell, rows)
     od, _ = oracle_round(rnd, sub, ell, cfg.seed, 0, rows=rows)
     ao = oracle.acceptance(sub, ell[rows], rnd.U[rows], rnd.W1, rnd.W2, rnd.anchor[rows], od["x"],

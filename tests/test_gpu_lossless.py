@@ -1,0 +1,92 @@
+"""Losslessness of whole rounds on the GPU ("DeepSeek DSpark explained",
+section 05: accepting with min(1, p/q) and resampling from max(p - q, 0)
+emits tokens distributed as the target; section 02: later positions are
+emitted only after every earlier draft was accepted).
+
+The tiny configuration's inputs (one request: U, the target rows, W1, W2,
+the anchor) are broadcast to 50,000 requests, each an independent sample
+(the request index is part of every Philox counter), over 20 rounds: 10^6
+rounds of the Markov-head draft and the verify.  At each position k the token
+emitted there, among the rounds that reach k, must follow p_k = softmax of
+target row k: a chi-square test with bins merged until every expected count
+is at least 5.  The same statement the oracle's own multi-position test pins
+on a 6-token vocabulary, here through the library's kernels at V = 1000."""
+import numpy as np
+import pytest
+
+import synth_inputs as S
+from roundkit import np_of
+
+pytestmark = pytest.mark.gpu
+
+N_REQ = 50_000
+ROUNDS = 20
+ALPHA = 1e-4  # per position; five positions
+
+
+def _merged_chi2(counts, probs, min_expected=5.0):
+    """Chi-square of counts against probs after merging the smallest bins
+    (in ascending order of probability) until every expected count is >= 5;
+    returns (statistic, degrees of freedom)."""
+    counts = np.asarray(counts, np.float64)
+    probs = np.asarray(probs, np.float64)
+    n = counts.sum()
+    order = np.argsort(probs)
+    c, e = [], []
+    acc_c = acc_e = 0.0
+    for i in order:
+        acc_c += counts[i]
+        acc_e += n * probs[i]
+        if acc_e >= min_expected:
+            c.append(acc_c)
+            e.append(acc_e)
+            acc_c = acc_e = 0.0
+    if acc_e > 0:  # the remainder joins the last bin
+        c[-1] += acc_c
+        e[-1] += acc_e
+    c, e = np.array(c), np.array(e)
+    return float(((c - e) ** 2 / e).sum()), len(c) - 1
+
+
+def test_emitted_tokens_follow_the_target_at_every_position():
+    import torch
+    from scipy.stats import chi2
+
+    import draft_sampling_verification_02_amd as ds
+    ds.load_library()
+    cfg = S.CONFIGS["tiny"]
+    rnd = S.make_round(cfg)
+    gamma, V = cfg.gamma, cfg.V
+    ell1 = np.full(1, gamma, np.int32)
+    trows = rnd.target_packed(ell1)  # [gamma + 1, V] rows of the one request
+    print(f"[lossless] tiny inputs x {N_REQ} requests x {ROUNDS} rounds", flush=True)
+    U = torch.from_numpy(rnd.U).cuda().expand(N_REQ, gamma, V).contiguous()
+    target = torch.from_numpy(trows).cuda().repeat(N_REQ, 1).contiguous()
+    W1 = torch.from_numpy(rnd.weights_device_layout()[0]).cuda()
+    W2 = torch.from_numpy(rnd.weights_device_layout()[1]).cuda()
+    anchor = torch.full((N_REQ,), int(rnd.anchor[0]), dtype=torch.int32, device="cuda")
+    temp = torch.full((N_REQ,), float(rnd.temperature[0]), dtype=torch.float32, device="cuda")
+    ell = torch.full((N_REQ,), gamma, dtype=torch.int32, device="cuda")
+    assert float(rnd.temperature[0]) == 1.0
+    counts = np.zeros((gamma + 1, V), np.int64)
+    d = v = None
+    for rid in range(ROUNDS):
+        d = ds.dspark_draft_sample(U, W1, W2, anchor, temp, cfg.seed, rid, out=d)
+        v = ds.dspark_verify(target, ell, U, W1, W2, anchor, d["x"], d["lse"], d["qx"], temp, cfg.seed, rid, out=v)
+        n, tok = np_of(v["n"]), np_of(v["tokens"])
+        for k in range(1, gamma + 2):
+            reach = n >= k - 1
+            counts[k - 1] += np.bincount(tok[reach, k - 1], minlength=V)
+    t64 = trows.astype(np.float64)
+    p = np.exp(t64 - t64.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    for k in range(1, gamma + 2):
+        stat, dof = _merged_chi2(counts[k - 1], p[k - 1])
+        crit = chi2.ppf(1 - ALPHA, dof)
+        print(f"[lossless] position {k}: {int(counts[k - 1].sum())} emitted, chi2 {stat:.1f} (dof {dof}, "
+              f"critical {crit:.1f})", flush=True)
+        assert stat < crit, (k, stat, crit)
+    # every round reaches position 1; later positions are reached less often
+    reached = counts.sum(1)
+    assert reached[0] == N_REQ * ROUNDS
+    assert np.all(np.diff(reached) <= 0)

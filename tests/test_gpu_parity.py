@@ -155,9 +155,11 @@ def test_long_block_config_parity():
     assert cd.ineligible_rate < 0.3
 
 
-def test_scheduled_config_sampled_parity():
-    """Batch 1024: the scheduler's literal choice is ell = 0 everywhere; the
-    GPU verifies all 1024 bonus rows, the oracle checks a sample of requests."""
+def test_scheduled_config_parity():
+    """Batch 1024: the scheduler's literal choice is ell = 0 everywhere, so
+    the GPU verifies 1024 bonus rows; a supplement schedules 256 groups of 4
+    requests independently (ell over 0..5).  The oracle checks every request
+    of both (one oracle draft, two verifies)."""
     cfg = S.CONFIGS["sched"]
     rnd = S.make_round(cfg)
     sps = S.sps_table_toy(0.2, cfg.B * (1 + cfg.gamma) + 1)
@@ -166,22 +168,35 @@ def test_scheduled_config_sampled_parity():
     # supplement: 256 groups of 4 requests scheduled independently
     ell_g = np.concatenate([ds.dspark_schedule(rnd.c[4 * g:4 * g + 4], S.sps_table_toy(0.2, 25))[0]
                             for g in range(cfg.B // 4)]).astype(np.int32)
+    assert len(set(ell_g.tolist())) > 3
     dev = to_device(rnd)
-    rows = np.arange(0, cfg.B, 16)
+    req = np.asarray(rnd.requests, np.int32)
+    od = oracle.draft(rnd.U, rnd.W1, rnd.W2, rnd.anchor, rnd.temperature, cfg.seed, 0, req_ids=req)
+    d = gpu_draft(dev, cfg.seed, 0)
+    gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+    cd = compare_draft(gd, od)
+    _say(f"[sched] draft {cd.report()}")
     for tag, e in (("literal", ell.astype(np.int32)), ("groups-of-4", ell_g)):
         target = rnd.target_packed(e)
         _say(f"[sched {tag}] rows={target.shape[0]}")
         td = torch.from_numpy(target).cuda()
         ed = torch.from_numpy(e).cuda()
-        d = gpu_draft(dev, cfg.seed, 0)
         v = gpu_verify(dev, td, ed, d, cfg.seed, 0)
-        gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+        torch.cuda.synchronize()
+        assert ds.dspark_verify_check(v["workspace"]) == 0
         gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
-        od, ov = oracle_round(rnd, packed_subset(target, e, rows), e, cfg.seed, 0, rows=rows)
-        cd = compare_draft(gd, od, rows=rows)
-        cv = compare_verify(gv, od, ov, rnd.temperature[rows], e[rows], rows=rows)
-        _say(f"[sched {tag}] draft {cd.report()} | verify {cv.report()}")
-        assert np.all(gv["n"] <= e)
+        ov = oracle.verify(target, e, rnd.U, rnd.W1, rnd.W2, rnd.anchor, od["x"], rnd.temperature, cfg.seed, 0,
+                           req_ids=req)
+        cv = compare_verify(gv, od, ov, rnd.temperature, e)
+        _say(f"[sched {tag}] verify {cv.report()}")
+        n, tok = gv["n"], gv["tokens"]
+        assert np.all((n >= 0) & (n <= e))
+        for b in range(cfg.B):
+            assert np.all(tok[b, :n[b]] == gd["x"][b, :n[b]])
+            assert 0 <= tok[b, n[b]] < cfg.V
+            assert np.all(tok[b, n[b] + 1:] == -1)
+        np.testing.assert_array_equal(gv["offsets"], np.concatenate([[0], np.cumsum(n + 1)]))
+        assert cv.ineligible_rate < 0.2
 
 
 # ---------------------------------------------------------------- edge cases

@@ -176,7 +176,7 @@ def test_rnn_round_large_batch_config(d):
                              dev["temperature"], cfg.seed, 0, diag=True, resid=True)
     torch.cuda.synchronize()
     assert ds.dspark_verify_check(v["workspace"]) == 0
-    rows = np.array([0, 3, 10, 64, 130, 255])
+    rows = np.arange(cfg.B)
     U, anchor, temp = rnd.U[rows], rnd.anchor[rows], rnd.temperature[rows]
     od = oracle.draft_rnn(U, rnd.W1, rnd.W2, Wg, h[rows], anchor, temp, cfg.seed, 0, req_ids=rows.astype(np.int32))
     sub = packed_subset(target, ell, rows)
@@ -214,8 +214,8 @@ def test_rnn_round_large_batch_config(d):
     lim = PROB_TOL + relx[:, :, None] * np.abs(do) * np.array([0.0, 1.0])
     assert np.all(np.abs(dg - do)[tested] <= lim[tested])
     assert np.all(np.abs(gv["resid"][el] - ov["resid"][el]) <= PROB_TOL + 2 * rel[el].max(initial=0.0))
-    _say(f"[rnn-large] verify: {el.sum()}/{len(rows)} eligible, n {gv['n'].tolist()} vs {ov['n'].tolist()}")
-    assert el.sum() >= 4
+    _say(f"[rnn-large] verify: {el.sum()}/{len(rows)} eligible, n differs on {int((gv['n'] != ov['n']).sum())}")
+    assert el.sum() >= len(rows) // 2
 
 
 def test_rnn_verify_with_embedding_rows_is_the_markov_verify():
