@@ -133,6 +133,10 @@ hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const in
 // ---- verify ----------------------------------------------------------
 
 struct VerifyPlan {
+    bool walk;                      // a workgroup a request walks its rows (else the position passes)
+    int nseg_first, seg_len_first;  // passes: segments of a target row in the first pass, entries each
+    int nseg, seg_len;              // the same for the later passes (entries a multiple of 4)
+    int nseg_max;                   // partials kept per request (at most 64 / rows a pass)
     int nbb;          // ceil(B / 32)
     DraftPlan tile;   // vocabulary walk of the resample / bonus draw
     int draw_nw;      // waves per workgroup of the draw
@@ -145,6 +149,12 @@ struct VerifyWork {
     int32_t *status;     // [4] word 0: OR of the requests' input flags
     int32_t *req_flags;  // [B] the status flags each request's inputs raise
     int32_t *off;        // [B + 1] packed row offsets in use
+    // position passes only, double buffered by pass parity (pass p reads the
+    // half pass p - 1 wrote), one slot per row a pass reduces
+    int32_t *act;        // [2, B] 1: the request's rows of that pass were reduced
+    float *seg_m, *seg_s, *seg_v;  // [2, rows, B, nseg] per-segment max, sum of 2^(z - max), best value
+    int32_t *seg_i;      // [2, rows, B, nseg] per-segment lowest-index argmax
+    float *seg_tx;       // [2, rows, B] t(x_j) / T in log2 units for the accept test
     float *fin_lse2;     // [B] logsumexp (log2 units) of the row the draw uses
     int32_t *prev;       // [B] x_{j-1} of a residual draw at position j (the anchor for j = 1)
     float *lse2q;        // [B] log2-unit logsumexp of q_j for a residual draw

@@ -57,7 +57,7 @@ constexpr int kStatusRowsOutOfRange = 4;
 constexpr int kModeDone = 0;
 constexpr int kModeResidual = 1;
 constexpr int kModeBonus = 2;
-constexpr int kPrepInWalkMaxBatch = 512;
+constexpr int kPrepInKernelMaxBatch = 512;
 
 // v of the first active lane, as a scalar
 __device__ __forceinline__ float uniform_f(float v) {
@@ -194,6 +194,10 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
 // the block, 6 us on the first row).  Each lane keeps two batches of 16 float4
 // groups.
 constexpr int kWalkThreads = 256;
+// batches from this size on are walked a workgroup a request (at 256 the walk
+// and the position passes took the same time; at 64 and 32 requests, which
+// leave most CUs idle, the passes were 1.7 and 2.3 times faster)
+constexpr int kWalkMinBatch = 192;
 constexpr int kWalkGroups = 16;
 // third word of a raw buffer descriptor (dword data, no swizzle) on gfx9-family chips
 constexpr int kBufferWord3 = 0x00020000;
@@ -598,6 +602,353 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
             p.prev[b] = p.erow_mode ? b * p.gamma + r_j - 1
                                     : min(max(r_j == 1 ? p.anchor[b] : s_x[r_j - 2], 0), p.V - 1);
             p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + r_j - 1] * kLog2e;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ position passes (small batches)
+
+// Rows a position pass reduces: one or two consecutive positions of the
+// requests still testing; the pass first decides the positions the previous
+// pass reduced.  A request that rejects at the first of a pair has the second
+// row read for nothing, against one launch less.  Few requests are still
+// testing late in the block, so there the launch costs more than the row:
+// the first kSinglePasses positions get a pass each, the rest go in pairs
+// (an odd one left first on its own), then one pass decides the last rows.
+// A batch whose rows at one position take at most kPairAllBytes pairs from
+// the first position on: a launch costs about 7 us, about 45 MB of reads,
+// against at most B V 4 bytes read for nothing a pair.
+constexpr int kPassRows = 2;  // row slots a pass can hold
+constexpr int kSinglePasses = 3;
+constexpr size_t kPairAllBytes = size_t(64) << 20;
+// segments of a row in the first position pass and in the later ones
+// (measured at the headline size: 8 first-pass segments take 1 us less than
+// 4; 16 or 64 later segments take 1-2 us a pass more than 32)
+constexpr int kSegFirst = 8, kSegLater = 32;
+static_assert(kSegFirst <= 64 / kPassRows && kSegLater <= 64 / kPassRows,
+              "the next pass merges a row's segment statistics in 64 / kPassRows lanes");
+
+struct PassParams {
+    const float *target;
+    const int32_t *x, *ell;
+    const float *qx, *temperature;
+    int B, gamma, V, j0, vec;  // j0: first position this pass reduces
+    int nseg, seg_len;  // this pass's segments of a row
+    int nseg_in;        // the previous pass's
+    int seg_stride;     // partials per request in the buffers
+    size_t row_stride;  // partials per row slot of a pass (B * seg_stride)
+    uint32_t key0, key1, round32;
+    int32_t *off;
+    // prep != 0 (first pass of a small batch): the pass also checks each
+    // request's inputs, computes its row offset and writes the output defaults
+    int prep, n_target_rows;
+    const int32_t *row_offsets;
+    int32_t *req_flags;
+    float *resid_out;
+    // pass p reads what pass p - 1 left and writes into the other half of
+    // each double buffer; slot q holds the pass's q-th row
+    const int32_t *act_in;  // [B] 1: the request's rows of the previous pass were reduced
+    const float *pm_in, *ps_in, *pv_in, *tx_in;
+    const int32_t *pi_in;
+    int32_t *act_out;
+    float *pm_out, *ps_out, *pv_out, *tx_out;
+    int32_t *pi_out;
+    int32_t *mode, *jpos, *prev;
+    float *fin_lse2, *lse2q;
+    int erow_mode;  // 1: the residual's head row is row b * gamma + k - 1 of W1 (the head's rows)
+    const int32_t *anchor;
+    const float *lse_q;
+    int32_t *n_accept_out, *tokens_out;
+    float *diag_out;
+};
+
+// Position k = j - 1 of request b, from its merged row statistics: the accept
+// test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
+// request takes the same decision; only `writer` stores it.  Returns whether
+// the request goes on to position j.
+// xk, qk: x_k and q_k(x_k) (any value when k > ell).
+__device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampled, float lse2, int amax, float tx2,
+                            int xk, float qk, bool writer) {
+    int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
+    bool bonus = false;
+    if (k <= L) {
+        bool acc;
+        float pk, ratio;
+        if (sampled) {
+            pk = fast_exp2(tx2 - lse2);
+            const float u = uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
+            acc = u * qk < pk;
+            ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
+        } else {
+            acc = (xk == amax);
+            pk = acc ? 1.f : 0.f;
+            ratio = pk;
+        }
+        if (writer && p.diag_out) {
+            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = pk;
+            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = ratio;
+        }
+        if (acc) {
+            if (writer) tok[k - 1] = xk;
+            return true;
+        }
+        if (writer) p.n_accept_out[b] = k - 1;
+    } else {
+        if (writer) p.n_accept_out[b] = L;
+        bonus = true;
+    }
+    if (!writer) return false;
+    p.jpos[b] = k;
+    if (!sampled) {
+        tok[k - 1] = amax;
+        p.mode[b] = kModeDone;
+        return false;
+    }
+    p.fin_lse2[b] = lse2;
+    if (bonus) {
+        p.mode[b] = kModeBonus;
+    } else {
+        p.mode[b] = kModeResidual;
+        // what the residual draw needs to rebuild q_k
+        p.prev[b] = p.erow_mode ? b * p.gamma + k - 1
+                                : min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
+        p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + k - 1] * kLog2e;
+    }
+    return false;
+}
+
+// Pass p, one wave per (request, row slot q < DOUT, vocabulary segment),
+// four requests to a workgroup.  First the request's DIN previous positions are
+// decided, in order, from the segment statistics pass p - 1 wrote; a request
+// that goes on streams segment sg of its row j0 + q: every lane keeps its own
+// running max / sum of exp2 and argmax over batches of eight float4 loads
+// (PIPE: two batches, one in flight while the other is reduced, for the long
+// segments of the first pass), and the wave merges them.  The waves never
+// wait for one another.
+template <bool PIPE, int DIN, int DOUT>
+__global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
+    static_assert(DIN >= 1 && DIN <= kPassRows && DOUT >= 1 && DOUT <= kPassRows,
+                  "row slots: the previous pass's (DIN) and this pass's (DOUT)");
+    constexpr int LPS = 64 / DIN;  // lanes holding one previous row slot's segment statistics
+    constexpr int LOG_LPS = DIN == 1 ? 6 : 5;
+    const int sg = blockIdx.x % p.nseg;
+    const int q = (blockIdx.x / p.nseg) % DOUT;
+    const int b = (blockIdx.x / (p.nseg * DOUT)) * 4 + (threadIdx.x >> 6);
+    const int j0 = p.j0, j = j0 + q;
+    const int lane = threadIdx.x & 63;
+    if (b >= p.B) return;
+    const bool writer = sg == 0 && q == 0;
+    int mode, offb, act, L;
+    float T;
+    float mm = kNegInf, s2 = 0.f, v2 = kNegInf;
+    int i2 = 0x7fffffff;
+    float tx2[DIN], qk[DIN];
+    int xk[DIN];
+    if constexpr (PIPE) {
+        // the first pass decides nothing: it needs the request's temperature
+        // and length and, for a small batch, does its input checks (the row
+        // offset is a wave sum over ell, read in the same round)
+        T = p.temperature[b];
+        L = p.ell[b];
+        act = 1;
+        if (p.prep) {  // uniform
+            int part = 0;
+            if (!p.row_offsets)
+                for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
+            const int o_cmp = wave_isum(part);
+            const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
+            mode = f == 0 ? kModeDone : -1;
+            if (writer) {
+                if (lane == 0) {
+                    p.off[b] = offb;
+                    p.mode[b] = mode;
+                    p.req_flags[b] = f;
+                    if (b == p.B - 1)
+                        p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L, 0), p.gamma);
+                }
+                output_defaults(b, p.gamma, lane, 64, p.n_accept_out, p.tokens_out, p.diag_out, p.resid_out);
+            }
+        } else {
+            mode = p.mode[b];
+            offb = p.off[b];
+        }
+    } else {
+        // every load the decisions need, issued together and unconditionally
+        // (clamped indices; what a case does not use is masked after): lane
+        // group h (of LPS lanes) holds the segment statistics of the previous
+        // pass's row slot h, read whatever the request's state
+        const int hq = min(lane / LPS, DIN - 1), c = min(lane % LPS, p.nseg_in - 1);
+        const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
+        mode = p.mode[b];
+        offb = p.off[b];
+        act = p.act_in[b];
+        T = p.temperature[b];
+        L = p.ell[b];
+        mm = p.pm_in[o_in];
+        s2 = p.ps_in[o_in];
+        v2 = p.pv_in[o_in];
+        i2 = p.pi_in[o_in];
+#pragma unroll
+        for (int u = 0; u < DIN; ++u) {
+            const int k = min(max(j0 - DIN + u, 1), p.gamma);  // position decided from slot u (clamped)
+            tx2[u] = p.tx_in[size_t(u) * p.B + b];
+            xk[u] = p.x[size_t(b) * p.gamma + k - 1];
+            qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::"v"(mode), "v"(offb), "v"(act), "v"(T), "v"(L), "v"(mm), "v"(s2), "v"(v2), "v"(i2));
+        if (!((lane / LPS) < DIN && (lane % LPS) < p.nseg_in)) {
+            mm = kNegInf;
+            s2 = 0.f;
+            v2 = kNegInf;
+            i2 = 0x7fffffff;
+        }
+    }
+    if (mode < 0 || act == 0) {
+        if (writer && lane == 0) p.act_out[b] = 0;
+        return;
+    }
+    const bool sampled = T > 0.f;
+    const float sc = sampled ? kLog2e / T : 1.0f;
+    if (!PIPE && j0 > 1) {
+        bfly_steps<0, LOG_LPS>([&](auto st) {  // within each lane group
+            constexpr int S = decltype(st)::value;
+            const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
+            const int i_o = bfly<S>(i2);
+            lse_merge(mm, s2, m_o, s_o);
+            argmax_merge(v2, i2, v_o, i_o);
+        });
+        float lse2[DIN];
+        int amax[DIN];
+#pragma unroll
+        for (int u = 0; u < DIN; ++u) {
+            const float mu = __shfl(mm, LPS * u), su = __shfl(s2, LPS * u);
+            lse2[u] = (mu == kNegInf) ? kNegInf : mu + fast_log2(su);
+            amax[u] = min(max(__shfl(i2, LPS * u), 0), p.V - 1);
+        }
+        int go_on = 0;
+        if (lane == 0) {
+            go_on = 1;
+#pragma unroll
+            for (int u = 0; u < DIN; ++u) {
+                const int k = j0 - DIN + u;
+                if (!go_on || k > L + 1) break;
+                go_on = pass_decide(p, b, L, k, sampled, lse2[u], amax[u], tx2[u], xk[u], qk[u], writer);
+            }
+        }
+        if (!__shfl(go_on, 0)) {
+            if (writer && lane == 0) p.act_out[b] = 0;
+            return;
+        }
+    }
+    if (j > L + 1) {  // no row at this slot (slot 0 always has one once the request goes on)
+        if (writer && lane == 0) p.act_out[b] = 0;
+        return;
+    }
+    const float *trow = p.target + size_t(offb + j - 1) * p.V;
+    const int v_lo = sg * p.seg_len, v_hi = min(p.V, v_lo + p.seg_len);
+    float m = kNegInf, s = 0.f, av = kNegInf;
+    int ai = 0x7fffffff;
+    if (p.vec) {
+        if constexpr (PIPE) {
+            // two batches of U float4 a lane, one in flight while the other is
+            // reduced
+            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
+            const int q_hi = v_hi >> 2;
+            constexpr int U = 8;
+            // loads past the segment re-read its last group and are masked when used
+            auto load = [&](float4(&xs)[U], int qb) __device__ {
+    #pragma unroll
+                for (int u = 0; u < U; ++u) xs[u] = load_stream(r4 + min(qb + lane + 64 * u, q_hi - 1));
+            };
+            // sampled rows keep no argmax (only greedy decisions use it); the
+            // request, and so the branch, is uniform across the wave
+            auto consume = [&](float4(&xs)[U], int qb) __device__ {
+                auto valid = [&](int u) { return qb + lane + 64 * u < q_hi; };
+                if (sampled)
+                    row_batch<false, U, 256>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
+                else
+                    row_batch<true, U, 256>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
+            };
+            // The loop body is straight-line, so that every consume sees the
+            // same loads in flight on every path into it; it runs while the
+            // batch after the pair exists, and the last one or two batches
+            // follow it.  The batch bounds are uniform across the wave.
+            constexpr int NB = 64 * U;  // float4 groups a batch
+            const int qs = v_lo >> 2;
+            float4 xa[U], xb[U];
+            load(xa, qs);
+            int qb = qs;
+            for (; qb + 2 * NB < q_hi; qb += 2 * NB) {
+                load(xb, qb + NB);
+                consume(xa, qb);
+                load(xa, qb + 2 * NB);
+                consume(xb, qb + NB);
+            }
+            if (qb + NB < q_hi) {
+                load(xb, qb + NB);
+                consume(xa, qb);
+                consume(xb, qb + NB);
+            } else {
+                consume(xa, qb);
+            }
+        } else {
+            // one batch of U float4 a lane at a time: fewer registers, twice
+            // the waves a SIMD for the short segments of the later passes
+            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
+            const int q_hi = v_hi >> 2;
+            constexpr int U = 8;
+            // one loop for each kind of row (the request, and so the kind, is
+            // uniform across the wave): each keeps only its own registers
+            auto walk = [&](auto argmax) __device__ {
+                constexpr bool AM = decltype(argmax)::value;
+                for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
+                    float4 xs[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int q = q0 + 64 * u;
+                        xs[u] = q < q_hi ? load_stream(r4 + q) : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+                    }
+                    row_batch<AM, U, 256>(xs, 4 * q0, [](int) { return true; }, sc, m, s, av, ai);  // masked at the load
+                }
+            };
+            if (sampled)
+                walk(std::integral_constant<bool, false>{});
+            else
+                walk(std::integral_constant<bool, true>{});
+        }
+    } else {
+        for (int v = v_lo + lane; v < v_hi; v += 64) {
+            const float xv = trow[v] * sc;
+            const float mn = fmaxf(m, xv);
+            if (mn != kNegInf) {
+                s = s * fast_exp2(m - mn) + fast_exp2(xv - mn);
+                m = mn;
+            }
+            if (xv > av) {
+                av = xv;
+                ai = v;
+            }
+        }
+    }
+    bfly_steps<0, 6>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float m_o = bfly<S>(m), s_o = bfly<S>(s), v_o = bfly<S>(av);
+        const int i_o = bfly<S>(ai);
+        lse_merge(m, s, m_o, s_o);
+        argmax_merge(av, ai, v_o, i_o);
+    });
+    if (lane == 0) {
+        const size_t o = q * p.row_stride + size_t(b) * p.seg_stride + sg;
+        p.pm_out[o] = m;
+        p.ps_out[o] = s;
+        p.pv_out[o] = av;
+        p.pi_out[o] = ai;
+        if (writer) p.act_out[b] = 1;
+        // t(x_j) for the accept test at j, from the segment that holds x_j
+        if (sampled && j <= L) {
+            const int xj = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
+            if (xj >= v_lo && xj < v_hi) p.tx_out[size_t(q) * p.B + b] = trow[xj] * sc;
         }
     }
 }
@@ -1009,14 +1360,30 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     }
 }
 
+// The position passes of a block of gamma: first row and row count of each
+// (`single` single rows, then pairs, an odd row left over first), then
+// the decide-only pass (rows 0 at j0 = gamma + 2).
+struct PassRows {
+    int j0, rows;
+};
+int pass_schedule(int gamma, int single, PassRows *out) {
+    int n = 0, j = 1;
+    const int last = gamma + 1;
+    for (; j <= last && j <= single; ++j) out[n++] = {j, 1};
+    if ((last - j + 1) % 2 == 1 && j <= last) out[n++] = {j++, 1};
+    for (; j <= last; j += 2) out[n++] = {j, 2};
+    out[n++] = {last + 1, 0};
+    return n;
+}
+
 template <typename WT, int R>
 hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyWork &w, hipStream_t s) {
     hipError_t e;
     // a small batch has its input checks and output defaults done by the
     // walk (each workgroup forms its request's row offset from ell, O(B)
     // reads); a large one by a workgroup of its own
-    const bool prep_in_walk = a.B <= kPrepInWalkMaxBatch;
-    if (!prep_in_walk) {
+    const bool prep_in_kernel = a.B <= kPrepInKernelMaxBatch;
+    if (!prep_in_kernel) {
         PrepParams pp{a.ell, a.row_offsets, a.B, a.gamma, a.n_target_rows, w.off,
                       w.mode, w.req_flags, a.n_accept_out, a.tokens_out, a.diag_out, a.resid_out};
         launch_kernel("verify_prep", verify_prep_kernel, dim3(1), dim3(1024), s, pp);
@@ -1024,7 +1391,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
-    {
+    if (pl.walk) {
         WalkParams wp{};
         wp.target = a.target;
         wp.x = a.x;
@@ -1039,7 +1406,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         wp.key1 = a.key1;
         wp.round32 = a.round32;
         wp.off = w.off;
-        wp.prep = prep_in_walk ? 1 : 0;
+        wp.prep = prep_in_kernel ? 1 : 0;
         wp.n_target_rows = a.n_target_rows;
         wp.row_offsets = a.row_offsets;
         wp.req_flags = w.req_flags;
@@ -1057,6 +1424,85 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         wp.diag_out = a.diag_out;
         launch_kernel("verify_walk", verify_walk_kernel, dim3(a.B), dim3(kWalkThreads), s, wp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        PassRows sched[DSPARK_MAX_GAMMA + 2];  // gamma is checked at the boundary
+        const int single = size_t(a.B) * a.V * sizeof(float) <= kPairAllBytes ? 0 : kSinglePasses;
+        const int npass = pass_schedule(a.gamma, single, sched);
+        for (int pass = 1; pass <= npass; ++pass) {
+            const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
+            const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
+            const size_t half = rs * kPassRows;
+            const PassRows cur = sched[pass - 1];
+            const int din = pass > 1 ? sched[pass - 2].rows : 1;  // rows this pass decides
+            const int dout = cur.rows > 0 ? cur.rows : 1;         // row slots of its grid
+            // the last pass only decides: one wave a request
+            const int nseg = pass == 1 ? pl.nseg_first : (cur.rows == 0 ? 1 : pl.nseg);
+            PassParams pp{};
+            pp.target = a.target;
+            pp.x = a.x;
+            pp.ell = a.ell;
+            pp.qx = a.qx;
+            pp.temperature = a.temperature;
+            pp.B = a.B;
+            pp.gamma = a.gamma;
+            pp.V = a.V;
+            pp.j0 = cur.j0;
+            pp.vec = vec_t;
+            pp.nseg = nseg;
+            pp.seg_len = pass == 1 ? pl.seg_len_first : pl.seg_len;
+            pp.nseg_in = pass == 2 ? pl.nseg_first : pl.nseg;
+            pp.seg_stride = pl.nseg_max;
+            pp.row_stride = rs;
+            pp.key0 = a.key0;
+            pp.key1 = a.key1;
+            pp.round32 = a.round32;
+            pp.off = w.off;
+            pp.prep = (pass == 1 && prep_in_kernel) ? 1 : 0;
+            pp.n_target_rows = a.n_target_rows;
+            pp.row_offsets = a.row_offsets;
+            pp.req_flags = w.req_flags;
+            pp.resid_out = a.resid_out;
+            pp.act_in = w.act + size_t(in) * a.B;
+            pp.pm_in = w.seg_m + in * half;
+            pp.ps_in = w.seg_s + in * half;
+            pp.pv_in = w.seg_v + in * half;
+            pp.pi_in = w.seg_i + in * half;
+            pp.tx_in = w.seg_tx + size_t(in) * kPassRows * a.B;
+            pp.act_out = w.act + size_t(out) * a.B;
+            pp.pm_out = w.seg_m + out * half;
+            pp.ps_out = w.seg_s + out * half;
+            pp.pv_out = w.seg_v + out * half;
+            pp.pi_out = w.seg_i + out * half;
+            pp.tx_out = w.seg_tx + size_t(out) * kPassRows * a.B;
+            pp.mode = w.mode;
+            pp.jpos = w.jpos;
+            pp.fin_lse2 = w.fin_lse2;
+            pp.prev = w.prev;
+            pp.erow_mode = a.erow_mode;
+            pp.lse2q = w.lse2q;
+            pp.anchor = a.anchor;
+            pp.lse_q = a.lse_q;
+            pp.n_accept_out = a.n_accept_out;
+            pp.tokens_out = a.tokens_out;
+            pp.diag_out = a.diag_out;
+            static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
+                                                "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
+            const dim3 grid(size_t((a.B + 3) / 4) * nseg * dout);
+            const char *name = names[std::min(pass, 8) - 1];
+            if (pass == 1 && dout == 1)
+                launch_kernel(name, (verify_pass_kernel<true, 1, 1>), grid, dim3(256), s, pp);
+            else if (pass == 1)
+                launch_kernel(name, (verify_pass_kernel<true, 1, 2>), grid, dim3(256), s, pp);
+            else if (din == 1 && dout == 1)
+                launch_kernel(name, (verify_pass_kernel<false, 1, 1>), grid, dim3(256), s, pp);
+            else if (din == 1)
+                launch_kernel(name, (verify_pass_kernel<false, 1, 2>), grid, dim3(256), s, pp);
+            else if (dout == 1)
+                launch_kernel(name, (verify_pass_kernel<false, 2, 1>), grid, dim3(256), s, pp);
+            else
+                launch_kernel(name, (verify_pass_kernel<false, 2, 2>), grid, dim3(256), s, pp);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     {
         DrawParams dp{};
@@ -1145,6 +1591,21 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
 VerifyPlan verify_plan(int B, int gamma, int V) {
     (void)gamma;
     VerifyPlan p{};
+    // a workgroup a request (the walk) once the batch fills most of the chip;
+    // smaller batches spread each row over many waves (the position passes)
+    p.walk = B >= kWalkMinBatch;
+    // Position passes split a row into segments of whole float4 groups: the
+    // first pass, which reads every request's row, in a few long ones (long
+    // streams per workgroup), the later ones, which read fewer and fewer rows,
+    // in up to kSegLater short ones (more waves per row).
+    const int n4 = (V + 3) / 4;
+    auto split = [&](int k, int &nseg, int &len) {
+        len = 4 * ((n4 + k - 1) / k);
+        nseg = (V + len - 1) / len;
+    };
+    split(kSegFirst, p.nseg_first, p.seg_len_first);
+    split(kSegLater, p.nseg, p.seg_len);
+    p.nseg_max = std::max(p.nseg_first, p.nseg);
     p.nbb = (B + 31) / 32;
     // 8-wave workgroups holding two one-tile stages of W2 rows and wave
     // regions (160 KB of LDS at bf16 rank 256): one a CU, so about 256 of them
@@ -1166,6 +1627,15 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     w.status = c.take<int32_t>(4);  // first: dspark_verify_check reads word 0
     w.req_flags = c.take<int32_t>(B);
     w.off = c.take<int32_t>(size_t(B) + 1);
+    if (!p.walk) {  // the position passes' double-buffered segment statistics
+        w.act = c.take<int32_t>(size_t(2) * B);
+        const size_t ns = size_t(2) * kPassRows * B * p.nseg_max;
+        w.seg_m = c.take<float>(ns);
+        w.seg_s = c.take<float>(ns);
+        w.seg_v = c.take<float>(ns);
+        w.seg_i = c.take<int32_t>(ns);
+        w.seg_tx = c.take<float>(size_t(2) * kPassRows * B);
+    }
     w.fin_lse2 = c.take<float>(B);
     w.prev = c.take<int32_t>(B);
     w.lse2q = c.take<float>(B);
