@@ -1,8 +1,8 @@
 """Build libdspark.so (HIP for gfx950) in-tree.
 
-Every translation unit is compiled by hipcc for gfx950 only, with packed-FP32
-instruction selection switched off, then linked into one shared library next
-to this file.  Run as a script or call ``build()``.
+Every translation unit is compiled by hipcc for gfx950 only, warnings
+(shadowed names included) as errors and packed-FP32 instruction selection
+switched off, then linked into one shared library next to this file.  Run as a script or call ``build()``.
 """
 import os
 import subprocess
@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "schedule.cpp", "draft.hip", "verify.hip", "accept.hip", "rnn.hip", "sts.hip", "debug.hip"]
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wshadow", "-Werror",
     "-Wno-unused-parameter", "-Wno-cuda-compat",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void sts_clear_kernel(StsParams p) {
         p.acc_p[i] = 0ull;
         p.acc_y[i] = 0u;
     }
-    if (blockIdx.x == 0 && threadIdx.x < p.gamma) p.acc_n[threadIdx.x] = 0u;
+    if (blockIdx.x == 0 && int(threadIdx.x) < p.gamma) p.acc_n[threadIdx.x] = 0u;
 }
 
 __global__ __launch_bounds__(kStsThreads) void sts_hist_kernel(StsParams p) {

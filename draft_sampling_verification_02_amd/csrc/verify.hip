@@ -362,10 +362,10 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         // for a small batch), its drafts, q(x) and accept thresholds u q
         int offb, md;
         if (p.prep) {
-            int part = 0;
+            int rows_before = 0;
             if (!p.row_offsets)
-                for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
-            const int o_cmp = wave_isum(part);
+                for (int i = lane; i < b; i += 64) rows_before += 1 + min(max(p.ell[i], 0), p.gamma);
+            const int o_cmp = wave_isum(rows_before);
             const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
             md = f == 0 ? kModeDone : -1;
             if (lane == 0) {
@@ -752,10 +752,10 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
         L = p.ell[b];
         act = 1;
         if (p.prep) {  // uniform
-            int part = 0;
+            int rows_before = 0;
             if (!p.row_offsets)
-                for (int i = lane; i < b; i += 64) part += 1 + min(max(p.ell[i], 0), p.gamma);
-            const int o_cmp = wave_isum(part);
+                for (int i = lane; i < b; i += 64) rows_before += 1 + min(max(p.ell[i], 0), p.gamma);
+            const int o_cmp = wave_isum(rows_before);
             const int f = check_request(p.ell, p.row_offsets, b, p.gamma, p.n_target_rows, o_cmp, &offb);
             mode = f == 0 ? kModeDone : -1;
             if (writer) {
@@ -1038,7 +1038,7 @@ constexpr int kDrawSmallWaves = 2;
 // noise from stream 4.  The two halves of a wave hold the two halves of the
 // tile and combine their sums with one lane-half exchange.
 template <typename WT, int R, bool VEC, int NWV>
-__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void verify_draw_kernel(
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV >= 4 ? 2 : 1, 2))) void verify_draw_kernel(
     DrawParams p) {
     using L = TileLDS<WT, R>;
     using TR = TileRows<VEC>;

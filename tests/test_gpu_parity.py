@@ -483,6 +483,7 @@ def test_q_equals_p_accepts_all_on_gpu():
     (256, 98309, 256, "bf16"),         # seven stages a chunk, a shorter last chunk with a tail
     (64, 40000, 128, "f32"),           # f32 factors through the same stage ring
     (256, 129280, 256, "bf16"),        # the large-batch round's shape
+    (270, 9001, 256, "bf16"),          # nine request blocks: a second workgroup with one block
 ])
 def test_bias_gemm_rowmax_matches_fp64(B, V, r, wdtype):
     """The matrix-unit tiling of the draft step on its own: rowmax[b] =
