@@ -536,6 +536,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg (and the parity gate)")
     ap.add_argument("--no-configs", action="store_true", help="skip the other configurations")
     ap.add_argument("--rounds", type=int, default=60, help="rounds timed one by one for the round-time distribution")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary measurements (bias product, cold step, heads, scheduler, calibration)")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="only time the bias product alone (warm and cold) and print its JSON (for counter runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte device buffer 5 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -575,6 +579,9 @@ def main():
     td = torch.from_numpy(target).cuda()
     ed = torch.from_numpy(ell).cuda()
     seed = cfg.seed
+    if args.gemm_only:
+        print(json.dumps({"bias_gemm_alone": _bias_gemm_alone(torch, ds, dev, B, V, r)}), flush=True)
+        return
 
     # round 0, compared with the oracle below
     d = ds.dspark_draft_sample(dev["U"], dev["W1"], dev["W2"], dev["anchor"], dev["temperature"], seed, 0,
@@ -630,14 +637,16 @@ def main():
                          dev["temperature"], seed, rid, out=v)
 
     # secondary GPU measurements (before the timed region)
-    gemm = _bias_gemm_alone(torch, ds, dev, B, V, r)
-    cold = _draft_step_cold(torch, ds, dev, B, gamma, V, r, seed)
-    sched = _schedule_time(ds, S)
-    conf = _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, 30)
-    accept = _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, 20)
-    rnn = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, 30, S.DEFAULT_HIDDEN)
-    rnn_wide = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, 30, 4 * S.DEFAULT_HIDDEN)
-    sts = _sts_fit(torch, ds, S)
+    gemm = cold = sched = conf = accept = rnn = rnn_wide = sts = None
+    if not args.no_secondary:
+        gemm = _bias_gemm_alone(torch, ds, dev, B, V, r)
+        cold = _draft_step_cold(torch, ds, dev, B, gamma, V, r, seed)
+        sched = _schedule_time(ds, S)
+        conf = _confidence_head(torch, ds, S, cfg, dev, td, ed, seed, 30)
+        accept = _acceptance(torch, ds, dev, td, ed, d, rnd, B, gamma, V, r, 20)
+        rnn = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, 30, S.DEFAULT_HIDDEN)
+        rnn_wide = _rnn_head(torch, ds, S, cfg, dev, td, ed, seed, 30, 4 * S.DEFAULT_HIDDEN)
+        sts = _sts_fit(torch, ds, S)
 
     # single-round times (also the rounds that lead into the timed region,
     # after the heavier secondary work)
@@ -682,7 +691,7 @@ def main():
     roofline = {"kernel": "draft_step", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": bytes_per_launch,
-                "frac_inputs_evicted": cold["step"]["frac"],
+                "frac_inputs_evicted": cold["step"]["frac"] if cold else None,
                 "mfma_bf16_tflops": round(flops_per_launch / ds_avg_s / 1e12, 1),
                 "mfma_frac": round(flops_per_launch / ds_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                 "kernel_source_hash": _kernel_hash()}
