@@ -32,6 +32,9 @@ struct Pending {
 struct Profiler {
     std::mutex mu;
     bool enabled = false;
+    // read without the lock on every launch: with profiling off a launch
+    // takes no lock
+    std::atomic<bool> on{false};
     std::vector<ProfEntry> entries;
     std::vector<Pending> pending;
     std::vector<hipEvent_t> pool;
@@ -63,6 +66,7 @@ Profiler &prof() {
 
 ProfEvents prof_events(const char *name) {
     Profiler &p = prof();
+    if (!p.on.load(std::memory_order_acquire)) return {};
     std::lock_guard<std::mutex> g(p.mu);
     if (!p.enabled) return {};
     Pending pd{p.entry_for(name), p.take_event(), p.take_event()};
@@ -540,6 +544,7 @@ int dspark_profile_enable(int enable) {
     Profiler &p = prof();
     std::lock_guard<std::mutex> g(p.mu);
     p.enabled = enable != 0;
+    p.on.store(p.enabled, std::memory_order_release);
     return DSPARK_OK;
 }
 
