@@ -15,10 +15,17 @@
 //
 // Kernels, in launch order:
 //   verify_prep      1 workgroup, for batches above 512 requests (smaller
-//                    ones have the first pass do it): packed row offsets
-//                    (scan of 1 + ell, or the caller's, checked), output
-//                    defaults, pass state.
-//   verify_pass      one launch a position for the first few positions, one
+//                    ones have the walk or the first pass do it): packed row
+//                    offsets (scan of 1 + ell, or the caller's, checked),
+//                    output defaults, request state.
+//   verify_walk      batches of 192 requests or more: one workgroup a
+//                    request streams its rows in position order for
+//                    logsumexp(t / T) in base 2 and the lowest-index argmax,
+//                    decides each position right after its row (the accept
+//                    test u*q < p, or the bonus row) and stops at the first
+//                    rejection, so no row past it is used.
+//   verify_pass      smaller batches, instead of the walk: one launch a
+//                    position for the first few positions, one
 //                    a pair of positions after them (from the first one on
 //                    for a small batch), and a last one that only decides; each runs over the requests still
 //                    testing: one wave per (request, row, vocabulary
@@ -29,7 +36,9 @@
 //                    logsumexp(t / T) in base 2 and the lowest-index argmax.
 //                    A request stops at its first rejection, so rows past it
 //                    are never read (but the second row of a pair).
-//   verify_draw      level 1: waves of 32 listed requests walk vocabulary
+//   verify_draw      level 1: every workgroup lists the drawing requests
+//                    (residual draws first, bonus draws last, in request
+//                    order); waves of 32 listed requests walk vocabulary
 //                    chunks; residual rows recompute q_j with the draft's
 //                    LDS-staged MFMA bias tile and sum max(p_j - q_j, 0) per
 //                    tile, bonus rows take tile logsumexps of p; the tiles
