@@ -76,22 +76,24 @@ def _logit_passes(phases, outcome, B, V, r):
     """The verify's logit passes against the HBM peak: algorithmic bytes over
     the event-timed average launch, the bytes counted from the outcomes of the
     same timed rounds (averages per round).  The walk reads rows 1 .. n + 1 of
-    every request (the first rejection's row or the bonus row); the draw reads
-    the target and U_j rows of every residual draw, the target row of every
+    every request (the first rejection's row or the bonus row), timed with the
+    tail kernel that reads a batch's last rows when it has one (the tail's
+    rows past a rejection are read but not counted); the draw reads the
+    target and U_j rows of every residual draw, the target row of every
     bonus draw, and W2 once when any draw is a residual one."""
     row = V * 4
     out = {}
 
-    def put(name, nbytes, key):
-        us = phases.get(key, {}).get("avg_us", 0.0)
+    def put(name, nbytes, keys):
+        us = sum(phases.get(k, {}).get("avg_us", 0.0) for k in keys)
         if us > 0:
             gbs = nbytes / (us * 1e-6) / 1e9
             out[name] = {"bytes": int(nbytes), "us": round(us, 2), "gbs": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
-    put("verify_walk", outcome["rows"] * row, "verify_walk")
+    put("verify_walk", outcome["rows"] * row, ("verify_walk", "verify_tail"))
     put("verify_draw", (2 * outcome["residual"] + outcome["bonus"]) * row + (V * r * 2 if outcome["residual"] else 0),
-        "verify_draw")
+        ("verify_draw",))
     out["per_round"] = {k: round(v, 2) for k, v in outcome.items()}
     return out
 

@@ -134,6 +134,7 @@ hipError_t launch_bias_gemm(const void *W1, const void *W2, int wdtype, const in
 
 struct VerifyPlan {
     bool walk;                      // a workgroup a request walks its rows (else the position passes)
+    int tail_from;                  // walk: rows from this one on read by the tail kernel (0: none)
     int nseg_first, seg_len_first;  // passes: segments of a target row in the first pass, entries each
     int nseg, seg_len;              // the same for the later passes (entries a multiple of 4)
     int nseg_max;                   // partials kept per request (at most 64 / rows a pass)
@@ -155,6 +156,10 @@ struct VerifyWork {
     float *seg_m, *seg_s, *seg_v;  // [2, rows, B, nseg] per-segment max, sum of 2^(z - max), best value
     int32_t *seg_i;      // [2, rows, B, nseg] per-segment lowest-index argmax
     float *seg_tx;       // [2, rows, B] t(x_j) / T in log2 units for the accept test
+    // walk tail only: the requests it takes, its row statistics
+    int32_t *tail_flag, *tail_cnt;  // [B] 1: in the tail; rows reduced so far
+    float *tail_lse2, *tail_tx;     // [B, gamma + 2 - tail_from] row logsumexp, t(x_j) / T (log2 units)
+    int32_t *tail_amax;             // [B, gamma + 2 - tail_from] row argmax
     float *fin_lse2;     // [B] logsumexp (log2 units) of the row the draw uses
     int32_t *prev;       // [B] x_{j-1} of a residual draw at position j (the anchor for j = 1)
     float *lse2q;        // [B] log2-unit logsumexp of q_j for a residual draw

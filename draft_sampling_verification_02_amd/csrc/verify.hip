@@ -235,7 +235,24 @@ struct WalkParams {
     const float *lse_q;
     int32_t *n_accept_out, *tokens_out;
     float *diag_out;
+    // tail_from > 0: a request still accepting when row tail_from is next
+    // stops there (mode kModeTail, tail_flag 1) and the tail kernel reads
+    // rows tail_from .. ell + 1; tail_* hold [B, gamma + 2 - tail_from] row
+    // statistics and [B] counts of those rows reduced
+    int tail_from;
+    int32_t *tail_flag, *tail_cnt, *tail_amax;
+    float *tail_lse2, *tail_tx;
 };
+
+// The walk leaves a request to the tail kernel (an intermediate mode, never
+// seen by the draw)
+constexpr int kModeTail = 3;
+// rows from this one on are read by the tail kernel, for batches of at most
+// kTailMaxBatch requests (more leave few CUs idle late in the block) and
+// blocks of at least kTailMinGamma drafts
+constexpr int kTailFrom = 4;
+constexpr int kTailMaxBatch = 320;
+constexpr int kTailMinGamma = 4;
 
 // One batch of U float4 groups of a row into a thread's running base-2
 // logsumexp (m, s) of x * sc; group u holds entries v0 + STRIDE u .. + 3 and
@@ -353,10 +370,164 @@ __device__ __forceinline__ void walk_row_scalar(const float *trow, int V, float 
     }
 }
 
+// The workgroup's LDS for merging a row's statistics: a slot a wave, in two
+// sets that alternate by row parity (the next row's writes never meet this
+// row's reads).
+struct WalkMergeLds {
+    float m[2][kWalkWaves], s[2][kWalkWaves], v[2][kWalkWaves];
+    int i[2][kWalkWaves];
+};
+
+// Row `par`'s statistics, complete in the threads' running states (m, s, av,
+// ai), merged over the workgroup; the states are reset for the next row.
+// Every wave merges the same statistics in the same order, and the results,
+// the row's base-2 logsumexp lse2 and its lowest-index argmax amax, come out
+// as scalars: the decision that follows is uniform to the compiler as well
+// (scalar branches, exact load counts across the walk's loop).
+__device__ __forceinline__ void walk_merge_row(WalkMergeLds &l, int par, int V, float &m, float &s, float &av,
+                                               int &ai, float &lse2, int &amax) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bfly_steps<0, 6>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float m_o = bfly<S>(m), s_o = bfly<S>(s), v_o = bfly<S>(av);
+        const int i_o = bfly<S>(ai);
+        lse_merge(m, s, m_o, s_o);
+        argmax_merge(av, ai, v_o, i_o);
+    });
+    if (lane == 0) {
+        l.m[par][wave] = m;
+        l.s[par][wave] = s;
+        l.v[par][wave] = av;
+        l.i[par][wave] = ai;
+    }
+    __syncthreads();
+    float mm = kNegInf, ss = 0.f, vv = kNegInf;
+    int ii = 0x7fffffff;
+    if (lane < kWalkWaves) {
+        mm = l.m[par][lane];
+        ss = l.s[par][lane];
+        vv = l.v[par][lane];
+        ii = l.i[par][lane];
+    }
+    bfly_steps<0, 4>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        const float m_o = bfly<S>(mm), s_o = bfly<S>(ss), v_o = bfly<S>(vv);
+        const int i_o = bfly<S>(ii);
+        lse_merge(mm, ss, m_o, s_o);
+        argmax_merge(vv, ii, v_o, i_o);
+    });
+    mm = uniform_f(mm);
+    ss = uniform_f(ss);
+    ii = __builtin_amdgcn_readfirstlane(ii);
+    m = kNegInf;
+    s = 0.f;
+    av = kNegInf;
+    ai = 0x7fffffff;
+    lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(ss);
+    amax = min(max(ii, 0), V - 1);
+}
+
+// The test of draft position j from its target row's statistics ([CE] 05,
+// the accept rule): a sampled row accepts x_j when u q(x_j) < p(x_j), with
+// p(x_j) = 2^(txs - lse2) (txs = t(x_j) log2(e) / T) and thr = u q(x_j); a
+// greedy row accepts when x_j is the row's argmax.  pk and ratio get the
+// position's diagnostics p(x_j) and min(1, p / q).
+__device__ __forceinline__ bool position_test(bool sampled, float txs, float lse2, int amax, int xj, float qk,
+                                              float thr, float &pk, float &ratio) {
+    if (sampled) {
+        pk = fast_exp2(txs - lse2);
+        ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
+        return thr < pk;
+    }
+    const bool acc = xj == amax;
+    pk = acc ? 1.f : 0.f;
+    ratio = pk;
+    return acc;
+}
+
+// Streams a request's rows j_first, j_first + 1, ... (row j at
+// target + (offb + j - 1) V, V a multiple of 4, rows 16-byte aligned) into
+// the threads' running statistics and calls finish(j) once row j is complete
+// in them; the stream goes on to row j + 1 while finish returns true, and
+// finish must return false at j_last.
+//
+// One pipeline over the batches of consecutive rows: thread t takes float4
+// groups t, t + NT, ... of each batch of NT U groups (a fixed share, so the
+// sums are formed in the same order on every run).  Two batches are in
+// flight, so the first batch of row j + 1 goes out before position j is
+// decided (and is dropped when the stream stops there): the loads do not
+// drain at a row boundary.  A batch past j_last gets an empty buffer
+// descriptor: it is issued like the others (the counts of loads in flight are
+// the same on every path) but touches no memory.  The row and batch of each
+// buffer are tracked as scalar counters.
+template <class Finish>
+__device__ __forceinline__ void walk_stream_rows(const float *target, int offb, int V, int j_first, int j_last,
+                                                 bool sampled, float sc, float &m, float &s, float &av, int &ai,
+                                                 Finish &&finish) {
+    constexpr int U = kWalkGroups, NB = kWalkThreads * U;
+    const int tid = threadIdx.x;
+    const int n4 = V >> 2;
+    const int nbr = (n4 + NB - 1) / NB;  // batches a row
+    const int last_qb = (nbr - 1) * NB;  // first group of a row's last batch
+    // Buffer loads: the row is a scalar descriptor whose range check returns
+    // 0 past its end (masked when reduced), and a group's offset is the
+    // thread's fixed part plus a scalar one, so a batch needs no address
+    // registers of its own.
+    const int voff = tid * 16;
+    auto load = [&](float4(&xs)[U], int j, int qb) __device__ {
+        const bool any = j <= j_last;  // uniform
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(target + size_t(offb + (any ? j : j_first) - 1) * V), 0, any ? n4 * 16 : 0,
+            kBufferWord3);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const v4f_t x =
+                __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (qb + kWalkThreads * u) * 16, kStreamPolicy);
+            xs[u] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    };
+    auto consume = [&](float4(&xs)[U], int qb) __device__ {
+        if (qb + NB <= n4) {  // uniform: a full batch
+            if (sampled)
+                walk_batch<false, true, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), U, sc, m, s, av, ai);
+            else
+                walk_batch<true, true, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), U, sc, m, s, av, ai);
+        } else {
+            const int nv = (n4 - qb - tid + kWalkThreads - 1) / kWalkThreads;  // this thread's groups in the row
+            if (sampled)
+                walk_batch<false, false, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), nv, sc, m, s, av, ai);
+            else
+                walk_batch<true, false, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), nv, sc, m, s, av, ai);
+        }
+    };
+    // (row, first group) of the batch in each buffer
+    int ja = j_first, qa = 0, jb, qb;
+    auto advance = [&](int j, int q, int &jn, int &qn) {
+        if (q == last_qb) {
+            jn = j + 1;
+            qn = 0;
+        } else {
+            jn = j;
+            qn = q + NB;
+        }
+    };
+    float4 xa[U], xb[U];
+    load(xa, ja, qa);
+    for (;;) {
+        advance(ja, qa, jb, qb);
+        load(xb, jb, qb);
+        consume(xa, qa);
+        if (qa == last_qb && !finish(ja)) break;
+        advance(jb, qb, ja, qa);
+        load(xa, ja, qa);
+        consume(xb, qb);
+        if (qb == last_qb && !finish(jb)) break;
+    }
+}
+
 __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_walk_kernel(
     WalkParams p) {
-    __shared__ float s_m[2][kWalkWaves], s_s[2][kWalkWaves], s_v[2][kWalkWaves];
-    __shared__ int s_i[2][kWalkWaves];
+    __shared__ WalkMergeLds s_mg;
     __shared__ int s_x[DSPARK_MAX_GAMMA];
     __shared__ float s_q[DSPARK_MAX_GAMMA], s_thr[DSPARK_MAX_GAMMA];
     __shared__ float s_dp[DSPARK_MAX_GAMMA], s_dr[DSPARK_MAX_GAMMA];  // p_k(x_k), min(1, p/q) of tested positions
@@ -405,7 +576,10 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(s_mode) < 0) {  // failed its input checks: outputs keep their defaults
-        if (tid == 0) p.mode[b] = -1;
+        if (tid == 0) {
+            p.mode[b] = -1;
+            if (p.tail_from) p.tail_flag[b] = 0;
+        }
         return;
     }
     const int offb = __builtin_amdgcn_readfirstlane(s_off);
@@ -431,71 +605,31 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     int r_n = 0, r_j = 0, r_mode = kModeDone, r_tok = -1;
     float r_lse2 = 0.f;
     // Row j is complete in the threads' states: merge it over the workgroup
-    // and decide position j.  Returns whether the walk goes on to row j + 1.
+    // and decide position j.  Returns whether the walk goes on to row j + 1
+    // (with its t(x_j) load issued).
     auto finish_row = [&](int j) -> bool {
-        const int par = j & 1;
-        bfly_steps<0, 6>([&](auto st) {
-            constexpr int S = decltype(st)::value;
-            const float m_o = bfly<S>(m), s_o = bfly<S>(s), v_o = bfly<S>(av);
-            const int i_o = bfly<S>(ai);
-            lse_merge(m, s, m_o, s_o);
-            argmax_merge(av, ai, v_o, i_o);
-        });
-        if (lane == 0) {
-            s_m[par][wave] = m;
-            s_s[par][wave] = s;
-            s_v[par][wave] = av;
-            s_i[par][wave] = ai;
-        }
-        __syncthreads();
-        // every wave merges the same statistics in the same order and takes
-        // the same decision (buffers alternate by row, so the next row's
-        // writes never meet this row's reads)
-        float mm = kNegInf, ss = 0.f, vv = kNegInf;
-        int ii = 0x7fffffff;
-        if (lane < kWalkWaves) {
-            mm = s_m[par][lane];
-            ss = s_s[par][lane];
-            vv = s_v[par][lane];
-            ii = s_i[par][lane];
-        }
-        bfly_steps<0, 4>([&](auto st) {
-            constexpr int S = decltype(st)::value;
-            const float m_o = bfly<S>(mm), s_o = bfly<S>(ss), v_o = bfly<S>(vv);
-            const int i_o = bfly<S>(ii);
-            lse_merge(mm, ss, m_o, s_o);
-            argmax_merge(vv, ii, v_o, i_o);
-        });
-        // lane 0's merge as scalars: the decision and the walk's loop are
-        // then uniform to the compiler as well (scalar branches, exact load
-        // counts across the loop)
-        mm = uniform_f(mm);
-        ss = uniform_f(ss);
-        ii = __builtin_amdgcn_readfirstlane(ii);
-        m = kNegInf;  // the thread's state for the next row
-        s = 0.f;
-        av = kNegInf;
-        ai = 0x7fffffff;
-        const float lse2 = (mm == kNegInf) ? kNegInf : mm + fast_log2(ss);
-        const int amax = min(max(ii, 0), p.V - 1);
+        float lse2;
+        int amax;
+        walk_merge_row(s_mg, j & 1, p.V, m, s, av, ai, lse2, amax);
         if (j <= L) {
-            bool acc;
             float pk, ratio;
-            if (sampled) {
-                const float qk = uniform_f(s_q[j - 1]);
-                pk = fast_exp2(txs - lse2);
-                acc = uniform_f(s_thr[j - 1]) < pk;
-                ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
-            } else {
-                acc = (__builtin_amdgcn_readfirstlane(s_x[j - 1]) == amax);
-                pk = acc ? 1.f : 0.f;
-                ratio = pk;
-            }
+            const bool acc =
+                position_test(sampled, txs, lse2, amax, __builtin_amdgcn_readfirstlane(s_x[j - 1]),
+                              uniform_f(s_q[j - 1]), uniform_f(s_thr[j - 1]), pk, ratio);
             if (tid == 0) {
                 s_dp[j - 1] = pk;
                 s_dr[j - 1] = ratio;
             }
-            if (acc) return true;
+            if (acc) {
+                if (j + 1 != p.tail_from) {
+                    locate_x(j + 1);
+                    return true;
+                }
+                r_n = j;  // the later rows go to the tail kernel
+                r_j = j + 1;
+                r_mode = kModeTail;
+                return false;
+            }
             r_n = j - 1;  // first rejection at j: the residual draw (sampled) or the target's argmax (greedy)
             r_mode = sampled ? kModeResidual : kModeDone;
         } else {
@@ -515,102 +649,160 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
             else
                 walk_row_scalar<true>(row_of(j), p.V, sc, m, s, av, ai);
             if (!finish_row(j)) break;
-            locate_x(j + 1);
         }
     } else {
-        // One pipeline over the batches of consecutive rows: thread t takes
-        // float4 groups t, t + NT, ... of each batch of NT U groups (a fixed
-        // share, so the sums are formed in the same order on every run).  Two
-        // batches are in flight, so the first batch of row j + 1 goes out
-        // before position j is decided (and is dropped when the walk stops
-        // there): the loads do not drain at a row boundary.  A batch past the
-        // last row the walk may read gets an empty buffer descriptor: it is
-        // issued like the others (the counts of loads in flight are the same on
-        // every path) but touches no memory.  The row and batch of each buffer
-        // are tracked as scalar counters.
-        constexpr int U = kWalkGroups, NB = kWalkThreads * U;
-        const int n4 = p.V >> 2;
-        const int nbr = (n4 + NB - 1) / NB;  // batches a row
-        const int last_qb = (nbr - 1) * NB;  // first group of a row's last batch
-        // Buffer loads: the row is a scalar descriptor whose range check
-        // returns 0 past its end (masked when reduced), and a group's offset
-        // is the thread's fixed part plus a scalar one, so a batch needs no
-        // address registers of its own.
-        const int voff = tid * 16;
-        auto load = [&](float4(&xs)[U], int j, int qb) __device__ {
-            const bool any = j <= L + 1;  // uniform
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float *>(row_of(any ? j : 1)), 0, any ? n4 * 16 : 0, kBufferWord3);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const v4f_t x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (qb + kWalkThreads * u) * 16,
-                                                                      kStreamPolicy);
-                xs[u] = make_float4(x[0], x[1], x[2], x[3]);
-            }
-        };
-        auto consume = [&](float4(&xs)[U], int qb) __device__ {
-            if (qb + NB <= n4) {  // uniform: a full batch
-                if (sampled)
-                    walk_batch<false, true, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), U, sc, m, s, av, ai);
-                else
-                    walk_batch<true, true, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), U, sc, m, s, av, ai);
-            } else {
-                const int nv = (n4 - qb - tid + kWalkThreads - 1) / kWalkThreads;  // this thread's groups in the row
-                if (sampled)
-                    walk_batch<false, false, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), nv, sc, m, s, av, ai);
-                else
-                    walk_batch<true, false, U, 4 * kWalkThreads>(xs, 4 * (qb + tid), nv, sc, m, s, av, ai);
-            }
-        };
-        // (row, first group) of the batch in each buffer
-        int ja = 1, qa = 0, jb, qb;
-        auto advance = [&](int j, int q, int &jn, int &qn) {
-            if (q == last_qb) {
-                jn = j + 1;
-                qn = 0;
-            } else {
-                jn = j;
-                qn = q + NB;
-            }
-        };
-        float4 xa[U], xb[U];
-        load(xa, ja, qa);
-        for (;;) {
-            advance(ja, qa, jb, qb);
-            load(xb, jb, qb);
-            consume(xa, qa);
-            if (qa == last_qb) {
-                if (!finish_row(ja)) break;
-                locate_x(ja + 1);
-            }
-            advance(jb, qb, ja, qa);
-            load(xa, ja, qa);
-            consume(xb, qb);
-            if (qb == last_qb) {
-                if (!finish_row(jb)) break;
-                locate_x(jb + 1);
-            }
-        }
+        walk_stream_rows(p.target, offb, p.V, 1, L + 1, sampled, sc, m, s, av, ai, finish_row);
     }
     if (tid == 0) {
         // the outcome: accepted drafts, the first rejection's or the bonus
-        // row's data for the draw, diagnostics of every tested position
+        // row's data for the draw, diagnostics of every tested position (a
+        // request left to the tail kernel: its accepted drafts and their
+        // diagnostics so far)
+        const bool tail = r_mode == kModeTail;
         int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
         for (int k = 1; k <= r_n; ++k) tok[k - 1] = s_x[k - 1];
-        if (!sampled) tok[r_j - 1] = r_tok;
+        if (!sampled && !tail) tok[r_j - 1] = r_tok;
         if (p.diag_out)
-            for (int k = 1; k <= min(r_j, L); ++k) {
+            for (int k = 1; k <= (tail ? r_n : min(r_j, L)); ++k) {
                 p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = s_dp[k - 1];
                 p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = s_dr[k - 1];
             }
         p.n_accept_out[b] = r_n;
         p.jpos[b] = r_j;
         p.mode[b] = r_mode;
-        if (sampled) p.fin_lse2[b] = r_lse2;
+        if (p.tail_from) {
+            p.tail_flag[b] = tail ? 1 : 0;
+            if (tail) p.tail_cnt[b] = 0;
+        }
+        if (sampled && !tail) p.fin_lse2[b] = r_lse2;
         if (r_mode == kModeResidual) {
             p.prev[b] = p.erow_mode ? b * p.gamma + r_j - 1
                                     : min(max(r_j == 1 ? p.anchor[b] : s_x[r_j - 2], 0), p.V - 1);
             p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + r_j - 1] * kLog2e;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ walk tail
+
+// Rows tail_from .. ell + 1 of the requests the walk left at row tail_from,
+// a workgroup a row, all at once: a request's later rows are read whether or
+// not an earlier one rejects (the rows past its first rejection are reduced
+// and left unused), so the block's last rows take about one row's time
+// instead of one each, on CUs the walk has left idle.  A row is streamed and
+// merged by the walk's own code, so its statistics have the walk's bits.
+// Each workgroup stores its row's statistics and counts itself in with one
+// device-scope atomic (release); the one that counts its request's last row
+// in (acquire) decides the request's positions in order, as the walk would,
+// and writes its outcome.  No workgroup waits for another.  Workgroup
+// s nt + t takes row tail_from + t of the s-th request of the batch with
+// tail_flag set (nt = gamma + 2 - tail_from).
+__global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_tail_kernel(
+    WalkParams p) {
+    static_assert(kTailFrom >= 2, "the walk decides row 1");
+    __shared__ WalkMergeLds s_mg;
+    __shared__ uint64_t s_ball[(kTailMaxBatch + 63) / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nt = p.gamma + 2 - p.tail_from;
+    const int slot = blockIdx.x / nt, t = blockIdx.x - slot * nt;
+    const int nch = (p.B + 63) / 64;
+    for (int c = wave; c < nch; c += kWalkWaves) {
+        const int bq = c * 64 + lane;
+        const uint64_t bal = __ballot(bq < p.B && p.tail_flag[bq] != 0);
+        if (lane == 0) s_ball[c] = bal;
+    }
+    __syncthreads();
+    int b = -1;
+    {
+        int rem = slot;
+        for (int c = 0; c < nch; ++c) {
+            uint64_t bal = s_ball[c];
+            const int pc = __popcll(bal);
+            if (rem < pc) {
+                for (int i = 0; i < rem; ++i) bal &= bal - 1;
+                b = c * 64 + __builtin_ctzll(bal);
+                break;
+            }
+            rem -= pc;
+        }
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    if (b < 0) return;
+    const int L = p.ell[b];  // checked by the walk
+    const int j = p.tail_from + t;
+    if (j > L + 1) return;
+    const float T = p.temperature[b];
+    const bool sampled = T > 0.f;
+    const float sc = sampled ? kLog2e / T : 1.0f;
+    const int offb = p.off[b];
+    float txs = kNegInf;
+    if (sampled && j <= L) {
+        const int q = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
+        txs = reinterpret_cast<const kconst_float *>(
+                  reinterpret_cast<uintptr_t>(p.target + size_t(offb + j - 1) * p.V))[q] *
+              sc;
+    }
+    float m = kNegInf, s = 0.f, av = kNegInf;
+    int ai = 0x7fffffff;
+    float lse2 = 0.f;
+    int amax = 0;
+    walk_stream_rows(p.target, offb, p.V, j, j, sampled, sc, m, s, av, ai, [&](int jr) -> bool {
+        walk_merge_row(s_mg, jr & 1, p.V, m, s, av, ai, lse2, amax);
+        return false;
+    });
+    if (wave != 0) return;
+    int last = 0;
+    if (lane == 0) {
+        const size_t o = size_t(b) * nt + t;
+        p.tail_lse2[o] = lse2;
+        p.tail_amax[o] = amax;
+        p.tail_tx[o] = txs;
+        last = __hip_atomic_fetch_add(p.tail_cnt + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+               L + 1 - p.tail_from;  // the request's other rows (L + 2 - tail_from in all) are in
+    }
+    if (!__builtin_amdgcn_readfirstlane(last)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // The request's rows in the tail, a lane each: every position's test at
+    // once, then the first that stops (a rejection, else the bonus row ell + 1)
+    const int jj = p.tail_from + lane;
+    const bool row = jj <= L + 1;
+    float l2 = 0.f, pk = 0.f, ratio = 0.f;
+    int am = 0, xj = -1;
+    bool acc = false;
+    if (row) {
+        const size_t o = size_t(b) * nt + lane;
+        l2 = __hip_atomic_load(p.tail_lse2 + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        am = __hip_atomic_load(p.tail_amax + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float tx = __hip_atomic_load(p.tail_tx + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (jj <= L) {
+            const size_t ox = size_t(b) * p.gamma + jj - 1;
+            xj = p.x[ox];
+            const float qk = p.qx[ox];
+            const float thr =
+                sampled ? uniform01(scalar_word(kStreamAccept, jj, uint32_t(b), p.round32, p.key0, p.key1)) * qk
+                        : 0.f;
+            acc = position_test(sampled, tx, l2, am, xj, qk, thr, pk, ratio);
+        }
+    }
+    const uint64_t stop = __ballot(row && (jj > L || !acc));  // lane ell + 1 - tail_from is set
+    const int jf = p.tail_from + __builtin_ctzll(stop);
+    int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
+    if (row && jj < jf) tok[jj - 1] = xj;
+    if (p.diag_out && row && jj <= min(jf, L)) {
+        p.diag_out[(size_t(b) * (p.gamma + 1) + (jj - 1)) * 2 + 0] = pk;
+        p.diag_out[(size_t(b) * (p.gamma + 1) + (jj - 1)) * 2 + 1] = ratio;
+    }
+    if (jj == jf) {
+        const bool rej = jf <= L;
+        const int r_mode = !sampled ? kModeDone : (rej ? kModeResidual : kModeBonus);
+        if (!sampled) tok[jf - 1] = am;
+        p.n_accept_out[b] = rej ? jf - 1 : L;
+        p.jpos[b] = jf;
+        p.mode[b] = r_mode;
+        if (sampled) p.fin_lse2[b] = l2;
+        if (r_mode == kModeResidual) {
+            p.prev[b] = p.erow_mode ? b * p.gamma + jf - 1 : min(max(p.x[size_t(b) * p.gamma + jf - 2], 0), p.V - 1);
+            p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + jf - 1] * kLog2e;
         }
     }
 }
@@ -1431,8 +1623,21 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         wp.n_accept_out = a.n_accept_out;
         wp.tokens_out = a.tokens_out;
         wp.diag_out = a.diag_out;
+        // the tail kernel streams rows the vector way only, and finds its
+        // requests among at most kTailMaxBatch
+        wp.tail_from = (vec_t && a.B <= kTailMaxBatch) ? pl.tail_from : 0;
+        wp.tail_flag = w.tail_flag;
+        wp.tail_cnt = w.tail_cnt;
+        wp.tail_amax = w.tail_amax;
+        wp.tail_lse2 = w.tail_lse2;
+        wp.tail_tx = w.tail_tx;
         launch_kernel("verify_walk", verify_walk_kernel, dim3(a.B), dim3(kWalkThreads), s, wp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (wp.tail_from) {
+            const int nt = a.gamma + 2 - wp.tail_from;
+            launch_kernel("verify_tail", verify_tail_kernel, dim3(size_t(a.B) * nt), dim3(kWalkThreads), s, wp);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     } else {
         PassRows sched[DSPARK_MAX_GAMMA + 2];  // gamma is checked at the boundary
         const int single = size_t(a.B) * a.V * sizeof(float) <= kPairAllBytes ? 0 : kSinglePasses;
@@ -1598,11 +1803,12 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
 }  // namespace
 
 VerifyPlan verify_plan(int B, int gamma, int V) {
-    (void)gamma;
     VerifyPlan p{};
     // a workgroup a request (the walk) once the batch fills most of the chip;
     // smaller batches spread each row over many waves (the position passes)
     p.walk = B >= kWalkMinBatch;
+    // the walk's last rows in parallel, while the batch leaves CUs idle then
+    p.tail_from = (p.walk && B <= kTailMaxBatch && gamma >= kTailMinGamma) ? kTailFrom : 0;
     // Position passes split a row into segments of whole float4 groups: the
     // first pass, which reads every request's row, in a few long ones (long
     // streams per workgroup), the later ones, which read fewer and fewer rows,
@@ -1629,7 +1835,6 @@ VerifyPlan verify_plan(int B, int gamma, int V) {
 }
 
 VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, size_t *bytes) {
-    (void)gamma;
     (void)V;
     Carve c(ws);
     VerifyWork w{};
@@ -1644,6 +1849,14 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
         w.seg_v = c.take<float>(ns);
         w.seg_i = c.take<int32_t>(ns);
         w.seg_tx = c.take<float>(size_t(2) * kPassRows * B);
+    }
+    if (p.tail_from) {
+        const size_t nt = size_t(B) * (gamma + 2 - p.tail_from);
+        w.tail_flag = c.take<int32_t>(B);
+        w.tail_cnt = c.take<int32_t>(B);
+        w.tail_lse2 = c.take<float>(nt);
+        w.tail_tx = c.take<float>(nt);
+        w.tail_amax = c.take<int32_t>(nt);
     }
     w.fin_lse2 = c.take<float>(B);
     w.prev = c.take<int32_t>(B);

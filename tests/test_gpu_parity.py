@@ -225,6 +225,7 @@ def _custom_round(B, gamma, V, r, wdtype, seed, greedy_every=0, ell=None, neg_in
     (70, 6, 4099, 64, "f32", 5),      # f32 weights, several tiles and chunks
     (40, 2, 2048 * 3 + 5, 128, "bf16", 0),
     (3, 32, 300, 256, "bf16", 2),     # longest block
+    (230, 6, 12288, 64, "bf16", 4),   # a walked batch: rows from the fourth on in the tail kernel
 ])
 def test_edge_shapes_parity(B, gamma, V, r, wdtype, greedy):
     rnd, ell, target = _custom_round(B, gamma, V, r, wdtype, seed=B * 31 + V, greedy_every=greedy)
@@ -260,14 +261,16 @@ def test_neg_inf_logits_parity():
             assert np.isfinite(rnd.U[b, k, gd["x"][b, k]])
 
 
-def test_nonfinite_inputs_stay_in_bounds_and_leave_other_requests_alone():
+@pytest.mark.parametrize("B,V", [(40, 3001), (256, 3000)])  # position passes / walk and tail kernel
+def test_nonfinite_inputs_stay_in_bounds_and_leave_other_requests_alone(B, V):
     """NaN and +inf inputs have no defined result, but a call with them must
     finish, write only where it may, and keep requests independent: base
     logits, target rows and a temperature poisoned for a few requests leave
     every other request's draft, verify and acceptance outputs bit for bit
     as in the clean call, and the poisoned requests still get tokens in
     range, counts within their lengths and -1 padding after them."""
-    B, gamma, V = 40, 4, 3001
+    gamma = 4
+    _say(f"[nonfinite] B={B} V={V}")
     rnd, ell, target = _custom_round(B, gamma, V, 64, "bf16", seed=12, greedy_every=6)
     off = S.pack_offsets(ell)
 
@@ -314,12 +317,14 @@ def test_nonfinite_inputs_stay_in_bounds_and_leave_other_requests_alone():
         assert np.all(tok[b, n[b] + 1:] == -1), b
 
 
-def test_round_replays_from_a_graph_as_it_runs_eagerly():
+@pytest.mark.parametrize("B,V", [(40, 3001), (256, 3000)])  # position passes / walk and tail kernel
+def test_round_replays_from_a_graph_as_it_runs_eagerly(B, V):
     """A round (draft + verify) makes no allocation, memset or host
     synchronisation, so a caller can capture it in a graph: replays, with
     eager rounds of other inputs between them, give the eager outputs bit
     for bit.  Two input sets, each captured once, replayed three times."""
-    rnd, ell, target = _custom_round(40, 4, 3001, 64, "bf16", seed=21, greedy_every=5)
+    _say(f"[graph] B={B} V={V}")
+    rnd, ell, target = _custom_round(B, 4, V, 64, "bf16", seed=21, greedy_every=5)
     dev = to_device(rnd)
     U2 = (dev["U"] + 0.25).contiguous()
     tds = [torch.from_numpy(target).cuda(), torch.from_numpy(target).cuda() * 0.5]
@@ -395,8 +400,45 @@ def test_row_offsets_given_equal_computed_and_bad_ell_flagged(B):
     assert torch.equal(v5["tokens"], v1["tokens"])
 
 
-def test_bitwise_determinism():
-    rnd, ell, target = _round("dspark5")
+def test_walk_tail_matches_the_walk_alone():
+    """A walked request's later rows read by the tail kernel give what the
+    walk gives reading them itself.  The first 256 requests of a 600-request
+    batch (walked without the tail kernel), verified as a batch of their own
+    (rows from the fourth on read by the tail kernel), get the same counts,
+    tokens and diagnostics bit for bit, and residual masses within float
+    rounding (the draw's chunks follow the batch size).  Random lengths and
+    a greedy request in four put requests at every stage of the tail."""
+    B, Bs, gamma, V = 600, 256, 6, 8192
+    cfg = S.Config("tail", B=B, gamma=gamma, V=V, r=64, wdtype="bf16", w_std=0.05, u_std=3.0, noise_std=0.4,
+                   seed=17, greedy_every=4)
+    rnd = S.make_round(cfg)
+    ell = np.random.default_rng(18).integers(0, gamma + 1, B).astype(np.int32)
+    target = rnd.target_packed(ell)
+    _say(f"[tail] B={B} / {Bs} gamma={gamma} V={V}")
+    dev = to_device(rnd)
+    td, ed = torch.from_numpy(target).cuda(), torch.from_numpy(ell).cuda()
+    d = gpu_draft(dev, 3, 5)
+    full = gpu_verify(dev, td, ed, d, 3, 5)
+    sub = {k: (t[:Bs].contiguous() if k in ("U", "anchor", "temperature") else t) for k, t in dev.items()}
+    dsub = {k: d[k][:Bs].contiguous() for k in ("x", "lse", "qx")}
+    nrows = int(S.pack_offsets(ell)[Bs])
+    part = gpu_verify(sub, td[:nrows].contiguous(), ed[:Bs].contiguous(), dsub, 3, 5)
+    torch.cuda.synchronize()
+    assert ds.dspark_verify_check(full["workspace"]) == 0 and ds.dspark_verify_check(part["workspace"]) == 0
+    n_full, n_part = np_of(full["n"])[:Bs], np_of(part["n"])
+    reach = [int(np.sum(n_part >= k)) for k in range(3, gamma + 1)]
+    _say(f"[tail] requests with at least 3 .. {gamma} drafts accepted: {reach}")
+    assert reach[0] >= 40 and reach[-1] >= 5
+    np.testing.assert_array_equal(n_part, n_full)
+    np.testing.assert_array_equal(np_of(part["tokens"]), np_of(full["tokens"])[:Bs])
+    assert np.array_equal(np_of(part["diag"]).view(np.uint32), np_of(full["diag"])[:Bs].view(np.uint32))
+    np.testing.assert_allclose(np_of(part["resid"]), np_of(full["resid"])[:Bs], rtol=1e-5, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", ["dspark5", "large"])  # position passes / walk and tail kernel
+def test_bitwise_determinism(name):
+    _say(f"[determinism] {name}")
+    rnd, ell, target = _round(name)
     dev = to_device(rnd)
     td = torch.from_numpy(target).cuda()
     ed = torch.from_numpy(ell).cuda()
