@@ -165,8 +165,7 @@ struct VerifyWork {
     float *lse2q;        // [B] log2-unit logsumexp of q_j for a residual draw
     int32_t *mode;       // [B] 0 done, 1 residual draw, 2 bonus draw, -1 invalid
     int32_t *jpos;       // [B] position of the emitted non-draft token
-    int32_t *slot;       // [B] draw slot: the request's entry in the draw list
-    // draw partials per (list slot, vocabulary chunk)
+    // draw partials per (request, vocabulary chunk)
     float *dw_sum;       // residual mass
     float *dw_bl;        // best tile score of the level-1 race
     int32_t *dw_bt;      // its tile

@@ -702,13 +702,26 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     static_assert(kTailFrom >= 2, "the walk decides row 1");
     __shared__ WalkMergeLds s_mg;
     __shared__ uint64_t s_ball[(kTailMaxBatch + 63) / 64];
+    // every request's length, row offset, temperature and draft at this
+    // workgroup's position, loaded with the flags (one round trip)
+    __shared__ int s_rq_ell[kTailMaxBatch], s_rq_off[kTailMaxBatch], s_rq_x[kTailMaxBatch];
+    __shared__ float s_rq_T[kTailMaxBatch];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nt = p.gamma + 2 - p.tail_from;
     const int slot = blockIdx.x / nt, t = blockIdx.x - slot * nt;
+    const int j = p.tail_from + t;
     const int nch = (p.B + 63) / 64;
     for (int c = wave; c < nch; c += kWalkWaves) {
         const int bq = c * 64 + lane;
-        const uint64_t bal = __ballot(bq < p.B && p.tail_flag[bq] != 0);
+        int fl = 0;
+        if (bq < p.B) {
+            fl = p.tail_flag[bq];
+            s_rq_ell[bq] = p.ell[bq];
+            s_rq_off[bq] = p.off[bq];
+            s_rq_T[bq] = p.temperature[bq];
+            s_rq_x[bq] = j <= p.gamma ? p.x[size_t(bq) * p.gamma + j - 1] : 0;
+        }
+        const uint64_t bal = __ballot(fl != 0);
         if (lane == 0) s_ball[c] = bal;
     }
     __syncthreads();
@@ -728,19 +741,34 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
     b = __builtin_amdgcn_readfirstlane(b);
     if (b < 0) return;
-    const int L = p.ell[b];  // checked by the walk
-    const int j = p.tail_from + t;
+    const int L = __builtin_amdgcn_readfirstlane(s_rq_ell[b]);  // checked by the walk
     if (j > L + 1) return;
-    const float T = p.temperature[b];
+    const float T = uniform_f(s_rq_T[b]);
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    const int offb = p.off[b];
+    const int offb = __builtin_amdgcn_readfirstlane(s_rq_off[b]);
     float txs = kNegInf;
     if (sampled && j <= L) {
-        const int q = min(max(p.x[size_t(b) * p.gamma + j - 1], 0), p.V - 1);
+        const int q = min(max(__builtin_amdgcn_readfirstlane(s_rq_x[b]), 0), p.V - 1);
         txs = reinterpret_cast<const kconst_float *>(
                   reinterpret_cast<uintptr_t>(p.target + size_t(offb + j - 1) * p.V))[q] *
               sc;
+    }
+    // The decision's inputs, loaded while the row streams: in wave 0, lane i
+    // takes the request's row tail_from + i (its draft, q(x), log-normaliser
+    // of q, and the draft before it)
+    const int jj = p.tail_from + lane;
+    const bool row = wave == 0 && jj <= L + 1;
+    int xj = -1, xprev = 0;
+    float qk = 0.f, lq = 0.f;
+    if (row) {
+        const size_t ox = size_t(b) * p.gamma + jj - 1;
+        xprev = p.x[ox - 1];
+        if (jj <= L) {
+            xj = p.x[ox];
+            qk = p.qx[ox];
+            lq = p.lse_q[ox];
+        }
     }
     float m = kNegInf, s = 0.f, av = kNegInf;
     int ai = 0x7fffffff;
@@ -762,12 +790,10 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
     if (!__builtin_amdgcn_readfirstlane(last)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // The request's rows in the tail, a lane each: every position's test at
-    // once, then the first that stops (a rejection, else the bonus row ell + 1)
-    const int jj = p.tail_from + lane;
-    const bool row = jj <= L + 1;
+    // every position's test at once, then the first that stops (a
+    // rejection, else the bonus row ell + 1)
     float l2 = 0.f, pk = 0.f, ratio = 0.f;
-    int am = 0, xj = -1;
+    int am = 0;
     bool acc = false;
     if (row) {
         const size_t o = size_t(b) * nt + lane;
@@ -775,9 +801,6 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         am = __hip_atomic_load(p.tail_amax + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float tx = __hip_atomic_load(p.tail_tx + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (jj <= L) {
-            const size_t ox = size_t(b) * p.gamma + jj - 1;
-            xj = p.x[ox];
-            const float qk = p.qx[ox];
             const float thr =
                 sampled ? uniform01(scalar_word(kStreamAccept, jj, uint32_t(b), p.round32, p.key0, p.key1)) * qk
                         : 0.f;
@@ -801,8 +824,8 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         p.mode[b] = r_mode;
         if (sampled) p.fin_lse2[b] = l2;
         if (r_mode == kModeResidual) {
-            p.prev[b] = p.erow_mode ? b * p.gamma + jf - 1 : min(max(p.x[size_t(b) * p.gamma + jf - 2], 0), p.V - 1);
-            p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + jf - 1] * kLog2e;
+            p.prev[b] = p.erow_mode ? b * p.gamma + jf - 1 : min(max(xprev, 0), p.V - 1);
+            p.lse2q[b] = lq * kLog2e;
         }
     }
 }
@@ -1166,7 +1189,6 @@ struct DrawParams {
     uint32_t key0, key1, round32;
     const int32_t *mode, *jpos, *off, *prev;
     const float *fin_lse2, *lse2q;
-    int32_t *slot;
     float *dw_sum, *dw_bl;
     int32_t *dw_bt;
 };
@@ -1285,8 +1307,6 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV >=
     const bool resid = e < nres;
     const bool ok = resid || (e >= bon0 && e < p.B);
     const int req = ok ? max(lreq[wave * 32 + n], 0) : 0;
-    const int slot = e;
-    if (chunk == 0 && h == 0 && ok) p.slot[req] = slot;  // for the level-2 draw
     const int j = wave_ok ? p.jpos[req] : 1;
     const float sc = wave_ok ? kLog2e / p.temperature[req] : 1.0f;
     const float lse2t = wave_ok ? p.fin_lse2[req] : 0.f;
@@ -1392,7 +1412,7 @@ __global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV >=
         if (wave_ok) stage(t_end - 1, ldsW0, ldsU0, ldsT0, true);
     }
     if (h == 0 && ok) {
-        const size_t o = size_t(slot) * p.nchunk + chunk;
+        const size_t o = size_t(req) * p.nchunk + chunk;  // by request: the finish needs no list
         p.dw_sum[o] = S;
         p.dw_bl[o] = best;
         p.dw_bt[o] = bt;
@@ -1409,7 +1429,7 @@ struct FinishParams {
     int B, gamma, V, nchunk, ntiles;
     uint32_t key0, key1, round32;
     int32_t *status;
-    const int32_t *mode, *n_accept, *slot, *off, *jpos, *prev, *req_flags;
+    const int32_t *mode, *n_accept, *off, *jpos, *prev, *req_flags;
     const float *fin_lse2, *lse2q;
     const float *dw_sum, *dw_bl;
     const int32_t *dw_bt;
@@ -1467,18 +1487,10 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
     const int lane = threadIdx.x & 63;
     const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (b >= p.B) return;
-    // the request's state in one round of loads (read whatever the mode; used
-    // only by drawing requests), then the chunk partials ahead of the W1 row
-    const int mode = p.mode[b];
-    const int slot = p.slot[b], j = p.jpos[b], off = p.off[b], prev = p.prev[b];
-    const float T = p.temperature[b], lse2t = p.fin_lse2[b], lse2q_in = p.lse2q[b];
-    // an empty use ahead of the branch keeps the compiler from sinking the
-    // loads after it, which would put a second round trip on the path
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::"v"(slot), "v"(j), "v"(off), "v"(prev), "v"(T), "v"(lse2t), "v"(lse2q_in));
-    if (mode != kModeResidual && mode != kModeBonus) return;
-    const float sc = kLog2e / T;
-    const float *trow = p.target + size_t(off + j - 1) * p.V;
+    // the request's state and its first batch of chunk partials (kept by
+    // request) in one round of loads, read whatever the mode (used only by
+    // drawing requests); the W1 row and the winning tile's entries follow in
+    // a second
     constexpr int PC = 4;
     float cs[PC], cb[PC];
     int ct[PC];
@@ -1486,14 +1498,25 @@ __global__ __launch_bounds__(256) void verify_finish_kernel(FinishParams p) {
 #pragma unroll
         for (int u = 0; u < PC; ++u) {
             const int c = c0 + lane + 64 * u;  // past the chunks: re-reads chunk 0, masked below
-            const size_t o = size_t(slot) * p.nchunk + (c < p.nchunk ? c : 0);
+            const size_t o = size_t(b) * p.nchunk + (c < p.nchunk ? c : 0);
             cs[u] = p.dw_sum[o];
             cb[u] = p.dw_bl[o];
             ct[u] = p.dw_bt[o];
         }
     };
+    const int mode = p.mode[b];
+    const int j = p.jpos[b], off = p.off[b], prev = p.prev[b];
+    const float T = p.temperature[b], lse2t = p.fin_lse2[b], lse2q_in = p.lse2q[b];
     load_batch(0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch ahead of the W1 fetch
+    // an empty use ahead of the branch keeps the compiler from sinking the
+    // loads after it, which would put another round trip on the path
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(j), "v"(off), "v"(prev), "v"(T), "v"(lse2t), "v"(lse2q_in));
+    asm volatile("" ::"v"(cs[0]), "v"(cs[1]), "v"(cs[2]), "v"(cs[3]), "v"(cb[0]), "v"(cb[1]), "v"(cb[2]),
+                 "v"(cb[3]), "v"(ct[0]), "v"(ct[1]), "v"(ct[2]), "v"(ct[3]));
+    if (mode != kModeResidual && mode != kModeBonus) return;
+    const float sc = kLog2e / T;
+    const float *trow = p.target + size_t(off + j - 1) * p.V;
     RowHalf<WT, R> w1;
     float lse2q = 0.f;
     if (mode == kModeResidual) {
@@ -1739,7 +1762,6 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         dp.key1 = a.key1;
         dp.round32 = a.round32;
         dp.mode = w.mode;
-        dp.slot = w.slot;
         dp.jpos = w.jpos;
         dp.off = w.off;
         dp.fin_lse2 = w.fin_lse2;
@@ -1782,7 +1804,6 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
         fp.req_flags = w.req_flags;
         fp.mode = w.mode;
         fp.n_accept = a.n_accept_out;
-        fp.slot = w.slot;
         fp.off = w.off;
         fp.fin_lse2 = w.fin_lse2;
         fp.jpos = w.jpos;
@@ -1863,7 +1884,6 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
     w.lse2q = c.take<float>(B);
     w.mode = c.take<int32_t>(B);
     w.jpos = c.take<int32_t>(B);
-    w.slot = c.take<int32_t>(B);
     const size_t nd = size_t(B) * p.tile.nchunk;
     w.dw_sum = c.take<float>(nd);
     w.dw_bl = c.take<float>(nd);
