@@ -226,6 +226,9 @@ def _custom_round(B, gamma, V, r, wdtype, seed, greedy_every=0, ell=None, neg_in
     (40, 2, 2048 * 3 + 5, 128, "bf16", 0),
     (3, 32, 300, 256, "bf16", 2),     # longest block
     (230, 6, 12288, 64, "bf16", 4),   # a walked batch: rows from the fourth on in the tail kernel
+    (320, 4, 8192, 64, "bf16", 5),    # the largest batch with a tail kernel, at the shortest block it serves
+    (321, 4, 8192, 64, "bf16", 5),    # one request more: the walk alone
+    (200, 9, 4096, 32, "f32", 3),     # f32 weights, a tail of up to seven rows a request
 ])
 def test_edge_shapes_parity(B, gamma, V, r, wdtype, greedy):
     rnd, ell, target = _custom_round(B, gamma, V, r, wdtype, seed=B * 31 + V, greedy_every=greedy)
