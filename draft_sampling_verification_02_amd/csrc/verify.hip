@@ -945,11 +945,11 @@ __device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampl
 // four requests to a workgroup.  First the request's DIN previous positions are
 // decided, in order, from the segment statistics pass p - 1 wrote; a request
 // that goes on streams segment sg of its row j0 + q: every lane keeps its own
-// running max / sum of exp2 and argmax over batches of eight float4 loads
-// (PIPE: two batches, one in flight while the other is reduced, for the long
-// segments of the first pass), and the wave merges them.  The waves never
-// wait for one another.
-template <bool PIPE, int DIN, int DOUT>
+// running max / sum of exp2 and argmax over batches of eight float4 loads,
+// two batches in flight (one is reduced while the next lands), and the wave
+// merges them.  The waves never wait for one another.  FIRST: the first pass,
+// which decides nothing.
+template <bool FIRST, int DIN, int DOUT>
 __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     static_assert(DIN >= 1 && DIN <= kPassRows && DOUT >= 1 && DOUT <= kPassRows,
                   "row slots: the previous pass's (DIN) and this pass's (DOUT)");
@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     int i2 = 0x7fffffff;
     float tx2[DIN], qk[DIN];
     int xk[DIN];
-    if constexpr (PIPE) {
+    if constexpr (FIRST) {
         // the first pass decides nothing: it needs the request's temperature
         // and length and, for a small batch, does its input checks (the row
         // offset is a wave sum over ell, read in the same round)
@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     }
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
-    if (!PIPE && j0 > 1) {
+    if (!FIRST && j0 > 1) {
         bfly_steps<0, LOG_LPS>([&](auto st) {  // within each lane group
             constexpr int S = decltype(st)::value;
             const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
@@ -1074,72 +1074,46 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
     float m = kNegInf, s = 0.f, av = kNegInf;
     int ai = 0x7fffffff;
     if (p.vec) {
-        if constexpr (PIPE) {
-            // two batches of U float4 a lane, one in flight while the other is
-            // reduced
-            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
-            const int q_hi = v_hi >> 2;
-            constexpr int U = 8;
-            // loads past the segment re-read its last group and are masked when used
-            auto load = [&](float4(&xs)[U], int qb) __device__ {
-    #pragma unroll
-                for (int u = 0; u < U; ++u) xs[u] = load_stream(r4 + min(qb + lane + 64 * u, q_hi - 1));
-            };
-            // sampled rows keep no argmax (only greedy decisions use it); the
-            // request, and so the branch, is uniform across the wave
-            auto consume = [&](float4(&xs)[U], int qb) __device__ {
-                auto valid = [&](int u) { return qb + lane + 64 * u < q_hi; };
-                if (sampled)
-                    row_batch<false, U, 256>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
-                else
-                    row_batch<true, U, 256>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
-            };
-            // The loop body is straight-line, so that every consume sees the
-            // same loads in flight on every path into it; it runs while the
-            // batch after the pair exists, and the last one or two batches
-            // follow it.  The batch bounds are uniform across the wave.
-            constexpr int NB = 64 * U;  // float4 groups a batch
-            const int qs = v_lo >> 2;
-            float4 xa[U], xb[U];
-            load(xa, qs);
-            int qb = qs;
-            for (; qb + 2 * NB < q_hi; qb += 2 * NB) {
-                load(xb, qb + NB);
-                consume(xa, qb);
-                load(xa, qb + 2 * NB);
-                consume(xb, qb + NB);
-            }
-            if (qb + NB < q_hi) {
-                load(xb, qb + NB);
-                consume(xa, qb);
-                consume(xb, qb + NB);
-            } else {
-                consume(xa, qb);
-            }
-        } else {
-            // one batch of U float4 a lane at a time: fewer registers, twice
-            // the waves a SIMD for the short segments of the later passes
-            const float4 *r4 = reinterpret_cast<const float4 *>(trow);
-            const int q_hi = v_hi >> 2;
-            constexpr int U = 8;
-            // one loop for each kind of row (the request, and so the kind, is
-            // uniform across the wave): each keeps only its own registers
-            auto walk = [&](auto argmax) __device__ {
-                constexpr bool AM = decltype(argmax)::value;
-                for (int q0 = (v_lo >> 2) + lane; q0 < q_hi; q0 += 64 * U) {
-                    float4 xs[U];
+        // two batches of U float4 a lane, one in flight while the other is
+        // reduced
+        const float4 *r4 = reinterpret_cast<const float4 *>(trow);
+        const int q_hi = v_hi >> 2;
+        constexpr int U = 8;
+        // loads past the segment re-read its last group and are masked when used
+        auto load = [&](float4(&xs)[U], int qb) __device__ {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int q = q0 + 64 * u;
-                        xs[u] = q < q_hi ? load_stream(r4 + q) : make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
-                    }
-                    row_batch<AM, U, 256>(xs, 4 * q0, [](int) { return true; }, sc, m, s, av, ai);  // masked at the load
-                }
-            };
+            for (int u = 0; u < U; ++u) xs[u] = load_stream(r4 + min(qb + lane + 64 * u, q_hi - 1));
+        };
+        // sampled rows keep no argmax (only greedy decisions use it); the
+        // request, and so the branch, is uniform across the wave
+        auto consume = [&](float4(&xs)[U], int qb) __device__ {
+            auto valid = [&](int u) { return qb + lane + 64 * u < q_hi; };
             if (sampled)
-                walk(std::integral_constant<bool, false>{});
+                row_batch<false, U, 256>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
             else
-                walk(std::integral_constant<bool, true>{});
+                row_batch<true, U, 256>(xs, 4 * (qb + lane), valid, sc, m, s, av, ai);
+        };
+        // The loop body is straight-line, so that every consume sees the
+        // same loads in flight on every path into it; it runs while the
+        // batch after the pair exists, and the last one or two batches
+        // follow it.  The batch bounds are uniform across the wave.
+        constexpr int NB = 64 * U;  // float4 groups a batch
+        const int qs = v_lo >> 2;
+        float4 xa[U], xb[U];
+        load(xa, qs);
+        int qb = qs;
+        for (; qb + 2 * NB < q_hi; qb += 2 * NB) {
+            load(xb, qb + NB);
+            consume(xa, qb);
+            load(xa, qb + 2 * NB);
+            consume(xb, qb + NB);
+        }
+        if (qb + NB < q_hi) {
+            load(xb, qb + NB);
+            consume(xa, qb);
+            consume(xb, qb + NB);
+        } else {
+            consume(xa, qb);
         }
     } else {
         for (int v = v_lo + lane; v < v_hi; v += 64) {

@@ -229,6 +229,7 @@ def _custom_round(B, gamma, V, r, wdtype, seed, greedy_every=0, ell=None, neg_in
     (320, 4, 8192, 64, "bf16", 5),    # the largest batch with a tail kernel, at the shortest block it serves
     (321, 4, 8192, 64, "bf16", 5),    # one request more: the walk alone
     (200, 9, 4096, 32, "f32", 3),     # f32 weights, a tail of up to seven rows a request
+    (200, 5, 4099, 32, "bf16", 4),    # a walked batch whose rows are not 16-byte aligned: scalar loads, no tail
 ])
 def test_edge_shapes_parity(B, gamma, V, r, wdtype, greedy):
     rnd, ell, target = _custom_round(B, gamma, V, r, wdtype, seed=B * 31 + V, greedy_every=greedy)
