@@ -24,6 +24,11 @@
 //                    decides each position right after its row (the accept
 //                    test u*q < p, or the bonus row) and stops at the first
 //                    rejection, so no row past it is used.
+//   verify_tail      after the walk, for walked batches of at most 320
+//                    requests and blocks of at least 4 drafts: the rows from
+//                    the fourth on of the requests still accepting after row
+//                    3, a workgroup a row, all at once; the last workgroup of
+//                    a request to finish decides its positions in order.
 //   verify_pass      smaller batches, instead of the walk: one launch a
 //                    position for the first few positions, one
 //                    a pair of positions after them (from the first one on
@@ -427,8 +432,8 @@ __device__ __forceinline__ void walk_merge_row(WalkMergeLds &l, int par, int V, 
     amax = min(max(ii, 0), V - 1);
 }
 
-// The test of draft position j from its target row's statistics ([CE] 05,
-// the accept rule): a sampled row accepts x_j when u q(x_j) < p(x_j), with
+// The test of draft position j from its target row's statistics (the accept
+// rule of "DeepSeek DSpark explained", section 05): a sampled row accepts x_j when u q(x_j) < p(x_j), with
 // p(x_j) = 2^(txs - lse2) (txs = t(x_j) log2(e) / T) and thr = u q(x_j); a
 // greedy row accepts when x_j is the row's argmax.  pk and ratio get the
 // position's diagnostics p(x_j) and min(1, p / q).
