@@ -439,6 +439,40 @@ def test_walk_tail_matches_the_walk_alone():
     np.testing.assert_allclose(np_of(part["resid"]), np_of(full["resid"])[:Bs], rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("B,gamma,V,kernels", [
+    (256, 5, 4096, {"verify_walk", "verify_tail"}),  # a walked batch with a tail
+    (320, 4, 4096, {"verify_walk", "verify_tail"}),  # the largest such batch, the shortest such block
+    (321, 5, 4096, {"verify_walk"}),                 # one request more
+    (256, 3, 4096, {"verify_walk"}),                 # a block too short for a tail
+    (256, 5, 4099, {"verify_walk"}),                 # rows that take scalar loads
+    (191, 5, 4096, {"verify_pass1"}),                # below the walk: position passes
+])
+def test_verify_launches_the_kernels_its_shape_calls_for(B, gamma, V, kernels):
+    """Which verify kernels a call launches, read back from the library's
+    launch profiler: the walk from 192 requests on, its tail kernel up to 320
+    requests with blocks of at least 4 drafts and 16-byte aligned rows."""
+    rnd, ell, target = _custom_round(B, gamma, V, 32, "bf16", seed=B + gamma, greedy_every=5)
+    _say(f"[launches] B={B} gamma={gamma} V={V}")
+    dev = to_device(rnd)
+    td, ed = torch.from_numpy(target).cuda(), torch.from_numpy(ell).cuda()
+    d = gpu_draft(dev, 1, 2)
+    torch.cuda.synchronize()
+    ds.dspark_profile_reset()
+    ds.dspark_profile_enable(True)
+    try:
+        v = gpu_verify(dev, td, ed, d, 1, 2)
+        torch.cuda.synchronize()
+        ds.dspark_profile_collect()
+    finally:
+        ds.dspark_profile_enable(False)
+    launched = {k for k, (n, _) in ds.dspark_profile_read().items() if n > 0 and k.startswith("verify_")}
+    ds.dspark_profile_reset()
+    assert ds.dspark_verify_check(v["workspace"]) == 0
+    for k in ("verify_walk", "verify_tail", "verify_pass1"):
+        assert (k in launched) == (k in kernels), (k, sorted(launched))
+    assert {"verify_draw", "verify_finish"} <= launched
+
+
 @pytest.mark.parametrize("name", ["dspark5", "large"])  # position passes / walk and tail kernel
 def test_bitwise_determinism(name):
     _say(f"[determinism] {name}")
