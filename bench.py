@@ -91,7 +91,8 @@ def _logit_passes(phases, outcome, B, V, r):
             out[name] = {"bytes": int(nbytes), "us": round(us, 2), "gbs": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
-    put("verify_walk", outcome["rows"] * row, ("verify_walk", "verify_tail"))
+    if "verify_walk" in phases:  # (the position passes of a small batch may end in the tail kernel too)
+        put("verify_walk", outcome["rows"] * row, ("verify_walk", "verify_tail"))
     put("verify_draw", (2 * outcome["residual"] + outcome["bonus"]) * row + (V * r * 2 if outcome["residual"] else 0),
         ("verify_draw",))
     out["per_round"] = {k: round(v, 2) for k, v in outcome.items()}

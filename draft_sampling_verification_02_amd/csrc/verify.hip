@@ -29,6 +29,10 @@
 //                    the fourth on of the requests still accepting after row
 //                    3, a workgroup a row, all at once; the last workgroup of
 //                    a request to finish decides its positions in order.
+//                    After the position passes instead of their last
+//                    launches, when that saves launches and the rows it may
+//                    read are few and cheap: it first decides the last pass's
+//                    positions itself.
 //   verify_pass      smaller batches, instead of the walk: one launch a
 //                    position for the first few positions, one
 //                    a pair of positions after them (from the first one on
@@ -72,6 +76,7 @@ constexpr int kModeDone = 0;
 constexpr int kModeResidual = 1;
 constexpr int kModeBonus = 2;
 constexpr int kPrepInKernelMaxBatch = 512;
+constexpr int kPassRows = 2;  // row slots a position pass can hold
 
 // v of the first active lane, as a scalar
 __device__ __forceinline__ float uniform_f(float v) {
@@ -191,6 +196,63 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
     // the status word is the OR of the requests' flags, formed by the finish
 }
 
+// Position k = j - 1 of request b, from its merged row statistics: the accept
+// test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
+// request takes the same decision; only `writer` stores it.  Returns whether
+// the request goes on to position j.
+// xk, qk: x_k and q_k(x_k) (any value when k > ell).  P: the position passes'
+// or the walk's parameters (the same output fields).
+template <class P>
+__device__ bool pass_decide(const P &p, int b, int L, int k, bool sampled, float lse2, int amax, float tx2,
+                            int xk, float qk, bool writer) {
+    int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
+    bool bonus = false;
+    if (k <= L) {
+        bool acc;
+        float pk, ratio;
+        if (sampled) {
+            pk = fast_exp2(tx2 - lse2);
+            const float u = uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
+            acc = u * qk < pk;
+            ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
+        } else {
+            acc = (xk == amax);
+            pk = acc ? 1.f : 0.f;
+            ratio = pk;
+        }
+        if (writer && p.diag_out) {
+            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = pk;
+            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = ratio;
+        }
+        if (acc) {
+            if (writer) tok[k - 1] = xk;
+            return true;
+        }
+        if (writer) p.n_accept_out[b] = k - 1;
+    } else {
+        if (writer) p.n_accept_out[b] = L;
+        bonus = true;
+    }
+    if (!writer) return false;
+    p.jpos[b] = k;
+    if (!sampled) {
+        tok[k - 1] = amax;
+        p.mode[b] = kModeDone;
+        return false;
+    }
+    p.fin_lse2[b] = lse2;
+    if (bonus) {
+        p.mode[b] = kModeBonus;
+    } else {
+        p.mode[b] = kModeResidual;
+        // what the residual draw needs to rebuild q_k
+        p.prev[b] = p.erow_mode ? b * p.gamma + k - 1
+                                : min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
+        p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + k - 1] * kLog2e;
+    }
+    return false;
+}
+
 // ------------------------------------------------------------------ position walk
 
 // One workgroup walks one request's target rows in position order: it streams
@@ -247,6 +309,15 @@ struct WalkParams {
     int tail_from;
     int32_t *tail_flag, *tail_cnt, *tail_amax;
     float *tail_lse2, *tail_tx;
+    // tail_din > 0: the tail kernel follows the position passes instead of
+    // the walk; the last pass reduced rows tail_from - tail_din ..
+    // tail_from - 1 of the requests with act_in set and left their segment
+    // statistics (as a pass's *_in buffers), which the tail kernel decides
+    // first
+    int tail_din, nseg_in, seg_stride;
+    size_t row_stride;
+    const int32_t *act_in, *pi_in;
+    const float *pm_in, *ps_in, *pv_in, *tx_in;
 };
 
 // The walk leaves a request to the tail kernel (an intermediate mode, never
@@ -702,10 +773,15 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
 // and writes its outcome.  No workgroup waits for another.  Workgroup
 // s nt + t takes row tail_from + t of the s-th request of the batch with
 // tail_flag set (nt = gamma + 2 - tail_from).
+// After the position passes (tail_din > 0) the requests are those the last
+// pass reduced rows for, and each workgroup first decides that pass's
+// positions from its segment statistics, as the next pass would (workgroup
+// t = 0 writes the outcome); a request that stops there reads no more rows.
 __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void verify_tail_kernel(
     WalkParams p) {
     static_assert(kTailFrom >= 2, "the walk decides row 1");
     __shared__ WalkMergeLds s_mg;
+    __shared__ int s_go;
     __shared__ uint64_t s_ball[(kTailMaxBatch + 63) / 64];
     // every request's length, row offset, temperature and draft at this
     // workgroup's position, loaded with the flags (one round trip)
@@ -720,7 +796,7 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         const int bq = c * 64 + lane;
         int fl = 0;
         if (bq < p.B) {
-            fl = p.tail_flag[bq];
+            fl = p.tail_din ? p.act_in[bq] : p.tail_flag[bq];
             s_rq_ell[bq] = p.ell[bq];
             s_rq_off[bq] = p.off[bq];
             s_rq_T[bq] = p.temperature[bq];
@@ -746,11 +822,67 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
     b = __builtin_amdgcn_readfirstlane(b);
     if (b < 0) return;
-    const int L = __builtin_amdgcn_readfirstlane(s_rq_ell[b]);  // checked by the walk
-    if (j > L + 1) return;
+    const int L = __builtin_amdgcn_readfirstlane(s_rq_ell[b]);  // checked by the walk or the first pass
     const float T = uniform_f(s_rq_T[b]);
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
+    if (p.tail_din) {  // uniform
+        if (j > L + 1 && t > 0) return;
+        if (wave == 0) {
+            // the last pass's segment statistics, 64 / din lanes a row slot
+            // (neutral where a lane holds none), merged within each group
+            const int din = p.tail_din, lps = 64 / din;
+            const int hq = min(lane / lps, din - 1), c = min(lane % lps, p.nseg_in - 1);
+            const size_t o_in = hq * p.row_stride + size_t(b) * p.seg_stride + c;
+            float mm = p.pm_in[o_in], s2 = p.ps_in[o_in], v2 = p.pv_in[o_in];
+            int i2 = p.pi_in[o_in];
+            float tx2[kPassRows], qk[kPassRows];
+            int xk[kPassRows];
+#pragma unroll
+            for (int u = 0; u < kPassRows; ++u) {
+                const int k = min(max(p.tail_from - din + u, 1), p.gamma);  // position decided from slot u (clamped)
+                tx2[u] = p.tx_in[size_t(min(u, din - 1)) * p.B + b];
+                xk[u] = p.x[size_t(b) * p.gamma + k - 1];
+                qk[u] = p.qx[size_t(b) * p.gamma + k - 1];
+            }
+            if (!((lane / lps) < din && (lane % lps) < p.nseg_in)) {
+                mm = kNegInf;
+                s2 = 0.f;
+                v2 = kNegInf;
+                i2 = 0x7fffffff;
+            }
+            auto step = [&](auto st) {
+                constexpr int S = decltype(st)::value;
+                const float m_o = bfly<S>(mm), s_o = bfly<S>(s2), v_o = bfly<S>(v2);
+                const int i_o = bfly<S>(i2);
+                lse_merge(mm, s2, m_o, s_o);
+                argmax_merge(v2, i2, v_o, i_o);
+            };
+            bfly_steps<0, 5>(step);
+            if (din == 1) step(std::integral_constant<int, 5>{});
+            float lse2[kPassRows];
+            int amax[kPassRows];
+#pragma unroll
+            for (int u = 0; u < kPassRows; ++u) {
+                const float mu = __shfl(mm, lps * min(u, din - 1)), su = __shfl(s2, lps * min(u, din - 1));
+                lse2[u] = (mu == kNegInf) ? kNegInf : mu + fast_log2(su);
+                amax[u] = min(max(__shfl(i2, lps * min(u, din - 1)), 0), p.V - 1);
+            }
+            int go_on = 0;
+            if (lane == 0) {
+                go_on = 1;
+                for (int u = 0; u < din; ++u) {
+                    const int k = p.tail_from - din + u;
+                    if (!go_on || k > L + 1) break;
+                    go_on = pass_decide(p, b, L, k, sampled, lse2[u], amax[u], tx2[u], xk[u], qk[u], t == 0);
+                }
+                s_go = go_on;
+            }
+        }
+        __syncthreads();
+        if (!__builtin_amdgcn_readfirstlane(s_go)) return;
+    }
+    if (j > L + 1) return;
     const int offb = __builtin_amdgcn_readfirstlane(s_rq_off[b]);
     float txs = kNegInf;
     if (sampled && j <= L) {
@@ -847,8 +979,20 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
 // A batch whose rows at one position take at most kPairAllBytes pairs from
 // the first position on: a launch costs about 7 us, about 45 MB of reads,
 // against at most B V 4 bytes read for nothing a pair.
-constexpr int kPassRows = 2;  // row slots a pass can hold
 constexpr int kSinglePasses = 3;
+// The position passes hand a block's last rows, at most kPassTailRows of
+// them, to the tail kernel when that saves at least kPassTailLaunches
+// launches (the last, decide-only pass included) and the rows it may read
+// are few (at most kPassTailReads, about one a CU) and cheap: small rows
+// (at most kPassTailSmallV entries), or rows late in the block, after at
+// least kPassTailAfter passes, where few requests are still testing.  A
+// launch costs about 4-5 us even with nothing to read; the tail kernel about
+// 7 us, plus one row's time at a CU's read rate for the requests it reads.
+constexpr int kPassTailRows = 4;
+constexpr int kPassTailLaunches = 3;
+constexpr int kPassTailReads = 256;
+constexpr int kPassTailSmallV = 65536;
+constexpr int kPassTailAfter = 3;
 constexpr size_t kPairAllBytes = size_t(64) << 20;
 // segments of a row in the first position pass and in the later ones
 // (measured at the headline size: 8 first-pass segments take 1 us less than
@@ -889,62 +1033,8 @@ struct PassParams {
     const float *lse_q;
     int32_t *n_accept_out, *tokens_out;
     float *diag_out;
+    int32_t *tail_cnt;  // non-null: the first pass zeroes each request's count for the tail kernel
 };
-
-// Position k = j - 1 of request b, from its merged row statistics: the accept
-// test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
-// request takes the same decision; only `writer` stores it.  Returns whether
-// the request goes on to position j.
-// xk, qk: x_k and q_k(x_k) (any value when k > ell).
-__device__ bool pass_decide(const PassParams &p, int b, int L, int k, bool sampled, float lse2, int amax, float tx2,
-                            int xk, float qk, bool writer) {
-    int32_t *tok = p.tokens_out + size_t(b) * (p.gamma + 1);
-    bool bonus = false;
-    if (k <= L) {
-        bool acc;
-        float pk, ratio;
-        if (sampled) {
-            pk = fast_exp2(tx2 - lse2);
-            const float u = uniform01(scalar_word(kStreamAccept, k, uint32_t(b), p.round32, p.key0, p.key1));
-            acc = u * qk < pk;
-            ratio = qk > 0.f ? fminf(1.f, pk / qk) : 1.f;
-        } else {
-            acc = (xk == amax);
-            pk = acc ? 1.f : 0.f;
-            ratio = pk;
-        }
-        if (writer && p.diag_out) {
-            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 0] = pk;
-            p.diag_out[(size_t(b) * (p.gamma + 1) + (k - 1)) * 2 + 1] = ratio;
-        }
-        if (acc) {
-            if (writer) tok[k - 1] = xk;
-            return true;
-        }
-        if (writer) p.n_accept_out[b] = k - 1;
-    } else {
-        if (writer) p.n_accept_out[b] = L;
-        bonus = true;
-    }
-    if (!writer) return false;
-    p.jpos[b] = k;
-    if (!sampled) {
-        tok[k - 1] = amax;
-        p.mode[b] = kModeDone;
-        return false;
-    }
-    p.fin_lse2[b] = lse2;
-    if (bonus) {
-        p.mode[b] = kModeBonus;
-    } else {
-        p.mode[b] = kModeResidual;
-        // what the residual draw needs to rebuild q_k
-        p.prev[b] = p.erow_mode ? b * p.gamma + k - 1
-                                : min(max(k == 1 ? p.anchor[b] : p.x[size_t(b) * p.gamma + k - 2], 0), p.V - 1);
-        p.lse2q[b] = p.lse_q[size_t(b) * p.gamma + k - 1] * kLog2e;
-    }
-    return false;
-}
 
 // Pass p, one wave per (request, row slot q < DOUT, vocabulary segment),
 // four requests to a workgroup.  First the request's DIN previous positions are
@@ -992,6 +1082,7 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
                     p.off[b] = offb;
                     p.mode[b] = mode;
                     p.req_flags[b] = f;
+                    if (p.tail_cnt) p.tail_cnt[b] = 0;
                     if (b == p.B - 1)
                         p.off[p.B] = p.row_offsets ? p.row_offsets[p.B] : o_cmp + 1 + min(max(L, 0), p.gamma);
                 }
@@ -1594,45 +1685,50 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     }
     const bool vec_t = (reinterpret_cast<uintptr_t>(a.target) % 16 == 0) && (a.V % 4 == 0);
     const bool vec_u = (reinterpret_cast<uintptr_t>(a.U) % 16 == 0) && (a.V % 4 == 0);
+    // the walk's parameters; the tail kernel takes them too
+    auto walk_params = [&]() {
+        WalkParams w_{};
+        w_.target = a.target;
+        w_.x = a.x;
+        w_.ell = a.ell;
+        w_.qx = a.qx;
+        w_.temperature = a.temperature;
+        w_.B = a.B;
+        w_.gamma = a.gamma;
+        w_.V = a.V;
+        w_.vec = vec_t;
+        w_.key0 = a.key0;
+        w_.key1 = a.key1;
+        w_.round32 = a.round32;
+        w_.off = w.off;
+        w_.prep = prep_in_kernel ? 1 : 0;
+        w_.n_target_rows = a.n_target_rows;
+        w_.row_offsets = a.row_offsets;
+        w_.req_flags = w.req_flags;
+        w_.resid_out = a.resid_out;
+        w_.mode = w.mode;
+        w_.jpos = w.jpos;
+        w_.prev = w.prev;
+        w_.fin_lse2 = w.fin_lse2;
+        w_.lse2q = w.lse2q;
+        w_.erow_mode = a.erow_mode;
+        w_.anchor = a.anchor;
+        w_.lse_q = a.lse_q;
+        w_.n_accept_out = a.n_accept_out;
+        w_.tokens_out = a.tokens_out;
+        w_.diag_out = a.diag_out;
+        w_.tail_flag = w.tail_flag;
+        w_.tail_cnt = w.tail_cnt;
+        w_.tail_amax = w.tail_amax;
+        w_.tail_lse2 = w.tail_lse2;
+        w_.tail_tx = w.tail_tx;
+        return w_;
+    };
     if (pl.walk) {
-        WalkParams wp{};
-        wp.target = a.target;
-        wp.x = a.x;
-        wp.ell = a.ell;
-        wp.qx = a.qx;
-        wp.temperature = a.temperature;
-        wp.B = a.B;
-        wp.gamma = a.gamma;
-        wp.V = a.V;
-        wp.vec = vec_t;
-        wp.key0 = a.key0;
-        wp.key1 = a.key1;
-        wp.round32 = a.round32;
-        wp.off = w.off;
-        wp.prep = prep_in_kernel ? 1 : 0;
-        wp.n_target_rows = a.n_target_rows;
-        wp.row_offsets = a.row_offsets;
-        wp.req_flags = w.req_flags;
-        wp.resid_out = a.resid_out;
-        wp.mode = w.mode;
-        wp.jpos = w.jpos;
-        wp.prev = w.prev;
-        wp.fin_lse2 = w.fin_lse2;
-        wp.lse2q = w.lse2q;
-        wp.erow_mode = a.erow_mode;
-        wp.anchor = a.anchor;
-        wp.lse_q = a.lse_q;
-        wp.n_accept_out = a.n_accept_out;
-        wp.tokens_out = a.tokens_out;
-        wp.diag_out = a.diag_out;
+        WalkParams wp = walk_params();
         // the tail kernel streams rows the vector way only, and finds its
         // requests among at most kTailMaxBatch
         wp.tail_from = (vec_t && a.B <= kTailMaxBatch) ? pl.tail_from : 0;
-        wp.tail_flag = w.tail_flag;
-        wp.tail_cnt = w.tail_cnt;
-        wp.tail_amax = w.tail_amax;
-        wp.tail_lse2 = w.tail_lse2;
-        wp.tail_tx = w.tail_tx;
         launch_kernel("verify_walk", verify_walk_kernel, dim3(a.B), dim3(kWalkThreads), s, wp);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (wp.tail_from) {
@@ -1643,11 +1739,27 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
     } else {
         PassRows sched[DSPARK_MAX_GAMMA + 2];  // gamma is checked at the boundary
         const int single = size_t(a.B) * a.V * sizeof(float) <= kPairAllBytes ? 0 : kSinglePasses;
-        const int npass = pass_schedule(a.gamma, single, sched);
+        int npass = pass_schedule(a.gamma, single, sched);
+        // the block's last rows, after the first pass that qualifies, go to
+        // the tail kernel (rows streamed the vector way, requests found among
+        // at most kTailMaxBatch, each request's tail count zeroed by the
+        // first pass's input checks)
+        int tail_from = 0, tail_din = 0;
+        if (vec_t && prep_in_kernel && a.B <= kTailMaxBatch)
+            for (int i = 0; i < npass && sched[i].rows > 0; ++i) {
+                const int jn = sched[i].j0 + sched[i].rows, left = a.gamma + 2 - jn;
+                if (left >= 1 && left <= kPassTailRows && npass - (i + 1) >= kPassTailLaunches &&
+                    a.B * left <= kPassTailReads && (a.V <= kPassTailSmallV || i + 1 >= kPassTailAfter)) {
+                    npass = i + 1;
+                    tail_from = jn;
+                    tail_din = sched[i].rows;
+                    break;
+                }
+            }
+        const size_t rs = size_t(a.B) * pl.nseg_max;  // one row slot
+        const size_t half = rs * kPassRows;
         for (int pass = 1; pass <= npass; ++pass) {
             const int in = (pass - 1) & 1, out = pass & 1;  // double-buffer halves
-            const size_t rs = size_t(a.B) * pl.nseg_max;     // one row slot
-            const size_t half = rs * kPassRows;
             const PassRows cur = sched[pass - 1];
             const int din = pass > 1 ? sched[pass - 2].rows : 1;  // rows this pass decides
             const int dout = cur.rows > 0 ? cur.rows : 1;         // row slots of its grid
@@ -1701,6 +1813,7 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
             pp.n_accept_out = a.n_accept_out;
             pp.tokens_out = a.tokens_out;
             pp.diag_out = a.diag_out;
+            pp.tail_cnt = tail_from ? w.tail_cnt : nullptr;
             static const char *const names[] = {"verify_pass1", "verify_pass2", "verify_pass3", "verify_pass4",
                                                 "verify_pass5", "verify_pass6", "verify_pass7", "verify_pass8+"};
             const dim3 grid(size_t((a.B + 3) / 4) * nseg * dout);
@@ -1717,6 +1830,24 @@ hipError_t launch_typed(const VerifyArgs &a, const VerifyPlan &pl, const VerifyW
                 launch_kernel(name, (verify_pass_kernel<false, 2, 1>), grid, dim3(256), s, pp);
             else
                 launch_kernel(name, (verify_pass_kernel<false, 2, 2>), grid, dim3(256), s, pp);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (tail_from) {
+            const int last = npass & 1;  // the half the last pass wrote
+            WalkParams tp = walk_params();
+            tp.tail_from = tail_from;
+            tp.tail_din = tail_din;
+            tp.nseg_in = npass == 1 ? pl.nseg_first : pl.nseg;
+            tp.seg_stride = pl.nseg_max;
+            tp.row_stride = rs;
+            tp.act_in = w.act + size_t(last) * a.B;
+            tp.pm_in = w.seg_m + last * half;
+            tp.ps_in = w.seg_s + last * half;
+            tp.pv_in = w.seg_v + last * half;
+            tp.pi_in = w.seg_i + last * half;
+            tp.tx_in = w.seg_tx + size_t(last) * kPassRows * a.B;
+            const int nt = a.gamma + 2 - tail_from;
+            launch_kernel("verify_tail", verify_tail_kernel, dim3(size_t(a.B) * nt), dim3(kWalkThreads), s, tp);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
@@ -1850,8 +1981,8 @@ VerifyWork verify_carve(void *ws, int B, int gamma, int V, const VerifyPlan &p, 
         w.seg_i = c.take<int32_t>(ns);
         w.seg_tx = c.take<float>(size_t(2) * kPassRows * B);
     }
-    if (p.tail_from) {
-        const size_t nt = size_t(B) * (gamma + 2 - p.tail_from);
+    if (B <= kTailMaxBatch) {  // the tail kernel's, after the walk or the passes (rows 2 .. gamma + 1 at most)
+        const size_t nt = size_t(B) * std::max(gamma, 1);
         w.tail_flag = c.take<int32_t>(B);
         w.tail_cnt = c.take<int32_t>(B);
         w.tail_lse2 = c.take<float>(nt);

@@ -4,9 +4,12 @@ emits tokens distributed as the target; section 02: later positions are
 emitted only after every earlier draft was accepted).
 
 The tiny configuration's inputs (one request: U, the target rows, W1, W2,
-the anchor) are broadcast to 50,000 requests, each an independent sample
-(the request index is part of every Philox counter), over 20 rounds: 10^6
-rounds of the Markov-head draft and the verify.  At each position k the token
+the anchor) are broadcast to many requests, each an independent sample (the
+request index is part of every Philox counter), for 10^6 request-rounds of
+the Markov-head draft and the verify: 50,000 requests over 20 rounds (the
+walk alone), 256 over 3,907 (the walk, its rows from the fourth on in the
+tail kernel) and 64 over 15,625 (position passes that hand the last rows to
+the tail kernel).  At each position k the token
 emitted there, among the rounds that reach k, must follow p_k = softmax of
 target row k: a chi-square test with bins merged until every expected count
 is at least 5.  The same statement the oracle's own multi-position test pins
@@ -19,9 +22,7 @@ from roundkit import np_of
 
 pytestmark = pytest.mark.gpu
 
-N_REQ = 50_000
-ROUNDS = 20
-ALPHA = 1e-4  # per position; five positions
+ALPHA = 1e-4  # per position; five positions, three batch shapes
 
 
 def _merged_chi2(counts, probs, min_expected=5.0):
@@ -48,7 +49,8 @@ def _merged_chi2(counts, probs, min_expected=5.0):
     return float(((c - e) ** 2 / e).sum()), len(c) - 1
 
 
-def test_emitted_tokens_follow_the_target_at_every_position():
+@pytest.mark.parametrize("N_REQ,ROUNDS", [(50_000, 20), (256, 3907), (64, 15_625)])
+def test_emitted_tokens_follow_the_target_at_every_position(N_REQ, ROUNDS):
     import torch
     from scipy.stats import chi2
 

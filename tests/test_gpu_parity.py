@@ -445,12 +445,18 @@ def test_walk_tail_matches_the_walk_alone():
     (321, 5, 4096, {"verify_walk"}),                 # one request more
     (256, 3, 4096, {"verify_walk"}),                 # a block too short for a tail
     (256, 5, 4099, {"verify_walk"}),                 # rows that take scalar loads
-    (191, 5, 4096, {"verify_pass1"}),                # below the walk: position passes
+    (191, 5, 4096, {"verify_pass1"}),                # below the walk: position passes (too many rows for the tail)
+    (40, 4, 4096, {"verify_pass1", "verify_tail"}),  # small rows: the passes hand the last four to the tail kernel
+    (40, 4, 4099, {"verify_pass1"}),                 # the same with rows that take scalar loads: passes only
+    (24, 1, 4096, {"verify_pass1"}),                 # one draft: both rows in the first pass
 ])
 def test_verify_launches_the_kernels_its_shape_calls_for(B, gamma, V, kernels):
     """Which verify kernels a call launches, read back from the library's
-    launch profiler: the walk from 192 requests on, its tail kernel up to 320
-    requests with blocks of at least 4 drafts and 16-byte aligned rows."""
+    launch profiler: the walk from 192 requests on, with the tail kernel up to
+    320 requests, blocks of at least 4 drafts and 16-byte aligned rows; below
+    192 the position passes, which hand the block's last rows to the tail
+    kernel when that saves launches and the rows it may read are few and
+    cheap."""
     rnd, ell, target = _custom_round(B, gamma, V, 32, "bf16", seed=B + gamma, greedy_every=5)
     _say(f"[launches] B={B} gamma={gamma} V={V}")
     dev = to_device(rnd)
