@@ -759,7 +759,7 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
 }
 
-// ------------------------------------------------------------------ walk tail
+// ------------------------------------------------------------------ a block's last rows (after the walk or the passes)
 
 // Rows tail_from .. ell + 1 of the requests the walk left at row tail_from,
 // a workgroup a row, all at once: a request's later rows are read whether or
