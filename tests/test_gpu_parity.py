@@ -372,10 +372,15 @@ def test_round_replays_from_a_graph_as_it_runs_eagerly(B, V):
             torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("B", [24, 600])  # input checks in the first pass / in a prep workgroup
-def test_row_offsets_given_equal_computed_and_bad_ell_flagged(B):
-    rnd, ell, target = _custom_round(B, 3, 500, 16, "bf16", seed=9)
-    _say(f"[offsets] B={B}")
+@pytest.mark.parametrize("B,gamma", [
+    (24, 3),   # input checks in the first pass
+    (40, 4),   # the same, the block's last rows in the tail kernel
+    (600, 3),  # input checks in a prep workgroup, then the walk
+    (256, 5),  # input checks in the walk, rows from the fourth on in the tail kernel
+])
+def test_row_offsets_given_equal_computed_and_bad_ell_flagged(B, gamma):
+    rnd, ell, target = _custom_round(B, gamma, 500, 16, "bf16", seed=9)
+    _say(f"[offsets] B={B} gamma={gamma}")
     dev = to_device(rnd)
     td = torch.from_numpy(target).cuda()
     d = gpu_draft(dev, 1, 1)
