@@ -34,17 +34,18 @@
 //                    read are few and cheap: it first decides the last pass's
 //                    positions itself.
 //   verify_pass      smaller batches, instead of the walk: one launch a
-//                    position for the first few positions, one
-//                    a pair of positions after them (from the first one on
-//                    for a small batch), and a last one that only decides; each runs over the requests still
-//                    testing: one wave per (request, row, vocabulary
-//                    segment) first decides the positions the previous
-//                    launch reduced, from the segment statistics it left
-//                    (the accept test u*q < p, or the bonus row), then, if
-//                    the request goes on, streams its segment of the row for
-//                    logsumexp(t / T) in base 2 and the lowest-index argmax.
-//                    A request stops at its first rejection, so rows past it
-//                    are never read (but the second row of a pair).
+//                    position for the first few positions, one a pair of
+//                    positions after them (from the first one on for a
+//                    small batch), and a last one that only decides.  Each
+//                    runs over the requests still testing: one wave per
+//                    (request, row, vocabulary segment) first decides the
+//                    positions the previous launch reduced, from the
+//                    segment statistics it left (the accept test u*q < p,
+//                    or the bonus row), then, if the request goes on,
+//                    streams its segment of the row for logsumexp(t / T) in
+//                    base 2 and the lowest-index argmax.  A request stops at
+//                    its first rejection, so no row past it is read, except
+//                    the second row of a pair.
 //   verify_draw      level 1: every workgroup lists the drawing requests
 //                    (residual draws first, bonus draws last, in request
 //                    order); waves of 32 listed requests walk vocabulary
