@@ -76,9 +76,10 @@ def _logit_passes(phases, outcome, B, V, r):
     """The verify's logit passes against the HBM peak: algorithmic bytes over
     the event-timed average launch, the bytes counted from the outcomes of the
     same timed rounds (averages per round).  The walk reads rows 1 .. n + 1 of
-    every request (the first rejection's row or the bonus row), timed with the
-    tail kernel that reads a batch's last rows when it has one (the tail's
-    rows past a rejection are read but not counted); the draw reads the
+    every request (up to the first rejection's row, or the bonus row of a
+    greedy request; a sampled request's bonus row is the draw's alone), timed
+    with the tail kernel that reads a batch's last rows when it has one (the
+    tail's rows past a rejection are read but not counted); the draw reads the
     target and U_j rows of every residual draw, the target row of every
     bonus draw, and W2 once when any draw is a residual one."""
     row = V * 4
@@ -101,16 +102,17 @@ def _logit_passes(phases, outcome, B, V, r):
 
 def _outcome_counter(torch, temperature, ell):
     """Accumulates, on the device, each round's rows read by the walk
-    (sum of n + 1), residual draws (sampled, n < ell) and bonus draws
-    (sampled, n = ell); .mean() gives the averages per round."""
+    (sum of n + 1, less the sampled bonus rows, which only the draw reads),
+    residual draws (sampled, n < ell) and bonus draws (sampled, n = ell);
+    .mean() gives the averages per round."""
     sampled = temperature > 0
     acc = torch.zeros(3, dtype=torch.float64, device="cuda")
     cnt = [0]
 
     def add(n):
-        rows = (n + 1).sum()
         res = ((n < ell) & sampled).sum()
         bon = ((n == ell) & sampled).sum()
+        rows = (n + 1).sum() - bon
         acc.add_(torch.stack([rows, res, bon]).to(torch.float64))
         cnt[0] += 1
 

@@ -198,9 +198,10 @@ __global__ __launch_bounds__(1024) void verify_prep_kernel(PrepParams p) {
 }
 
 // Position k = j - 1 of request b, from its merged row statistics: the accept
-// test (k <= ell) or the bonus row (k = ell + 1).  Every workgroup of the
-// request takes the same decision; only `writer` stores it.  Returns whether
-// the request goes on to position j.
+// test (k <= ell) or the bonus row (k = ell + 1, greedy only).  A sampled
+// request that accepts x_ell has its bonus outcome written at once.  Every
+// workgroup of the request takes the same decision; only `writer` stores it.
+// Returns whether the request goes on to position j.
 // xk, qk: x_k and q_k(x_k) (any value when k > ell).  P: the position passes'
 // or the walk's parameters (the same output fields).
 template <class P>
@@ -227,9 +228,15 @@ __device__ bool pass_decide(const P &p, int b, int L, int k, bool sampled, float
         }
         if (acc) {
             if (writer) tok[k - 1] = xk;
-            return true;
+            // a sampled request goes on only while a draft is left to test:
+            // the draw takes its bonus token from row ell + 1 itself, and
+            // that row's statistics are never used
+            if (!sampled || k < L) return true;
+            bonus = true;
+            k = L + 1;
+            lse2 = 0.f;
         }
-        if (writer) p.n_accept_out[b] = k - 1;
+        if (writer) p.n_accept_out[b] = bonus ? L : k - 1;
     } else {
         if (writer) p.n_accept_out[b] = L;
         bonus = true;
@@ -661,6 +668,9 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     }
     const int offb = __builtin_amdgcn_readfirstlane(s_off);
     const int L = L_raw;  // in [0, gamma] once the checks passed
+    // the last row the request may need: a sampled request's bonus token is
+    // drawn from row ell + 1 by the draw, which uses none of its statistics
+    const int jl = sampled ? L : L + 1;
     const float sc = sampled ? kLog2e / T : 1.0f;
     auto row_of = [&](int j) { return p.target + size_t(offb + j - 1) * p.V; };
     // the thread's state for the current row: running base-2 logsumexp and
@@ -678,8 +688,9 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         }
     };
     // the walk's outcome, the same in every thread; no global store is made
-    // before the walk ends (the outputs go out after it)
-    int r_n = 0, r_j = 0, r_mode = kModeDone, r_tok = -1;
+    // before the walk ends (the outputs go out after it); a sampled request
+    // with no draft to test is a bonus draw without a row read
+    int r_n = 0, r_j = 1, r_mode = jl == 0 ? kModeBonus : kModeDone, r_tok = -1;
     float r_lse2 = 0.f;
     // Row j is complete in the threads' states: merge it over the workgroup
     // and decide position j.  Returns whether the walk goes on to row j + 1
@@ -698,6 +709,12 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
                 s_dr[j - 1] = ratio;
             }
             if (acc) {
+                if (j == jl) {  // sampled, every draft accepted: the bonus draw
+                    r_n = L;
+                    r_j = L + 1;
+                    r_mode = kModeBonus;
+                    return false;
+                }
                 if (j + 1 != p.tail_from) {
                     locate_x(j + 1);
                     return true;
@@ -710,8 +727,8 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
             r_n = j - 1;  // first rejection at j: the residual draw (sampled) or the target's argmax (greedy)
             r_mode = sampled ? kModeResidual : kModeDone;
         } else {
-            r_n = L;  // every draft accepted: the bonus token from row ell + 1
-            r_mode = sampled ? kModeBonus : kModeDone;
+            r_n = L;  // greedy, every draft accepted: the bonus token is row ell + 1's argmax
+            r_mode = kModeDone;
         }
         r_j = j;
         r_lse2 = lse2;
@@ -720,15 +737,15 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     };
     locate_x(1);
     if (!p.vec) {
-        for (int j = 1; j <= L + 1; ++j) {
+        for (int j = 1; j <= jl; ++j) {
             if (sampled)
                 walk_row_scalar<false>(row_of(j), p.V, sc, m, s, av, ai);
             else
                 walk_row_scalar<true>(row_of(j), p.V, sc, m, s, av, ai);
             if (!finish_row(j)) break;
         }
-    } else {
-        walk_stream_rows(p.target, offb, p.V, 1, L + 1, sampled, sc, m, s, av, ai, finish_row);
+    } else if (jl > 0) {
+        walk_stream_rows(p.target, offb, p.V, 1, jl, sampled, sc, m, s, av, ai, finish_row);
     }
     if (tid == 0) {
         // the outcome: accepted drafts, the first rejection's or the bonus
@@ -762,8 +779,9 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
 
 // ------------------------------------------------------------------ a block's last rows (after the walk or the passes)
 
-// Rows tail_from .. ell + 1 of the requests the walk left at row tail_from,
-// a workgroup a row, all at once: a request's later rows are read whether or
+// Rows tail_from .. ell + 1 (.. ell for a sampled request, whose bonus row
+// only the draw reads) of the requests the walk left at row tail_from, a
+// workgroup a row, all at once: a request's later rows are read whether or
 // not an earlier one rejects (the rows past its first rejection are reduced
 // and left unused), so the block's last rows take about one row's time
 // instead of one each, on CUs the walk has left idle.  A row is streamed and
@@ -827,8 +845,9 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
     const float T = uniform_f(s_rq_T[b]);
     const bool sampled = T > 0.f;
     const float sc = sampled ? kLog2e / T : 1.0f;
+    const int jl = sampled ? L : L + 1;  // the request's last row (as in the walk)
     if (p.tail_din) {  // uniform
-        if (j > L + 1 && t > 0) return;
+        if (j > jl && t > 0) return;
         if (wave == 0) {
             // the last pass's segment statistics, 64 / din lanes a row slot
             // (neutral where a lane holds none), merged within each group
@@ -883,7 +902,7 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         __syncthreads();
         if (!__builtin_amdgcn_readfirstlane(s_go)) return;
     }
-    if (j > L + 1) return;
+    if (j > jl) return;
     const int offb = __builtin_amdgcn_readfirstlane(s_rq_off[b]);
     float txs = kNegInf;
     if (sampled && j <= L) {
@@ -924,16 +943,16 @@ __global__ __launch_bounds__(kWalkThreads) __attribute__((amdgpu_waves_per_eu(1,
         p.tail_amax[o] = amax;
         p.tail_tx[o] = txs;
         last = __hip_atomic_fetch_add(p.tail_cnt + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-               L + 1 - p.tail_from;  // the request's other rows (L + 2 - tail_from in all) are in
+               jl - p.tail_from;  // the request's other rows (jl + 1 - tail_from in all) are in
     }
     if (!__builtin_amdgcn_readfirstlane(last)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // every position's test at once, then the first that stops (a
-    // rejection, else the bonus row ell + 1)
+    // rejection, else the bonus row ell + 1, read for a greedy request only)
     float l2 = 0.f, pk = 0.f, ratio = 0.f;
     int am = 0;
     bool acc = false;
-    if (row) {
+    if (row && jj <= jl) {
         const size_t o = size_t(b) * nt + lane;
         l2 = __hip_atomic_load(p.tail_lse2 + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         am = __hip_atomic_load(p.tail_amax + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1162,8 +1181,19 @@ __global__ __launch_bounds__(256) void verify_pass_kernel(PassParams p) {
             return;
         }
     }
-    if (j > L + 1) {  // no row at this slot (slot 0 always has one once the request goes on)
-        if (writer && lane == 0) p.act_out[b] = 0;
+    // the last row the request may need: a sampled request's bonus token is
+    // drawn from row ell + 1 by the draw, which uses none of its statistics
+    const int jl = sampled ? L : L + 1;
+    if (j > jl) {  // no row at this slot (slot 0 has one once the request goes on, but in the first pass)
+        if (writer && lane == 0) {
+            p.act_out[b] = 0;
+            if (FIRST) {  // sampled with no draft to test: the bonus draw, no row read
+                p.n_accept_out[b] = 0;
+                p.jpos[b] = 1;
+                p.mode[b] = kModeBonus;
+                p.fin_lse2[b] = 0.f;
+            }
+        }
         return;
     }
     const float *trow = p.target + size_t(offb + j - 1) * p.V;

@@ -249,6 +249,44 @@ def test_edge_shapes_parity(B, gamma, V, r, wdtype, greedy):
     assert cv.eligible.sum() >= 0.5 * B
 
 
+@pytest.mark.parametrize("B,gamma,V,greedy", [
+    (256, 5, 4096, 4),   # walked, rows from the fourth on in the tail kernel
+    (600, 3, 4096, 5),   # walked, input checks in a workgroup of their own
+    (40, 4, 4096, 3),    # position passes, the last rows in the tail kernel
+    (24, 3, 4099, 0),    # position passes, rows not 16-byte aligned
+])
+def test_drafts_from_the_target_distribution_end_on_the_bonus_token(B, gamma, V, greedy):
+    """Zero bias factors make q_k the target's p_k ("DeepSeek DSpark
+    explained", section 05: p/q = 1), so every draft passes and every request
+    ends with the bonus token from row ell + 1: drawn from p for a sampled
+    request (a row the draw reads but the verify passes never need), the row's
+    argmax for a greedy one.  Verify lengths are ragged, zero included."""
+    rnd, ell, _ = _custom_round(B, gamma, V, 32, "bf16", seed=B + V, greedy_every=greedy)
+    rnd = dataclasses.replace(rnd, W1_bits=np.zeros_like(rnd.W1_bits), W2_bits=np.zeros_like(rnd.W2_bits),
+                              W1=np.zeros_like(rnd.W1), W2=np.zeros_like(rnd.W2))
+    rows = []
+    for i in range(B):
+        rows.extend(rnd.U[i, k] for k in range(int(ell[i])))
+        rows.append(rnd.target_row(i, int(ell[i]) + 1))
+    target = np.ascontiguousarray(np.stack(rows), dtype=np.float32)
+    _say(f"[bonus] B={B} gamma={gamma} V={V} greedy_every={greedy} ell={ell.tolist()[:8]}")
+    dev = to_device(rnd)
+    d = gpu_draft(dev, 11, 2)
+    v = gpu_verify(dev, torch.from_numpy(target).cuda(), torch.from_numpy(ell).cuda(), d, 11, 2)
+    assert ds.dspark_verify_check(v["workspace"]) == 0
+    gd = {k: np_of(t) for k, t in d.items() if k != "workspace"}
+    gv = {k: np_of(t) for k, t in v.items() if k != "workspace"}
+    od, ov = oracle_round(rnd, target, ell, 11, 2)
+    np.testing.assert_array_equal(ov["n"], ell)  # the oracle accepts every draft
+    cd = compare_draft(gd, od)
+    cv = compare_verify(gv, od, ov, rnd.temperature, ell)
+    _say(f"[bonus] draft {cd.report()} | verify {cv.report()}")
+    assert cv.eligible.sum() >= 0.9 * B
+    # an fp32 u q < p can only fail for a uniform within rounding of 1
+    assert (gv["n"] == ell).sum() >= B - 1
+    assert np.all(gv["resid"][gv["n"] == ell] == -1.0)
+
+
 def test_neg_inf_logits_parity():
     rnd, ell, target = _custom_round(40, 4, 777, 16, "bf16", seed=5, neg_inf_frac=0.3)
     dev = to_device(rnd)
