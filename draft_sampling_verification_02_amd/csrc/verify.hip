@@ -22,8 +22,9 @@
 //                    request streams its rows in position order for
 //                    logsumexp(t / T) in base 2 and the lowest-index argmax,
 //                    decides each position right after its row (the accept
-//                    test u*q < p, or the bonus row) and stops at the first
-//                    rejection, so no row past it is used.
+//                    test u*q < p, or a greedy request's bonus row) and stops
+//                    at the first rejection, so no row past it is used.  A
+//                    sampled request's bonus row is read by the draw only.
 //   verify_tail      after the walk, for walked batches of at most 320
 //                    requests and blocks of at least 4 drafts: the rows from
 //                    the fourth on of the requests still accepting after row
@@ -266,8 +267,10 @@ __device__ bool pass_decide(const P &p, int b, int L, int k, bool sampled, float
 // One workgroup walks one request's target rows in position order: it streams
 // row j for the base-2 logsumexp of t / T (and the lowest-index argmax of a
 // greedy row), decides position j from it (the accept test for j <= ell, the
-// bonus row for j = ell + 1) and goes on to row j + 1 only after an accepted
-// draft, so no row past the first rejection is read.  The decision needs the
+// bonus row for j = ell + 1, which only a greedy request reads: a sampled
+// one ends at x_ell, its bonus token drawn from the row by the draw) and goes
+// on to row j + 1 only after an accepted draft, so no row past the first
+// rejection is read.  The decision needs the
 // whole row, and the whole row is this workgroup's: its waves meet once a row
 // in LDS, and every wave merges the same statistics and takes the same
 // decision, so no other workgroup and no fence is involved.  A batch fills
