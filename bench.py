@@ -106,7 +106,7 @@ def _outcome_counter(torch, temperature, ell):
     residual draws (sampled, n < ell) and bonus draws (sampled, n = ell);
     .mean() gives the averages per round."""
     sampled = temperature > 0
-    acc = torch.zeros(3, dtype=torch.float64, device="cuda")
+    acc = torch.zeros(3, dtype=torch.float64, device=temperature.device)
     cnt = [0]
 
     def add(n):
